@@ -1,0 +1,242 @@
+"""Seeded synthetic inputs for the routed 2-bit MoE layer (inputs only).
+
+Nothing here computes any part of the layer: this module draws Gaussian
+tensors with a counter-based generator and quantizes routed-expert weights
+into canonical 84-byte super-blocks.  The CPU oracle and the GPU library both
+consume what it returns, so neither depends on the other.
+
+Workloads (the five layer shapes the method is measured on):
+
+* ``tiny``     T=16,   H=256,  E=8,   I=128,  k=2, fp32 x N(0,1), fp32 router N(0,0.05)
+* ``decode1``  T=1,    H=4096, E=256, I=2048, k=8, bf16 x N(0,1), bf16 router N(0,0.02)
+* ``decode16`` T=16,   as decode1, x_t = 0.5*x_s + sqrt(0.75)*z_t (shared component)
+* ``prefill``  T=2048, as decode1
+* ``skewed``   T=8192, as decode1 plus a Zipf(1.1) router bias and a bf16
+  shared expert with intermediate 2048
+
+Routed expert weights are N(0,0.02) before quantization in every workload.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+_lib = None
+
+DEFAULT_SEED = 20261203
+BLOCK_BYTES = 84
+BLOCK_WEIGHTS = 256
+
+# stream kinds
+K_X, K_XSHARED, K_ROUTER, K_BIASPERM, K_GATE, K_UP, K_DOWN, K_SHG, K_SHU, K_SHD = range(1, 11)
+
+
+def build_lib(force: bool = False) -> str:
+    """Compile libsynth.so (plain C, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        cmd = ["gcc", "-O3", "-march=x86-64-v2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+               _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build_lib()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        L.synth_philox4x32_10.argtypes = [P, P, P]
+        L.synth_normal_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_double, ctypes.c_int64, P]
+        L.synth_f32_to_bf16.argtypes = [P, ctypes.c_int64, P]
+        L.synth_quantize.argtypes = [P, ctypes.c_int64, P]
+        L.synth_q2k_matrices.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_double, P]
+        L.synth_u32.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, P]
+        L.synth_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    c = np.asarray(counter, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().synth_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def stream_id(wl_id: int, kind: int, index: int = 0) -> int:
+    assert 0 <= index < (1 << 20) and 0 <= kind < 256 and 0 <= wl_id < 16
+    return (wl_id << 28) | (kind << 20) | index
+
+
+def normal_f32(seed: int, stream: int, sigma: float, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    lib().synth_normal_f32(seed, stream, sigma, n, _ptr(out))
+    return out.reshape(shape)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().synth_f32_to_bf16(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32 values."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_blocks(w: np.ndarray) -> np.ndarray:
+    """RTN-quantize fp32 weights (size multiple of 256, row-major) to canonical blocks."""
+    w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    assert w.size % BLOCK_WEIGHTS == 0
+    nb = w.size // BLOCK_WEIGHTS
+    out = np.empty(nb * BLOCK_BYTES, dtype=np.uint8)
+    lib().synth_quantize(_ptr(w), nb, _ptr(out))
+    return out
+
+
+def q2k_matrices(seed: int, stream_base: int, n_mats: int, rows: int, cols: int, sigma: float) -> np.ndarray:
+    """n_mats matrices [rows, cols] of N(0,sigma) weights quantized to canonical blocks.
+
+    Returns uint8 [n_mats, rows*cols/256*84]; matrix e is stream stream_base+e.
+    """
+    assert (rows * cols) % BLOCK_WEIGHTS == 0
+    per = rows * cols // BLOCK_WEIGHTS * BLOCK_BYTES
+    out = np.empty((n_mats, per), dtype=np.uint8)
+    lib().synth_q2k_matrices(seed, stream_base, n_mats, rows, cols, sigma, _ptr(out))
+    return out
+
+
+def u32(seed: int, stream: int, n: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint32)
+    lib().synth_u32(seed, stream, n, _ptr(out))
+    return out
+
+
+def num_threads() -> int:
+    return int(lib().synth_num_threads())
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    wl_id: int
+    T: int
+    H: int
+    E: int
+    I: int
+    k: int
+    Is: int = 0
+    x_dtype: str = "bf16"          # "f32" or "bf16"
+    router_dtype: str = "bf16"
+    router_sigma: float = 0.02
+    w_sigma: float = 0.02
+    x_shared_rho: float = 0.0      # x_t = rho*x_s + sqrt(1-rho^2)*z_t
+    zipf_s: float = 0.0            # router bias from a Zipf(s) law, 0 = no bias
+    zipf_scale: float = 0.75
+    description: str = ""
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 0, T=16, H=256, E=8, I=128, k=2, x_dtype="f32", router_dtype="f32",
+                     router_sigma=0.05, description="tiny layer, fp32 activations and router"),
+    "decode1": Workload("decode1", 1, T=1, H=4096, E=256, I=2048, k=8,
+                        description="decode, one token"),
+    "decode16": Workload("decode16", 2, T=16, H=4096, E=256, I=2048, k=8, x_shared_rho=0.5,
+                         description="decode micro-batch of 16 correlated tokens"),
+    "prefill": Workload("prefill", 3, T=2048, H=4096, E=256, I=2048, k=8,
+                        description="prefill chunk of 2048 tokens"),
+    "skewed": Workload("skewed", 4, T=8192, H=4096, E=256, I=2048, k=8, Is=2048, zipf_s=1.1,
+                       description="long prefill, Zipf-skewed routing, bf16 shared expert"),
+}
+
+
+@dataclass
+class LayerInputs:
+    wl: Workload
+    seed: int
+    T: int
+    x: np.ndarray              # fp32 [T,H] (tiny) or bf16 bits uint16 [T,H]
+    router_w: np.ndarray       # fp32 [E,H] or bf16 bits [E,H]
+    router_bias: np.ndarray | None  # fp32 [E]
+    gate: np.ndarray           # uint8 [E, I*H/256*84] canonical blocks, W[I,H] row-major
+    up: np.ndarray             # uint8 [E, I*H/256*84]
+    down: np.ndarray           # uint8 [E, H*I/256*84], W[H,I] row-major
+    sh_gate: np.ndarray | None = None  # bf16 bits [Is,H]
+    sh_up: np.ndarray | None = None    # bf16 bits [Is,H]
+    sh_down: np.ndarray | None = None  # bf16 bits [H,Is]
+    extra: dict = field(default_factory=dict)
+
+    def x_f32(self) -> np.ndarray:
+        return self.x if self.wl.x_dtype == "f32" else bf16_bits_to_f32(self.x)
+
+    def router_f32(self) -> np.ndarray:
+        return self.router_w if self.wl.router_dtype == "f32" else bf16_bits_to_f32(self.router_w)
+
+
+def make_x(wl: Workload, seed: int, T: int, batch: int = 0) -> np.ndarray:
+    """Activations for batch number `batch` (fresh tokens per batch)."""
+    z = normal_f32(seed, stream_id(wl.wl_id, K_X, batch), 1.0, (T, wl.H))
+    if wl.x_shared_rho:
+        xs = normal_f32(seed, stream_id(wl.wl_id, K_XSHARED, batch), 1.0, (1, wl.H))
+        rho = wl.x_shared_rho
+        z = (rho * xs.astype(np.float64) + math.sqrt(1.0 - rho * rho) * z.astype(np.float64)).astype(np.float32)
+    return z if wl.x_dtype == "f32" else f32_to_bf16_bits(z)
+
+
+def zipf_bias(wl: Workload, seed: int) -> np.ndarray:
+    """b_e = scale*(ln p_r(e) - mean ln p), p_r ~ r^-s, ranks r assigned by a seeded permutation."""
+    E = wl.E
+    r = u32(seed, stream_id(wl.wl_id, K_BIASPERM), E)
+    perm = list(range(E))
+    for i in range(E - 1, 0, -1):  # Fisher-Yates driven by the stream
+        j = int(r[i]) % (i + 1)
+        perm[i], perm[j] = perm[j], perm[i]
+    ranks = np.array(perm, dtype=np.float64) + 1.0   # expert e has rank perm[e]+1
+    lnp = -wl.zipf_s * np.log(ranks)
+    return (wl.zipf_scale * (lnp - lnp.mean())).astype(np.float32)
+
+
+def make_layer(wl: Workload | str, seed: int = DEFAULT_SEED, T: int | None = None,
+               experts: bool = True) -> LayerInputs:
+    """All inputs of one layer.  `T` overrides the workload's token count."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    T = wl.T if T is None else T
+    E, H, I = wl.E, wl.H, wl.I
+    x = make_x(wl, seed, T)
+    rw = normal_f32(seed, stream_id(wl.wl_id, K_ROUTER), wl.router_sigma, (E, H))
+    if wl.router_dtype == "bf16":
+        rw = f32_to_bf16_bits(rw)
+    bias = zipf_bias(wl, seed) if wl.zipf_s else None
+    if experts:
+        gate = q2k_matrices(seed, stream_id(wl.wl_id, K_GATE), E, I, H, wl.w_sigma)
+        up = q2k_matrices(seed, stream_id(wl.wl_id, K_UP), E, I, H, wl.w_sigma)
+        down = q2k_matrices(seed, stream_id(wl.wl_id, K_DOWN), E, H, I, wl.w_sigma)
+    else:
+        gate = up = down = None
+    shg = shu = shd = None
+    if wl.Is:
+        shg = f32_to_bf16_bits(normal_f32(seed, stream_id(wl.wl_id, K_SHG), wl.w_sigma, (wl.Is, H)))
+        shu = f32_to_bf16_bits(normal_f32(seed, stream_id(wl.wl_id, K_SHU), wl.w_sigma, (wl.Is, H)))
+        shd = f32_to_bf16_bits(normal_f32(seed, stream_id(wl.wl_id, K_SHD), wl.w_sigma, (H, wl.Is)))
+    return LayerInputs(wl, seed, T, x, rw, bias, gate, up, down, shg, shu, shd)
