@@ -1,0 +1,183 @@
+/*
+ * ds4moe -- routed 2-bit mixture-of-experts FFN layer for AMD MI355X (gfx950).
+ *
+ * One layer of a DeepSeek-V4-Flash-style model whose routed experts are stored
+ * in asymmetric 2-bit super-blocks while the router and the shared expert stay
+ * at higher precision (ds4 README, "Models" section, as translated on
+ * molayo1419.me: only the routed MoE experts are quantized; routing, shared
+ * experts and projections are left alone).  Per token t the layer computes
+ *
+ *   l[t,e] = fp32( sum_h x[t,h] * Wr[e,h] + b[e] )      (fp64 accumulation)
+ *   s      = sqrt(softplus(l)), softplus evaluated in the stable form
+ *            max(l,0) + log1p(exp(-|l|)), log1p(u) by the series
+ *            u - u^2/2 + u^3/3 - u^4/4 when u < 1/32 (opensource-hub.com
+ *            "antirez/ds4" page, FAQ #1, router numeric test)
+ *   top-k experts by logit, ties to the lower index; w_j = s_j / sum_i s_i
+ *   h_j    = silu(Wg_e x_t) * (Wu_e x_t)                (dequant-fused)
+ *   y[t]   = sum_j w_j * (Wd_e h_j)  [+ shared expert FFN(x_t), bf16 weights]
+ *
+ * CONVENTIONS (all entry points)
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
+ *     every buffer; the library never allocates, frees or keeps a pointer
+ *     after a call returns.  Scratch memory comes from the caller's workspace,
+ *     sized by ds4moe_workspace_bytes().
+ *   - Calls only enqueue work on `stream` (a hipStream_t passed as void*,
+ *     NULL = the null stream) and return; there is no host synchronisation.
+ *   - The small descriptor structs are HOST memory, read during the call only.
+ *   - Every argument is validated on the host before anything is launched; a
+ *     non-zero ds4moe_status is returned and nothing is enqueued.  A HIP launch
+ *     failure returns DS4MOE_ERR_HIP.  No exceptions cross this boundary.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Same inputs, same stream order => bitwise identical outputs (no
+ *     floating-point atomics anywhere).
+ *   - Calls that share a workspace must not overlap.
+ */
+#ifndef DS4MOE_H
+#define DS4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DS4MOE_OK = 0,
+  DS4MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  DS4MOE_ERR_SHAPE = 2,       /* a size is out of the supported range */
+  DS4MOE_ERR_DTYPE = 3,       /* unknown dtype code */
+  DS4MOE_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  DS4MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  DS4MOE_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  DS4MOE_ERR_HIP = 7          /* a HIP launch or runtime call failed */
+} ds4moe_status;
+
+typedef enum { DS4MOE_F32 = 0, DS4MOE_BF16 = 1 } ds4moe_dtype;
+
+typedef enum { DS4MOE_MODE_ROUTE = 0, DS4MOE_MODE_DECODE = 1, DS4MOE_MODE_PREFILL = 2 } ds4moe_mode;
+
+/* Layer shape (host struct).
+ *   hidden        H: multiple of 256, 256..65536
+ *   inter         I: routed expert intermediate; multiple of 16 and either a
+ *                 multiple of 256 or a divisor of 256
+ *   n_experts     E: top_k <= E <= 256
+ *   top_k         k: 1..16
+ *   shared_inter  Is: 0 (no shared expert) or a multiple of 32
+ *   x_dtype       dtype of x: DS4MOE_F32 or DS4MOE_BF16
+ *   router_dtype  dtype of Wr: DS4MOE_F32 or DS4MOE_BF16 */
+typedef struct {
+  int32_t hidden;
+  int32_t inter;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t shared_inter;
+  int32_t x_dtype;
+  int32_t router_dtype;
+} ds4moe_dims;
+
+/* Weights (host struct of device pointers).
+ *   router_w   [E,H] row-major, router_dtype
+ *   router_bias [E] fp32, or NULL: added to the logit, so it moves both the
+ *              selection and the weights
+ *   gate, up   E packed matrices W[I,H] each (ds4moe_pack_q2k layout),
+ *              expert e at byte offset e * ds4moe_packed_bytes(I, H)
+ *   down       E packed matrices W[H,I], expert e at e * ds4moe_packed_bytes(H, I)
+ *   sh_gate, sh_up  [Is,H] bf16 row-major; sh_down [H,Is] bf16; all NULL
+ *              when shared_inter == 0.  The shared expert is computed with
+ *              fp16 operands: its weights must lie inside the binary16 range. */
+typedef struct {
+  const void *router_w;
+  const float *router_bias;
+  const void *gate;
+  const void *up;
+  const void *down;
+  const void *sh_gate;
+  const void *sh_up;
+  const void *sh_down;
+} ds4moe_weights;
+
+/* Optional routing outputs (host struct of device pointers; each may be NULL).
+ *   topk_idx [T,k] int32  selected experts in rank order (logit descending,
+ *                         ties to the lower expert index)
+ *   topk_w   [T,k] fp32   normalised weights, sum over j = 1
+ *   counts   [E]   int32  assignments per expert
+ *   offsets  [E+1] int32  exclusive prefix sum of counts, offsets[E] = T*k
+ *   perm     [T*k] int32  assignment ids a = t*k + j grouped by expert, in
+ *                         increasing t within an expert
+ *   logits   [T,E] fp32   router logits */
+typedef struct {
+  int32_t *topk_idx;
+  float *topk_w;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *perm;
+  float *logits;
+} ds4moe_routing;
+
+/* Bytes of one packed matrix of `rows` x `cols` weights (cols = reduction
+ * length).  Same byte count as the canonical blocks (84 bytes per 256
+ * weights, 2.625 bits per weight) when cols is a multiple of 256; a divisor
+ * of 256 is padded to 256.  Returns 0 for an unsupported shape. */
+size_t ds4moe_packed_bytes(int64_t rows, int64_t cols);
+
+/* Repack canonical super-blocks into the HBM layout the GEMV/GEMM kernels
+ * stream (the canonical block is the 2-bit K-quant super-block named in the
+ * ds4 README "Models" section: 256 weights = 16 sub-blocks of 16, 4-bit
+ * scale (low nibble) and 4-bit min (high nibble) per sub-block, 2-bit codes
+ * four per byte lowest bits first, fp16 d and dmin; w = d*scale*q - dmin*min).
+ *   dst        packed output, n_mats * ds4moe_packed_bytes(rows, cols) bytes
+ *   canonical  n_mats matrices of rows*cols/256 blocks of 84 bytes each:
+ *              scales[16] @0, qs[64] @16, d @80, dmin @82 (little-endian);
+ *              blocks tile the row-major flattened matrix
+ *   rows       multiple of 16;  cols  multiple of 16, and a multiple of 256
+ *              or a divisor of 256
+ * Packed layout: units of 16 rows x 256 columns, 1344 bytes each, unit
+ * (row_tile, col_chunk) at ((row_tile * nchunks) + col_chunk) * 1344:
+ *   [0,1024)    2-bit codes, 16 bytes per MFMA lane (lane = 16*g + r, row r);
+ *               dword u of lane (r,g) holds sub-block 4u+g of row r, element
+ *               i at bits 4*(i%8) + 2*(i/8)
+ *   [1024,1280) per row 16 bytes: halfword g of bytes 0-7 holds the scales of
+ *               sub-blocks g, 4+g, 8+g, 12+g as nibbles 0..3; bytes 8-15
+ *               hold the 16 mins as nibbles in sub-block order
+ *   [1280,1344) per row d (bits 0-15) and dmin (bits 16-31), binary16
+ * The conversion is exact: no value is altered. */
+int ds4moe_pack_q2k(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, void *stream);
+
+/* Dequantize packed matrices to fp32, row-major [n_mats, rows, cols]:
+ * w = d*scale*q - dmin*min, every product exact, one rounding (bitwise equal
+ * to the correctly rounded value of the block's definition). */
+int ds4moe_dequant_q2k(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, void *stream);
+
+/* Workspace bytes needed by a call with `T` tokens in `mode`
+ * (ds4moe_mode).  Returns 0 if dims is NULL or invalid. */
+size_t ds4moe_workspace_bytes(const ds4moe_dims *dims, int32_t T, int32_t mode);
+
+/* Router only: logits, scores, top-k, weights, per-expert histogram, scan and
+ * stable permutation.  x [T,H] in dims->x_dtype; T >= 0 (0 = no-op).
+ * Needs router_w (and router_bias if any) in `w`; `out` (host struct) must
+ * not be NULL but any field may be.  ws: ds4moe_workspace_bytes(dims, T, 0). */
+int ds4moe_route(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
+                 ds4moe_routing *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Whole layer for a small batch, 1 <= T <= 16 (decode).  y [T,H] fp32 is
+ * overwritten.  route_out (host struct, nullable) receives the routing.
+ * ws: ds4moe_workspace_bytes(dims, T, DS4MOE_MODE_DECODE). */
+int ds4moe_forward_decode(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
+                          ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Whole layer for any T >= 0 (prefill; T = 0 is a no-op).  Same arguments as
+ * ds4moe_forward_decode; ws: ds4moe_workspace_bytes(dims, T, DS4MOE_MODE_PREFILL). */
+int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
+                           ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *ds4moe_status_str(int status);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int ds4moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DS4MOE_H */

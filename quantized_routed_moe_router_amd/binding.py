@@ -1,0 +1,158 @@
+"""ctypes binding of libds4moe.so: the same entry points as include/ds4moe.h.
+
+Argument marshalling only -- every step of the layer runs in the library's
+HIP kernels.  Tensors are torch tensors on the GPU (torch provides device
+memory and streams); their data pointers are handed to the library.  torch is
+imported before the library is loaded so that both share one HIP runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must be loaded before libds4moe.so: one HIP runtime)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libds4moe.so")
+
+DS4MOE_OK = 0
+DS4MOE_ERR_NULL = 1
+DS4MOE_ERR_SHAPE = 2
+DS4MOE_ERR_DTYPE = 3
+DS4MOE_ERR_ALIGN = 4
+DS4MOE_ERR_WORKSPACE = 5
+DS4MOE_ERR_UNSUPPORTED = 6
+DS4MOE_ERR_HIP = 7
+DS4MOE_F32 = 0
+DS4MOE_BF16 = 1
+MODE_ROUTE, MODE_DECODE, MODE_PREFILL = 0, 1, 2
+
+EXPORTED = ("ds4moe_packed_bytes", "ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_workspace_bytes",
+            "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_status_str",
+            "ds4moe_version")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("router_dtype", ctypes.c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("router_w", "router_bias", "gate", "up", "down", "sh_gate", "sh_up", "sh_down")]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_w", "counts", "offsets", "perm", "logits")]
+
+
+class Ds4MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({status_str(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library; fail loudly if it is missing (no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_routed_moe_router_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.ds4moe_packed_bytes.argtypes = [I64, I64]
+        L.ds4moe_packed_bytes.restype = ctypes.c_size_t
+        L.ds4moe_pack_q2k.argtypes = [P, P, I64, I64, I64, P]
+        L.ds4moe_dequant_q2k.argtypes = [P, P, I64, I64, I64, P]
+        L.ds4moe_workspace_bytes.argtypes = [P, I32, I32]
+        L.ds4moe_workspace_bytes.restype = ctypes.c_size_t
+        L.ds4moe_route.argtypes = [P, P, P, I32, P, P, ctypes.c_size_t, P]
+        L.ds4moe_forward_decode.argtypes = [P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+        L.ds4moe_forward_prefill.argtypes = [P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+        L.ds4moe_status_str.argtypes = [ctypes.c_int]
+        L.ds4moe_status_str.restype = ctypes.c_char_p
+        L.ds4moe_version.restype = ctypes.c_int
+        for fn in ("ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_route", "ds4moe_forward_decode",
+                   "ds4moe_forward_prefill"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().ds4moe_status_str(int(status)).decode()
+
+
+def _ptr(t) -> ctypes.c_void_p | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status: int, what: str) -> None:
+    if status != DS4MOE_OK:
+        raise Ds4MoeError(status, what)
+
+
+def make_dims(H, I, E, k, Is=0, x_dtype=DS4MOE_BF16, router_dtype=DS4MOE_BF16) -> Dims:
+    return Dims(H, I, E, k, Is, x_dtype, router_dtype)
+
+
+def make_weights(router_w, gate, up, down, router_bias=None, sh_gate=None, sh_up=None, sh_down=None) -> Weights:
+    return Weights(*(_ptr(t) for t in (router_w, router_bias, gate, up, down, sh_gate, sh_up, sh_down)))
+
+
+def make_routing(topk_idx=None, topk_w=None, counts=None, offsets=None, perm=None, logits=None) -> Routing:
+    return Routing(*(_ptr(t) for t in (topk_idx, topk_w, counts, offsets, perm, logits)))
+
+
+# ---------------------------------------------------------------- entry points
+
+
+def ds4moe_packed_bytes(rows: int, cols: int) -> int:
+    return int(lib().ds4moe_packed_bytes(rows, cols))
+
+
+def ds4moe_pack_q2k(dst, canonical, n_mats: int, rows: int, cols: int, stream=None) -> None:
+    _check(lib().ds4moe_pack_q2k(_ptr(dst), _ptr(canonical), n_mats, rows, cols, _stream(stream)), "pack_q2k")
+
+
+def ds4moe_dequant_q2k(dst, packed, n_mats: int, rows: int, cols: int, stream=None) -> None:
+    _check(lib().ds4moe_dequant_q2k(_ptr(dst), _ptr(packed), n_mats, rows, cols, _stream(stream)), "dequant_q2k")
+
+
+def ds4moe_workspace_bytes(dims: Dims, T: int, mode: int) -> int:
+    return int(lib().ds4moe_workspace_bytes(ctypes.byref(dims), T, mode))
+
+
+def ds4moe_route(dims: Dims, weights: Weights, x, T: int, routing: Routing, ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().ds4moe_route(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, ctypes.byref(routing),
+                              _ptr(ws), ws_bytes, _stream(stream)), "route")
+
+
+def ds4moe_forward_decode(dims: Dims, weights: Weights, x, T: int, y, routing: Routing | None, ws, ws_bytes: int,
+                          stream=None) -> None:
+    r = ctypes.byref(routing) if routing is not None else None
+    _check(lib().ds4moe_forward_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(y), r,
+                                       _ptr(ws), ws_bytes, _stream(stream)), "forward_decode")
+
+
+def ds4moe_forward_prefill(dims: Dims, weights: Weights, x, T: int, y, routing: Routing | None, ws, ws_bytes: int,
+                           stream=None) -> None:
+    r = ctypes.byref(routing) if routing is not None else None
+    _check(lib().ds4moe_forward_prefill(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(y), r,
+                                        _ptr(ws), ws_bytes, _stream(stream)), "forward_prefill")

@@ -1,0 +1,295 @@
+// C ABI of the ds4moe library: argument validation (host only, before any
+// launch), workspace layout, and the launch sequences of the three calls.
+#include <hip/hip_runtime.h>
+
+#include "../../include/ds4moe.h"
+#include "launch.h"
+
+using namespace ds4;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kTileDecode = 16;
+constexpr int kTilePrefill = 64;
+constexpr int64_t kMaxTokens = 1 << 20;
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int validate_dims(const ds4moe_dims *d) {
+  if (!d) return DS4MOE_ERR_NULL;
+  if (d->x_dtype != DS4MOE_F32 && d->x_dtype != DS4MOE_BF16) return DS4MOE_ERR_DTYPE;
+  if (d->router_dtype != DS4MOE_F32 && d->router_dtype != DS4MOE_BF16) return DS4MOE_ERR_DTYPE;
+  if (d->hidden < 256 || d->hidden > 65536 || d->hidden % 256) return DS4MOE_ERR_SHAPE;
+  if (d->inter < 16 || d->inter > 32768 || d->inter % 16) return DS4MOE_ERR_SHAPE;
+  if (d->inter % 256 && 256 % d->inter) return DS4MOE_ERR_SHAPE;
+  if (d->top_k < 1 || d->top_k > 16) return DS4MOE_ERR_SHAPE;
+  if (d->n_experts < d->top_k || d->n_experts > 256) return DS4MOE_ERR_SHAPE;
+  if (d->shared_inter < 0 || d->shared_inter > 65536 || d->shared_inter % 32) return DS4MOE_ERR_SHAPE;
+  return DS4MOE_OK;
+}
+
+struct Layout {
+  size_t logits, idx, w, counts, offsets, perm, pos, tiles, ntiles;
+  size_t x16, xs_hi, xs_lo, h, hs_hi, hs_lo, yp, hsh, ysh;
+  size_t total;
+  int tile_n, max_tiles, Ipad;
+};
+
+Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const int64_t E = d.n_experts, k = d.top_k, H = d.hidden, Is = d.shared_inter;
+  const int64_t A = T * k;
+  L.Ipad = d.inter % 256 ? 256 : d.inter;
+  L.tile_n = mode == DS4MOE_MODE_PREFILL ? kTilePrefill : kTileDecode;
+  L.max_tiles = (int)(A / L.tile_n + (A < E ? A : E));
+  L.logits = take(sizeof(float) * T * E);
+  L.idx = take(sizeof(int32_t) * A);
+  L.w = take(sizeof(float) * A);
+  L.counts = take(sizeof(int32_t) * E);
+  L.offsets = take(sizeof(int32_t) * (E + 1));
+  L.perm = take(sizeof(int32_t) * A);
+  if (mode != DS4MOE_MODE_ROUTE) {
+    L.pos = take(sizeof(int32_t) * A);
+    L.tiles = take(sizeof(TileT) * (size_t)L.max_tiles);
+    L.ntiles = take(16);
+    L.x16 = take(2 * T * H);
+    L.xs_hi = take(2 * T * (H / 16));
+    L.xs_lo = take(2 * T * (H / 16));
+    L.h = take(2 * A * L.Ipad);
+    L.hs_hi = take(2 * A * (L.Ipad / 16));
+    L.hs_lo = take(2 * A * (L.Ipad / 16));
+    L.yp = take(sizeof(float) * A * H);
+    if (Is > 0) {
+      L.hsh = take(2 * T * Is);
+      L.ysh = take(sizeof(float) * T * H);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+int validate_weights(const ds4moe_dims &d, const ds4moe_weights *w, bool experts) {
+  if (!w) return DS4MOE_ERR_NULL;
+  if (!w->router_w) return DS4MOE_ERR_NULL;
+  if (!aligned(w->router_w, 16) || !aligned(w->router_bias, 4)) return DS4MOE_ERR_ALIGN;
+  if (!experts) return DS4MOE_OK;
+  if (!w->gate || !w->up || !w->down) return DS4MOE_ERR_NULL;
+  if (!aligned(w->gate, 16) || !aligned(w->up, 16) || !aligned(w->down, 16)) return DS4MOE_ERR_ALIGN;
+  if (d.shared_inter > 0) {
+    if (!w->sh_gate || !w->sh_up || !w->sh_down) return DS4MOE_ERR_NULL;
+    if (!aligned(w->sh_gate, 16) || !aligned(w->sh_up, 16) || !aligned(w->sh_down, 16)) return DS4MOE_ERR_ALIGN;
+  }
+  return DS4MOE_OK;
+}
+
+int validate_routing(const ds4moe_routing *r) {
+  if (!r) return DS4MOE_OK;
+  if (!aligned(r->topk_idx, 4) || !aligned(r->topk_w, 4) || !aligned(r->counts, 4) || !aligned(r->offsets, 4) ||
+      !aligned(r->perm, 4) || !aligned(r->logits, 4))
+    return DS4MOE_ERR_ALIGN;
+  return DS4MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DS4MOE_OK : DS4MOE_ERR_HIP; }
+
+#define TRY(expr)                          \
+  do {                                     \
+    const hipError_t _e = (expr);          \
+    if (_e != hipSuccess) return DS4MOE_ERR_HIP; \
+  } while (0)
+
+// Common front half: validation shared by the three calls.
+int check_call(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, const float *y,
+               bool need_y, const ds4moe_routing *r, void *ws, size_t ws_bytes, int mode, Layout *L) {
+  int st = validate_dims(dims);
+  if (st) return st;
+  if (T < 0 || T > kMaxTokens) return DS4MOE_ERR_SHAPE;
+  if (mode == DS4MOE_MODE_DECODE && (T < 1 || T > 16)) return DS4MOE_ERR_SHAPE;
+  st = validate_weights(*dims, w, mode != DS4MOE_MODE_ROUTE);
+  if (st) return st;
+  st = validate_routing(r);
+  if (st) return st;
+  if (T == 0) return DS4MOE_OK;
+  if (!x || (need_y && !y)) return DS4MOE_ERR_NULL;
+  if (!aligned(x, 16) || (need_y && !aligned(y, 16))) return DS4MOE_ERR_ALIGN;
+  *L = make_layout(*dims, T, mode);
+  if (!ws) return DS4MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return DS4MOE_ERR_ALIGN;
+  if (ws_bytes < L->total) return DS4MOE_ERR_WORKSPACE;
+  return DS4MOE_OK;
+}
+
+struct Ptrs {
+  float *logits, *w;
+  int32_t *idx, *counts, *offsets, *perm;
+};
+
+Ptrs routing_ptrs(void *ws, const Layout &L, const ds4moe_routing *r) {
+  Ptrs p;
+  p.logits = (r && r->logits) ? r->logits : at<float>(ws, L.logits);
+  p.idx = (r && r->topk_idx) ? r->topk_idx : at<int32_t>(ws, L.idx);
+  p.w = (r && r->topk_w) ? r->topk_w : at<float>(ws, L.w);
+  p.counts = (r && r->counts) ? r->counts : at<int32_t>(ws, L.counts);
+  p.offsets = (r && r->offsets) ? r->offsets : at<int32_t>(ws, L.offsets);
+  p.perm = (r && r->perm) ? r->perm : at<int32_t>(ws, L.perm);
+  return p;
+}
+
+int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
+            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream, int mode) {
+  Layout L;
+  int st = check_call(dims, w, x, T, y, true, route_out, ws, ws_bytes, mode, &L);
+  if (st || T == 0) return st;
+  const ds4moe_dims &d = *dims;
+  hipStream_t s = (hipStream_t)stream;
+  const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
+  const Ptrs p = routing_ptrs(ws, L, route_out);
+  const bool small = mode == DS4MOE_MODE_DECODE;
+
+  if (T <= 16)
+    TRY(launch_router_small(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
+  else
+    TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
+
+  XPrep xp{x, xb, at<_Float16>(ws, L.x16), at<_Float16>(ws, L.xs_hi), at<_Float16>(ws, L.xs_lo)};
+  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, at<int32_t>(ws, L.pos),
+              at<TileT>(ws, L.tiles), at<int32_t>(ws, L.ntiles), L.tile_n};
+  if (small) {
+    TRY(launch_route_small(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, s));
+  } else {
+    TRY(launch_topk(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, s));
+    TRY(launch_permute(T, d.n_experts, d.top_k, ro, s));
+  }
+
+  GemmArgs ga{};
+  ga.gate = (const uint8_t *)w->gate;
+  ga.up = (const uint8_t *)w->up;
+  ga.down = (const uint8_t *)w->down;
+  ga.gu_bytes = ds4moe_packed_bytes(d.inter, d.hidden);
+  ga.d_bytes = ds4moe_packed_bytes(d.hidden, d.inter);
+  ga.tiles = ro.tiles;
+  ga.ntiles = ro.ntiles;
+  ga.perm = p.perm;
+  ga.k = d.top_k;
+  ga.H = d.hidden;
+  ga.I = d.inter;
+  ga.Ipad = L.Ipad;
+  ga.x16 = xp.x16;
+  ga.xs_hi = xp.xs_hi;
+  ga.xs_lo = xp.xs_lo;
+  ga.h = at<_Float16>(ws, L.h);
+  ga.hs_hi = at<_Float16>(ws, L.hs_hi);
+  ga.hs_lo = at<_Float16>(ws, L.hs_lo);
+  ga.yp = at<float>(ws, L.yp);
+  TRY(launch_gateup(ga, L.max_tiles, small, s));
+  TRY(launch_down(ga, L.max_tiles, small, s));
+
+  float *ysh = nullptr;
+  if (d.shared_inter > 0) {
+    _Float16 *hsh = at<_Float16>(ws, L.hsh);
+    ysh = at<float>(ws, L.ysh);
+    TRY(launch_shared_gateup((const uint16_t *)w->sh_gate, (const uint16_t *)w->sh_up, xp.x16, hsh, T, d.hidden,
+                             d.shared_inter, s));
+    TRY(launch_shared_down((const uint16_t *)w->sh_down, hsh, ysh, T, d.hidden, d.shared_inter, s));
+  }
+  TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s));
+  return DS4MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ds4moe_status_str(int status) {
+  switch (status) {
+    case DS4MOE_OK: return "ok";
+    case DS4MOE_ERR_NULL: return "required pointer is NULL";
+    case DS4MOE_ERR_SHAPE: return "size out of the supported range";
+    case DS4MOE_ERR_DTYPE: return "unknown dtype";
+    case DS4MOE_ERR_ALIGN: return "pointer not aligned";
+    case DS4MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case DS4MOE_ERR_UNSUPPORTED: return "unsupported request";
+    case DS4MOE_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int ds4moe_version(void) { return kVersion; }
+
+size_t ds4moe_packed_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % 16) return 0;
+  if (cols % 256 && 256 % cols) return 0;
+  const int64_t nchunks = (cols + 255) / 256;
+  return (size_t)(rows / 16) * (size_t)nchunks * 1344u;
+}
+
+int ds4moe_pack_q2k(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, void *stream) {
+  if (n_mats < 0) return DS4MOE_ERR_SHAPE;
+  if (!ds4moe_packed_bytes(rows, cols)) return DS4MOE_ERR_SHAPE;
+  if (n_mats == 0) return DS4MOE_OK;
+  if (!dst || !canonical) return DS4MOE_ERR_NULL;
+  if (!aligned(dst, 16)) return DS4MOE_ERR_ALIGN;
+  return hip_status(launch_pack(dst, canonical, n_mats, rows, cols, (hipStream_t)stream));
+}
+
+int ds4moe_dequant_q2k(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, void *stream) {
+  if (n_mats < 0) return DS4MOE_ERR_SHAPE;
+  if (!ds4moe_packed_bytes(rows, cols)) return DS4MOE_ERR_SHAPE;
+  if (n_mats == 0) return DS4MOE_OK;
+  if (!dst || !packed) return DS4MOE_ERR_NULL;
+  if (!aligned(dst, 4) || !aligned(packed, 16)) return DS4MOE_ERR_ALIGN;
+  return hip_status(launch_dequant(dst, packed, n_mats, rows, cols, (hipStream_t)stream));
+}
+
+size_t ds4moe_workspace_bytes(const ds4moe_dims *dims, int32_t T, int32_t mode) {
+  if (validate_dims(dims) != DS4MOE_OK) return 0;
+  if (T < 0 || T > kMaxTokens) return 0;
+  if (mode != DS4MOE_MODE_ROUTE && mode != DS4MOE_MODE_DECODE && mode != DS4MOE_MODE_PREFILL) return 0;
+  if (T == 0) return 256;
+  return make_layout(*dims, T, mode).total;
+}
+
+int ds4moe_route(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, ds4moe_routing *out,
+                 void *ws, size_t ws_bytes, void *stream) {
+  if (!out) return DS4MOE_ERR_NULL;
+  Layout L;
+  int st = check_call(dims, w, x, T, nullptr, false, out, ws, ws_bytes, DS4MOE_MODE_ROUTE, &L);
+  if (st || T == 0) return st;
+  const ds4moe_dims &d = *dims;
+  hipStream_t s = (hipStream_t)stream;
+  const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
+  const Ptrs p = routing_ptrs(ws, L, out);
+  if (T <= 16)
+    TRY(launch_router_small(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
+  else
+    TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
+  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, kTileDecode};
+  TRY(launch_topk(p.logits, T, d.n_experts, d.top_k, d.hidden, nullptr, ro, s));
+  TRY(launch_permute(T, d.n_experts, d.top_k, ro, s));
+  return DS4MOE_OK;
+}
+
+int ds4moe_forward_decode(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
+                          ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream) {
+  return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, DS4MOE_MODE_DECODE);
+}
+
+int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
+                           ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream) {
+  return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, DS4MOE_MODE_PREFILL);
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Device-side types and helpers shared by the ds4moe kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 half_t;
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+// Packed expert layout: one unit = 16 rows x 256 reduction columns.
+#define DS4_UNIT_BYTES 1344
+#define DS4_SCALE_OFF 1024
+#define DS4_DD_OFF 1280
+
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  half_t h;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+__device__ __forceinline__ h8 cat8(h2 a, h2 b, h2 c, h2 d) {
+  h8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// fp4 (e2m1) nibble pairs -> fp16 pairs.  The scale operand acts as a power
+// of two (only its exponent is used); nibble 0b00qq is q/2, so scale 2 gives
+// q exactly.  SEL picks the byte of `w`; the low nibble lands in element 0.
+#define CVT_FP4(w, scale, SEL) __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w), (scale), (SEL))
+
+// A-operand fragment of one MFMA step: 8 codes of one sub-block times the
+// sub-block scale, exact small integers in fp16.  HALF selects elements 0-7
+// (bits 0-1 of each nibble) or 8-15 (bits 2-3).
+template <int HALF>
+__device__ __forceinline__ h8 dequant_frag(uint32_t raw, h2 sc2) {
+  const uint32_t nib = (raw >> (2 * HALF)) & 0x33333333u;
+  h2 p0 = CVT_FP4(nib, 2.0f, 0) * sc2;
+  h2 p1 = CVT_FP4(nib, 2.0f, 1) * sc2;
+  h2 p2 = CVT_FP4(nib, 2.0f, 2) * sc2;
+  h2 p3 = CVT_FP4(nib, 2.0f, 3) * sc2;
+  return cat8(p0, p1, p2, p3);
+}
+
+// Eight 4-bit mins (one nibble each) -> exact fp16 values m = lo + 4*hi.
+__device__ __forceinline__ h8 min_frag(uint32_t mdw) {
+  const uint32_t lo = mdw & 0x33333333u;
+  const uint32_t hi = (mdw >> 2) & 0x33333333u;
+  h2 p0 = CVT_FP4(lo, 2.0f, 0) + CVT_FP4(hi, 8.0f, 0);
+  h2 p1 = CVT_FP4(lo, 2.0f, 1) + CVT_FP4(hi, 8.0f, 1);
+  h2 p2 = CVT_FP4(lo, 2.0f, 2) + CVT_FP4(hi, 8.0f, 2);
+  h2 p3 = CVT_FP4(lo, 2.0f, 3) + CVT_FP4(hi, 8.0f, 3);
+  return cat8(p0, p1, p2, p3);
+}
+
+__device__ __forceinline__ h2 splat_h2(float v) {
+  h2 r;
+  r[0] = (half_t)v;
+  r[1] = r[0];
+  return r;
+}
+
+__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ h8 zero_h8() {
+  h8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (half_t)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ h8 load_h8(const half_t *p) { return *reinterpret_cast<const h8 *>(p); }

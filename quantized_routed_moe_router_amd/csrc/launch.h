@@ -1,0 +1,77 @@
+// Host-side launch wrappers of the ds4moe kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ds4 {
+
+struct TileT {
+  int32_t e, p0, n, pad;
+};
+
+// Activation preparation done per token next to the router: x -> fp16 and
+// per-16-element sums (split into fp16 hi + lo) for the min term.
+struct XPrep {
+  const void *x;       // [T,H] x_dtype
+  bool x_bf16;
+  _Float16 *x16;       // [T,H]
+  _Float16 *xs_hi;     // [T,H/16]
+  _Float16 *xs_lo;     // [T,H/16]
+};
+
+struct RouteOut {
+  int32_t *idx;        // [T,k]
+  float *w;            // [T,k]
+  int32_t *counts;     // [E]
+  int32_t *offsets;    // [E+1]
+  int32_t *perm;       // [T*k]
+  int32_t *pos;        // [T*k] inverse of perm (nullable)
+  TileT *tiles;        // [max_tiles] (nullable)
+  int32_t *ntiles;     // [1]       (nullable)
+  int tile_n;          // tokens per tile
+};
+
+struct GemmArgs {
+  // routed experts
+  const uint8_t *gate, *up, *down;   // packed, E matrices each
+  size_t gu_bytes, d_bytes;          // bytes per expert matrix
+  const TileT *tiles;
+  const int32_t *ntiles;
+  const int32_t *perm;
+  int k, H, I, Ipad;
+  const _Float16 *x16, *xs_hi, *xs_lo;
+  _Float16 *h, *hs_hi, *hs_lo;       // [T*k, Ipad], [T*k, Ipad/16]
+  float *yp;                         // [T*k, H]
+};
+
+hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols,
+                       hipStream_t s);
+hipError_t launch_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols,
+                          hipStream_t s);
+
+hipError_t launch_router_small(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
+                               float *logits, int T, int E, int H, hipStream_t s);
+hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
+                               float *logits, int T, int E, int H, hipStream_t s);
+// wave per token: top-k, weights and (if xp != nullptr) activation preparation
+hipError_t launch_topk(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
+                       hipStream_t s);
+// one workgroup: histogram, scan, stable permutation, tile list
+hipError_t launch_permute(int T, int E, int k, RouteOut ro, hipStream_t s);
+// one workgroup, T <= 16: top-k + activation preparation + permutation
+hipError_t launch_route_small(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
+                              hipStream_t s);
+
+// grouped GEMMs over the tile list (max_tiles = grid bound)
+hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream_t s);
+hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t s);
+hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,
+                          int k, int H, hipStream_t s);
+// dense shared expert, bf16 weights
+hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, _Float16 *hs, int T,
+                                int H, int Is, hipStream_t s);
+hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, float *ysh, int T, int H, int Is,
+                              hipStream_t s);
+
+}  // namespace ds4

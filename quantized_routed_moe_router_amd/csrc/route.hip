@@ -1,0 +1,440 @@
+// Router: fp64-accumulated logits, sqrt(softplus) scores, top-k by wavefront
+// reductions, weight normalisation, activation preparation, and the
+// token-to-expert histogram / scan / stable permutation.
+//
+// Score: the router numeric test described on the opensource-hub.com
+// "antirez/ds4" page (FAQ #1) shows log(1 + exp(x)) in fp32 losing precision
+// near logit -12; the fix evaluates log1p by a four-term series when
+// exp(x) < 1/32, with the series input clamped.  Here softplus(l) is
+// max(l,0) + log1p(u), u = exp(-|l|) <= 1, which is the same thing for l <= 0
+// and never overflows for large l.
+#include "common.h"
+#include "launch.h"
+
+namespace ds4 {
+
+template <bool BF16>
+__device__ __forceinline__ void load4_as_double(const void *p, int64_t idx, double out[4]) {
+  if (BF16) {
+    const u2 v = *reinterpret_cast<const u2 *>(reinterpret_cast<const uint16_t *>(p) + idx);
+    out[0] = (double)bf16_bits_to_float((uint16_t)(v.x & 0xFFFF));
+    out[1] = (double)bf16_bits_to_float((uint16_t)(v.x >> 16));
+    out[2] = (double)bf16_bits_to_float((uint16_t)(v.y & 0xFFFF));
+    out[3] = (double)bf16_bits_to_float((uint16_t)(v.y >> 16));
+  } else {
+    const f4 v = *reinterpret_cast<const f4 *>(reinterpret_cast<const float *>(p) + idx);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  }
+}
+
+// ---------------------------------------------------------------- logits, T <= 16
+// One wave per expert; each lane accumulates its 4-wide column slices of H for
+// every token in fp64 (every product of two fp32 numbers is exact in fp64),
+// then a fixed butterfly sums the 64 lanes.
+template <bool XB, bool WB>
+__global__ __launch_bounds__(256) void k_router_small(const void *__restrict__ x, const void *__restrict__ wr,
+                                                      const float *__restrict__ bias, float *__restrict__ logits,
+                                                      int T, int E, int H) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  double acc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) acc[t] = 0.0;
+  for (int h = 4 * lane; h < H; h += 256) {
+    double w4[4];
+    load4_as_double<WB>(wr, (int64_t)e * H + h, w4);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      if (t < T) {
+        double x4[4];
+        load4_as_double<XB>(x, (int64_t)t * H + h, x4);
+        acc[t] = fma(x4[0], w4[0], acc[t]);
+        acc[t] = fma(x4[1], w4[1], acc[t]);
+        acc[t] = fma(x4[2], w4[2], acc[t]);
+        acc[t] = fma(x4[3], w4[3], acc[t]);
+      }
+    }
+  }
+  const double b = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    if (t < T) {
+      double v = acc[t];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0) logits[(int64_t)t * E + e] = (float)(v + b);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- logits, tiled
+// 64 tokens x 64 experts per workgroup, 4x4 outputs per thread, sequential
+// fp64 FMA over h = 0..H-1 (the same order as a plain loop).
+template <bool XB, bool WB>
+__global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x, const void *__restrict__ wr,
+                                                      const float *__restrict__ bias, float *__restrict__ logits,
+                                                      int T, int E, int H) {
+  __shared__ float xs[32][68];  // [k][token]
+  __shared__ float ws[32][68];  // [k][expert]
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const int tr = (tid >> 4) * 4, er = (tid & 15) * 4;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  // loader: thread -> (row = tid/4, 8 consecutive k at 8*(tid%4))
+  const int lrow = tid >> 2, lk = (tid & 3) * 8;
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    {
+      double v[8];
+      const int t = t0 + lrow;
+      if (t < T) {
+        load4_as_double<XB>(x, (int64_t)t * H + k0 + lk, v);
+        load4_as_double<XB>(x, (int64_t)t * H + k0 + lk + 4, v + 4);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xs[lk + i][lrow] = (float)v[i];
+      const int e = e0 + lrow;
+      if (e < E) {
+        load4_as_double<WB>(wr, (int64_t)e * H + k0 + lk, v);
+        load4_as_double<WB>(wr, (int64_t)e * H + k0 + lk + 4, v + 4);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ws[lk + i][lrow] = (float)v[i];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < 32; ++kk) {
+      const f4 xv = *reinterpret_cast<const f4 *>(&xs[kk][tr]);
+      const f4 wv = *reinterpret_cast<const f4 *>(&ws[kk][er]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma((double)xv[i], (double)wv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + tr + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + er + j;
+      if (e < E) logits[(int64_t)t * E + e] = (float)(acc[i][j] + (bias ? (double)bias[e] : 0.0));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- score
+// s = sqrt(max(l,0) + log1p(u)), u = exp(-|l|); log1p(u) by the series
+// u - u^2/2 + u^3/3 - u^4/4 for u < 1/32 (series input clamped to 1/32),
+// log(1 + u) otherwise.  Max relative error vs. the exact value < 3e-6.
+__device__ __forceinline__ float router_score(float l) {
+  const float u = expf(-fabsf(l));
+  const float uc = fminf(u, 0.03125f);
+  const float ser = uc * (1.0f - uc * (0.5f - uc * (0.33333334f - uc * 0.25f)));
+  const float lp = (u < 0.03125f) ? ser : logf(1.0f + u);
+  return sqrtf(fmaxf(l, 0.0f) + lp);
+}
+
+// order-preserving key: larger logit first, then lower expert index; NaN last
+__device__ __forceinline__ uint64_t rank_key(float l, int e) {
+  uint32_t u = __float_as_uint(l);
+  uint32_t ord;
+  if (l != l) {
+    ord = 0u;
+  } else {
+    if (u == 0x80000000u) u = 0u;  // -0 == +0
+    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  if (ord == 0u) return __uint_as_float(0x7FC00000u);
+  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Top-k for token t by one wave; writes idx/w; optional activation prep.
+__device__ void topk_token(const float *__restrict__ logits, int t, int E, int k, int H, const XPrep *xp,
+                           RouteOut ro, const void *xptr, bool x_bf16, _Float16 *x16, _Float16 *xs_hi,
+                           _Float16 *xs_lo) {
+  const int lane = threadIdx.x & 63;
+  uint64_t keys[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    keys[i] = e < E ? rank_key(logits[(int64_t)t * E + e], e) : 0ull;
+  }
+  uint32_t taken = 0;
+  float sel_l[16];
+  int sel_e[16];
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool live = (lane + 64 * i < E) && !((taken >> i) & 1u);
+      if (live && (best == 0 || keys[i] > best)) best = keys[i];
+    }
+    // keys of live experts are never 0 (low half = ~e > 0 for e < 2^32-1)
+    best = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    if ((e & 63) == lane) taken |= 1u << (e >> 6);
+    sel_e[j] = e;
+    sel_l[j] = key_logit(best);
+  }
+  // scores in rank order, normalised in fp32
+  float s[16], S = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    s[j] = router_score(sel_l[j]);
+    S += s[j];
+  }
+  for (int j = 0; j < k; ++j) {
+    if (lane == j) {
+      ro.idx[(int64_t)t * k + j] = sel_e[j];
+      ro.w[(int64_t)t * k + j] = s[j] / S;
+    }
+  }
+  if (x16) {
+    // x -> fp16, and per-16-element sums of the fp16 values, split hi + lo
+    const int nsub = H >> 4;
+    for (int j = lane; j < nsub; j += 64) {
+      const int64_t base = (int64_t)t * H + 16 * j;
+      float v[16];
+      if (x_bf16) {
+        const u4 a = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base);
+        const u4 b = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base + 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_bits_to_float((uint16_t)(a[i] & 0xFFFF));
+          v[2 * i + 1] = bf16_bits_to_float((uint16_t)(a[i] >> 16));
+          v[8 + 2 * i] = bf16_bits_to_float((uint16_t)(b[i] & 0xFFFF));
+          v[8 + 2 * i + 1] = bf16_bits_to_float((uint16_t)(b[i] >> 16));
+        }
+      } else {
+        const float *p = reinterpret_cast<const float *>(xptr) + base;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f4 a = *reinterpret_cast<const f4 *>(p + 4 * q);
+          v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
+        }
+      }
+      h8 o0, o1;
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        o0[i] = (half_t)v[i];
+        sum += (float)o0[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        o1[i] = (half_t)v[8 + i];
+        sum += (float)o1[i];
+      }
+      *reinterpret_cast<h8 *>(x16 + base) = o0;
+      *reinterpret_cast<h8 *>(x16 + base + 8) = o1;
+      const half_t hi = (half_t)sum;
+      xs_hi[(int64_t)t * nsub + j] = hi;
+      xs_lo[(int64_t)t * nsub + j] = (half_t)(sum - (float)hi);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k, int H,
+                                              XPrep xp, bool do_x, RouteOut ro) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token(logits, t, E, k, H, nullptr, ro, xp.x, xp.x_bf16, do_x ? xp.x16 : nullptr, xp.xs_hi, xp.xs_lo);
+}
+
+// ---------------------------------------------------------------- permutation
+// Whole workgroup (1024 threads).  Counts by LDS integer atomics (order does
+// not matter for integers), exclusive scan by one wave, then a stable
+// placement in chunks of 1024 tokens: for each expert a bitmask of the chunk's
+// tokens that chose it; the rank of token t = number of set bits below t.
+__device__ void permute_block(const int32_t *__restrict__ idx, int T, int E, int k, RouteOut ro,
+                              int32_t *s_cnt, int32_t *s_base, int32_t *s_tbase, uint32_t *s_mask) {
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  for (int e = tid; e < E; e += nthr) s_cnt[e] = 0;
+  __syncthreads();
+  const int64_t nA = (int64_t)T * k;
+  for (int64_t a = tid; a < nA; a += nthr) atomicAdd(&s_cnt[idx[a]], 1);
+  __syncthreads();
+  if (tid < 64) {
+    // exclusive scans of counts and of tiles per expert; 4 experts per lane
+    const int lane = tid;
+    int c[4], nt[4], sc = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      c[i] = e < E ? s_cnt[e] : 0;
+      nt[i] = (ro.tiles && c[i] > 0) ? (c[i] + ro.tile_n - 1) / ro.tile_n : 0;
+      sc += c[i];
+      st += nt[i];
+    }
+    int ic = sc, it = st;  // inclusive wave scans
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int oc = __shfl_up(ic, off), ot = __shfl_up(it, off);
+      if (lane >= off) {
+        ic += oc;
+        it += ot;
+      }
+    }
+    int rc = ic - sc, rt = it - st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        s_base[e] = rc;
+        s_tbase[e] = rt;
+        ro.counts[e] = c[i];
+        ro.offsets[e] = rc;
+      }
+      rc += c[i];
+      rt += nt[i];
+    }
+    if (lane == 63) {
+      ro.offsets[E] = ic;
+      if (ro.ntiles) *ro.ntiles = it;
+    }
+  }
+  __syncthreads();
+  if (ro.tiles) {
+    for (int e = tid; e < E; e += nthr) {
+      const int c = s_cnt[e];
+      const int nt = (c + ro.tile_n - 1) / ro.tile_n;
+      for (int i = 0; i < nt; ++i) {
+        TileT tl;
+        tl.e = e;
+        tl.p0 = s_base[e] + i * ro.tile_n;
+        tl.n = min(ro.tile_n, c - i * ro.tile_n);
+        tl.pad = 0;
+        ro.tiles[s_tbase[e] + i] = tl;
+      }
+    }
+  }
+  // stable placement, chunks of nthr tokens (nthr <= 1024, 32 words per expert)
+  const int words = nthr / 32;
+  for (int t0 = 0; t0 < T; t0 += nthr) {
+    for (int i = tid; i < E * words; i += nthr) s_mask[i] = 0u;
+    __syncthreads();
+    const int t = t0 + tid;
+    if (t < T)
+      for (int j = 0; j < k; ++j) atomicOr(&s_mask[idx[(int64_t)t * k + j] * words + (tid >> 5)], 1u << (tid & 31));
+    __syncthreads();
+    if (t < T) {
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[(int64_t)t * k + j];
+        const uint32_t *m = s_mask + e * words;
+        int rank = __popc(m[tid >> 5] & ((1u << (tid & 31)) - 1u));
+        for (int w = 0; w < (tid >> 5); ++w) rank += __popc(m[w]);
+        const int p = s_base[e] + rank;
+        const int a = t * k + j;
+        ro.perm[p] = a;
+        if (ro.pos) ro.pos[a] = p;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += nthr) {
+      int c = 0;
+      for (int w = 0; w < words; ++w) c += __popc(s_mask[e * words + w]);
+      s_base[e] += c;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_permute(int T, int E, int k, RouteOut ro) {
+  __shared__ int32_t s_cnt[256], s_base[256], s_tbase[256];
+  __shared__ uint32_t s_mask[256 * 32];
+  permute_block(ro.idx, T, E, k, ro, s_cnt, s_base, s_tbase, s_mask);
+}
+
+// T <= 16: waves 0..T-1 route one token each, then the block permutes.
+__global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ logits, int T, int E, int k,
+                                                      int H, XPrep xp, bool do_x, RouteOut ro) {
+  __shared__ int32_t s_cnt[256], s_base[256], s_tbase[256];
+  __shared__ uint32_t s_mask[256 * 32];
+  const int t = threadIdx.x >> 6;
+  if (t < T)
+    topk_token(logits, t, E, k, H, nullptr, ro, xp.x, xp.x_bf16, do_x ? xp.x16 : nullptr, xp.xs_hi, xp.xs_lo);
+  __threadfence_block();
+  __syncthreads();
+  permute_block(ro.idx, T, E, k, ro, s_cnt, s_base, s_tbase, s_mask);
+}
+
+// ---------------------------------------------------------------- launchers
+template <bool XB, bool WB>
+static hipError_t router_small_t(const void *x, const void *wr, const float *bias, float *logits, int T, int E,
+                                 int H, hipStream_t s) {
+  hipLaunchKernelGGL((k_router_small<XB, WB>), dim3((E + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, T, E, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_small(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
+                               float *logits, int T, int E, int H, hipStream_t s) {
+  if (x_bf16 && w_bf16) return router_small_t<true, true>(x, wr, bias, logits, T, E, H, s);
+  if (x_bf16) return router_small_t<true, false>(x, wr, bias, logits, T, E, H, s);
+  if (w_bf16) return router_small_t<false, true>(x, wr, bias, logits, T, E, H, s);
+  return router_small_t<false, false>(x, wr, bias, logits, T, E, H, s);
+}
+
+template <bool XB, bool WB>
+static hipError_t router_tiled_t(const void *x, const void *wr, const float *bias, float *logits, int T, int E,
+                                 int H, hipStream_t s) {
+  hipLaunchKernelGGL((k_router_tiled<XB, WB>), dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s, x, wr, bias,
+                     logits, T, E, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
+                               float *logits, int T, int E, int H, hipStream_t s) {
+  if (x_bf16 && w_bf16) return router_tiled_t<true, true>(x, wr, bias, logits, T, E, H, s);
+  if (x_bf16) return router_tiled_t<true, false>(x, wr, bias, logits, T, E, H, s);
+  if (w_bf16) return router_tiled_t<false, true>(x, wr, bias, logits, T, E, H, s);
+  return router_tiled_t<false, false>(x, wr, bias, logits, T, E, H, s);
+}
+
+hipError_t launch_topk(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
+                       hipStream_t s) {
+  XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, H, x, xp != nullptr, ro);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(int T, int E, int k, RouteOut ro, hipStream_t s) {
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, T, E, k, ro);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_small(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
+                              hipStream_t s) {
+  XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
+  hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, logits, T, E, k, H, x, xp != nullptr, ro);
+  return hipGetLastError();
+}
+
+}  // namespace ds4

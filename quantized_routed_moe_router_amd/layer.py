@@ -1,0 +1,120 @@
+"""Device-resident layer: packed expert weights in HBM plus a reusable workspace.
+
+Plumbing around the C ABI only: torch allocates device memory; packing,
+routing and the expert FFNs all run in libds4moe.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def _as_bf16(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+class DeviceLayer:
+    def __init__(self, H, I, E, k, Is=0, x_dtype=B.DS4MOE_BF16, router_dtype=B.DS4MOE_BF16, device="cuda:0"):
+        self.H, self.I, self.E, self.k, self.Is = H, I, E, k, Is
+        self.device = torch.device(device)
+        self.dims = B.make_dims(H, I, E, k, Is, x_dtype, router_dtype)
+        self.x_dtype, self.router_dtype = x_dtype, router_dtype
+        self.gu_bytes = B.ds4moe_packed_bytes(I, H)
+        self.d_bytes = B.ds4moe_packed_bytes(H, I)
+        self._ws = None
+        self.router_w = self.router_bias = None
+        self.gate = self.up = self.down = None
+        self.sh_gate = self.sh_up = self.sh_down = None
+
+    # ------------------------------------------------------------ weights
+    def pack(self, canonical: np.ndarray, rows: int, cols: int, stream=None) -> torch.Tensor:
+        """Upload E canonical-block matrices and repack them on the GPU."""
+        n = canonical.shape[0]
+        src = _dev(canonical.reshape(n, -1), self.device)
+        dst = torch.empty(n * B.ds4moe_packed_bytes(rows, cols), dtype=torch.uint8, device=self.device)
+        B.ds4moe_pack_q2k(dst, src, n, rows, cols, stream)
+        torch.cuda.current_stream(self.device).synchronize()
+        del src
+        return dst
+
+    def set_router(self, router_w: np.ndarray, router_bias: np.ndarray | None = None):
+        if self.router_dtype == B.DS4MOE_BF16:
+            self.router_w = _as_bf16(router_w, self.device)
+        else:
+            self.router_w = _dev(router_w.astype(np.float32), self.device)
+        self.router_bias = None if router_bias is None else _dev(router_bias.astype(np.float32), self.device)
+
+    def set_experts(self, gate: np.ndarray, up: np.ndarray, down: np.ndarray):
+        self.gate = self.pack(gate, self.I, self.H)
+        self.up = self.pack(up, self.I, self.H)
+        self.down = self.pack(down, self.H, self.I)
+
+    def set_shared(self, sh_gate, sh_up, sh_down):
+        self.sh_gate = _as_bf16(sh_gate, self.device)
+        self.sh_up = _as_bf16(sh_up, self.device)
+        self.sh_down = _as_bf16(sh_down, self.device)
+
+    def weights(self, gate=None, up=None, down=None) -> B.Weights:
+        return B.make_weights(self.router_w, gate if gate is not None else self.gate,
+                              up if up is not None else self.up, down if down is not None else self.down,
+                              self.router_bias, self.sh_gate, self.sh_up, self.sh_down)
+
+    # ------------------------------------------------------------ activations
+    def x_tensor(self, x: np.ndarray) -> torch.Tensor:
+        if self.x_dtype == B.DS4MOE_BF16:
+            return _as_bf16(x, self.device)
+        return _dev(x.astype(np.float32), self.device)
+
+    def workspace(self, T: int, mode: int) -> torch.Tensor:
+        need = B.ds4moe_workspace_bytes(self.dims, T, mode)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def routing_buffers(self, T: int) -> dict:
+        d = self.device
+        return dict(topk_idx=torch.empty(T, self.k, dtype=torch.int32, device=d),
+                    topk_w=torch.empty(T, self.k, dtype=torch.float32, device=d),
+                    counts=torch.empty(self.E, dtype=torch.int32, device=d),
+                    offsets=torch.empty(self.E + 1, dtype=torch.int32, device=d),
+                    perm=torch.empty(T * self.k, dtype=torch.int32, device=d),
+                    logits=torch.empty(T, self.E, dtype=torch.float32, device=d))
+
+    def forward(self, x: torch.Tensor, mode: int = B.MODE_PREFILL, y=None, routing: dict | None = None,
+                stream=None, weights: B.Weights | None = None) -> torch.Tensor:
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty(T, self.H, dtype=torch.float32, device=self.device)
+        ws = self.workspace(T, mode)
+        r = B.make_routing(**routing) if routing is not None else None
+        w = weights if weights is not None else self.weights()
+        fn = B.ds4moe_forward_decode if mode == B.MODE_DECODE else B.ds4moe_forward_prefill
+        fn(self.dims, w, x, T, y, r, ws, ws.numel(), stream)
+        return y
+
+    def route(self, x: torch.Tensor, stream=None) -> dict:
+        T = x.shape[0]
+        bufs = self.routing_buffers(T)
+        ws = self.workspace(T, B.MODE_ROUTE)
+        B.ds4moe_route(self.dims, self.weights(), x, T, B.make_routing(**bufs), ws, ws.numel(), stream)
+        return bufs
+
+
+def from_layer_inputs(L, device="cuda:0", experts: bool = True) -> DeviceLayer:
+    """Build a DeviceLayer from a synth.LayerInputs-like object (duck-typed)."""
+    wl = L.wl
+    xd = B.DS4MOE_F32 if wl.x_dtype == "f32" else B.DS4MOE_BF16
+    rd = B.DS4MOE_F32 if wl.router_dtype == "f32" else B.DS4MOE_BF16
+    dl = DeviceLayer(wl.H, wl.I, wl.E, wl.k, wl.Is, xd, rd, device)
+    dl.set_router(L.router_w, L.router_bias)
+    if experts:
+        dl.set_experts(L.gate, L.up, L.down)
+    if wl.Is:
+        dl.set_shared(L.sh_gate, L.sh_up, L.sh_down)
+    return dl

@@ -15,6 +15,8 @@ Workloads (the five layer shapes the method is measured on):
   shared expert with intermediate 2048
 
 Routed expert weights are N(0,0.02) before quantization in every workload.
+The four H=4096 workloads are one layer (same router and expert weights,
+drawn from streams keyed by the layer) fed different activations.
 """
 from __future__ import annotations
 
@@ -153,12 +155,13 @@ class Workload:
     x_shared_rho: float = 0.0      # x_t = rho*x_s + sqrt(1-rho^2)*z_t
     zipf_s: float = 0.0            # router bias from a Zipf(s) law, 0 = no bias
     zipf_scale: float = 0.75
+    layer_id: int = 1              # weight streams: workloads of one shape share a layer
     description: str = ""
 
 
 WORKLOADS = {
     "tiny": Workload("tiny", 0, T=16, H=256, E=8, I=128, k=2, x_dtype="f32", router_dtype="f32",
-                     router_sigma=0.05, description="tiny layer, fp32 activations and router"),
+                     router_sigma=0.05, layer_id=0, description="tiny layer, fp32 activations and router"),
     "decode1": Workload("decode1", 1, T=1, H=4096, E=256, I=2048, k=8,
                         description="decode, one token"),
     "decode16": Workload("decode16", 2, T=16, H=4096, E=256, I=2048, k=8, x_shared_rho=0.5,
@@ -224,19 +227,36 @@ def make_layer(wl: Workload | str, seed: int = DEFAULT_SEED, T: int | None = Non
     T = wl.T if T is None else T
     E, H, I = wl.E, wl.H, wl.I
     x = make_x(wl, seed, T)
-    rw = normal_f32(seed, stream_id(wl.wl_id, K_ROUTER), wl.router_sigma, (E, H))
+    lid = wl.layer_id
+    rw = normal_f32(seed, stream_id(lid, K_ROUTER), wl.router_sigma, (E, H))
     if wl.router_dtype == "bf16":
         rw = f32_to_bf16_bits(rw)
     bias = zipf_bias(wl, seed) if wl.zipf_s else None
     if experts:
-        gate = q2k_matrices(seed, stream_id(wl.wl_id, K_GATE), E, I, H, wl.w_sigma)
-        up = q2k_matrices(seed, stream_id(wl.wl_id, K_UP), E, I, H, wl.w_sigma)
-        down = q2k_matrices(seed, stream_id(wl.wl_id, K_DOWN), E, H, I, wl.w_sigma)
+        gate = q2k_matrices(seed, stream_id(lid, K_GATE), E, I, H, wl.w_sigma)
+        up = q2k_matrices(seed, stream_id(lid, K_UP), E, I, H, wl.w_sigma)
+        down = q2k_matrices(seed, stream_id(lid, K_DOWN), E, H, I, wl.w_sigma)
     else:
         gate = up = down = None
     shg = shu = shd = None
     if wl.Is:
-        shg = f32_to_bf16_bits(normal_f32(seed, stream_id(wl.wl_id, K_SHG), wl.w_sigma, (wl.Is, H)))
-        shu = f32_to_bf16_bits(normal_f32(seed, stream_id(wl.wl_id, K_SHU), wl.w_sigma, (wl.Is, H)))
-        shd = f32_to_bf16_bits(normal_f32(seed, stream_id(wl.wl_id, K_SHD), wl.w_sigma, (H, wl.Is)))
+        shg = f32_to_bf16_bits(normal_f32(seed, stream_id(lid, K_SHG), wl.w_sigma, (wl.Is, H)))
+        shu = f32_to_bf16_bits(normal_f32(seed, stream_id(lid, K_SHU), wl.w_sigma, (wl.Is, H)))
+        shd = f32_to_bf16_bits(normal_f32(seed, stream_id(lid, K_SHD), wl.w_sigma, (H, wl.Is)))
     return LayerInputs(wl, seed, T, x, rw, bias, gate, up, down, shg, shu, shd)
+
+
+def derive(base: LayerInputs, wl: Workload | str, T: int | None = None, batch: int = 0) -> LayerInputs:
+    """Inputs of workload `wl` reusing `base`'s router and expert weights (the
+    workloads of one shape share a layer); x, bias and shared expert follow
+    `wl`'s recipe."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    b = base.wl
+    assert (wl.H, wl.E, wl.I, wl.layer_id) == (b.H, b.E, b.I, b.layer_id)
+    T = wl.T if T is None else T
+    shared = make_layer(wl, base.seed, T=1, experts=False) if (wl.Is or wl.zipf_s) else None
+    return LayerInputs(wl, base.seed, T, make_x(wl, base.seed, T, batch), base.router_w,
+                       shared.router_bias if shared is not None else None, base.gate, base.up, base.down,
+                       shared.sh_gate if shared is not None else None, shared.sh_up if shared is not None else None,
+                       shared.sh_down if shared is not None else None)

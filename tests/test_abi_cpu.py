@@ -1,0 +1,148 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and every invalid argument is rejected on the host with the
+documented status before anything is launched (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_routed_moe_router_amd as q
+from quantized_routed_moe_router_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds4moe.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds4moe_\w+)\s*\(", txt)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 9
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(B.EXPORTED) == set(names)
+
+
+def test_single_hip_runtime_loaded():
+    maps = open("/proc/self/maps").read()
+    paths = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(paths) == 1, paths
+
+
+def test_version_and_status_strings():
+    assert B.lib().ds4moe_version() >= 100
+    for s in range(8):
+        assert B.status_str(s)
+    assert B.status_str(99) == "unknown status"
+
+
+def test_packed_bytes():
+    assert q.ds4moe_packed_bytes(2048, 4096) == 2048 * 4096 // 256 * 84 == 2752512
+    assert q.ds4moe_packed_bytes(4096, 2048) == 2752512
+    assert q.ds4moe_packed_bytes(256, 128) == 16 * 1 * 1344      # K=128 padded to 256
+    assert q.ds4moe_packed_bytes(15, 256) == 0
+    assert q.ds4moe_packed_bytes(16, 384) == 0
+    assert q.ds4moe_packed_bytes(16, 8) == 0
+
+
+def dims(**kw):
+    d = dict(H=4096, I=2048, E=256, k=8, Is=0, x_dtype=B.DS4MOE_BF16, router_dtype=B.DS4MOE_BF16)
+    d.update(kw)
+    return B.make_dims(d["H"], d["I"], d["E"], d["k"], d["Is"], d["x_dtype"], d["router_dtype"])
+
+
+def test_workspace_bytes():
+    d = dims()
+    assert B.ds4moe_workspace_bytes(d, 0, B.MODE_PREFILL) == 256
+    a = B.ds4moe_workspace_bytes(d, 16, B.MODE_DECODE)
+    b = B.ds4moe_workspace_bytes(d, 2048, B.MODE_PREFILL)
+    r = B.ds4moe_workspace_bytes(d, 2048, B.MODE_ROUTE)
+    assert 0 < r < b and a > 0
+    assert b >= 2048 * 8 * 4096 * 4                  # per-assignment outputs
+    assert B.ds4moe_workspace_bytes(dims(H=100), 16, 1) == 0
+    assert B.ds4moe_workspace_bytes(d, 16, 7) == 0
+    assert B.lib().ds4moe_workspace_bytes(None, 16, 1) == 0
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(H=100), B.DS4MOE_ERR_SHAPE), (dict(H=0), B.DS4MOE_ERR_SHAPE), (dict(I=8), B.DS4MOE_ERR_SHAPE),
+    (dict(I=384), B.DS4MOE_ERR_SHAPE), (dict(k=0), B.DS4MOE_ERR_SHAPE), (dict(k=17, E=32), B.DS4MOE_ERR_SHAPE),
+    (dict(E=4, k=8), B.DS4MOE_ERR_SHAPE), (dict(E=300), B.DS4MOE_ERR_SHAPE), (dict(Is=100), B.DS4MOE_ERR_SHAPE),
+    (dict(x_dtype=5), B.DS4MOE_ERR_DTYPE), (dict(router_dtype=-1), B.DS4MOE_ERR_DTYPE),
+])
+def test_bad_dims_rejected(bad, status):
+    w = B.make_weights(16, 16, 16, 16)
+    y = 16
+    assert B.lib().ds4moe_forward_prefill(ctypes.byref(dims(**bad)), ctypes.byref(w), ctypes.c_void_p(16), 4,
+                                          ctypes.c_void_p(y), None, ctypes.c_void_p(256), 1 << 40, None) == status
+
+
+def call(fn, d=None, w=None, x=16, T=4, y=16, r=None, ws=256, ws_bytes=1 << 40):
+    d = d or dims()
+    w = w if w is not None else B.make_weights(16, 16, 16, 16)
+    L = B.lib()
+    args = [ctypes.byref(d), ctypes.byref(w) if w is not False else None, ctypes.c_void_p(x), T]
+    if fn != "ds4moe_route":
+        args.append(ctypes.c_void_p(y))
+    args.append(ctypes.byref(r) if r is not None else (None if fn != "ds4moe_route" else None))
+    args += [ctypes.c_void_p(ws), ws_bytes, None]
+    return getattr(L, fn)(*args)
+
+
+@pytest.mark.parametrize("fn", ["ds4moe_forward_decode", "ds4moe_forward_prefill"])
+def test_forward_argument_errors(fn):
+    assert call(fn, w=False) == B.DS4MOE_ERR_NULL
+    assert call(fn, w=B.make_weights(None, 16, 16, 16)) == B.DS4MOE_ERR_NULL
+    assert call(fn, w=B.make_weights(16, None, 16, 16)) == B.DS4MOE_ERR_NULL
+    assert call(fn, w=B.make_weights(17, 16, 16, 16)) == B.DS4MOE_ERR_ALIGN
+    assert call(fn, w=B.make_weights(16, 16, 24, 16)) == B.DS4MOE_ERR_ALIGN
+    assert call(fn, w=B.make_weights(16, 16, 16, 16, router_bias=18)) == B.DS4MOE_ERR_ALIGN
+    assert call(fn, x=0) == B.DS4MOE_ERR_NULL
+    assert call(fn, y=0) == B.DS4MOE_ERR_NULL
+    assert call(fn, x=8) == B.DS4MOE_ERR_ALIGN
+    assert call(fn, ws=0) == B.DS4MOE_ERR_WORKSPACE
+    assert call(fn, ws=128) == B.DS4MOE_ERR_ALIGN
+    assert call(fn, ws_bytes=1000) == B.DS4MOE_ERR_WORKSPACE
+    assert call(fn, T=-1) == B.DS4MOE_ERR_SHAPE
+    assert call(fn, r=B.make_routing(topk_idx=18)) == B.DS4MOE_ERR_ALIGN
+    # shared expert declared but weights missing
+    assert call(fn, d=dims(Is=2048)) == B.DS4MOE_ERR_NULL
+    # prefill: T = 0 is a no-op that touches nothing; decode needs 1 <= T <= 16
+    expect = B.DS4MOE_OK if fn == "ds4moe_forward_prefill" else B.DS4MOE_ERR_SHAPE
+    assert call(fn, T=0, x=0, y=0, ws=0) == expect
+
+
+def test_decode_token_range():
+    assert call("ds4moe_forward_decode", T=17) == B.DS4MOE_ERR_SHAPE
+    assert call("ds4moe_forward_decode", T=0) == B.DS4MOE_ERR_SHAPE
+    assert call("ds4moe_forward_prefill", T=(1 << 20) + 1) == B.DS4MOE_ERR_SHAPE
+
+
+def test_route_argument_errors():
+    L = B.lib()
+    d, w, r = dims(), B.make_weights(16, None, None, None), B.make_routing()
+    assert L.ds4moe_route(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(16), 4, None, ctypes.c_void_p(256),
+                          1 << 40, None) == B.DS4MOE_ERR_NULL
+    assert L.ds4moe_route(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(16), 4, ctypes.byref(r),
+                          ctypes.c_void_p(256), 10, None) == B.DS4MOE_ERR_WORKSPACE
+    assert L.ds4moe_route(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(16), 0, ctypes.byref(r),
+                          None, 0, None) == B.DS4MOE_OK
+
+
+def test_pack_dequant_argument_errors():
+    L = B.lib()
+    v = ctypes.c_void_p
+    assert L.ds4moe_pack_q2k(v(16), v(16), 1, 15, 256, None) == B.DS4MOE_ERR_SHAPE
+    assert L.ds4moe_pack_q2k(v(16), v(16), -1, 16, 256, None) == B.DS4MOE_ERR_SHAPE
+    assert L.ds4moe_pack_q2k(None, v(16), 1, 16, 256, None) == B.DS4MOE_ERR_NULL
+    assert L.ds4moe_pack_q2k(v(8), v(16), 1, 16, 256, None) == B.DS4MOE_ERR_ALIGN
+    assert L.ds4moe_pack_q2k(v(16), v(16), 0, 16, 256, None) == B.DS4MOE_OK
+    assert L.ds4moe_dequant_q2k(v(16), None, 1, 16, 256, None) == B.DS4MOE_ERR_NULL
+    assert L.ds4moe_dequant_q2k(v(16), v(8), 1, 16, 256, None) == B.DS4MOE_ERR_ALIGN
+    assert L.ds4moe_dequant_q2k(v(16), v(16), 1, 16, 100, None) == B.DS4MOE_ERR_SHAPE

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars: dequantized weights, logits, top-k indices, counts, offsets and the
+permutation bit-exact; top-k weights within 3e-6 relative (the router test
+tolerance of the ds4 FAQ); layer output within 2e-3 per-token normwise
+relative error, max_t max_j |y-r| / max_j |r|; two runs bitwise equal.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_Y = 2e-3
+TOL_W = 3e-6
+
+
+def _q():
+    import quantized_routed_moe_router_amd as q
+    return q
+
+
+def per_token_err(y, r):
+    y = np.asarray(y, np.float64)
+    r = np.asarray(r, np.float64)
+    num = np.abs(y - r).max(axis=1)
+    den = np.abs(r).max(axis=1)
+    return float((num / np.maximum(den, 1e-30)).max())
+
+
+def check_routing(rt, L, tokens=None, label=""):
+    """rt: dict of device routing tensors for all T tokens; oracle on tokens."""
+    x = L.x if L.wl.x_dtype == "f32" else oracle.bf16_to_f32(L.x)
+    wr = L.router_w if L.wl.router_dtype == "f32" else oracle.bf16_to_f32(L.router_w)
+    lg = oracle.logits(x, wr, L.router_bias)
+    g_lg = rt["logits"].cpu().numpy()
+    mism = int((g_lg.view(np.uint32) != lg.view(np.uint32)).sum())
+    assert mism == 0, f"{label}: {mism} logits differ"
+    idx, w, _ = oracle.topk(lg, L.wl.k)
+    assert np.array_equal(rt["topk_idx"].cpu().numpy(), idx), label
+    gw = rt["topk_w"].cpu().numpy()
+    assert np.max(np.abs(gw - w) / np.abs(w)) <= TOL_W, label
+    counts, offsets, perm = oracle.permute(idx, L.wl.E)
+    assert np.array_equal(rt["counts"].cpu().numpy(), counts), label
+    assert np.array_equal(rt["offsets"].cpu().numpy(), offsets), label
+    assert np.array_equal(rt["perm"].cpu().numpy(), perm), label
+    return idx
+
+
+# ------------------------------------------------------------------ fixtures
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    q = _q()
+    L = synth.make_layer("tiny")
+    return L, q.from_layer_inputs(L)
+
+
+@pytest.fixture(scope="session")
+def full():
+    q = _q()
+    L = synth.make_layer("prefill")
+    dl = q.from_layer_inputs(L)
+    return L, dl
+
+
+@pytest.fixture(scope="session")
+def full_shared(full):
+    q = _q()
+    L0, dl0 = full
+    Ls = synth.derive(L0, "skewed", T=1)
+    dl = q.DeviceLayer(4096, 2048, 256, 8, 2048, q.DS4MOE_BF16, q.DS4MOE_BF16)
+    dl.set_router(Ls.router_w, Ls.router_bias)
+    dl.gate, dl.up, dl.down = dl0.gate, dl0.up, dl0.down
+    dl.set_shared(Ls.sh_gate, Ls.sh_up, Ls.sh_down)
+    return L0, dl
+
+
+# ------------------------------------------------------------------ dequant
+
+
+def test_dequant_bitwise_tiny(tiny):
+    q = _q()
+    L, dl = tiny
+    E, H, I = L.wl.E, L.wl.H, L.wl.I
+    for packed, canon, rows, cols in ((dl.gate, L.gate, I, H), (dl.up, L.up, I, H), (dl.down, L.down, H, I)):
+        out = torch.empty(E, rows, cols, dtype=torch.float32, device=dl.device)
+        q.ds4moe_dequant_q2k(out, packed, E, rows, cols)
+        ref = oracle.dequant_f32(canon).reshape(E, rows, cols)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_bitwise_full_sample(full):
+    q = _q()
+    L, dl = full
+    H, I = L.wl.H, L.wl.I
+    for e in (0, 77, 255):
+        for packed, canon, rows, cols, nb in ((dl.gate, L.gate, I, H, dl.gu_bytes), (dl.down, L.down, H, I, dl.d_bytes)):
+            out = torch.empty(rows, cols, dtype=torch.float32, device=dl.device)
+            q.ds4moe_dequant_q2k(out, packed[e * nb:(e + 1) * nb], 1, rows, cols)
+            ref = oracle.dequant_f32(canon[e]).reshape(rows, cols)
+            assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), (e, rows)
+
+
+def test_dequant_special_blocks():
+    """Hand-built blocks (negative and subnormal d, zero block) survive pack+dequant."""
+    q = _q()
+    blk = np.zeros((16, 84), np.uint8)
+    rng = np.random.default_rng(5)
+    blk[:, :80] = rng.integers(0, 256, size=(16, 80))
+    blk[0, 80:84] = [0x01, 0x00, 0x00, 0x00]          # subnormal d, zero dmin
+    blk[1, 80:84] = [0x00, 0xBC, 0x00, 0x38]          # d = -1, dmin = 0.5
+    blk[2, :] = 0                                     # all-zero block
+    blk[3, 80:84] = [0xFF, 0x7B, 0xFF, 0x7B]          # largest finite d, dmin
+    canon = blk.reshape(1, -1)                        # one matrix 16 x 256
+    dev = torch.device("cuda:0")
+    src = torch.from_numpy(canon).to(dev)
+    packed = torch.empty(q.ds4moe_packed_bytes(16, 256), dtype=torch.uint8, device=dev)
+    q.ds4moe_pack_q2k(packed, src, 1, 16, 256)
+    out = torch.empty(16, 256, dtype=torch.float32, device=dev)
+    q.ds4moe_dequant_q2k(out, packed, 1, 16, 256)
+    ref = oracle.dequant_f32(canon).reshape(16, 256)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ tiny layer
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_tiny_layer(tiny, mode):
+    q = _q()
+    L, dl = tiny
+    x = dl.x_tensor(L.x)
+    bufs = dl.routing_buffers(L.T)
+    m = q.MODE_DECODE if mode == "decode" else q.MODE_PREFILL
+    y = dl.forward(x, m, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"tiny/{mode}")
+    ref, _, _ = oracle.layer_inputs(L)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"tiny {mode}: per-token rel err {err:.3e}")
+    assert err <= TOL_Y
+
+
+def test_tiny_route_only(tiny):
+    L, dl = tiny
+    bufs = dl.route(dl.x_tensor(L.x))
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label="tiny/route")
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 17, 63, 64, 65, 100, 257])
+def test_tiny_ragged_prefill(tiny, T):
+    q = _q()
+    L0, dl = tiny
+    L = synth.make_layer("tiny", T=T)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"ragged T={T}")
+    ref, _, _ = oracle.layer_inputs(L)
+    assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
+
+
+def test_tiny_all_tokens_one_expert(tiny):
+    """A large bias on expert 3 sends every token there (several tiles), most
+    experts get none."""
+    q = _q()
+    L0, dl0 = tiny
+    T = 200
+    L = synth.make_layer("tiny", T=T)
+    bias = np.zeros(L.wl.E, np.float32)
+    bias[3] = 100.0
+    L.router_bias = bias
+    dl = q.DeviceLayer(L.wl.H, L.wl.I, L.wl.E, L.wl.k, 0, q.DS4MOE_F32, q.DS4MOE_F32)
+    dl.set_router(L.router_w, bias)
+    dl.gate, dl.up, dl.down = dl0.gate, dl0.up, dl0.down
+    for m in (q.MODE_PREFILL,):
+        bufs = dl.routing_buffers(T)
+        y = dl.forward(dl.x_tensor(L.x), m, routing=bufs)
+        torch.cuda.synchronize()
+        idx = check_routing(bufs, L, label="one-expert")
+        assert np.all(idx[:, 0] == 3)
+        ref, _, _ = oracle.layer_inputs(L)
+        assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
+
+
+@pytest.mark.parametrize("k,E", [(1, 8), (8, 8)])
+def test_tiny_topk_extremes(k, E):
+    """k = 1 (weight exactly 1) and k = E (every expert selected)."""
+    q = _q()
+    wl = synth.Workload("tiny_k", 0, T=33, H=256, E=E, I=128, k=k, x_dtype="f32", router_dtype="f32",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(L.T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"k={k}")
+    if k == 1:
+        assert np.all(bufs["topk_w"].cpu().numpy() == 1.0)
+    ref, _, _ = oracle.layer_inputs(L)
+    assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
+
+
+def test_prefill_zero_tokens_is_noop(tiny):
+    q = _q()
+    L, dl = tiny
+    y = torch.full((1, L.wl.H), 7.0, device=dl.device)
+    x = dl.x_tensor(L.x[:1])
+    ws = dl.workspace(1, q.MODE_PREFILL)
+    q.ds4moe_forward_prefill(dl.dims, dl.weights(), x, 0, y, None, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+# ------------------------------------------------------------------ full size
+
+
+def _full_case(full, name, mode, sample=None, shared=None):
+    q = _q()
+    L0, dl = shared if shared is not None else full
+    L = synth.derive(L0, name)
+    x = dl.x_tensor(L.x)
+    bufs = dl.routing_buffers(L.T)
+    m = q.MODE_DECODE if mode == "decode" else q.MODE_PREFILL
+    y = dl.forward(x, m, routing=bufs)
+    torch.cuda.synchronize()
+    idx = check_routing(bufs, L, label=name)
+    toks = list(range(L.T)) if sample is None else sample(idx)
+    ref, ridx, _ = oracle.layer_inputs(L, tokens=toks)
+    assert np.array_equal(ridx, idx[toks])
+    err = per_token_err(y.cpu().numpy()[toks], ref)
+    print(f"{name}: {len(toks)} tokens checked, per-token rel err {err:.3e}")
+    assert err <= TOL_Y
+    return y, idx
+
+
+def test_full_decode1(full):
+    _full_case(full, "decode1", "decode")
+
+
+def test_full_decode16(full):
+    _, idx = _full_case(full, "decode16", "decode")
+    d = len(np.unique(idx))
+    print(f"decode16: {d} distinct experts")
+    assert 40 <= d <= 128
+
+
+def _sample_tokens(idx, n=12):
+    """First, last, and tokens routed to the most and least loaded experts."""
+    T = idx.shape[0]
+    counts = np.bincount(idx.reshape(-1), minlength=256)
+    hot = int(np.argmax(counts))
+    cold = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    toks = {0, T - 1, T // 2}
+    toks |= set(np.where((idx == hot).any(axis=1))[0][:4].tolist())
+    toks |= set(np.where((idx == cold).any(axis=1))[0][:4].tolist())
+    rng = np.random.default_rng(T)
+    toks |= set(rng.integers(0, T, size=n).tolist())
+    return sorted(toks)
+
+
+def test_full_prefill_sampled(full):
+    _full_case(full, "prefill", "prefill", sample=_sample_tokens)
+
+
+def test_full_skewed_sampled(full, full_shared):
+    y, idx = _full_case(full, "skewed", "prefill", sample=_sample_tokens, shared=full_shared)
+    counts = np.bincount(idx.reshape(-1), minlength=256)
+    print(f"skewed loads: min {counts.min()} median {int(np.median(counts))} max {counts.max()}")
+    assert counts.max() > 1000
+
+
+def test_full_deterministic(full):
+    q = _q()
+    L0, dl = full
+    L = synth.derive(L0, "prefill", T=512)
+    x = dl.x_tensor(L.x)
+    y1 = dl.forward(x, q.MODE_PREFILL).clone()
+    y2 = dl.forward(x, q.MODE_PREFILL).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    L = synth.derive(L0, "decode16")
+    x = dl.x_tensor(L.x)
+    y1 = dl.forward(x, q.MODE_DECODE).clone()
+    y2 = dl.forward(x, q.MODE_DECODE).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_full_route_only_matches_forward(full):
+    L0, dl = full
+    L = synth.derive(L0, "prefill")
+    rt = dl.route(dl.x_tensor(L.x))
+    torch.cuda.synchronize()
+    check_routing(rt, L, label="route-only prefill")
