@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X: tokens/s per layer plus the roofline
+fraction of the dominant kernel, with the CPU oracle timed beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode1|decode16|prefill|skewed|tiny|all]
+
+A step is one whole layer call (router -> top-k -> permute -> gate/up+SwiGLU ->
+down -> combine [+ shared expert]) on one batch of synthetic tokens whose
+inputs are already resident in HBM.  Decode workloads rotate over several
+copies of the layer's packed experts and over fresh token batches so the
+2.1 GB of expert weights stream from HBM rather than from the 256 MB
+Infinity Cache.  Prints one JSON line per workload (default: decode1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
+
+DEFAULTS = {  # workload: (steps, warmup, layer copies, token batches)
+    "tiny": (2000, 100, 1, 16),
+    "decode1": (2000, 200, 4, 64),
+    "decode16": (1000, 100, 4, 64),
+    "prefill": (50, 5, 1, 4),
+    "skewed": (20, 3, 1, 2),
+}
+
+
+def cpu_baseline(L, budget_s: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    import synth  # noqa: F401
+    T = L.T
+    t0 = time.perf_counter()
+    oracle.layer_inputs(L, tokens=[0])
+    one = time.perf_counter() - t0
+    n = int(max(1, min(T, budget_s / max(one, 1e-3))))
+    toks = list(range(n))
+    t0 = time.perf_counter()
+    oracle.layer_inputs(L, tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of the {T} tokens of one {L.wl.name} batch, full layer "
+                      f"(fp64 C, OpenMP), {dt:.1f} s"}
+
+
+def run_workload(name: str, args) -> dict:
+    import torch
+
+    import quantized_routed_moe_router_amd as q
+    from quantized_routed_moe_router_amd import binding as B
+    import synth
+
+    steps, warmup, n_layers, n_batches = DEFAULTS[name]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+    n_layers = args.layers if args.layers is not None else n_layers
+    wl = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+
+    t0 = time.perf_counter()
+    base = synth.make_layer("prefill" if wl.layer_id == 1 else name, seed=args.seed)
+    L = synth.derive(base, name) if wl.layer_id == 1 else base
+    dl = q.from_layer_inputs(L, dev)
+    layers = [dl.weights()]
+    copies = []
+    for i in range(1, n_layers):  # same bytes at other HBM addresses
+        g, u, d = dl.gate.clone(), dl.up.clone(), dl.down.clone()
+        copies.append((g, u, d))
+        layers.append(dl.weights(g, u, d))
+    xs = [dl.x_tensor(synth.make_x(wl, args.seed, L.T, batch=b)) for b in range(n_batches)]
+    T = L.T
+    mode = q.MODE_DECODE if T <= 16 else q.MODE_PREFILL
+    y = torch.empty(T, wl.H, dtype=torch.float32, device=dev)
+    ws = dl.workspace(T, mode)
+    fwd = q.ds4moe_forward_decode if mode == q.MODE_DECODE else q.ds4moe_forward_prefill
+    stream = torch.cuda.current_stream(dev)
+    setup_s = time.perf_counter() - t0
+
+    # experts hit by each batch (for the algorithmic bytes of decode steps)
+    distinct = []
+    for b in range(n_batches):
+        rt = dl.route(xs[b])
+        distinct.append(int((rt["counts"] > 0).sum().item()))
+
+    def step(i, events=None):
+        w = layers[i % n_layers]
+        x = xs[i % n_batches]
+        if events is None:
+            fwd(dl.dims, w, x, T, y, None, ws, ws.numel(), stream)
+        else:
+            B.ds4moe_forward_timed(mode, dl.dims, w, x, T, y, None, ws, ws.numel(), events, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+
+    # second pass with stage events: per-kernel durations on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(B.N_STAGE_EVENTS)] for _ in range(steps)]
+    for row in ev:  # torch creates the underlying hipEvent on first record
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    elapsed_ev = time.perf_counter() - t2
+    stage_ms = {s: 0.0 for s in B.STAGES}
+    per_step_gateup = []
+    for i in range(steps):
+        for j, s in enumerate(B.STAGES):
+            dt = ev[i][j].elapsed_time(ev[i][j + 1])
+            stage_ms[s] += dt
+            if s == "gateup":
+                per_step_gateup.append(dt)
+    stage_ms = {s: v / steps for s, v in stage_ms.items()}
+
+    H, I, E, k = wl.H, wl.I, wl.E, wl.k
+    gu_bytes = dl.gu_bytes
+    if mode == q.MODE_DECODE:
+        # gate + up packed bytes of the experts each step touches
+        gu_total = sum(2 * gu_bytes * distinct[i % n_batches] for i in range(steps))
+        achieved = gu_total / (sum(per_step_gateup) * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_gateup", "algorithmic_bytes_per_launch": gu_total / steps}
+        layer_bytes = np.mean([d * 3 * gu_bytes for d in distinct]) + E * H * 2 + T * H * (2 + 4)
+        layer = {"bytes_per_step": float(layer_bytes),
+                 "achieved_GBs": round(layer_bytes / (elapsed / steps) / 1e9, 1),
+                 "frac": round(layer_bytes / (elapsed / steps) / 1e9 / HBM_PEAK_GBS, 4)}
+    else:
+        flops = 2.0 * T * k * 2 * H * I
+        achieved = flops / (stage_ms["gateup"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": None,
+                "kernel": "k_gateup", "algorithmic_flops_per_launch": flops}
+        lf = 2.0 * T * k * 3 * H * I + (2.0 * T * 3 * H * wl.Is if wl.Is else 0.0)
+        layer = {"flops_per_step": lf, "achieved_TFs": round(lf / (elapsed / steps) / 1e12, 2),
+                 "frac": round(lf / (elapsed / steps) / 1e12 / MFMA_F16_PEAK_TFS, 4)}
+
+    out = {
+        "metric": "MoE-layer tokens/s", "value": round(T * steps / elapsed, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(elapsed / steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": name, "T": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
+                   "shared_inter": wl.Is, "layer_copies": n_layers, "token_batches": n_batches,
+                   "seed": args.seed, "distinct_experts_mean": float(np.mean(distinct))},
+        "roofline": roof,
+        "layer_roofline": layer,
+        "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "ms_per_step_with_stage_events": round(elapsed_ev / steps * 1e3, 5),
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    del copies, xs, dl
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode1", choices=[*DEFAULTS, "all"])
+    ap.add_argument("--layers", type=int, default=None, help="rotated copies of the packed experts")
+    ap.add_argument("--seed", type=int, default=20261203)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is benchmarked on a single MI355X "
+              "(no sharding, no collectives); run it without --gpus or with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    names = [n for n in DEFAULTS if n != "tiny"] if args.workload == "all" else [args.workload]
+    for n in names:
+        print(json.dumps(run_workload(n, args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

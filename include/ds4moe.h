@@ -171,6 +171,21 @@ int ds4moe_forward_decode(const ds4moe_dims *dims, const ds4moe_weights *w, cons
 int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
                            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream);
 
+/* Number of events ds4moe_forward_timed records. */
+#define DS4MOE_N_STAGE_EVENTS 7
+
+/* For measurement: the same work as ds4moe_forward_decode (mode
+ * DS4MOE_MODE_DECODE) or ds4moe_forward_prefill (DS4MOE_MODE_PREFILL), which
+ * additionally records the caller's events (hipEvent_t, created by the caller,
+ * host array of DS4MOE_N_STAGE_EVENTS handles) on `stream` at the stage
+ * boundaries: [0] before the router, [1] after the logits, [2] after top-k,
+ * activation preparation and permutation, [3] after gate/up + SwiGLU, [4]
+ * after down, [5] after the shared expert, [6] after the combine.  Any other
+ * mode returns DS4MOE_ERR_SHAPE; a NULL events array DS4MOE_ERR_NULL. */
+int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
+                         float *y, ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *const *events,
+                         void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *ds4moe_status_str(int status);
 

@@ -29,7 +29,9 @@ MODE_ROUTE, MODE_DECODE, MODE_PREFILL = 0, 1, 2
 
 EXPORTED = ("ds4moe_packed_bytes", "ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_workspace_bytes",
             "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_status_str",
-            "ds4moe_version")
+            "ds4moe_version", "ds4moe_forward_timed")
+N_STAGE_EVENTS = 7
+STAGES = ("router", "route", "gateup", "down", "shared", "combine")
 
 
 class Dims(ctypes.Structure):
@@ -61,7 +63,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_routed_moe_router_amd.build`")
+            raise ImportError(f"{LIB_PATH} is not built; run `python quantized_routed_moe_router_amd/build.py`")
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         L.ds4moe_packed_bytes.argtypes = [I64, I64]
@@ -73,11 +75,12 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_route.argtypes = [P, P, P, I32, P, P, ctypes.c_size_t, P]
         L.ds4moe_forward_decode.argtypes = [P, P, P, I32, P, P, P, ctypes.c_size_t, P]
         L.ds4moe_forward_prefill.argtypes = [P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+        L.ds4moe_forward_timed.argtypes = [I32, P, P, P, I32, P, P, P, ctypes.c_size_t, P, P]
         L.ds4moe_status_str.argtypes = [ctypes.c_int]
         L.ds4moe_status_str.restype = ctypes.c_char_p
         L.ds4moe_version.restype = ctypes.c_int
         for fn in ("ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_route", "ds4moe_forward_decode",
-                   "ds4moe_forward_prefill"):
+                   "ds4moe_forward_prefill", "ds4moe_forward_timed"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -156,3 +159,14 @@ def ds4moe_forward_prefill(dims: Dims, weights: Weights, x, T: int, y, routing: 
     r = ctypes.byref(routing) if routing is not None else None
     _check(lib().ds4moe_forward_prefill(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(y), r,
                                         _ptr(ws), ws_bytes, _stream(stream)), "forward_prefill")
+
+
+def ds4moe_forward_timed(mode: int, dims: Dims, weights: Weights, x, T: int, y, routing: Routing | None, ws,
+                         ws_bytes: int, events, stream=None) -> None:
+    """events: N_STAGE_EVENTS torch.cuda.Event objects (or raw hipEvent_t ints)."""
+    raw = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events]
+    assert len(raw) == N_STAGE_EVENTS
+    arr = (ctypes.c_void_p * N_STAGE_EVENTS)(*raw)
+    r = ctypes.byref(routing) if routing is not None else None
+    _check(lib().ds4moe_forward_timed(mode, ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(y), r,
+                                      _ptr(ws), ws_bytes, arr, _stream(stream)), "forward_timed")

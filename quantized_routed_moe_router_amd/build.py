@@ -1,6 +1,6 @@
 """Build libds4moe.so in-tree with hipcc for gfx950.
 
-    python -m quantized_routed_moe_router_amd.build
+    python quantized_routed_moe_router_amd/build.py   (does not import the package)
 """
 from __future__ import annotations
 

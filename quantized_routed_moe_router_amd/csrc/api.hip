@@ -149,12 +149,17 @@ Ptrs routing_ptrs(void *ws, const Layout &L, const ds4moe_routing *r) {
 }
 
 int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
-            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream, int mode) {
+            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream, int mode,
+            void *const *events = nullptr) {
   Layout L;
   int st = check_call(dims, w, x, T, y, true, route_out, ws, ws_bytes, mode, &L);
   if (st || T == 0) return st;
   const ds4moe_dims &d = *dims;
   hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  };
+  TRY(mark(0));
   const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
   const Ptrs p = routing_ptrs(ws, L, route_out);
   const bool small = mode == DS4MOE_MODE_DECODE;
@@ -163,6 +168,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     TRY(launch_router_small(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
   else
     TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
+  TRY(mark(1));
 
   XPrep xp{x, xb, at<_Float16>(ws, L.x16), at<_Float16>(ws, L.xs_hi), at<_Float16>(ws, L.xs_lo)};
   RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, at<int32_t>(ws, L.pos),
@@ -173,6 +179,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     TRY(launch_topk(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, s));
     TRY(launch_permute(T, d.n_experts, d.top_k, ro, s));
   }
+  TRY(mark(2));
 
   GemmArgs ga{};
   ga.gate = (const uint8_t *)w->gate;
@@ -195,7 +202,9 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.hs_lo = at<_Float16>(ws, L.hs_lo);
   ga.yp = at<float>(ws, L.yp);
   TRY(launch_gateup(ga, L.max_tiles, small, s));
+  TRY(mark(3));
   TRY(launch_down(ga, L.max_tiles, small, s));
+  TRY(mark(4));
 
   float *ysh = nullptr;
   if (d.shared_inter > 0) {
@@ -205,7 +214,9 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
                              d.shared_inter, s));
     TRY(launch_shared_down((const uint16_t *)w->sh_down, hsh, ysh, T, d.hidden, d.shared_inter, s));
   }
+  TRY(mark(5));
   TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s));
+  TRY(mark(6));
   return DS4MOE_OK;
 }
 
@@ -290,6 +301,16 @@ int ds4moe_forward_decode(const ds4moe_dims *dims, const ds4moe_weights *w, cons
 int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
                            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream) {
   return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, DS4MOE_MODE_PREFILL);
+}
+
+int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
+                         float *y, ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *const *events,
+                         void *stream) {
+  if (mode != DS4MOE_MODE_DECODE && mode != DS4MOE_MODE_PREFILL) return DS4MOE_ERR_SHAPE;
+  if (!events) return DS4MOE_ERR_NULL;
+  for (int i = 0; i < DS4MOE_N_STAGE_EVENTS; ++i)
+    if (!events[i]) return DS4MOE_ERR_NULL;
+  return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, mode, events);
 }
 
 }  // extern "C"
