@@ -107,8 +107,8 @@ def run_workload(name: str, args) -> dict:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t1
 
-    # second pass with stage events: per-kernel durations on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(B.N_STAGE_EVENTS)] for _ in range(steps)]
+    # second pass with per-kernel events stamped by each kernel's own dispatch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * B.N_TIMED_KERNELS)] for _ in range(steps)]
     for row in ev:  # torch creates the underlying hipEvent on first record
         for e in row:
             e.record(stream)
@@ -118,11 +118,11 @@ def run_workload(name: str, args) -> dict:
         step(i, ev[i])
     torch.cuda.synchronize()
     elapsed_ev = time.perf_counter() - t2
-    stage_ms = {s: 0.0 for s in B.STAGES}
+    stage_ms = {s: 0.0 for s in B.KERNEL_SLOTS}
     per_step_gateup = []
     for i in range(steps):
-        for j, s in enumerate(B.STAGES):
-            dt = ev[i][j].elapsed_time(ev[i][j + 1])
+        for j, s in enumerate(B.KERNEL_SLOTS):
+            dt = ev[i][2 * j].elapsed_time(ev[i][2 * j + 1])
             stage_ms[s] += dt
             if s == "gateup":
                 per_step_gateup.append(dt)
@@ -161,8 +161,8 @@ def run_workload(name: str, args) -> dict:
                    "seed": args.seed, "distinct_experts_mean": float(np.mean(distinct))},
         "roofline": roof,
         "layer_roofline": layer,
-        "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()},
-        "ms_per_step_with_stage_events": round(elapsed_ev / steps * 1e3, 5),
+        "kernel_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "ms_per_step_with_kernel_events": round(elapsed_ev / steps * 1e3, 5),
         "setup_s": round(setup_s, 1),
     }
     if not args.no_cpu_baseline:

@@ -171,17 +171,20 @@ int ds4moe_forward_decode(const ds4moe_dims *dims, const ds4moe_weights *w, cons
 int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
                            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream);
 
-/* Number of events ds4moe_forward_timed records. */
-#define DS4MOE_N_STAGE_EVENTS 7
+/* Kernel slots timed by ds4moe_forward_timed. */
+#define DS4MOE_N_TIMED_KERNELS 8
 
 /* For measurement: the same work as ds4moe_forward_decode (mode
- * DS4MOE_MODE_DECODE) or ds4moe_forward_prefill (DS4MOE_MODE_PREFILL), which
- * additionally records the caller's events (hipEvent_t, created by the caller,
- * host array of DS4MOE_N_STAGE_EVENTS handles) on `stream` at the stage
- * boundaries: [0] before the router, [1] after the logits, [2] after top-k,
- * activation preparation and permutation, [3] after gate/up + SwiGLU, [4]
- * after down, [5] after the shared expert, [6] after the combine.  Any other
- * mode returns DS4MOE_ERR_SHAPE; a NULL events array DS4MOE_ERR_NULL. */
+ * DS4MOE_MODE_DECODE) or ds4moe_forward_prefill (DS4MOE_MODE_PREFILL); each
+ * kernel is launched with a start/stop event pair that its own dispatch
+ * stamps (hipExtLaunchKernelGGL), so event elapsed times are kernel
+ * durations.  `events` is a host array of 2*DS4MOE_N_TIMED_KERNELS hipEvent_t
+ * created by the caller; pair i = (events[2i], events[2i+1]) times slot i:
+ * 0 router logits, 1 top-k (decode: top-k + permutation), 2 permutation
+ * (prefill), 3 gate/up + SwiGLU, 4 down, 5 shared gate/up, 6 shared down,
+ * 7 combine.  A slot with no kernel in the call gets both events recorded
+ * back to back.  Any other mode returns DS4MOE_ERR_SHAPE; a NULL array or
+ * event DS4MOE_ERR_NULL. */
 int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
                          float *y, ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *const *events,
                          void *stream);

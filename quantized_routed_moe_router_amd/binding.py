@@ -30,8 +30,8 @@ MODE_ROUTE, MODE_DECODE, MODE_PREFILL = 0, 1, 2
 EXPORTED = ("ds4moe_packed_bytes", "ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_workspace_bytes",
             "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_status_str",
             "ds4moe_version", "ds4moe_forward_timed")
-N_STAGE_EVENTS = 7
-STAGES = ("router", "route", "gateup", "down", "shared", "combine")
+N_TIMED_KERNELS = 8
+KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine")
 
 
 class Dims(ctypes.Structure):
@@ -163,10 +163,11 @@ def ds4moe_forward_prefill(dims: Dims, weights: Weights, x, T: int, y, routing: 
 
 def ds4moe_forward_timed(mode: int, dims: Dims, weights: Weights, x, T: int, y, routing: Routing | None, ws,
                          ws_bytes: int, events, stream=None) -> None:
-    """events: N_STAGE_EVENTS torch.cuda.Event objects (or raw hipEvent_t ints)."""
+    """events: 2*N_TIMED_KERNELS torch.cuda.Event objects (already created) or raw
+    hipEvent_t ints; pair i times kernel slot KERNEL_SLOTS[i]."""
     raw = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events]
-    assert len(raw) == N_STAGE_EVENTS
-    arr = (ctypes.c_void_p * N_STAGE_EVENTS)(*raw)
+    assert len(raw) == 2 * N_TIMED_KERNELS
+    arr = (ctypes.c_void_p * (2 * N_TIMED_KERNELS))(*raw)
     r = ctypes.byref(routing) if routing is not None else None
     _check(lib().ds4moe_forward_timed(mode, ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(y), r,
                                       _ptr(ws), ws_bytes, arr, _stream(stream)), "forward_timed")

@@ -31,8 +31,9 @@ int validate_dims(const ds4moe_dims *d) {
 }
 
 struct Layout {
-  size_t logits, idx, w, counts, offsets, perm, pos, tiles, ntiles;
-  size_t x16, xs_hi, xs_lo, h, hs_hi, hs_lo, yp, hsh, ysh;
+  size_t logits, part, idx, w, counts, offsets, perm, pos, tiles, ntiles;
+  size_t x16, xs_hi, xs_lo, h, hs_hi, hs_lo, yp, hsh, ysh, zeros;
+  int nzeros;
   size_t total;
   int tile_n, max_tiles, Ipad;
 };
@@ -51,6 +52,7 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
   L.tile_n = mode == DS4MOE_MODE_PREFILL ? kTilePrefill : kTileDecode;
   L.max_tiles = (int)(A / L.tile_n + (A < E ? A : E));
   L.logits = take(sizeof(float) * T * E);
+  L.part = T <= 16 ? take(sizeof(double) * (H / 256) * T * E) : 0;
   L.idx = take(sizeof(int32_t) * A);
   L.w = take(sizeof(float) * A);
   L.counts = take(sizeof(int32_t) * E);
@@ -67,6 +69,8 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
     L.hs_hi = take(2 * A * (L.Ipad / 16));
     L.hs_lo = take(2 * A * (L.Ipad / 16));
     L.yp = take(sizeof(float) * A * H);
+    L.nzeros = (int)(H > L.Ipad ? H : L.Ipad);
+    L.zeros = take(2 * (size_t)L.nzeros);
     if (Is > 0) {
       L.hsh = take(2 * T * Is);
       L.ysh = take(sizeof(float) * T * H);
@@ -148,38 +152,44 @@ Ptrs routing_ptrs(void *ws, const Layout &L, const ds4moe_routing *r) {
   return p;
 }
 
+// kernel slots of ds4moe_forward_timed
+enum { SL_ROUTER = 0, SL_ROUTE, SL_PERMUTE, SL_GATEUP, SL_DOWN, SL_SHGATEUP, SL_SHDOWN, SL_COMBINE, SL_N };
+
 int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
             ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream, int mode,
-            void *const *events = nullptr) {
+            const Timing *tms = nullptr) {
   Layout L;
   int st = check_call(dims, w, x, T, y, true, route_out, ws, ws_bytes, mode, &L);
   if (st || T == 0) return st;
   const ds4moe_dims &d = *dims;
   hipStream_t s = (hipStream_t)stream;
-  auto mark = [&](int i) -> hipError_t {
-    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  bool used[SL_N] = {};
+  auto tm = [&](int slot) -> const Timing * {
+    if (!tms) return nullptr;
+    used[slot] = true;
+    return tms + slot;
   };
-  TRY(mark(0));
   const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
   const Ptrs p = routing_ptrs(ws, L, route_out);
   const bool small = mode == DS4MOE_MODE_DECODE;
 
-  if (T <= 16)
-    TRY(launch_router_small(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
-  else
-    TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
-  TRY(mark(1));
-
   XPrep xp{x, xb, at<_Float16>(ws, L.x16), at<_Float16>(ws, L.xs_hi), at<_Float16>(ws, L.xs_lo)};
   RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, at<int32_t>(ws, L.pos),
-              at<TileT>(ws, L.tiles), at<int32_t>(ws, L.ntiles), L.tile_n};
-  if (small) {
-    TRY(launch_route_small(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, s));
+              at<TileT>(ws, L.tiles), at<int32_t>(ws, L.ntiles), L.tile_n, at<_Float16>(ws, L.zeros), L.nzeros};
+  if (T <= 16)
+    TRY(launch_router_sliced(x, xb, w->router_w, wb, at<double>(ws, L.part), T, d.n_experts, d.hidden, &xp, s,
+                             tm(SL_ROUTER)));
+  else
+    TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s,
+                            tm(SL_ROUTER)));
+
+  if (T <= 16) {
+    TRY(launch_route_small(at<double>(ws, L.part), d.hidden / 256, w->router_bias, p.logits, T, d.n_experts,
+                           d.top_k, ro, s, tm(SL_ROUTE)));
   } else {
-    TRY(launch_topk(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, s));
-    TRY(launch_permute(T, d.n_experts, d.top_k, ro, s));
+    TRY(launch_topk(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, s, tm(SL_ROUTE)));
+    TRY(launch_permute(T, d.n_experts, d.top_k, ro, s, tm(SL_PERMUTE)));
   }
-  TRY(mark(2));
 
   GemmArgs ga{};
   ga.gate = (const uint8_t *)w->gate;
@@ -201,22 +211,27 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.hs_hi = at<_Float16>(ws, L.hs_hi);
   ga.hs_lo = at<_Float16>(ws, L.hs_lo);
   ga.yp = at<float>(ws, L.yp);
-  TRY(launch_gateup(ga, L.max_tiles, small, s));
-  TRY(mark(3));
-  TRY(launch_down(ga, L.max_tiles, small, s));
-  TRY(mark(4));
+  ga.zeros = at<_Float16>(ws, L.zeros);
+  TRY(launch_gateup(ga, L.max_tiles, small, s, tm(SL_GATEUP)));
+  TRY(launch_down(ga, L.max_tiles, small, s, tm(SL_DOWN)));
 
   float *ysh = nullptr;
   if (d.shared_inter > 0) {
     _Float16 *hsh = at<_Float16>(ws, L.hsh);
     ysh = at<float>(ws, L.ysh);
     TRY(launch_shared_gateup((const uint16_t *)w->sh_gate, (const uint16_t *)w->sh_up, xp.x16, hsh, T, d.hidden,
-                             d.shared_inter, s));
-    TRY(launch_shared_down((const uint16_t *)w->sh_down, hsh, ysh, T, d.hidden, d.shared_inter, s));
+                             d.shared_inter, s, tm(SL_SHGATEUP)));
+    TRY(launch_shared_down((const uint16_t *)w->sh_down, hsh, ysh, T, d.hidden, d.shared_inter, s,
+                           tm(SL_SHDOWN)));
   }
-  TRY(mark(5));
-  TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s));
-  TRY(mark(6));
+  TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s, tm(SL_COMBINE)));
+  if (tms) {  // slots without a kernel in this call: empty intervals
+    for (int i = 0; i < SL_N; ++i) {
+      if (used[i]) continue;
+      TRY(hipEventRecord(tms[i].start, s));
+      TRY(hipEventRecord(tms[i].stop, s));
+    }
+  }
   return DS4MOE_OK;
 }
 
@@ -283,11 +298,15 @@ int ds4moe_route(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x
   hipStream_t s = (hipStream_t)stream;
   const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
   const Ptrs p = routing_ptrs(ws, L, out);
-  if (T <= 16)
-    TRY(launch_router_small(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
-  else
-    TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
-  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, kTileDecode};
+  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, kTileDecode, nullptr, 0};
+  if (T <= 16) {
+    TRY(launch_router_sliced(x, xb, w->router_w, wb, at<double>(ws, L.part), T, d.n_experts, d.hidden, nullptr,
+                             s));
+    TRY(launch_route_small(at<double>(ws, L.part), d.hidden / 256, w->router_bias, p.logits, T, d.n_experts,
+                           d.top_k, ro, s));
+    return DS4MOE_OK;
+  }
+  TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
   TRY(launch_topk(p.logits, T, d.n_experts, d.top_k, d.hidden, nullptr, ro, s));
   TRY(launch_permute(T, d.n_experts, d.top_k, ro, s));
   return DS4MOE_OK;
@@ -306,11 +325,16 @@ int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, con
 int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
                          float *y, ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *const *events,
                          void *stream) {
+  static_assert(SL_N == DS4MOE_N_TIMED_KERNELS, "kernel slots");
   if (mode != DS4MOE_MODE_DECODE && mode != DS4MOE_MODE_PREFILL) return DS4MOE_ERR_SHAPE;
   if (!events) return DS4MOE_ERR_NULL;
-  for (int i = 0; i < DS4MOE_N_STAGE_EVENTS; ++i)
-    if (!events[i]) return DS4MOE_ERR_NULL;
-  return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, mode, events);
+  Timing tms[SL_N];
+  for (int i = 0; i < SL_N; ++i) {
+    if (!events[2 * i] || !events[2 * i + 1]) return DS4MOE_ERR_NULL;
+    tms[i].start = (hipEvent_t)events[2 * i];
+    tms[i].stop = (hipEvent_t)events[2 * i + 1];
+  }
+  return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, mode, tms);
 }
 
 }  // extern "C"

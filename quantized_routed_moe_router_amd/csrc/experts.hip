@@ -308,6 +308,182 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a, int nrb) {
   }
 }
 
+// ------------------------------------------------------------------ decode GEMV
+// Small batches (<= 16 tokens per expert): bandwidth-bound weight streaming.
+// Workgroup = one tile x one 16-row tile (of gate and up, or of down); its 4
+// waves split the super-blocks of the reduction dimension, each wave issues
+// the loads of a whole batch of SBW super-blocks before any arithmetic (so
+// each wave keeps up to SBW*1344*matrices bytes in flight), and the four
+// partial sums are added through LDS in wave order.
+template <int SBW>
+__global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
+  const int tile_id = blockIdx.x / n_rt;
+  const int rt = blockIdx.x - tile_id * n_rt;
+  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
+  const TileT tl = a.tiles[tile_id];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nsb = a.H >> 8;
+  const int per = (nsb + WAVES - 1) / WAVES;
+  const int sb0 = wave * per, sb1 = min(nsb, sb0 + per);
+  const bool valid = r16 < tl.n;
+  const int pidx = tl.p0 + (valid ? r16 : 0);
+  const int tok = a.perm[pidx] / a.k;
+  // lanes without a token read zeros instead of selecting per step
+  const half_t *xrow = valid ? a.x16 + (size_t)tok * a.H : a.zeros;
+  const half_t *xsrow = valid ? ((g >> 1) ? a.xs_lo : a.xs_hi) + (size_t)tok * (a.H >> 4) + 8 * (g & 1) : a.zeros;
+  const uint8_t *G = a.gate + (size_t)tl.e * a.gu_bytes + (size_t)rt * nsb * DS4_UNIT_BYTES;
+  const uint8_t *U = a.up + (size_t)tl.e * a.gu_bytes + (size_t)rt * nsb * DS4_UNIT_BYTES;
+  f4 yg = (f4){0.f, 0.f, 0.f, 0.f}, yu = yg;
+  for (int b0 = sb0; b0 < sb1; b0 += SBW) {
+    UnitRegs ug[SBW], uu[SBW];
+#pragma unroll
+    for (int i = 0; i < SBW; ++i) {
+      const int sb = min(b0 + i, sb1 - 1);
+      ug[i] = load_unit(G + (size_t)sb * DS4_UNIT_BYTES, lane);
+      uu[i] = load_unit(U + (size_t)sb * DS4_UNIT_BYTES, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < SBW; ++i) {
+      if (b0 + i >= sb1) break;
+      const int kb = (b0 + i) * 256;
+      h8 b[9];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) b[s] = load_h8(xrow + kb + 16 * (4 * (s >> 1) + g) + 8 * (s & 1));
+      b[8] = load_h8(xsrow + (b0 + i) * 16);
+      const UnitDecoded dg = decode_unit(ug[i], g);
+      const UnitDecoded du = decode_unit(uu[i], g);
+      f4 ag = (f4){0.f, 0.f, 0.f, 0.f}, au = ag;
+#define DEC_STEP(S)                                   \
+  ag = mfma16(step_frag<S>(ug[i], dg), b[S], ag);     \
+  au = mfma16(step_frag<S>(uu[i], du), b[S], au);
+      DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
+#undef DEC_STEP
+      const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
+      const f4 mg = mfma16(dg.mfrag, b[8], z);
+      const f4 mu = mfma16(du.mfrag, b[8], z);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        yg[q] = fmaf(dg.d[q], ag[q], yg[q]);
+        yg[q] = fmaf(-dg.dmin[q], mg[q], yg[q]);
+        yu[q] = fmaf(du.d[q], au[q], yu[q]);
+        yu[q] = fmaf(-du.dmin[q], mu[q], yu[q]);
+      }
+    }
+  }
+  __shared__ f4 red[2][WAVES][64];
+  red[0][wave][lane] = yg;
+  red[1][wave][lane] = yu;
+  __syncthreads();
+  if (wave != 0) return;
+  yg = red[0][0][lane];
+  yu = red[1][0][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) {
+    const f4 pg = red[0][w][lane], pu = red[1][w][lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      yg[q] += pg[q];
+      yu[q] += pu[q];
+    }
+  }
+  half_t hv[4];
+  float ssum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hv[q] = (half_t)(yg[q] / (1.0f + expf(-yg[q])) * yu[q]);
+    ssum += (float)hv[q];
+  }
+  ssum += __shfl_xor(ssum, 16);
+  ssum += __shfl_xor(ssum, 32);
+  if (valid) {
+    const int nj = a.Ipad >> 4;
+    uint2 pk;
+    __builtin_memcpy(&pk, hv, 8);
+    *reinterpret_cast<uint2 *>(a.h + (size_t)pidx * a.Ipad + rt * 16 + 4 * g) = pk;
+    if (g == 0) {
+      const half_t hi = (half_t)ssum;
+      a.hs_hi[(size_t)pidx * nj + rt] = hi;
+      a.hs_lo[(size_t)pidx * nj + rt] = (half_t)(ssum - (float)hi);
+    }
+  }
+}
+
+template <int SBW>
+__global__ __launch_bounds__(256) void k_down_dec(GemmArgs a, int n_rt) {
+  const int tile_id = blockIdx.x / n_rt;
+  const int rt = blockIdx.x - tile_id * n_rt;
+  if (tile_id >= *a.ntiles) return;
+  const TileT tl = a.tiles[tile_id];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nsb = a.Ipad >> 8;
+  const int nj = a.Ipad >> 4, nj_real = a.I >> 4;
+  const int per = (nsb + WAVES - 1) / WAVES;
+  const int sb0 = wave * per, sb1 = min(nsb, sb0 + per);
+  const bool valid = r16 < tl.n;
+  const int pidx = tl.p0 + (valid ? r16 : 0);
+  const half_t *hrow = valid ? a.h + (size_t)pidx * a.Ipad : a.zeros;
+  const half_t *hsrow = valid ? ((g >> 1) ? a.hs_lo : a.hs_hi) + (size_t)pidx * nj + 8 * (g & 1) : a.zeros;
+  const bool padded = a.I != a.Ipad;
+  const uint8_t *D = a.down + (size_t)tl.e * a.d_bytes + (size_t)rt * nsb * DS4_UNIT_BYTES;
+  f4 y = (f4){0.f, 0.f, 0.f, 0.f};
+  for (int b0 = sb0; b0 < sb1; b0 += SBW) {
+    UnitRegs ud[SBW];
+#pragma unroll
+    for (int i = 0; i < SBW; ++i) ud[i] = load_unit(D + (size_t)min(b0 + i, sb1 - 1) * DS4_UNIT_BYTES, lane);
+#pragma unroll
+    for (int i = 0; i < SBW; ++i) {
+      if (b0 + i >= sb1) break;
+      const int kb = (b0 + i) * 256;
+      h8 b[9];
+      if (!padded) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) b[s] = load_h8(hrow + kb + 16 * (4 * (s >> 1) + g) + 8 * (s & 1));
+        b[8] = load_h8(hsrow + (b0 + i) * 16);
+      } else {  // reduction length not a multiple of 256: columns >= I read as zero
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int col = kb + 16 * (4 * (s >> 1) + g) + 8 * (s & 1);
+          b[s] = col < a.I ? load_h8(hrow + col) : zero_h8();
+        }
+        const int j0 = (b0 + i) * 16 + 8 * (g & 1);
+        h8 v = zero_h8();
+        if (j0 < nj_real) {
+          v = load_h8(hsrow + (b0 + i) * 16);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (j0 + e >= nj_real) v[e] = (half_t)0.0f;
+        }
+        b[8] = v;
+      }
+      const UnitDecoded dd = decode_unit(ud[i], g);
+      f4 ac = (f4){0.f, 0.f, 0.f, 0.f};
+#define DEC_STEP(S) ac = mfma16(step_frag<S>(ud[i], dd), b[S], ac);
+      DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
+#undef DEC_STEP
+      const f4 mm = mfma16(dd.mfrag, b[8], (f4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        y[q] = fmaf(dd.d[q], ac[q], y[q]);
+        y[q] = fmaf(-dd.dmin[q], mm[q], y[q]);
+      }
+    }
+  }
+  __shared__ f4 red[WAVES][64];
+  red[wave][lane] = y;
+  __syncthreads();
+  if (wave != 0) return;
+  y = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) {
+    const f4 p = red[w][lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] += p[q];
+  }
+  if (valid) *reinterpret_cast<f4 *>(a.yp + (size_t)pidx * a.H + rt * 16 + 4 * g) = y;
+}
+
 // ------------------------------------------------------------------ combine
 // y[t] = sum_j w[t,j] * Yp[pos(t,j)] in rank order, then + shared output.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ yp, const int32_t *__restrict__ pos,
@@ -453,56 +629,60 @@ __global__ __launch_bounds__(256) void k_shared_down(const uint16_t *__restrict_
 }
 
 // ------------------------------------------------------------------ launchers
-// Decode batches (<= 16 tokens per expert): one n-tile per workgroup.
+// Decode batches (<= 16 tokens per expert): the split-reduction GEMV kernels.
 // Prefill: four n-tiles (64 tokens) per workgroup.
-hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream_t s) {
+hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
+  if (small) {
+    const int n_rt = a.I >> 4;
+    DS4_LAUNCH(tm, (k_gateup_dec<4>), dim3((unsigned)((int64_t)n_rt * max_tiles)), dim3(256), 0, s, a, n_rt);
+    return hipGetLastError();
+  }
   constexpr int R = 1;
   const int rows_per_wg = 16 * R * WAVES;
   const int nrb = (a.I + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
-  if (small)
-    hipLaunchKernelGGL((k_gateup<R, 1>), grid, dim3(256), 0, s, a, nrb);
-  else
-    hipLaunchKernelGGL((k_gateup<R, 4>), grid, dim3(256), 0, s, a, nrb);
+  DS4_LAUNCH(tm, (k_gateup<R, 4>), grid, dim3(256), 0, s, a, nrb);
   return hipGetLastError();
 }
 
-hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t s) {
+hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
+  if (small) {
+    const int n_rt = a.H >> 4;
+    DS4_LAUNCH(tm, (k_down_dec<2>), dim3((unsigned)((int64_t)n_rt * max_tiles)), dim3(256), 0, s, a, n_rt);
+    return hipGetLastError();
+  }
   constexpr int R = 1;
   const int rows_per_wg = 16 * R * WAVES;
   const int nrb = (a.H + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
-  if (small)
-    hipLaunchKernelGGL((k_down<R, 1>), grid, dim3(256), 0, s, a, nrb);
-  else
-    hipLaunchKernelGGL((k_down<R, 4>), grid, dim3(256), 0, s, a, nrb);
+  DS4_LAUNCH(tm, (k_down<R, 4>), grid, dim3(256), 0, s, a, nrb);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,
-                          int k, int H, hipStream_t s) {
+                          int k, int H, hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, yp, pos, w, ysh, y, T, k, H);
+  DS4_LAUNCH(tm, k_combine, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, yp, pos, w, ysh, y, T, k, H);
   return hipGetLastError();
 }
 
 hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, _Float16 *hs, int T,
-                                int H, int Is, hipStream_t s) {
+                                int H, int Is, hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
   constexpr int R = 1, NT = 4;
   const dim3 grid((Is + 16 * R * WAVES - 1) / (16 * R * WAVES), (T + 16 * NT - 1) / (16 * NT));
-  hipLaunchKernelGGL((k_shared_gateup<R, NT>), grid, dim3(256), 0, s, wg, wu, x16, hs, T, H, Is);
+  DS4_LAUNCH(tm, (k_shared_gateup<R, NT>), grid, dim3(256), 0, s, wg, wu, x16, hs, T, H, Is);
   return hipGetLastError();
 }
 
 hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, float *ysh, int T, int H, int Is,
-                              hipStream_t s) {
+                              hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
   constexpr int R = 1, NT = 4;
   const dim3 grid((H + 16 * R * WAVES - 1) / (16 * R * WAVES), (T + 16 * NT - 1) / (16 * NT));
-  hipLaunchKernelGGL((k_shared_down<R, NT>), grid, dim3(256), 0, s, wd, hs, ysh, T, H, Is);
+  DS4_LAUNCH(tm, (k_shared_down<R, NT>), grid, dim3(256), 0, s, wd, hs, ysh, T, H, Is);
   return hipGetLastError();
 }
 

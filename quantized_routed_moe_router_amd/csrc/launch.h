@@ -1,10 +1,17 @@
 // Host-side launch wrappers of the ds4moe kernels (internal to the library).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace ds4 {
+
+// Optional per-kernel timing: start/stop events stamped by the kernel's own
+// dispatch (hipExtLaunchKernelGGL); nullptr = plain launch.
+struct Timing {
+  hipEvent_t start, stop;
+};
 
 struct TileT {
   int32_t e, p0, n, pad;
@@ -30,6 +37,8 @@ struct RouteOut {
   TileT *tiles;        // [max_tiles] (nullable)
   int32_t *ntiles;     // [1]       (nullable)
   int tile_n;          // tokens per tile
+  _Float16 *zeros;     // cleared here each call: read by GEMM lanes with no token
+  int nzeros;          // halves
 };
 
 struct GemmArgs {
@@ -43,6 +52,7 @@ struct GemmArgs {
   const _Float16 *x16, *xs_hi, *xs_lo;
   _Float16 *h, *hs_hi, *hs_lo;       // [T*k, Ipad], [T*k, Ipad/16]
   float *yp;                         // [T*k, H]
+  const _Float16 *zeros;             // >= max(H, Ipad) zero halves
 };
 
 hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols,
@@ -50,28 +60,39 @@ hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t
 hipError_t launch_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols,
                           hipStream_t s);
 
-hipError_t launch_router_small(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
-                               float *logits, int T, int E, int H, hipStream_t s);
 hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
-                               float *logits, int T, int E, int H, hipStream_t s);
+                               float *logits, int T, int E, int H, hipStream_t s, const Timing *tm = nullptr);
 // wave per token: top-k, weights and (if xp != nullptr) activation preparation
 hipError_t launch_topk(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
-                       hipStream_t s);
+                       hipStream_t s, const Timing *tm = nullptr);
 // one workgroup: histogram, scan, stable permutation, tile list
-hipError_t launch_permute(int T, int E, int k, RouteOut ro, hipStream_t s);
-// one workgroup, T <= 16: top-k + activation preparation + permutation
-hipError_t launch_route_small(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
-                              hipStream_t s);
+hipError_t launch_permute(int T, int E, int k, RouteOut ro, hipStream_t s, const Timing *tm = nullptr);
+// T <= 16: logits as fp64 partial sums per 256-column slice [H/256][T][E],
+// with the activation preparation (if xp != nullptr)
+hipError_t launch_router_sliced(const void *x, bool x_bf16, const void *wr, bool w_bf16, double *part, int T,
+                                int E, int H, const XPrep *xp, hipStream_t s, const Timing *tm = nullptr);
+// one workgroup, T <= 16: slice sums + bias -> logits, top-k, permutation
+hipError_t launch_route_small(const double *part, int nslice, const float *bias, float *logits, int T, int E,
+                              int k, RouteOut ro, hipStream_t s, const Timing *tm = nullptr);
 
 // grouped GEMMs over the tile list (max_tiles = grid bound)
-hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream_t s);
-hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t s);
+hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t s, const Timing *tm = nullptr);
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,
-                          int k, int H, hipStream_t s);
+                          int k, int H, hipStream_t s, const Timing *tm = nullptr);
 // dense shared expert, bf16 weights
 hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, _Float16 *hs, int T,
-                                int H, int Is, hipStream_t s);
+                                int H, int Is, hipStream_t s, const Timing *tm = nullptr);
 hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, float *ysh, int T, int H, int Is,
-                              hipStream_t s);
+                              hipStream_t s, const Timing *tm = nullptr);
+
+// Launch `kernel` plainly, or with dispatch-stamped timing events.
+#define DS4_LAUNCH(tm, kernel, grid, block, shmem, stream, ...)                                                  \
+  do {                                                                                                         \
+    if (tm)                                                                                                    \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (tm)->start, (tm)->stop, 0, __VA_ARGS__);      \
+    else                                                                                                       \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                                     \
+  } while (0)
 
 }  // namespace ds4

@@ -27,43 +27,92 @@ __device__ __forceinline__ void load4_as_double(const void *p, int64_t idx, doub
   }
 }
 
-// ---------------------------------------------------------------- logits, T <= 16
-// One wave per expert; each lane accumulates its 4-wide column slices of H for
-// every token in fp64 (every product of two fp32 numbers is exact in fp64),
-// then a fixed butterfly sums the 64 lanes.
+// ---------------------------------------------------------------- logits, T <= 16, sliced
+// Grid (E/4 expert groups) x (H/256 column slices): wave = one expert, lane =
+// 4 columns of the slice, every token.  Partial sums of a slice are reduced
+// over the 64 lanes in lane order through LDS and stored per slice in fp64;
+// the routing kernel adds the slices in slice order.  Workgroups of expert
+// group 0 also convert their slice of x to fp16 and form the 16-column sums.
 template <bool XB, bool WB>
-__global__ __launch_bounds__(256) void k_router_small(const void *__restrict__ x, const void *__restrict__ wr,
-                                                      const float *__restrict__ bias, float *__restrict__ logits,
-                                                      int T, int E, int H) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
+__global__ __launch_bounds__(256) void k_router_sliced(const void *__restrict__ x, const void *__restrict__ wr,
+                                                       double *__restrict__ part, int T, int E, int H, XPrep xp,
+                                                       bool do_x) {
+  __shared__ double red[4][16][65];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 4 + wave;
+  const int slice = blockIdx.y;
+  const int h = slice * 256 + 4 * lane;
   double acc[16];
 #pragma unroll
   for (int t = 0; t < 16; ++t) acc[t] = 0.0;
-  for (int h = 4 * lane; h < H; h += 256) {
+  if (e < E) {
     double w4[4];
     load4_as_double<WB>(wr, (int64_t)e * H + h, w4);
+    double x4[16][4];
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (t < T) load4_as_double<XB>(x, (int64_t)t * H + h, x4[t]);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       if (t < T) {
-        double x4[4];
-        load4_as_double<XB>(x, (int64_t)t * H + h, x4);
-        acc[t] = fma(x4[0], w4[0], acc[t]);
-        acc[t] = fma(x4[1], w4[1], acc[t]);
-        acc[t] = fma(x4[2], w4[2], acc[t]);
-        acc[t] = fma(x4[3], w4[3], acc[t]);
+        acc[t] = fma(x4[t][0], w4[0], acc[t]);
+        acc[t] = fma(x4[t][1], w4[1], acc[t]);
+        acc[t] = fma(x4[t][2], w4[2], acc[t]);
+        acc[t] = fma(x4[t][3], w4[3], acc[t]);
       }
     }
   }
-  const double b = bias ? (double)bias[e] : 0.0;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
+  for (int t = 0; t < 16; ++t)
+    if (t < T) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  if (lane < T && e < E) {
+    double v = 0.0;
+    for (int l = 0; l < 64; ++l) v += red[wave][lane][l];
+    part[((int64_t)slice * T + lane) * E + e] = v;
+  }
+  if (do_x && blockIdx.x == 0) {
+    const int t = threadIdx.x >> 4, j = threadIdx.x & 15;  // token, sub-block of this slice
     if (t < T) {
-      double v = acc[t];
+      const int64_t base = (int64_t)t * H + slice * 256 + 16 * j;
+      float v[16];
+      if (xp.x_bf16) {
+        const u4 a = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(x) + base);
+        const u4 b = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(x) + base + 8);
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0) logits[(int64_t)t * E + e] = (float)(v + b);
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_bits_to_float((uint16_t)(a[i] & 0xFFFF));
+          v[2 * i + 1] = bf16_bits_to_float((uint16_t)(a[i] >> 16));
+          v[8 + 2 * i] = bf16_bits_to_float((uint16_t)(b[i] & 0xFFFF));
+          v[8 + 2 * i + 1] = bf16_bits_to_float((uint16_t)(b[i] >> 16));
+        }
+      } else {
+        const float *p = reinterpret_cast<const float *>(x) + base;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f4 a = *reinterpret_cast<const f4 *>(p + 4 * q);
+          v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
+        }
+      }
+      h8 o0, o1;
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        o0[i] = (half_t)v[i];
+        sum += (float)o0[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        o1[i] = (half_t)v[8 + i];
+        sum += (float)o1[i];
+      }
+      *reinterpret_cast<h8 *>(xp.x16 + base) = o0;
+      *reinterpret_cast<h8 *>(xp.x16 + base + 8) = o1;
+      const int nsub = H >> 4;
+      const int jj = slice * 16 + j;
+      const half_t hi = (half_t)sum;
+      xp.xs_hi[(int64_t)t * nsub + jj] = hi;
+      xp.xs_lo[(int64_t)t * nsub + jj] = (half_t)(sum - (float)hi);
     }
   }
 }
@@ -167,97 +216,119 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
+// max with the value DPP-shifted right by N lanes inside each 16-lane row
+// (lanes with no source keep their own value)
+template <int N>
+__device__ __forceinline__ uint64_t dpp_max_shr(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, 0x110 | N, 0xF, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, 0x110 | N, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
 }
 
-// Top-k for token t by one wave; writes idx/w; optional activation prep.
-__device__ void topk_token(const float *__restrict__ logits, int t, int E, int k, int H, const XPrep *xp,
-                           RouteOut ro, const void *xptr, bool x_bf16, _Float16 *x16, _Float16 *xs_hi,
-                           _Float16 *xs_lo) {
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// wave-wide max: row prefix maxima by DPP, then the four row maxima
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_shr<1>(v);
+  v = dpp_max_shr<2>(v);
+  v = dpp_max_shr<4>(v);
+  v = dpp_max_shr<8>(v);
+  uint64_t m = readlane_u64(v, 15);
+  const uint64_t m1 = readlane_u64(v, 31), m2 = readlane_u64(v, 47), m3 = readlane_u64(v, 63);
+  m = m1 > m ? m1 : m;
+  m = m2 > m ? m2 : m;
+  m = m3 > m ? m3 : m;
+  return m;
+}
+
+// Top-k of one token by one wave from the logits of experts lane + 64*i held
+// in registers; lane j < k writes rank j (index and normalised weight) to
+// global memory and, if s_idx is given, the index to LDS as well.
+__device__ void topk_select(const float lv[4], int t, int E, int k, RouteOut ro, int32_t *s_idx) {
   const int lane = threadIdx.x & 63;
   uint64_t keys[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    keys[i] = e < E ? rank_key(logits[(int64_t)t * E + e], e) : 0ull;
+    keys[i] = e < E ? rank_key(lv[i], e) : 0ull;  // live keys are never 0
   }
-  uint32_t taken = 0;
   float sel_l[16];
   int sel_e[16];
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool live = (lane + 64 * i < E) && !((taken >> i) & 1u);
-      if (live && (best == 0 || keys[i] > best)) best = keys[i];
-    }
-    // keys of live experts are never 0 (low half = ~e > 0 for e < 2^32-1)
+    for (int i = 0; i < 4; ++i) best = keys[i] > best ? keys[i] : best;
     best = wave_max_u64(best);
     const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-    if ((e & 63) == lane) taken |= 1u << (e >> 6);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (keys[i] == best) keys[i] = 0ull;  // keys are unique: removes the winner
     sel_e[j] = e;
     sel_l[j] = key_logit(best);
   }
-  // scores in rank order, normalised in fp32
-  float s[16], S = 0.0f;
+  float sc[16], S = 0.0f;
   for (int j = 0; j < k; ++j) {
-    s[j] = router_score(sel_l[j]);
-    S += s[j];
+    sc[j] = router_score(sel_l[j]);
+    S += sc[j];
   }
   for (int j = 0; j < k; ++j) {
     if (lane == j) {
       ro.idx[(int64_t)t * k + j] = sel_e[j];
-      ro.w[(int64_t)t * k + j] = s[j] / S;
+      ro.w[(int64_t)t * k + j] = sc[j] / S;
+      if (s_idx) s_idx[t * k + j] = sel_e[j];
     }
   }
-  if (x16) {
-    // x -> fp16, and per-16-element sums of the fp16 values, split hi + lo
-    const int nsub = H >> 4;
-    for (int j = lane; j < nsub; j += 64) {
-      const int64_t base = (int64_t)t * H + 16 * j;
-      float v[16];
-      if (x_bf16) {
-        const u4 a = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base);
-        const u4 b = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base + 8);
+}
+
+// x[t] -> fp16 and the per-16-element sums of the fp16 values (hi + lo), one wave.
+__device__ void xprep_token(int t, int H, const void *xptr, bool x_bf16, _Float16 *x16, _Float16 *xs_hi,
+                            _Float16 *xs_lo) {
+  const int lane = threadIdx.x & 63;
+  const int nsub = H >> 4;
+  for (int j = lane; j < nsub; j += 64) {
+    const int64_t base = (int64_t)t * H + 16 * j;
+    float v[16];
+    if (x_bf16) {
+      const u4 a = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base);
+      const u4 b = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base + 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf16_bits_to_float((uint16_t)(a[i] & 0xFFFF));
-          v[2 * i + 1] = bf16_bits_to_float((uint16_t)(a[i] >> 16));
-          v[8 + 2 * i] = bf16_bits_to_float((uint16_t)(b[i] & 0xFFFF));
-          v[8 + 2 * i + 1] = bf16_bits_to_float((uint16_t)(b[i] >> 16));
-        }
-      } else {
-        const float *p = reinterpret_cast<const float *>(xptr) + base;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f4 a = *reinterpret_cast<const f4 *>(p + 4 * q);
-          v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
-        }
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_float((uint16_t)(a[i] & 0xFFFF));
+        v[2 * i + 1] = bf16_bits_to_float((uint16_t)(a[i] >> 16));
+        v[8 + 2 * i] = bf16_bits_to_float((uint16_t)(b[i] & 0xFFFF));
+        v[8 + 2 * i + 1] = bf16_bits_to_float((uint16_t)(b[i] >> 16));
       }
-      h8 o0, o1;
-      float sum = 0.0f;
+    } else {
+      const float *p = reinterpret_cast<const float *>(xptr) + base;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o0[i] = (half_t)v[i];
-        sum += (float)o0[i];
+      for (int q = 0; q < 4; ++q) {
+        const f4 a = *reinterpret_cast<const f4 *>(p + 4 * q);
+        v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o1[i] = (half_t)v[8 + i];
-        sum += (float)o1[i];
-      }
-      *reinterpret_cast<h8 *>(x16 + base) = o0;
-      *reinterpret_cast<h8 *>(x16 + base + 8) = o1;
-      const half_t hi = (half_t)sum;
-      xs_hi[(int64_t)t * nsub + j] = hi;
-      xs_lo[(int64_t)t * nsub + j] = (half_t)(sum - (float)hi);
     }
+    h8 o0, o1;
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o0[i] = (half_t)v[i];
+      sum += (float)o0[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o1[i] = (half_t)v[8 + i];
+      sum += (float)o1[i];
+    }
+    *reinterpret_cast<h8 *>(x16 + base) = o0;
+    *reinterpret_cast<h8 *>(x16 + base + 8) = o1;
+    const half_t hi = (half_t)sum;
+    xs_hi[(int64_t)t * nsub + j] = hi;
+    xs_lo[(int64_t)t * nsub + j] = (half_t)(sum - (float)hi);
   }
 }
 
@@ -265,7 +336,12 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
                                               XPrep xp, bool do_x, RouteOut ro) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token(logits, t, E, k, H, nullptr, ro, xp.x, xp.x_bf16, do_x ? xp.x16 : nullptr, xp.xs_hi, xp.xs_lo);
+  const int lane = threadIdx.x & 63;
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lv[i] = (lane + 64 * i < E) ? logits[(int64_t)t * E + lane + 64 * i] : 0.0f;
+  topk_select(lv, t, E, k, ro, nullptr);
+  if (do_x) xprep_token(t, H, xp.x, xp.x_bf16, xp.x16, xp.xs_hi, xp.xs_lo);
 }
 
 // ---------------------------------------------------------------- permutation
@@ -277,6 +353,8 @@ __device__ void permute_block(const int32_t *__restrict__ idx, int T, int E, int
                               int32_t *s_cnt, int32_t *s_base, int32_t *s_tbase, uint32_t *s_mask) {
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
+  if (ro.zeros)
+    for (int i = tid; i < ro.nzeros; i += nthr) ro.zeros[i] = (half_t)0.0f;
   for (int e = tid; e < E; e += nthr) s_cnt[e] = 0;
   __syncthreads();
   const int64_t nA = (int64_t)T * k;
@@ -373,68 +451,97 @@ __global__ __launch_bounds__(1024) void k_permute(int T, int E, int k, RouteOut 
   permute_block(ro.idx, T, E, k, ro, s_cnt, s_base, s_tbase, s_mask);
 }
 
-// T <= 16: waves 0..T-1 route one token each, then the block permutes.
-__global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ logits, int T, int E, int k,
-                                                      int H, XPrep xp, bool do_x, RouteOut ro) {
+// T <= 16: the whole block adds the slice partial sums of every (token,
+// expert) in slice order plus the bias (loads of all slices in flight at
+// once), then waves 0..T-1 route one token each from LDS, then the block
+// permutes.
+__global__ __launch_bounds__(1024) void k_route_small(const double *__restrict__ part, int nslice,
+                                                      const float *__restrict__ bias, float *__restrict__ logits,
+                                                      int T, int E, int k, RouteOut ro) {
   __shared__ int32_t s_cnt[256], s_base[256], s_tbase[256];
   __shared__ uint32_t s_mask[256 * 32];
-  const int t = threadIdx.x >> 6;
-  if (t < T)
-    topk_token(logits, t, E, k, H, nullptr, ro, xp.x, xp.x_bf16, do_x ? xp.x16 : nullptr, xp.xs_hi, xp.xs_lo);
-  __threadfence_block();
+  __shared__ int32_t s_idx[16 * 16];
+  __shared__ float s_lg[16 * 256];
+  const int n = T * E;
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    // slices in increasing order; loads issued 8 at a time ahead of the adds
+    double v = 0.0;
+    for (int q0 = 0; q0 < nslice; q0 += 8) {
+      double pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = (q0 + u < nslice) ? part[(int64_t)(q0 + u) * n + i] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (q0 + u < nslice) v += pv[u];
+    }
+    const int e = i % E;
+    if (bias) v += (double)bias[e];
+    const float l = (float)v;
+    s_lg[i] = l;
+    logits[i] = l;
+  }
   __syncthreads();
-  permute_block(ro.idx, T, E, k, ro, s_cnt, s_base, s_tbase, s_mask);
+  const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (t < T) {
+    float lv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lv[q] = (lane + 64 * q < E) ? s_lg[t * E + lane + 64 * q] : 0.0f;
+    topk_select(lv, t, E, k, ro, s_idx);
+  }
+  __syncthreads();
+  permute_block(s_idx, T, E, k, ro, s_cnt, s_base, s_tbase, s_mask);
 }
 
 // ---------------------------------------------------------------- launchers
 template <bool XB, bool WB>
-static hipError_t router_small_t(const void *x, const void *wr, const float *bias, float *logits, int T, int E,
-                                 int H, hipStream_t s) {
-  hipLaunchKernelGGL((k_router_small<XB, WB>), dim3((E + 3) / 4), dim3(256), 0, s, x, wr, bias, logits, T, E, H);
-  return hipGetLastError();
-}
-
-hipError_t launch_router_small(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
-                               float *logits, int T, int E, int H, hipStream_t s) {
-  if (x_bf16 && w_bf16) return router_small_t<true, true>(x, wr, bias, logits, T, E, H, s);
-  if (x_bf16) return router_small_t<true, false>(x, wr, bias, logits, T, E, H, s);
-  if (w_bf16) return router_small_t<false, true>(x, wr, bias, logits, T, E, H, s);
-  return router_small_t<false, false>(x, wr, bias, logits, T, E, H, s);
-}
-
-template <bool XB, bool WB>
 static hipError_t router_tiled_t(const void *x, const void *wr, const float *bias, float *logits, int T, int E,
-                                 int H, hipStream_t s) {
-  hipLaunchKernelGGL((k_router_tiled<XB, WB>), dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s, x, wr, bias,
-                     logits, T, E, H);
+                                 int H, hipStream_t s, const Timing *tm) {
+  DS4_LAUNCH(tm, (k_router_tiled<XB, WB>), dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s, x, wr, bias,
+             logits, T, E, H);
   return hipGetLastError();
 }
 
 hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
-                               float *logits, int T, int E, int H, hipStream_t s) {
-  if (x_bf16 && w_bf16) return router_tiled_t<true, true>(x, wr, bias, logits, T, E, H, s);
-  if (x_bf16) return router_tiled_t<true, false>(x, wr, bias, logits, T, E, H, s);
-  if (w_bf16) return router_tiled_t<false, true>(x, wr, bias, logits, T, E, H, s);
-  return router_tiled_t<false, false>(x, wr, bias, logits, T, E, H, s);
+                               float *logits, int T, int E, int H, hipStream_t s, const Timing *tm) {
+  if (x_bf16 && w_bf16) return router_tiled_t<true, true>(x, wr, bias, logits, T, E, H, s, tm);
+  if (x_bf16) return router_tiled_t<true, false>(x, wr, bias, logits, T, E, H, s, tm);
+  if (w_bf16) return router_tiled_t<false, true>(x, wr, bias, logits, T, E, H, s, tm);
+  return router_tiled_t<false, false>(x, wr, bias, logits, T, E, H, s, tm);
 }
 
 hipError_t launch_topk(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
-                       hipStream_t s) {
+                       hipStream_t s, const Timing *tm) {
   XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, H, x, xp != nullptr, ro);
+  DS4_LAUNCH(tm, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, H, x, xp != nullptr, ro);
   return hipGetLastError();
 }
 
-hipError_t launch_permute(int T, int E, int k, RouteOut ro, hipStream_t s) {
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, T, E, k, ro);
+hipError_t launch_permute(int T, int E, int k, RouteOut ro, hipStream_t s, const Timing *tm) {
+  DS4_LAUNCH(tm, k_permute, dim3(1), dim3(1024), 0, s, T, E, k, ro);
   return hipGetLastError();
 }
 
-hipError_t launch_route_small(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
-                              hipStream_t s) {
-  XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, logits, T, E, k, H, x, xp != nullptr, ro);
+hipError_t launch_route_small(const double *part, int nslice, const float *bias, float *logits, int T, int E,
+                              int k, RouteOut ro, hipStream_t s, const Timing *tm) {
+  DS4_LAUNCH(tm, k_route_small, dim3(1), dim3(1024), 0, s, part, nslice, bias, logits, T, E, k, ro);
   return hipGetLastError();
+}
+
+template <bool XB, bool WB>
+static hipError_t router_sliced_t(const void *x, const void *wr, double *part, int T, int E, int H,
+                                  const XPrep *xp, hipStream_t s, const Timing *tm) {
+  XPrep xx = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
+  DS4_LAUNCH(tm, (k_router_sliced<XB, WB>), dim3((E + 3) / 4, H / 256), dim3(256), 0, s, x, wr, part, T, E, H, xx,
+             xp != nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_sliced(const void *x, bool x_bf16, const void *wr, bool w_bf16, double *part, int T,
+                                int E, int H, const XPrep *xp, hipStream_t s, const Timing *tm) {
+  if (x_bf16 && w_bf16) return router_sliced_t<true, true>(x, wr, part, T, E, H, xp, s, tm);
+  if (x_bf16) return router_sliced_t<true, false>(x, wr, part, T, E, H, xp, s, tm);
+  if (w_bf16) return router_sliced_t<false, true>(x, wr, part, T, E, H, xp, s, tm);
+  return router_sliced_t<false, false>(x, wr, part, T, E, H, xp, s, tm);
 }
 
 }  // namespace ds4
