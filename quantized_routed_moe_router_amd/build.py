@@ -17,7 +17,10 @@ ARCH = "gfx950"
 
 # Packed fp32 instructions are kept out of the generated code on purpose.
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared", "-Wall", "-Wno-unused-function",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include")]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # keep MFMA accumulators in VGPRs: the scale corrections read them every super-block
+         "-mllvm", "-amdgpu-mfma-vgpr-form=true",
+         "-I", os.path.join(ROOT, "include")]
 
 
 def sources():

@@ -20,6 +20,18 @@
 namespace ds4 {
 
 #define WAVES 4
+#ifndef GEMM_R_GU
+#define GEMM_R_GU 1
+#endif
+#ifndef GEMM_R_DN
+#define GEMM_R_DN 2
+#endif
+#ifndef GEMM_NW_GU
+#define GEMM_NW_GU 4
+#endif
+#ifndef GEMM_NW_DN
+#define GEMM_NW_DN 4
+#endif
 
 struct UnitRegs {
   u4 code;   // 4 raw dwords: sub-blocks g, 4+g, 8+g, 12+g of row r
@@ -67,244 +79,257 @@ __device__ __forceinline__ int step_col(int g) {
   return 16 * (4 * (S >> 1) + g) + 8 * (S & 1);
 }
 
-// ------------------------------------------------------------------ gate/up
-// Workgroup: one tile (expert, <= 16*NT tokens) x 64*R rows of gate and up.
-// Wave w: row tiles (blockIdx.x*WAVES + w)*R .. +R-1.
-template <int R, int NT>
-__global__ __launch_bounds__(256) void k_gateup(GemmArgs a, int nrb) {
-  const int tile_id = blockIdx.x / nrb;
-  const int rb = blockIdx.x - tile_id * nrb;
-  if (tile_id >= *a.ntiles) return;
-  const TileT tl = a.tiles[tile_id];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int n_rt = a.I >> 4;
-  const int rt0 = (rb * WAVES + wave) * R;
-  if (rt0 >= n_rt) return;
-  const int nsb = a.H >> 8;
-  const uint8_t *G = a.gate + (size_t)tl.e * a.gu_bytes;
-  const uint8_t *U = a.up + (size_t)tl.e * a.gu_bytes;
+// ------------------------------------------------------------------ prefill grouped GEMM
+// Workgroup = one tile of up to 64 tokens x (WAVES*R*16) rows of NM packed
+// matrices (NM = 2: gate and up with the SwiGLU epilogue; NM = 1: down).
+// Per super-block the tile's activations (64 x 256 fp16) and their 16-column
+// sums (hi, lo) are staged in LDS; the next super-block's activations and
+// packed weights are already loading into registers while the current one
+// is multiplied.  Each wave dequantizes its own rows' A fragments.
+constexpr int GEMM_NT = 4;            // 16-token n-tiles per workgroup
+constexpr int SB_STRIDE = 264;        // halves per staged token row (256 + pad)
+constexpr int SS_STRIDE = 40;         // halves per staged sum row (32 + pad)
 
-  const half_t *xrow[NT];
-  const half_t *xsrow[NT];
-  bool valid[NT];
-  int pidx[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = 16 * nt + r16;
-    valid[nt] = c < tl.n;
-    pidx[nt] = tl.p0 + (valid[nt] ? c : 0);
-    const int tok = a.perm[pidx[nt]] / a.k;
-    xrow[nt] = a.x16 + (size_t)tok * a.H;
-    xsrow[nt] = ((g >> 1) ? a.xs_lo : a.xs_hi) + (size_t)tok * (a.H >> 4) + 8 * (g & 1);
-  }
-  int rts[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rts[r] = min(rt0 + r, n_rt - 1);
+template <int NM>
+struct GemmCtx {
+  const uint8_t *W[NM];               // this wave's matrices, row tile rt0
+  int nsb;
+  size_t rt_stride;                   // bytes between consecutive row tiles
+};
 
-  f4 yg[R][NT], yu[R][NT];
+template <int NM, int R>
+__device__ __forceinline__ void gemm_load_a(UnitRegs (&u)[R][NM], const GemmCtx<NM> &c, const int (&rts)[R], int sb,
+                                            int lane) {
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      yg[r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-      yu[r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-    }
-
-  for (int sb = 0; sb < nsb; ++sb) {
-    UnitRegs ug[R], uu[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const size_t off = ((size_t)rts[r] * nsb + sb) * DS4_UNIT_BYTES;
-      ug[r] = load_unit(G + off, lane);
-      uu[r] = load_unit(U + off, lane);
-    }
-    UnitDecoded dg[R], du[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      dg[r] = decode_unit(ug[r], g);
-      du[r] = decode_unit(uu[r], g);
-    }
-    f4 ag[R][NT], au[R][NT];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        ag[r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-        au[r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-      }
-    const int kb = sb * 256;
-#define GU_STEP(S)                                                                    \
-  {                                                                                   \
-    h8 b[NT];                                                                         \
-    _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) b[nt] =                         \
-        valid[nt] ? load_h8(xrow[nt] + kb + step_col<S>(g)) : zero_h8();              \
-    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                   \
-      const h8 A0 = step_frag<S>(ug[r], dg[r]);                                       \
-      const h8 A1 = step_frag<S>(uu[r], du[r]);                                       \
-      _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                             \
-        ag[r][nt] = mfma16(A0, b[nt], ag[r][nt]);                                     \
-        au[r][nt] = mfma16(A1, b[nt], au[r][nt]);                                     \
-      }                                                                               \
-    }                                                                                 \
-  }
-    GU_STEP(0) GU_STEP(1) GU_STEP(2) GU_STEP(3) GU_STEP(4) GU_STEP(5) GU_STEP(6) GU_STEP(7)
-#undef GU_STEP
-    // min term
-    h8 bm[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bm[nt] = valid[nt] ? load_h8(xsrow[nt] + sb * 16) : zero_h8();
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
-        const f4 mg = mfma16(dg[r].mfrag, bm[nt], z);
-        const f4 mu = mfma16(du[r].mfrag, bm[nt], z);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          yg[r][nt][i] = fmaf(dg[r].d[i], ag[r][nt][i], yg[r][nt][i]);
-          yg[r][nt][i] = fmaf(-dg[r].dmin[i], mg[i], yg[r][nt][i]);
-          yu[r][nt][i] = fmaf(du[r].d[i], au[r][nt][i], yu[r][nt][i]);
-          yu[r][nt][i] = fmaf(-du[r].dmin[i], mu[i], yu[r][nt][i]);
-        }
-      }
-  }
-
-  // SwiGLU epilogue: h = silu(gate) * up -> fp16; per-16-row sums for the
-  // down projection's min term (one sub-block of its reduction dimension).
-  const int nj = a.Ipad >> 4;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool rv = rt0 + r < n_rt;
-    const int row0 = (rt0 + r) * 16 + 4 * g;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      half_t hv[4];
-      float ssum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float gv = yg[r][nt][i], uv = yu[r][nt][i];
-        const float hh = gv / (1.0f + expf(-gv)) * uv;
-        hv[i] = (half_t)hh;
-        ssum += (float)hv[i];
-      }
-      ssum += __shfl_xor(ssum, 16);
-      ssum += __shfl_xor(ssum, 32);
-      if (valid[nt] && rv) {
-        uint2 pk;
-        __builtin_memcpy(&pk, hv, 8);
-        *reinterpret_cast<uint2 *>(a.h + (size_t)pidx[nt] * a.Ipad + row0) = pk;
-        if (g == 0) {
-          const half_t hi = (half_t)ssum;
-          a.hs_hi[(size_t)pidx[nt] * nj + rt0 + r] = hi;
-          a.hs_lo[(size_t)pidx[nt] * nj + rt0 + r] = (half_t)(ssum - (float)hi);
-        }
-      }
-    }
-  }
+    for (int m = 0; m < NM; ++m)
+      u[r][m] = load_unit(c.W[m] + (size_t)rts[r] * c.rt_stride + (size_t)sb * DS4_UNIT_BYTES, lane);
 }
 
-// ------------------------------------------------------------------ down
-template <int R, int NT>
-__global__ __launch_bounds__(256) void k_down(GemmArgs a, int nrb) {
+// Activation staging: thread -> token row (tid/4)%64, chunk column tid%4;
+// with NW waves each thread stages 8*4/NW of the row's 32 chunks of 8 halves
+// (chunks lc + 4i), and threads of the first 256 also one chunk of sums
+// (lc: hi 0-7, hi 8-15, lo 0-7, lo 8-15).
+template <int NCH>
+struct Stage {
+  u4 b[NCH];
+  u4 s;
+};
+
+template <int NCH, bool PADDED>
+__device__ __forceinline__ void stage_load(Stage<NCH> &st, const half_t *brow, const half_t *shi, const half_t *slo,
+                                           int sb, int lc, int part, int kreal, int jreal) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int col = sb * 256 + (lc + 4 * (part * NCH + i)) * 8;
+    st.b[i] = (!PADDED || col < kreal) ? *reinterpret_cast<const u4 *>(brow + col) : (u4){0u, 0u, 0u, 0u};
+  }
+  if (part != 0) return;
+  const int j0 = sb * 16 + 8 * (lc & 1);
+  const half_t *sp = (lc >> 1) ? slo : shi;
+  if (!PADDED) {
+    st.s = *reinterpret_cast<const u4 *>(sp + j0);
+    return;
+  }
+  u4 v = (u4){0u, 0u, 0u, 0u};
+  if (j0 < jreal) {
+    v = *reinterpret_cast<const u4 *>(sp + j0);
+    if (j0 + 8 > jreal) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (j0 + 2 * q >= jreal) v[q] = 0u;
+        else if (j0 + 2 * q + 1 >= jreal) v[q] &= 0xFFFFu;
+      }
+    }
+  }
+  st.s = v;
+}
+
+template <int NCH>
+__device__ __forceinline__ void stage_store(const Stage<NCH> &st, half_t *sB, half_t *sS, int lr, int lc, int part) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+    *reinterpret_cast<u4 *>(sB + lr * SB_STRIDE + (lc + 4 * (part * NCH + i)) * 8) = st.b[i];
+  if (part == 0) *reinterpret_cast<u4 *>(sS + lr * SS_STRIDE + lc * 8) = st.s;
+}
+
+template <int NM, int R>
+__device__ __forceinline__ void gemm_compute_sb(const UnitRegs (&u)[R][NM], const half_t *sB, const half_t *sS,
+                                                f4 (&y)[NM][R][GEMM_NT], int r16, int g) {
+  UnitDecoded dc[R][NM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) dc[r][m] = decode_unit(u[r][m], g);
+  f4 acc[NM][R][GEMM_NT];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int nt = 0; nt < GEMM_NT; ++nt) acc[m][r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+#define GEMM_STEP(S)                                                                          \
+  {                                                                                           \
+    h8 b[GEMM_NT];                                                                            \
+    _Pragma("unroll") for (int nt = 0; nt < GEMM_NT; ++nt) b[nt] =                            \
+        load_h8(sB + (16 * nt + r16) * SB_STRIDE + step_col<S>(g));                           \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                           \
+      _Pragma("unroll") for (int m = 0; m < NM; ++m) {                                        \
+        const h8 A = step_frag<S>(u[r][m], dc[r][m]);                                         \
+        _Pragma("unroll") for (int nt = 0; nt < GEMM_NT; ++nt) acc[m][r][nt] =                \
+            mfma16(A, b[nt], acc[m][r][nt]);                                                  \
+      }                                                                                       \
+    }                                                                                         \
+  }
+  GEMM_STEP(0) GEMM_STEP(1) GEMM_STEP(2) GEMM_STEP(3) GEMM_STEP(4) GEMM_STEP(5) GEMM_STEP(6) GEMM_STEP(7)
+#undef GEMM_STEP
+  h8 bm[GEMM_NT];
+#pragma unroll
+  for (int nt = 0; nt < GEMM_NT; ++nt) bm[nt] = load_h8(sS + (16 * nt + r16) * SS_STRIDE + 8 * g);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < GEMM_NT; ++nt) {
+        const f4 mm = mfma16(dc[r][m].mfrag, bm[nt], (f4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          y[m][r][nt][q] = fmaf(dc[r][m].d[q], acc[m][r][nt][q], y[m][r][nt][q]);
+          y[m][r][nt][q] = fmaf(-dc[r][m].dmin[q], mm[q], y[m][r][nt][q]);
+        }
+      }
+}
+
+template <int NM, int R, int NW, bool PADDED>
+__global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
+  __shared__ __attribute__((aligned(16))) half_t sB[64 * SB_STRIDE];
+  __shared__ __attribute__((aligned(16))) half_t sS[64 * SS_STRIDE];
   const int tile_id = blockIdx.x / nrb;
   const int rb = blockIdx.x - tile_id * nrb;
-  if (tile_id >= *a.ntiles) return;
+  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
   const TileT tl = a.tiles[tile_id];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int n_rt = a.H >> 4;
-  const int rt0 = (rb * WAVES + wave) * R;
-  if (rt0 >= n_rt) return;
-  const int nsb = a.Ipad >> 8;
-  const int nj = a.Ipad >> 4;       // h-sum row stride
-  const int nj_real = a.I >> 4;
-  const uint8_t *D = a.down + (size_t)tl.e * a.d_bytes;
-
-  const half_t *hrow[NT];
-  const half_t *hsrow[NT];
-  bool valid[NT];
-  int pidx[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = 16 * nt + r16;
-    valid[nt] = c < tl.n;
-    pidx[nt] = tl.p0 + (valid[nt] ? c : 0);
-    hrow[nt] = a.h + (size_t)pidx[nt] * a.Ipad;
-    hsrow[nt] = ((g >> 1) ? a.hs_lo : a.hs_hi) + (size_t)pidx[nt] * nj + 8 * (g & 1);
-  }
+  constexpr bool GU = NM == 2;
+  const int K = GU ? a.H : a.Ipad;
+  const int kreal = GU ? a.H : a.I;
+  const int jreal = kreal >> 4;
+  const int nsb = K >> 8;
+  const int n_rt = (GU ? a.I : a.H) >> 4;
+  const int rt0 = (rb * NW + wave) * R;
   int rts[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rts[r] = min(rt0 + r, n_rt - 1);
 
-  f4 y[R][NT];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) y[r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+  // activation rows staged by this thread
+  constexpr int NCH = 32 / NW;
+  const int lr = (tid >> 2) & 63, lc = tid & 3, part = tid >> 8;
+  const bool lvalid = lr < tl.n;
+  const half_t *brow, *shi, *slo;
+  if (GU) {
+    const int tok = a.perm[tl.p0 + (lvalid ? lr : 0)] / a.k;
+    brow = a.x16 + (size_t)tok * a.H;
+    shi = a.xs_hi + (size_t)tok * (a.H >> 4);
+    slo = a.xs_lo + (size_t)tok * (a.H >> 4);
+  } else {
+    const size_t p = (size_t)(tl.p0 + (lvalid ? lr : 0));
+    brow = a.h + p * a.Ipad;
+    shi = a.hs_hi + p * (a.Ipad >> 4);
+    slo = a.hs_lo + p * (a.Ipad >> 4);
+  }
+  if (!lvalid) brow = shi = slo = a.zeros;
 
-  for (int sb = 0; sb < nsb; ++sb) {
-    UnitRegs ud[R];
+  GemmCtx<NM> c;
+  c.nsb = nsb;
+  c.rt_stride = (size_t)nsb * DS4_UNIT_BYTES;
+  if (GU) {
+    c.W[0] = a.gate + (size_t)tl.e * a.gu_bytes;
+    c.W[NM - 1] = a.up + (size_t)tl.e * a.gu_bytes;
+  } else {
+    c.W[0] = a.down + (size_t)tl.e * a.d_bytes;
+  }
+
+  f4 y[NM][R][GEMM_NT];
 #pragma unroll
-    for (int r = 0; r < R; ++r) ud[r] = load_unit(D + ((size_t)rts[r] * nsb + sb) * DS4_UNIT_BYTES, lane);
-    UnitDecoded dd[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) dd[r] = decode_unit(ud[r], g);
-    f4 ac[R][NT];
+  for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) ac[r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-    const int kb = sb * 256;
-#define DN_STEP(S)                                                                    \
-  {                                                                                   \
-    const int col = kb + step_col<S>(g);                                              \
-    h8 b[NT];                                                                         \
-    _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) b[nt] =                         \
-        (valid[nt] && col < a.I) ? load_h8(hrow[nt] + col) : zero_h8();               \
-    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                   \
-      const h8 A0 = step_frag<S>(ud[r], dd[r]);                                       \
-      _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) ac[r][nt] =                   \
-          mfma16(A0, b[nt], ac[r][nt]);                                               \
-    }                                                                                 \
-  }
-    DN_STEP(0) DN_STEP(1) DN_STEP(2) DN_STEP(3) DN_STEP(4) DN_STEP(5) DN_STEP(6) DN_STEP(7)
-#undef DN_STEP
-    h8 bm[NT];
-    const int j0 = sb * 16 + 8 * (g & 1);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      h8 v = zero_h8();
-      if (valid[nt] && j0 < nj_real) {
-        v = load_h8(hsrow[nt] + sb * 16);
-        if (j0 + 8 > nj_real) {
-#pragma unroll
-          for (int b = 0; b < 8; ++b)
-            if (j0 + b >= nj_real) v[b] = (half_t)0.0f;
-        }
-      }
-      bm[nt] = v;
+      for (int nt = 0; nt < GEMM_NT; ++nt) y[m][r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  Stage<NCH> st;
+  UnitRegs ua[R][NM], ub[R][NM];
+  stage_load<NCH, PADDED>(st, brow, shi, slo, 0, lc, part, kreal, jreal);
+  gemm_load_a<NM, R>(ua, c, rts, 0, lane);
+  for (int sb = 0; sb < nsb; sb += 2) {
+    // even super-block: weights in ua, prefetch into ub
+    __syncthreads();
+    stage_store<NCH>(st, sB, sS, lr, lc, part);
+    __syncthreads();
+    if (sb + 1 < nsb) {
+      stage_load<NCH, PADDED>(st, brow, shi, slo, sb + 1, lc, part, kreal, jreal);
+      gemm_load_a<NM, R>(ub, c, rts, sb + 1, lane);
     }
+    gemm_compute_sb<NM, R>(ua, sB, sS, y, r16, g);
+    if (sb + 1 >= nsb) break;
+    // odd super-block: weights in ub, prefetch into ua
+    __syncthreads();
+    stage_store<NCH>(st, sB, sS, lr, lc, part);
+    __syncthreads();
+    if (sb + 2 < nsb) {
+      stage_load<NCH, PADDED>(st, brow, shi, slo, sb + 2, lc, part, kreal, jreal);
+      gemm_load_a<NM, R>(ua, c, rts, sb + 2, lane);
+    }
+    gemm_compute_sb<NM, R>(ub, sB, sS, y, r16, g);
+  }
+
+  if (rt0 >= n_rt) return;
+  if (GU) {
+    const int nj = a.Ipad >> 4;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
+      const bool rv = rt0 + r < n_rt;
+      const int row0 = (rt0 + r) * 16 + 4 * g;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const f4 mm = mfma16(dd[r].mfrag, bm[nt], (f4){0.f, 0.f, 0.f, 0.f});
+      for (int nt = 0; nt < GEMM_NT; ++nt) {
+        const int col = 16 * nt + r16;
+        const bool valid = col < tl.n;
+        half_t hv[4];
+        float ssum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          y[r][nt][i] = fmaf(dd[r].d[i], ac[r][nt][i], y[r][nt][i]);
-          y[r][nt][i] = fmaf(-dd[r].dmin[i], mm[i], y[r][nt][i]);
+        for (int q = 0; q < 4; ++q) {
+          const float gv = y[0][r][nt][q], uv = y[NM - 1][r][nt][q];
+          hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+          ssum += (float)hv[q];
+        }
+        ssum += __shfl_xor(ssum, 16);
+        ssum += __shfl_xor(ssum, 32);
+        if (valid && rv) {
+          const size_t p = (size_t)(tl.p0 + col);
+          uint2 pk;
+          __builtin_memcpy(&pk, hv, 8);
+          *reinterpret_cast<uint2 *>(a.h + p * a.Ipad + row0) = pk;
+          if (g == 0) {
+            const half_t hi = (half_t)ssum;
+            a.hs_hi[p * nj + rt0 + r] = hi;
+            a.hs_lo[p * nj + rt0 + r] = (half_t)(ssum - (float)hi);
+          }
         }
       }
-  }
+    }
+  } else {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (rt0 + r >= n_rt) continue;
-    const int row0 = (rt0 + r) * 16 + 4 * g;
+    for (int r = 0; r < R; ++r) {
+      if (rt0 + r >= n_rt) continue;
+      const int row0 = (rt0 + r) * 16 + 4 * g;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      if (valid[nt]) *reinterpret_cast<f4 *>(a.yp + (size_t)pidx[nt] * a.H + row0) = y[r][nt];
+      for (int nt = 0; nt < GEMM_NT; ++nt) {
+        const int col = 16 * nt + r16;
+        if (col < tl.n) *reinterpret_cast<f4 *>(a.yp + (size_t)(tl.p0 + col) * a.H + row0) = y[0][r][nt];
+      }
+    }
   }
 }
 
@@ -638,11 +663,11 @@ hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream
     DS4_LAUNCH(tm, (k_gateup_dec<4>), dim3((unsigned)((int64_t)n_rt * max_tiles)), dim3(256), 0, s, a, n_rt);
     return hipGetLastError();
   }
-  constexpr int R = 1;
-  const int rows_per_wg = 16 * R * WAVES;
+  constexpr int R = GEMM_R_GU, NW = GEMM_NW_GU;
+  const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.I + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
-  DS4_LAUNCH(tm, (k_gateup<R, 4>), grid, dim3(256), 0, s, a, nrb);
+  DS4_LAUNCH(tm, (k_moe_gemm<2, R, NW, false>), grid, dim3(64 * NW), 0, s, a, nrb);
   return hipGetLastError();
 }
 
@@ -653,11 +678,14 @@ hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t
     DS4_LAUNCH(tm, (k_down_dec<2>), dim3((unsigned)((int64_t)n_rt * max_tiles)), dim3(256), 0, s, a, n_rt);
     return hipGetLastError();
   }
-  constexpr int R = 1;
-  const int rows_per_wg = 16 * R * WAVES;
+  constexpr int R = GEMM_R_DN, NW = GEMM_NW_DN;
+  const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.H + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
-  DS4_LAUNCH(tm, (k_down<R, 4>), grid, dim3(256), 0, s, a, nrb);
+  if (a.I == a.Ipad)
+    DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, false>), grid, dim3(64 * NW), 0, s, a, nrb);
+  else
+    DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, true>), grid, dim3(64 * NW), 0, s, a, nrb);
   return hipGetLastError();
 }
 
