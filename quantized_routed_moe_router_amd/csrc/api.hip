@@ -31,7 +31,7 @@ int validate_dims(const ds4moe_dims *d) {
 }
 
 struct Layout {
-  size_t logits, part, idx, w, counts, offsets, perm, pos, tiles, ntiles;
+  size_t logits, part, idx, w, counts, offsets, perm, pos, tiles, ntiles, ccnt, cbase, lrank;
   size_t x16, xs_hi, xs_lo, h, hs_hi, hs_lo, yp, hsh, ysh, zeros;
   int nzeros;
   size_t total;
@@ -58,6 +58,12 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
   L.counts = take(sizeof(int32_t) * E);
   L.offsets = take(sizeof(int32_t) * (E + 1));
   L.perm = take(sizeof(int32_t) * A);
+  if (T > 16) {
+    const int64_t nch = chunk_count((int)T);
+    L.ccnt = take(sizeof(int32_t) * nch * E);
+    L.cbase = take(sizeof(int32_t) * nch * E);
+    L.lrank = take(sizeof(int32_t) * A);
+  }
   if (mode != DS4MOE_MODE_ROUTE) {
     L.pos = take(sizeof(int32_t) * A);
     L.tiles = take(sizeof(TileT) * (size_t)L.max_tiles);
@@ -187,8 +193,8 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     TRY(launch_route_small(at<double>(ws, L.part), d.hidden / 256, w->router_bias, p.logits, T, d.n_experts,
                            d.top_k, ro, s, tm(SL_ROUTE)));
   } else {
-    TRY(launch_topk(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, s, tm(SL_ROUTE)));
-    TRY(launch_permute(T, d.n_experts, d.top_k, ro, s, tm(SL_PERMUTE)));
+    TRY(launch_route_chunked(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, at<int32_t>(ws, L.ccnt),
+                             at<int32_t>(ws, L.cbase), at<int32_t>(ws, L.lrank), s, tm(SL_ROUTE), tm(SL_PERMUTE)));
   }
 
   GemmArgs ga{};
@@ -307,8 +313,8 @@ int ds4moe_route(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x
     return DS4MOE_OK;
   }
   TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));
-  TRY(launch_topk(p.logits, T, d.n_experts, d.top_k, d.hidden, nullptr, ro, s));
-  TRY(launch_permute(T, d.n_experts, d.top_k, ro, s));
+  TRY(launch_route_chunked(p.logits, T, d.n_experts, d.top_k, d.hidden, nullptr, ro, at<int32_t>(ws, L.ccnt),
+                           at<int32_t>(ws, L.cbase), at<int32_t>(ws, L.lrank), s));
   return DS4MOE_OK;
 }
 

@@ -62,11 +62,11 @@ hipError_t launch_dequant(float *dst, const void *packed, int64_t n_mats, int64_
 
 hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,
                                float *logits, int T, int E, int H, hipStream_t s, const Timing *tm = nullptr);
-// wave per token: top-k, weights and (if xp != nullptr) activation preparation
-hipError_t launch_topk(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
-                       hipStream_t s, const Timing *tm = nullptr);
-// one workgroup: histogram, scan, stable permutation, tile list
-hipError_t launch_permute(int T, int E, int k, RouteOut ro, hipStream_t s, const Timing *tm = nullptr);
+// large T: top-k + activation prep + per-chunk counts/ranks, scan, placement
+int chunk_count(int T);
+hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
+                                int32_t *ccnt, int32_t *base, int32_t *lrank, hipStream_t s,
+                                const Timing *tm_topk = nullptr, const Timing *tm_perm = nullptr);
 // T <= 16: logits as fp64 partial sums per 256-column slice [H/256][T][E],
 // with the activation preparation (if xp != nullptr)
 hipError_t launch_router_sliced(const void *x, bool x_bf16, const void *wr, bool w_bf16, double *part, int T,

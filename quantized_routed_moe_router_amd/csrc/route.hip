@@ -117,24 +117,26 @@ __global__ __launch_bounds__(256) void k_router_sliced(const void *__restrict__ 
   }
 }
 
-// ---------------------------------------------------------------- logits, tiled
-// 64 tokens x 64 experts per workgroup, 4x4 outputs per thread, sequential
-// fp64 FMA over h = 0..H-1 (the same order as a plain loop).
+// ---------------------------------------------------------------- logits, MFMA fp64
+// 64 tokens x 64 experts per workgroup; wave w owns tokens 16w..16w+15 and
+// all 64 experts (four 16x16 fp64 accumulators).  Operands are staged in LDS
+// as fp32 (bf16 and fp32 inputs are exact there) and widened to fp64;
+// v_mfma_f64_16x16x4_f64 accumulates in fp64, where every product of two
+// fp32 numbers is exact.
+typedef double d4 __attribute__((ext_vector_type(4)));
+
 template <bool XB, bool WB>
-__global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x, const void *__restrict__ wr,
-                                                      const float *__restrict__ bias, float *__restrict__ logits,
-                                                      int T, int E, int H) {
+__global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x, const void *__restrict__ wr,
+                                                     const float *__restrict__ bias, float *__restrict__ logits,
+                                                     int T, int E, int H) {
   __shared__ float xs[32][68];  // [k][token]
   __shared__ float ws[32][68];  // [k][expert]
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  const int tr = (tid >> 4) * 4, er = (tid & 15) * 4;
-  double acc[4][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  d4 acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  // loader: thread -> (row = tid/4, 8 consecutive k at 8*(tid%4))
+  for (int n = 0; n < 4; ++n) acc[n] = (d4){0.0, 0.0, 0.0, 0.0};
   const int lrow = tid >> 2, lk = (tid & 3) * 8;
   for (int k0 = 0; k0 < H; k0 += 32) {
     {
@@ -161,25 +163,28 @@ __global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x
       for (int i = 0; i < 8; ++i) ws[lk + i][lrow] = (float)v[i];
     }
     __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < 32; ++kk) {
-      const f4 xv = *reinterpret_cast<const f4 *>(&xs[kk][tr]);
-      const f4 wv = *reinterpret_cast<const f4 *>(&ws[kk][er]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int kk = 0; kk < 32; kk += 4) {
+      const double a = (double)xs[kk + g][16 * wave + r16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma((double)xv[i], (double)wv[j], acc[i][j]);
+      for (int n = 0; n < 4; ++n) {
+        const double b = (double)ws[kk + g][16 * n + r16];
+        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[n], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
+  // D (fp64 16x16x4): lane holds rows (tokens) g, g+4, g+8, g+12 of the wave's 16,
+  // column (expert) r16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + tr + i;
-    if (t >= T) continue;
+  for (int n = 0; n < 4; ++n) {
+    const int e = e0 + 16 * n + r16;
+    if (e >= E) continue;
+    const double b = bias ? (double)bias[e] : 0.0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + er + j;
-      if (e < E) logits[(int64_t)t * E + e] = (float)(acc[i][j] + (bias ? (double)bias[e] : 0.0));
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * wave + g + 4 * i;
+      if (t < T) logits[(int64_t)t * E + e] = (float)(acc[n][i] + b);
     }
   }
 }
@@ -249,8 +254,8 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 // Top-k of one token by one wave from the logits of experts lane + 64*i held
 // in registers; lane j < k writes rank j (index and normalised weight) to
-// global memory and, if s_idx is given, the index to LDS as well.
-__device__ void topk_select(const float lv[4], int t, int E, int k, RouteOut ro, int32_t *s_idx) {
+// global memory and, if s_row is given, the index to s_row[j] (LDS) as well.
+__device__ void topk_select(const float lv[4], int t, int E, int k, RouteOut ro, int32_t *s_row) {
   const int lane = threadIdx.x & 63;
   uint64_t keys[4];
 #pragma unroll
@@ -281,7 +286,7 @@ __device__ void topk_select(const float lv[4], int t, int E, int k, RouteOut ro,
     if (lane == j) {
       ro.idx[(int64_t)t * k + j] = sel_e[j];
       ro.w[(int64_t)t * k + j] = sc[j] / S;
-      if (s_idx) s_idx[t * k + j] = sel_e[j];
+      if (s_row) s_row[j] = sel_e[j];
     }
   }
 }
@@ -332,16 +337,138 @@ __device__ void xprep_token(int t, int H, const void *xptr, bool x_bf16, _Float1
   }
 }
 
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k, int H,
-                                              XPrep xp, bool do_x, RouteOut ro) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int lane = threadIdx.x & 63;
-  float lv[4];
+// Large T: one workgroup per chunk of 64 tokens (wave w: tokens 16w..16w+15).
+// Besides top-k and the activation preparation it records, for the stable
+// permutation, the chunk's count per expert and each assignment's rank among
+// the chunk's assignments to the same expert (earlier tokens first).
+constexpr int CHUNK = 64;
+
+__global__ __launch_bounds__(256) void k_topk_chunk(const float *__restrict__ logits, int T, int E, int k, int H,
+                                                    XPrep xp, bool do_x, RouteOut ro, int32_t *__restrict__ ccnt,
+                                                    int32_t *__restrict__ lrank) {
+  __shared__ int32_t s_idx[CHUNK * 16];
+  __shared__ uint32_t s_mask[256 * 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * CHUNK;
+  for (int i = threadIdx.x; i < E * 2; i += 256) s_mask[i] = 0u;
+  for (int q = 0; q < CHUNK / 4; ++q) {
+    const int tl = 16 * wave + q;
+    const int t = c0 + tl;
+    if (t >= T) break;
+    float lv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lv[i] = (lane + 64 * i < E) ? logits[(int64_t)t * E + lane + 64 * i] : 0.0f;
-  topk_select(lv, t, E, k, ro, nullptr);
-  if (do_x) xprep_token(t, H, xp.x, xp.x_bf16, xp.x16, xp.xs_hi, xp.xs_lo);
+    for (int i = 0; i < 4; ++i) lv[i] = (lane + 64 * i < E) ? logits[(int64_t)t * E + lane + 64 * i] : 0.0f;
+    topk_select(lv, t, E, k, ro, s_idx + tl * k);
+    if (do_x) xprep_token(t, H, xp.x, xp.x_bf16, xp.x16, xp.xs_hi, xp.xs_lo);
+  }
+  __syncthreads();
+  const int nt = min(CHUNK, T - c0);
+  for (int a = threadIdx.x; a < nt * k; a += 256) {
+    const int tl = a / k;
+    atomicOr(&s_mask[s_idx[a] * 2 + (tl >> 5)], 1u << (tl & 31));
+  }
+  __syncthreads();
+  for (int a = threadIdx.x; a < nt * k; a += 256) {
+    const int tl = a / k;
+    const uint32_t *m = s_mask + s_idx[a] * 2;
+    int r = __popc(m[tl >> 5] & ((1u << (tl & 31)) - 1u));
+    if (tl >= 32) r += __popc(m[0]);
+    lrank[(int64_t)c0 * k + a] = r;
+  }
+  for (int e = threadIdx.x; e < E; e += 256)
+    ccnt[(int64_t)blockIdx.x * E + e] = __popc(s_mask[2 * e]) + __popc(s_mask[2 * e + 1]);
+}
+
+// One workgroup: per-expert exclusive prefix over chunks (base), counts,
+// offsets, tile list, and the zero row for the GEMMs.
+__global__ __launch_bounds__(1024) void k_scan_chunks(int T, int E, int k, int nchunk,
+                                                      const int32_t *__restrict__ ccnt, int32_t *__restrict__ base,
+                                                      RouteOut ro) {
+  __shared__ int32_t s_cnt[256], s_off[256], s_tb[256];
+  const int tid = threadIdx.x;
+  if (ro.zeros)
+    for (int i = tid; i < ro.nzeros; i += 1024) ro.zeros[i] = (half_t)0.0f;
+  if (tid < E) {
+    int run = 0;
+    for (int c0 = 0; c0 < nchunk; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (c0 + u < nchunk) ? ccnt[(int64_t)(c0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < nchunk) {
+          base[(int64_t)(c0 + u) * E + tid] = run;
+          run += v[u];
+        }
+    }
+    s_cnt[tid] = run;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    int c[4], nt[4], sc = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      c[i] = e < E ? s_cnt[e] : 0;
+      nt[i] = (ro.tiles && c[i] > 0) ? (c[i] + ro.tile_n - 1) / ro.tile_n : 0;
+      sc += c[i];
+      st += nt[i];
+    }
+    int ic = sc, it = st;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int oc = __shfl_up(ic, off), ot = __shfl_up(it, off);
+      if (lane >= off) {
+        ic += oc;
+        it += ot;
+      }
+    }
+    int rc = ic - sc, rt = it - st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        s_off[e] = rc;
+        s_tb[e] = rt;
+        ro.counts[e] = c[i];
+        ro.offsets[e] = rc;
+      }
+      rc += c[i];
+      rt += nt[i];
+    }
+    if (lane == 63) {
+      ro.offsets[E] = ic;
+      if (ro.ntiles) *ro.ntiles = it;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E && ro.tiles; e += 1024) {
+    const int c = s_cnt[e];
+    const int nt = (c + ro.tile_n - 1) / ro.tile_n;
+    for (int i = 0; i < nt; ++i) {
+      TileT tl;
+      tl.e = e;
+      tl.p0 = s_off[e] + i * ro.tile_n;
+      tl.n = min(ro.tile_n, c - i * ro.tile_n);
+      tl.pad = 0;
+      ro.tiles[s_tb[e] + i] = tl;
+    }
+  }
+}
+
+// One workgroup per chunk: perm[offsets[e] + base[chunk][e] + rank] = a.
+__global__ __launch_bounds__(256) void k_place_chunks(int T, int E, int k, const int32_t *__restrict__ base,
+                                                      const int32_t *__restrict__ lrank, RouteOut ro) {
+  const int c0 = blockIdx.x * CHUNK;
+  const int nt = min(CHUNK, T - c0);
+  for (int i = threadIdx.x; i < nt * k; i += 256) {
+    const int64_t a = (int64_t)c0 * k + i;
+    const int e = ro.idx[a];
+    const int p = ro.offsets[e] + base[(int64_t)blockIdx.x * E + e] + lrank[a];
+    ro.perm[p] = (int32_t)a;
+    if (ro.pos) ro.pos[a] = p;
+  }
 }
 
 // ---------------------------------------------------------------- permutation
@@ -445,12 +572,6 @@ __device__ void permute_block(const int32_t *__restrict__ idx, int T, int E, int
   }
 }
 
-__global__ __launch_bounds__(1024) void k_permute(int T, int E, int k, RouteOut ro) {
-  __shared__ int32_t s_cnt[256], s_base[256], s_tbase[256];
-  __shared__ uint32_t s_mask[256 * 32];
-  permute_block(ro.idx, T, E, k, ro, s_cnt, s_base, s_tbase, s_mask);
-}
-
 // T <= 16: the whole block adds the slice partial sums of every (token,
 // expert) in slice order plus the bias (loads of all slices in flight at
 // once), then waves 0..T-1 route one token each from LDS, then the block
@@ -486,7 +607,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const double *__restrict__
     float lv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) lv[q] = (lane + 64 * q < E) ? s_lg[t * E + lane + 64 * q] : 0.0f;
-    topk_select(lv, t, E, k, ro, s_idx);
+    topk_select(lv, t, E, k, ro, s_idx + t * k);
   }
   __syncthreads();
   permute_block(s_idx, T, E, k, ro, s_cnt, s_base, s_tbase, s_mask);
@@ -496,7 +617,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const double *__restrict__
 template <bool XB, bool WB>
 static hipError_t router_tiled_t(const void *x, const void *wr, const float *bias, float *logits, int T, int E,
                                  int H, hipStream_t s, const Timing *tm) {
-  DS4_LAUNCH(tm, (k_router_tiled<XB, WB>), dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s, x, wr, bias,
+  DS4_LAUNCH(tm, (k_router_mfma<XB, WB>), dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s, x, wr, bias,
              logits, T, E, H);
   return hipGetLastError();
 }
@@ -509,15 +630,22 @@ hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool 
   return router_tiled_t<false, false>(x, wr, bias, logits, T, E, H, s, tm);
 }
 
-hipError_t launch_topk(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
-                       hipStream_t s, const Timing *tm) {
-  XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
-  DS4_LAUNCH(tm, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, H, x, xp != nullptr, ro);
-  return hipGetLastError();
-}
+int chunk_count(int T) { return (T + CHUNK - 1) / CHUNK; }
 
-hipError_t launch_permute(int T, int E, int k, RouteOut ro, hipStream_t s, const Timing *tm) {
-  DS4_LAUNCH(tm, k_permute, dim3(1), dim3(1024), 0, s, T, E, k, ro);
+hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
+                                int32_t *ccnt, int32_t *base, int32_t *lrank, hipStream_t s, const Timing *tm_topk,
+                                const Timing *tm_perm) {
+  const int nchunk = chunk_count(T);
+  XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
+  DS4_LAUNCH(tm_topk, k_topk_chunk, dim3(nchunk), dim3(256), 0, s, logits, T, E, k, H, x, xp != nullptr, ro, ccnt,
+             lrank);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the permutation slot times the scan; the placement follows it directly
+  DS4_LAUNCH(tm_perm, k_scan_chunks, dim3(1), dim3(1024), 0, s, T, E, k, nchunk, ccnt, base, ro);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_place_chunks, dim3(nchunk), dim3(256), 0, s, T, E, k, base, lrank, ro);
   return hipGetLastError();
 }
 
