@@ -13,6 +13,8 @@ constexpr int kVersion = 100;  // 0.1.0
 constexpr int kTileDecode = 16;
 constexpr int kTilePrefill = 64;
 constexpr int64_t kMaxTokens = 1 << 20;
+// decode kernels address their activations as 32-bit byte offsets into the workspace
+constexpr int64_t DS4_WS_WINDOW = (int64_t)1 << 31;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -36,8 +38,11 @@ struct Layout {
   int nzeros;
   size_t total;
   int tile_n, max_tiles, Ipad;
+  bool sliced;  // T <= 16 routing (sliced router + one-workgroup routing); else the chunked path
 };
 
+// Routing of small batches (decode, and route-only calls with T <= 16) uses
+// the sliced router; prefill always uses the MFMA router and chunked top-k.
 Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
   Layout L{};
   size_t off = 0;
@@ -48,35 +53,42 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
   };
   const int64_t E = d.n_experts, k = d.top_k, H = d.hidden, Is = d.shared_inter;
   const int64_t A = T * k;
+  L.sliced = T <= 16 && mode != DS4MOE_MODE_PREFILL;
   L.Ipad = d.inter % 256 ? 256 : d.inter;
   L.tile_n = mode == DS4MOE_MODE_PREFILL ? kTilePrefill : kTileDecode;
-  L.max_tiles = (int)(A / L.tile_n + (A < E ? A : E));
+  L.max_tiles = mode == DS4MOE_MODE_DECODE ? (int)(A < E ? A : E) : (int)(A / L.tile_n + (A < E ? A : E));
   L.logits = take(sizeof(float) * T * E);
-  L.part = T <= 16 ? take(sizeof(double) * (H / 256) * T * E) : 0;
+  L.part = L.sliced ? take(sizeof(double) * router_slices((int)H) * T * E) : 0;
   L.idx = take(sizeof(int32_t) * A);
   L.w = take(sizeof(float) * A);
   L.counts = take(sizeof(int32_t) * E);
   L.offsets = take(sizeof(int32_t) * (E + 1));
   L.perm = take(sizeof(int32_t) * A);
-  if (T > 16) {
+  if (!L.sliced) {
     const int64_t nch = chunk_count((int)T);
     L.ccnt = take(sizeof(int32_t) * nch * E);
     L.cbase = take(sizeof(int32_t) * nch * E);
     L.lrank = take(sizeof(int32_t) * A);
   }
   if (mode != DS4MOE_MODE_ROUTE) {
-    L.pos = take(sizeof(int32_t) * A);
-    L.tiles = take(sizeof(TileT) * (size_t)L.max_tiles);
     L.ntiles = take(16);
     L.x16 = take(2 * T * H);
     L.xs_hi = take(2 * T * (H / 16));
     L.xs_lo = take(2 * T * (H / 16));
-    L.h = take(2 * A * L.Ipad);
-    L.hs_hi = take(2 * A * (L.Ipad / 16));
-    L.hs_lo = take(2 * A * (L.Ipad / 16));
-    L.yp = take(sizeof(float) * A * H);
-    L.nzeros = (int)(H > L.Ipad ? H : L.Ipad);
-    L.zeros = take(2 * (size_t)L.nzeros);
+    // rows of h: assignments (prefill) or (tile, token) pairs (decode)
+    const int64_t hrows = mode == DS4MOE_MODE_DECODE ? (int64_t)L.max_tiles * T : A;
+    L.h = take(2 * hrows * L.Ipad);
+    L.hs_hi = take(2 * hrows * (L.Ipad / 16));
+    L.hs_lo = take(2 * hrows * (L.Ipad / 16));
+    if (mode == DS4MOE_MODE_DECODE) {
+      L.tiles = take(sizeof(DecTile) * (size_t)L.max_tiles);
+    } else {
+      L.tiles = take(sizeof(TileT) * (size_t)L.max_tiles);
+      L.pos = take(sizeof(int32_t) * A);
+      L.yp = take(sizeof(float) * A * H);
+      L.nzeros = (int)(H > L.Ipad ? H : L.Ipad);
+      L.zeros = take(2 * (size_t)L.nzeros);
+    }
     if (Is > 0) {
       L.hsh = take(2 * T * Is);
       L.ysh = take(sizeof(float) * T * H);
@@ -177,22 +189,28 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   };
   const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
   const Ptrs p = routing_ptrs(ws, L, route_out);
-  const bool small = mode == DS4MOE_MODE_DECODE;
 
   XPrep xp{x, xb, at<_Float16>(ws, L.x16), at<_Float16>(ws, L.xs_hi), at<_Float16>(ws, L.xs_lo)};
-  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, at<int32_t>(ws, L.pos),
-              at<TileT>(ws, L.tiles), at<int32_t>(ws, L.ntiles), L.tile_n, at<_Float16>(ws, L.zeros), L.nzeros};
-  if (T <= 16)
+  const bool dec = mode == DS4MOE_MODE_DECODE;
+  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, L.tile_n, nullptr, 0};
+  if (!dec) {
+    ro.pos = at<int32_t>(ws, L.pos);
+    ro.tiles = at<TileT>(ws, L.tiles);
+    ro.ntiles = at<int32_t>(ws, L.ntiles);
+    ro.zeros = at<_Float16>(ws, L.zeros);
+    ro.nzeros = L.nzeros;
+  }
+  DecTile *dtiles = nullptr;
+  if (dec) dtiles = at<DecTile>(ws, L.tiles);
+  int32_t *ntiles = at<int32_t>(ws, L.ntiles);
+  if (L.sliced) {
     TRY(launch_router_sliced(x, xb, w->router_w, wb, at<double>(ws, L.part), T, d.n_experts, d.hidden, &xp, s,
                              tm(SL_ROUTER)));
-  else
+    TRY(launch_route_dec(at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, T, d.n_experts,
+                         d.top_k, ro, dtiles, ntiles, s, tm(SL_ROUTE)));
+  } else {
     TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s,
                             tm(SL_ROUTER)));
-
-  if (T <= 16) {
-    TRY(launch_route_small(at<double>(ws, L.part), d.hidden / 256, w->router_bias, p.logits, T, d.n_experts,
-                           d.top_k, ro, s, tm(SL_ROUTE)));
-  } else {
     TRY(launch_route_chunked(p.logits, T, d.n_experts, d.top_k, d.hidden, &xp, ro, at<int32_t>(ws, L.ccnt),
                              at<int32_t>(ws, L.cbase), at<int32_t>(ws, L.lrank), s, tm(SL_ROUTE), tm(SL_PERMUTE)));
   }
@@ -204,7 +222,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.gu_bytes = ds4moe_packed_bytes(d.inter, d.hidden);
   ga.d_bytes = ds4moe_packed_bytes(d.hidden, d.inter);
   ga.tiles = ro.tiles;
-  ga.ntiles = ro.ntiles;
+  ga.ntiles = ntiles;
   ga.perm = p.perm;
   ga.k = d.top_k;
   ga.H = d.hidden;
@@ -216,21 +234,44 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.h = at<_Float16>(ws, L.h);
   ga.hs_hi = at<_Float16>(ws, L.hs_hi);
   ga.hs_lo = at<_Float16>(ws, L.hs_lo);
-  ga.yp = at<float>(ws, L.yp);
-  ga.zeros = at<_Float16>(ws, L.zeros);
-  TRY(launch_gateup(ga, L.max_tiles, small, s, tm(SL_GATEUP)));
-  TRY(launch_down(ga, L.max_tiles, small, s, tm(SL_DOWN)));
+  ga.yp = dec ? nullptr : at<float>(ws, L.yp);
+  ga.zeros = ro.zeros;
+  ga.dtiles = dtiles;
+  ga.wsb = (const uint8_t *)ws;
+  ga.ws_len = (uint32_t)(L.total < (size_t)DS4_WS_WINDOW ? L.total : (size_t)DS4_WS_WINDOW);
+  ga.o_x16 = (uint32_t)L.x16;
+  ga.o_xs_hi = (uint32_t)L.xs_hi;
+  ga.o_xs_lo = (uint32_t)L.xs_lo;
+  ga.o_h = (uint32_t)L.h;
+  ga.o_hs_hi = (uint32_t)L.hs_hi;
+  ga.o_hs_lo = (uint32_t)L.hs_lo;
+  ga.T = T;
+  ga.y = y;
 
   float *ysh = nullptr;
-  if (d.shared_inter > 0) {
+  auto shared = [&]() -> int {
+    if (d.shared_inter <= 0) return DS4MOE_OK;
     _Float16 *hsh = at<_Float16>(ws, L.hsh);
     ysh = at<float>(ws, L.ysh);
     TRY(launch_shared_gateup((const uint16_t *)w->sh_gate, (const uint16_t *)w->sh_up, xp.x16, hsh, T, d.hidden,
                              d.shared_inter, s, tm(SL_SHGATEUP)));
     TRY(launch_shared_down((const uint16_t *)w->sh_down, hsh, ysh, T, d.hidden, d.shared_inter, s,
                            tm(SL_SHDOWN)));
+    return DS4MOE_OK;
+  };
+  if (dec) {
+    TRY(launch_gateup_dec(ga, L.max_tiles, s, tm(SL_GATEUP)));
+    st = shared();
+    if (st) return st;
+    ga.ysh = ysh;
+    TRY(launch_down_combine_dec(ga, s, tm(SL_DOWN)));
+  } else {
+    TRY(launch_gateup(ga, L.max_tiles, s, tm(SL_GATEUP)));
+    TRY(launch_down(ga, L.max_tiles, s, tm(SL_DOWN)));
+    st = shared();
+    if (st) return st;
+    TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s, tm(SL_COMBINE)));
   }
-  TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s, tm(SL_COMBINE)));
   if (tms) {  // slots without a kernel in this call: empty intervals
     for (int i = 0; i < SL_N; ++i) {
       if (used[i]) continue;
@@ -305,11 +346,11 @@ int ds4moe_route(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x
   const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
   const Ptrs p = routing_ptrs(ws, L, out);
   RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, kTileDecode, nullptr, 0};
-  if (T <= 16) {
+  if (L.sliced) {
     TRY(launch_router_sliced(x, xb, w->router_w, wb, at<double>(ws, L.part), T, d.n_experts, d.hidden, nullptr,
                              s));
-    TRY(launch_route_small(at<double>(ws, L.part), d.hidden / 256, w->router_bias, p.logits, T, d.n_experts,
-                           d.top_k, ro, s));
+    TRY(launch_route_dec(at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, T, d.n_experts,
+                         d.top_k, ro, nullptr, nullptr, s));
     return DS4MOE_OK;
   }
   TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s));

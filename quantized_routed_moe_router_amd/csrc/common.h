@@ -51,16 +51,10 @@ __device__ __forceinline__ h8 dequant_frag(uint32_t raw, h2 sc2) {
   return cat8(p0, p1, p2, p3);
 }
 
-// Eight 4-bit mins (one nibble each) -> exact fp16 values m = lo + 4*hi.
-__device__ __forceinline__ h8 min_frag(uint32_t mdw) {
-  const uint32_t lo = mdw & 0x33333333u;
-  const uint32_t hi = (mdw >> 2) & 0x33333333u;
-  h2 p0 = CVT_FP4(lo, 2.0f, 0) + CVT_FP4(hi, 8.0f, 0);
-  h2 p1 = CVT_FP4(lo, 2.0f, 1) + CVT_FP4(hi, 8.0f, 1);
-  h2 p2 = CVT_FP4(lo, 2.0f, 2) + CVT_FP4(hi, 8.0f, 2);
-  h2 p3 = CVT_FP4(lo, 2.0f, 3) + CVT_FP4(hi, 8.0f, 3);
-  return cat8(p0, p1, p2, p3);
-}
+// fp8 (OCP e4m3) byte pairs -> fp16 pairs.  A byte b <= 15 encodes b * 2^-9
+// exactly (exponent field 0 or 1), so scale 512 gives the small integer b.
+// HI picks the upper 16 bits of `w`; the low byte lands in element 0.
+#define CVT_FP8(w, HI) __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((w), 512.0f, (HI))
 
 __device__ __forceinline__ h2 splat_h2(float v) {
   h2 r;
@@ -81,3 +75,16 @@ __device__ __forceinline__ h8 zero_h8() {
 }
 
 __device__ __forceinline__ h8 load_h8(const half_t *p) { return *reinterpret_cast<const h8 *>(p); }
+
+// Raw buffer access over one region (wave-uniform descriptor).  Lanes with an
+// offset at or beyond the region's length read zeros without touching memory,
+// so masked loads need no branch.
+constexpr uint32_t DS4_OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ h8 buf_load_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}

@@ -32,6 +32,12 @@ namespace ds4 {
 #ifndef GEMM_NW_DN
 #define GEMM_NW_DN 4
 #endif
+#ifndef GU_DEC_PD
+#define GU_DEC_PD 2
+#endif
+#ifndef DN_DEC_PD
+#define DN_DEC_PD 3
+#endif
 
 struct UnitRegs {
   u4 code;   // 4 raw dwords: sub-blocks g, 4+g, 8+g, 12+g of row r
@@ -47,30 +53,47 @@ __device__ __forceinline__ UnitRegs load_unit(const uint8_t *__restrict__ unit, 
   return u;
 }
 
+// The same unit through a buffer descriptor (offset out of range: all zeros,
+// which decode to zero weights).
+__device__ __forceinline__ UnitRegs load_unit_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, int lane) {
+  UnitRegs u;
+  u.code = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * lane, 0, 0));
+  u.scale = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off + DS4_SCALE_OFF + 16 * (lane & 15), 0, 0));
+  u.dd = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off + DS4_DD_OFF + 16 * (lane >> 4), 0, 0));
+  return u;
+}
+
 struct UnitDecoded {
-  h2 sc[4];   // sub-block scales for q = 0..3 (sub-block 4q+g)
-  h8 mfrag;   // min-MFMA A fragment: m of sub-blocks 8*(g&1) .. +7
-  float d[4], dmin[4];
+  h2 sc01, sc23;  // scales of sub-blocks (g, 4+g) and (8+g, 12+g)
+  h8 mfrag;       // min-MFMA A fragment: m of sub-blocks 8*(g&1) .. +7
+  uint32_t dd[4]; // rows 4g..4g+3: d | dmin<<16 (binary16)
 };
+
+__device__ __forceinline__ float dd_d(uint32_t v) { return half_bits_to_float((uint16_t)(v & 0xFFFFu)); }
+__device__ __forceinline__ float dd_dmin(uint32_t v) { return half_bits_to_float((uint16_t)(v >> 16)); }
 
 __device__ __forceinline__ UnitDecoded decode_unit(const UnitRegs &u, int g) {
   UnitDecoded o;
   const uint32_t sw = (g < 2) ? u.scale.x : u.scale.y;
-  const uint32_t hw = (g & 1) ? (sw >> 16) : (sw & 0xFFFFu);
+  const uint32_t hw = (g & 1) ? (sw >> 16) : sw;
+  o.sc01 = CVT_FP8(hw & 0x0F0Fu, false);
+  o.sc23 = CVT_FP8((hw >> 4) & 0x0F0Fu, false);
+  const uint32_t mdw = (g & 1) ? u.scale.w : u.scale.z;
+  const uint32_t lo = mdw & 0x0F0F0F0Fu, hi = (mdw >> 4) & 0x0F0F0F0Fu;
+  o.mfrag = cat8(CVT_FP8(lo, false), CVT_FP8(lo, true), CVT_FP8(hi, false), CVT_FP8(hi, true));
 #pragma unroll
-  for (int q = 0; q < 4; ++q) o.sc[q] = splat_h2((float)((hw >> (4 * q)) & 15u));
-  o.mfrag = min_frag((g & 1) ? u.scale.w : u.scale.z);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o.d[i] = half_bits_to_float((uint16_t)(u.dd[i] & 0xFFFFu));
-    o.dmin[i] = half_bits_to_float((uint16_t)(u.dd[i] >> 16));
-  }
+  for (int i = 0; i < 4; ++i) o.dd[i] = u.dd[i];
   return o;
 }
 
 template <int S>
 __device__ __forceinline__ h8 step_frag(const UnitRegs &u, const UnitDecoded &dc) {
-  return dequant_frag<(S & 1)>(u.code[S >> 1], dc.sc[S >> 1]);
+  constexpr int Q = S >> 1;  // sub-block 4*Q + g
+  const h2 pair = (Q < 2) ? dc.sc01 : dc.sc23;
+  h2 sc2;
+  sc2[0] = pair[Q & 1];
+  sc2[1] = pair[Q & 1];
+  return dequant_frag<(S & 1)>(u.code[Q], sc2);
 }
 
 // offset of the 8 activations a lane (group g) feeds at step S of a super-block
@@ -196,8 +219,8 @@ __device__ __forceinline__ void gemm_compute_sb(const UnitRegs (&u)[R][NM], cons
         const f4 mm = mfma16(dc[r][m].mfrag, bm[nt], (f4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          y[m][r][nt][q] = fmaf(dc[r][m].d[q], acc[m][r][nt][q], y[m][r][nt][q]);
-          y[m][r][nt][q] = fmaf(-dc[r][m].dmin[q], mm[q], y[m][r][nt][q]);
+          y[m][r][nt][q] = fmaf(dd_d(dc[r][m].dd[q]), acc[m][r][nt][q], y[m][r][nt][q]);
+          y[m][r][nt][q] = fmaf(-dd_dmin(dc[r][m].dd[q]), mm[q], y[m][r][nt][q]);
         }
       }
 }
@@ -333,180 +356,234 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   }
 }
 
-// ------------------------------------------------------------------ decode GEMV
-// Small batches (<= 16 tokens per expert): bandwidth-bound weight streaming.
-// Workgroup = one tile x one 16-row tile (of gate and up, or of down); its 4
-// waves split the super-blocks of the reduction dimension, each wave issues
-// the loads of a whole batch of SBW super-blocks before any arithmetic (so
-// each wave keeps up to SBW*1344*matrices bytes in flight), and the four
-// partial sums are added through LDS in wave order.
-template <int SBW>
+// ------------------------------------------------------------------ small batches
+// T <= 16 tokens: token t is MFMA column t of every tile (a zero column where
+// the token did not choose the tile's expert), so h and y are indexed by
+// token: h[(tile*T + t)*Ipad + row].  Weight bytes are streamed once per used
+// expert through a PD-deep register pipeline: the loads of reduction step
+// i+PD are in flight while step i is dequantized and multiplied.
+
+// gate/up + SwiGLU.  Workgroup = one tile x two 16-row tiles; wave = (row
+// tile, half of the reduction); the halves meet in LDS (lower half first).
+template <int PD>
 __global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
-  const int tile_id = blockIdx.x / n_rt;
-  const int rt = blockIdx.x - tile_id * n_rt;
+  const int nrb = (n_rt + 1) >> 1;
+  const int tile_id = blockIdx.x / nrb;
+  const int rb = blockIdx.x - tile_id * nrb;
   if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
-  const TileT tl = a.tiles[tile_id];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
+  const int rt = 2 * rb + (wave >> 1), kh = wave & 1;
+  const int e = a.dtiles[tile_id].e;
+  const uint32_t tmask = a.dtiles[tile_id].tmask;
+  const bool valid = (tmask >> r16) & 1u;  // implies r16 < T
   const int nsb = a.H >> 8;
-  const int per = (nsb + WAVES - 1) / WAVES;
-  const int sb0 = wave * per, sb1 = min(nsb, sb0 + per);
-  const bool valid = r16 < tl.n;
-  const int pidx = tl.p0 + (valid ? r16 : 0);
-  const int tok = a.perm[pidx] / a.k;
-  // lanes without a token read zeros instead of selecting per step
-  const half_t *xrow = valid ? a.x16 + (size_t)tok * a.H : a.zeros;
-  const half_t *xsrow = valid ? ((g >> 1) ? a.xs_lo : a.xs_hi) + (size_t)tok * (a.H >> 4) + 8 * (g & 1) : a.zeros;
-  const uint8_t *G = a.gate + (size_t)tl.e * a.gu_bytes + (size_t)rt * nsb * DS4_UNIT_BYTES;
-  const uint8_t *U = a.up + (size_t)tl.e * a.gu_bytes + (size_t)rt * nsb * DS4_UNIT_BYTES;
+  const int half = (nsb + 1) >> 1;
+  const int sb0 = kh * half;
+  const int nit = max(0, min(nsb, sb0 + half) - sb0);
+  const uint32_t gub = (uint32_t)a.gu_bytes;
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gate + (size_t)e * a.gu_bytes, gub);
+  const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.up + (size_t)e * a.gu_bytes, gub);
+  const uint32_t roff = ((uint32_t)min(rt, n_rt - 1) * nsb + sb0) * DS4_UNIT_BYTES;
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
+  // byte offsets of this lane's activations (out of range: zeros)
+  const uint32_t xoff =
+      valid ? a.o_x16 + 2u * ((uint32_t)r16 * a.H + (uint32_t)sb0 * 256 + 16 * g) : DS4_OOB;
+  const uint32_t xsoff =
+      valid ? ((g >> 1) ? a.o_xs_lo : a.o_xs_hi) + 2u * ((uint32_t)r16 * (a.H >> 4) + 8 * (g & 1) + sb0 * 16)
+            : DS4_OOB;
+
+  struct Stage {
+    UnitRegs wg, wu;
+    h8 b[9];
+  };
+  Stage st[PD];
   f4 yg = (f4){0.f, 0.f, 0.f, 0.f}, yu = yg;
-  for (int b0 = sb0; b0 < sb1; b0 += SBW) {
-    UnitRegs ug[SBW], uu[SBW];
+  // every step issues the same loads (steps past the end read zeros), so the
+  // load counter waits are static and the pipeline never drains
+  auto load = [&](Stage &sg, int i) {
+    const bool in = i < nit;
+    const uint32_t wo = in ? roff + (uint32_t)i * DS4_UNIT_BYTES : DS4_OOB;
+    sg.wg = load_unit_buf(gr, wo, lane);
+    sg.wu = load_unit_buf(ur, wo, lane);
+    const uint32_t xo = in ? xoff + 512u * i : DS4_OOB;
+    const uint32_t so = in ? xsoff + 32u * i : DS4_OOB;
 #pragma unroll
-    for (int i = 0; i < SBW; ++i) {
-      const int sb = min(b0 + i, sb1 - 1);
-      ug[i] = load_unit(G + (size_t)sb * DS4_UNIT_BYTES, lane);
-      uu[i] = load_unit(U + (size_t)sb * DS4_UNIT_BYTES, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < SBW; ++i) {
-      if (b0 + i >= sb1) break;
-      const int kb = (b0 + i) * 256;
-      h8 b[9];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) b[s] = load_h8(xrow + kb + 16 * (4 * (s >> 1) + g) + 8 * (s & 1));
-      b[8] = load_h8(xsrow + (b0 + i) * 16);
-      const UnitDecoded dg = decode_unit(ug[i], g);
-      const UnitDecoded du = decode_unit(uu[i], g);
-      f4 ag = (f4){0.f, 0.f, 0.f, 0.f}, au = ag;
-#define DEC_STEP(S)                                   \
-  ag = mfma16(step_frag<S>(ug[i], dg), b[S], ag);     \
-  au = mfma16(step_frag<S>(uu[i], du), b[S], au);
-      DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
+    for (int q = 0; q < 8; ++q) sg.b[q] = buf_load_h8(ws, xo + 2u * (64 * (q >> 1) + 8 * (q & 1)));
+    sg.b[8] = buf_load_h8(ws, so);
+  };
+  auto compute = [&](const Stage &sg) {
+    const UnitDecoded dg = decode_unit(sg.wg, g);
+    const UnitDecoded du = decode_unit(sg.wu, g);
+    f4 ag = (f4){0.f, 0.f, 0.f, 0.f}, au = ag;
+#define DEC_STEP(S)                                    \
+  ag = mfma16(step_frag<S>(sg.wg, dg), sg.b[S], ag);   \
+  au = mfma16(step_frag<S>(sg.wu, du), sg.b[S], au);
+    DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
 #undef DEC_STEP
-      const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
-      const f4 mg = mfma16(dg.mfrag, b[8], z);
-      const f4 mu = mfma16(du.mfrag, b[8], z);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        yg[q] = fmaf(dg.d[q], ag[q], yg[q]);
-        yg[q] = fmaf(-dg.dmin[q], mg[q], yg[q]);
-        yu[q] = fmaf(du.d[q], au[q], yu[q]);
-        yu[q] = fmaf(-du.dmin[q], mu[q], yu[q]);
-      }
-    }
-  }
-  __shared__ f4 red[2][WAVES][64];
-  red[0][wave][lane] = yg;
-  red[1][wave][lane] = yu;
-  __syncthreads();
-  if (wave != 0) return;
-  yg = red[0][0][lane];
-  yu = red[1][0][lane];
-#pragma unroll
-  for (int w = 1; w < WAVES; ++w) {
-    const f4 pg = red[0][w][lane], pu = red[1][w][lane];
+    const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
+    const f4 mg = mfma16(dg.mfrag, sg.b[8], z);
+    const f4 mu = mfma16(du.mfrag, sg.b[8], z);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      yg[q] += pg[q];
-      yu[q] += pu[q];
+      yg[q] = fmaf(dd_d(dg.dd[q]), ag[q], yg[q]);
+      yg[q] = fmaf(-dd_dmin(dg.dd[q]), mg[q], yg[q]);
+      yu[q] = fmaf(dd_d(du.dd[q]), au[q], yu[q]);
+      yu[q] = fmaf(-dd_dmin(du.dd[q]), mu[q], yu[q]);
+    }
+  };
+#pragma unroll
+  for (int sgi = 0; sgi < PD; ++sgi) load(st[sgi], sgi);
+  for (int i0 = 0; i0 < nit; i0 += PD) {
+#pragma unroll
+    for (int sgi = 0; sgi < PD; ++sgi) {
+      compute(st[sgi]);
+      load(st[sgi], i0 + sgi + PD);
     }
   }
+
+  __shared__ f4 red[2][2][64];  // [row tile of the workgroup][gate, up]
+  const int rl = wave >> 1;
+  if (kh == 1) {
+    red[rl][0][lane] = yg;
+    red[rl][1][lane] = yu;
+  }
+  __syncthreads();
+  if (kh == 1 || rt >= n_rt) return;  // uniform per wave
+  const f4 pg = red[rl][0][lane], pu = red[rl][1][lane];
   half_t hv[4];
   float ssum = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    hv[q] = (half_t)(yg[q] / (1.0f + expf(-yg[q])) * yu[q]);
+    const float gv = yg[q] + pg[q], uv = yu[q] + pu[q];
+    hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
     ssum += (float)hv[q];
   }
   ssum += __shfl_xor(ssum, 16);
   ssum += __shfl_xor(ssum, 32);
-  if (valid) {
-    const int nj = a.Ipad >> 4;
+  if (r16 < a.T) {  // tokens that did not choose the expert get exact zeros
+    const size_t p = (size_t)tile_id * a.T + r16;
     uint2 pk;
     __builtin_memcpy(&pk, hv, 8);
-    *reinterpret_cast<uint2 *>(a.h + (size_t)pidx * a.Ipad + rt * 16 + 4 * g) = pk;
+    *reinterpret_cast<uint2 *>(a.h + p * a.Ipad + rt * 16 + 4 * g) = pk;
     if (g == 0) {
+      const int nj = a.Ipad >> 4;
       const half_t hi = (half_t)ssum;
-      a.hs_hi[(size_t)pidx * nj + rt] = hi;
-      a.hs_lo[(size_t)pidx * nj + rt] = (half_t)(ssum - (float)hi);
+      a.hs_hi[p * nj + rt] = hi;
+      a.hs_lo[p * nj + rt] = (half_t)(ssum - (float)hi);
     }
   }
 }
 
-template <int SBW>
-__global__ __launch_bounds__(256) void k_down_dec(GemmArgs a, int n_rt) {
-  const int tile_id = blockIdx.x / n_rt;
-  const int rt = blockIdx.x - tile_id * n_rt;
-  if (tile_id >= *a.ntiles) return;
-  const TileT tl = a.tiles[tile_id];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// down fused with the combine.  Workgroup = one 16-row tile of y, 8 waves;
+// wave w takes tiles w, w+8, ... (experts ascending), scales each tile's
+// contribution to token t by the token's routing weight, and the eight
+// partial sums are added in wave order, then the shared-expert output.
+template <int PD, bool PADDED>
+__global__ __launch_bounds__(512) void k_down_dec(GemmArgs a) {
+  const int rt = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
+  const int ntl = *a.ntiles;
   const int nsb = a.Ipad >> 8;
   const int nj = a.Ipad >> 4, nj_real = a.I >> 4;
-  const int per = (nsb + WAVES - 1) / WAVES;
-  const int sb0 = wave * per, sb1 = min(nsb, sb0 + per);
-  const bool valid = r16 < tl.n;
-  const int pidx = tl.p0 + (valid ? r16 : 0);
-  const half_t *hrow = valid ? a.h + (size_t)pidx * a.Ipad : a.zeros;
-  const half_t *hsrow = valid ? ((g >> 1) ? a.hs_lo : a.hs_hi) + (size_t)pidx * nj + 8 * (g & 1) : a.zeros;
-  const bool padded = a.I != a.Ipad;
-  const uint8_t *D = a.down + (size_t)tl.e * a.d_bytes + (size_t)rt * nsb * DS4_UNIT_BYTES;
+  const int mt = wave < ntl ? (ntl - wave + 7) >> 3 : 0;  // tiles of this wave (<= 32)
+  const int nit = mt * nsb;
+  int e_l = 0;        // lane L: expert of this wave's L-th tile
+  uint32_t m_l = 0u;  // ... and its token mask
+  if (lane < mt) {
+    e_l = a.dtiles[wave + 8 * lane].e;
+    m_l = a.dtiles[wave + 8 * lane].tmask;
+  }
+  // wait for them here, before any weight load is in flight, so that the
+  // pipelined loop below never has to drain the load counter for them
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
+  const uint32_t hs_base = ((g >> 1) ? a.o_hs_lo : a.o_hs_hi) + 2u * (8 * (g & 1));
+
+  struct Stage {
+    UnitRegs wd;
+    h8 b[9];
+    float wt;
+  };
+  Stage st[PD];
   f4 y = (f4){0.f, 0.f, 0.f, 0.f};
-  for (int b0 = sb0; b0 < sb1; b0 += SBW) {
-    UnitRegs ud[SBW];
+  int lt = 0, lsb = 0;  // tile and super-block of the next load
+  // every step issues the same loads (steps past the end read zeros), so the
+  // load counter waits are static and the pipeline never drains
+  auto load = [&](Stage &sg) {
+    const bool in = lt < mt;
+    const int tile = min(wave + 8 * lt, ntl - 1);
+    const int e = __builtin_amdgcn_readlane(e_l, lt & 63);
+    const uint32_t tmask = in ? (uint32_t)__builtin_amdgcn_readlane((int)m_l, lt & 63) : 0u;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.down + (size_t)e * a.d_bytes, (uint32_t)a.d_bytes);
+    sg.wd = load_unit_buf(wr, in ? ((uint32_t)rt * nsb + lsb) * DS4_UNIT_BYTES : DS4_OOB, lane);
+    // h of token r16 if it chose the expert (zeros otherwise, weight 0)
+    const bool routed = (tmask >> r16) & 1u;  // implies r16 < T
+    const uint32_t p = (uint32_t)tile * a.T + r16;
+    const uint32_t hoff = routed ? a.o_h + 2u * (p * a.Ipad + lsb * 256 + 16 * g) : DS4_OOB;
+    const uint32_t soff = routed ? hs_base + 2u * (p * nj + lsb * 16) : DS4_OOB;
 #pragma unroll
-    for (int i = 0; i < SBW; ++i) ud[i] = load_unit(D + (size_t)min(b0 + i, sb1 - 1) * DS4_UNIT_BYTES, lane);
+    for (int q = 0; q < 8; ++q) {
+      uint32_t o = hoff + 2u * (64 * (q >> 1) + 8 * (q & 1));
+      if (PADDED && lsb * 256 + 16 * (4 * (q >> 1) + g) + 8 * (q & 1) >= a.I) o = DS4_OOB;  // columns >= I
+      sg.b[q] = buf_load_h8(ws, o);
+    }
+    h8 v = buf_load_h8(ws, soff);
+    if (PADDED) {
+      const int j0 = lsb * 16 + 8 * (g & 1);
 #pragma unroll
-    for (int i = 0; i < SBW; ++i) {
-      if (b0 + i >= sb1) break;
-      const int kb = (b0 + i) * 256;
-      h8 b[9];
-      if (!padded) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) b[s] = load_h8(hrow + kb + 16 * (4 * (s >> 1) + g) + 8 * (s & 1));
-        b[8] = load_h8(hsrow + (b0 + i) * 16);
-      } else {  // reduction length not a multiple of 256: columns >= I read as zero
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int col = kb + 16 * (4 * (s >> 1) + g) + 8 * (s & 1);
-          b[s] = col < a.I ? load_h8(hrow + col) : zero_h8();
-        }
-        const int j0 = (b0 + i) * 16 + 8 * (g & 1);
-        h8 v = zero_h8();
-        if (j0 < nj_real) {
-          v = load_h8(hsrow + (b0 + i) * 16);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (j0 + e >= nj_real) v[e] = (half_t)0.0f;
-        }
-        b[8] = v;
-      }
-      const UnitDecoded dd = decode_unit(ud[i], g);
-      f4 ac = (f4){0.f, 0.f, 0.f, 0.f};
-#define DEC_STEP(S) ac = mfma16(step_frag<S>(ud[i], dd), b[S], ac);
-      DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
+      for (int q = 0; q < 8; ++q)
+        if (j0 + q >= nj_real) v[q] = (half_t)0.0f;
+    }
+    sg.b[8] = v;
+    sg.wt = a.dtiles[tile].w[r16];  // 0 for tokens that did not choose the expert
+    if (++lsb == nsb) {
+      lsb = 0;
+      ++lt;
+    }
+  };
+  auto compute = [&](const Stage &sg) {
+    const UnitDecoded dd = decode_unit(sg.wd, g);
+    f4 ac = (f4){0.f, 0.f, 0.f, 0.f};
+#define DEC_STEP(S) ac = mfma16(step_frag<S>(sg.wd, dd), sg.b[S], ac);
+    DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
 #undef DEC_STEP
-      const f4 mm = mfma16(dd.mfrag, b[8], (f4){0.f, 0.f, 0.f, 0.f});
+    const f4 mm = mfma16(dd.mfrag, sg.b[8], (f4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        y[q] = fmaf(dd.d[q], ac[q], y[q]);
-        y[q] = fmaf(-dd.dmin[q], mm[q], y[q]);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const float v = fmaf(dd_d(dd.dd[q]), ac[q], -dd_dmin(dd.dd[q]) * mm[q]);
+      y[q] = fmaf(sg.wt, v, y[q]);
+    }
+  };
+#pragma unroll
+  for (int sgi = 0; sgi < PD; ++sgi) load(st[sgi]);
+  for (int i0 = 0; i0 < nit; i0 += PD) {
+#pragma unroll
+    for (int sgi = 0; sgi < PD; ++sgi) {
+      compute(st[sgi]);
+      load(st[sgi]);
     }
   }
-  __shared__ f4 red[WAVES][64];
+  __shared__ f4 red[8][64];
   red[wave][lane] = y;
   __syncthreads();
   if (wave != 0) return;
-  y = red[0][lane];
 #pragma unroll
-  for (int w = 1; w < WAVES; ++w) {
+  for (int w = 1; w < 8; ++w) {
     const f4 p = red[w][lane];
 #pragma unroll
     for (int q = 0; q < 4; ++q) y[q] += p[q];
   }
-  if (valid) *reinterpret_cast<f4 *>(a.yp + (size_t)pidx * a.H + rt * 16 + 4 * g) = y;
+  if (r16 < a.T) {
+    const size_t o = (size_t)r16 * a.H + rt * 16 + 4 * g;
+    if (a.ysh) {
+      const f4 v = *reinterpret_cast<const f4 *>(a.ysh + o);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] += v[q];
+    }
+    *reinterpret_cast<f4 *>(a.y + o) = y;
+  }
 }
 
 // ------------------------------------------------------------------ combine
@@ -654,15 +731,9 @@ __global__ __launch_bounds__(256) void k_shared_down(const uint16_t *__restrict_
 }
 
 // ------------------------------------------------------------------ launchers
-// Decode batches (<= 16 tokens per expert): the split-reduction GEMV kernels.
 // Prefill: four n-tiles (64 tokens) per workgroup.
-hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream_t s, const Timing *tm) {
+hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
-  if (small) {
-    const int n_rt = a.I >> 4;
-    DS4_LAUNCH(tm, (k_gateup_dec<4>), dim3((unsigned)((int64_t)n_rt * max_tiles)), dim3(256), 0, s, a, n_rt);
-    return hipGetLastError();
-  }
   constexpr int R = GEMM_R_GU, NW = GEMM_NW_GU;
   const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.I + rows_per_wg - 1) / rows_per_wg;
@@ -671,13 +742,8 @@ hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t s, const Timing *tm) {
+hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
-  if (small) {
-    const int n_rt = a.H >> 4;
-    DS4_LAUNCH(tm, (k_down_dec<2>), dim3((unsigned)((int64_t)n_rt * max_tiles)), dim3(256), 0, s, a, n_rt);
-    return hipGetLastError();
-  }
   constexpr int R = GEMM_R_DN, NW = GEMM_NW_DN;
   const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.H + rows_per_wg - 1) / rows_per_wg;
@@ -686,6 +752,23 @@ hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t
     DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, false>), grid, dim3(64 * NW), 0, s, a, nrb);
   else
     DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, true>), grid, dim3(64 * NW), 0, s, a, nrb);
+  return hipGetLastError();
+}
+
+// Small batches (T <= 16).
+hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
+  if (max_tiles <= 0) return hipSuccess;
+  const int n_rt = a.I >> 4;
+  const int nrb = (n_rt + 1) >> 1;
+  DS4_LAUNCH(tm, (k_gateup_dec<GU_DEC_PD>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(256), 0, s, a, n_rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm) {
+  if (a.I == a.Ipad)
+    DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, false>), dim3((unsigned)(a.H >> 4)), dim3(512), 0, s, a);
+  else
+    DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, true>), dim3((unsigned)(a.H >> 4)), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

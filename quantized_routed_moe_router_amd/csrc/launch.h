@@ -17,6 +17,15 @@ struct TileT {
   int32_t e, p0, n, pad;
 };
 
+// Small-batch (T <= 16) work item: one used expert, the tokens that chose it
+// (bit t of tmask) and their routing weights (0 for other tokens).
+struct DecTile {
+  int32_t e;
+  uint32_t tmask;
+  int32_t pad0, pad1;
+  float w[16];
+};
+
 // Activation preparation done per token next to the router: x -> fp16 and
 // per-16-element sums (split into fp16 hi + lo) for the min term.
 struct XPrep {
@@ -53,6 +62,14 @@ struct GemmArgs {
   _Float16 *h, *hs_hi, *hs_lo;       // [T*k, Ipad], [T*k, Ipad/16]
   float *yp;                         // [T*k, H]
   const _Float16 *zeros;             // >= max(H, Ipad) zero halves
+  // small batches: activations addressed as byte offsets inside the workspace
+  const uint8_t *wsb;
+  uint32_t ws_len;
+  uint32_t o_x16, o_xs_hi, o_xs_lo, o_h, o_hs_hi, o_hs_lo;
+  const DecTile *dtiles;
+  int T;
+  const float *ysh;                  // [T,H] shared-expert output or nullptr
+  float *y;                          // [T,H]
 };
 
 hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols,
@@ -67,17 +84,22 @@ int chunk_count(int T);
 hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
                                 int32_t *ccnt, int32_t *base, int32_t *lrank, hipStream_t s,
                                 const Timing *tm_topk = nullptr, const Timing *tm_perm = nullptr);
-// T <= 16: logits as fp64 partial sums per 256-column slice [H/256][T][E],
+// T <= 16: logits as fp64 partial sums per column slice [router_slices(H)][T][E],
 // with the activation preparation (if xp != nullptr)
+int router_slices(int H);
 hipError_t launch_router_sliced(const void *x, bool x_bf16, const void *wr, bool w_bf16, double *part, int T,
                                 int E, int H, const XPrep *xp, hipStream_t s, const Timing *tm = nullptr);
-// one workgroup, T <= 16: slice sums + bias -> logits, top-k, permutation
-hipError_t launch_route_small(const double *part, int nslice, const float *bias, float *logits, int T, int E,
-                              int k, RouteOut ro, hipStream_t s, const Timing *tm = nullptr);
+// one workgroup, T <= 16: slice sums + bias -> logits, top-k, counts, offsets,
+// permutation and (dt != nullptr) the small-batch tiles
+hipError_t launch_route_dec(const double *part, int nslice, const float *bias, float *logits, int T, int E, int k,
+                            RouteOut ro, DecTile *dt, int32_t *ntile, hipStream_t s, const Timing *tm = nullptr);
 
 // grouped GEMMs over the tile list (max_tiles = grid bound)
-hipError_t launch_gateup(const GemmArgs &a, int max_tiles, bool small, hipStream_t s, const Timing *tm = nullptr);
-hipError_t launch_down(const GemmArgs &a, int max_tiles, bool small, hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
+// small batches: gate/up over the DecTile list, and down fused with the combine (writes y)
+hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm = nullptr);
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,
                           int k, int H, hipStream_t s, const Timing *tm = nullptr);
 // dense shared expert, bf16 weights

@@ -61,18 +61,20 @@ __global__ __launch_bounds__(64) void k_pack(uint8_t *__restrict__ dst, const ui
         mn[j] = b >> 4;
       }
     }
+    // halfword gg: byte 0 = scales of sub-blocks gg (low nibble) and 8+gg (high),
+    // byte 1 = scales of 4+gg and 12+gg; w2/w3: mins of sub-blocks 0-7 / 8-15,
+    // byte b holding sub-block b (low nibble) and 4+b (high)
     uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
     for (int gg = 0; gg < 4; ++gg) {
-      uint32_t hw = 0;
-      for (int q = 0; q < 4; ++q) hw |= sc[4 * q + gg] << (4 * q);
+      const uint32_t hw = (sc[gg] | (sc[8 + gg] << 4)) | ((sc[4 + gg] | (sc[12 + gg] << 4)) << 8);
       if (gg == 0) w0 |= hw;
       if (gg == 1) w0 |= hw << 16;
       if (gg == 2) w1 |= hw;
       if (gg == 3) w1 |= hw << 16;
     }
-    for (int b = 0; b < 8; ++b) {
-      w2 |= mn[b] << (4 * b);
-      w3 |= mn[8 + b] << (4 * b);
+    for (int b = 0; b < 4; ++b) {
+      w2 |= (mn[b] | (mn[4 + b] << 4)) << (8 * b);
+      w3 |= (mn[8 + b] | (mn[12 + b] << 4)) << (8 * b);
     }
     *reinterpret_cast<u4 *>(u + DS4_SCALE_OFF + 16 * lane) = (u4){w0, w1, w2, w3};
     // d and dmin of the block holding this row's chunk
@@ -102,9 +104,10 @@ __global__ __launch_bounds__(256) void k_dequant(float *__restrict__ dst, const 
   const uint32_t raw = *reinterpret_cast<const uint32_t *>(u + 16 * (16 * g + r) + 4 * q);
   const uint32_t code = (raw >> (4 * (i & 7) + 2 * (i >> 3))) & 3u;
   const uint16_t schw = *reinterpret_cast<const uint16_t *>(u + DS4_SCALE_OFF + 16 * r + 2 * g);
-  const uint32_t sc = (schw >> (4 * q)) & 15u;
-  const uint8_t mb = u[DS4_SCALE_OFF + 16 * r + 8 + (j >> 1)];
-  const uint32_t mn = (mb >> (4 * (j & 1))) & 15u;
+  const uint32_t sc = (schw >> (8 * (q & 1) + 4 * (q >> 1))) & 15u;
+  const int jj = j & 7;
+  const uint8_t mb = u[DS4_SCALE_OFF + 16 * r + 8 + 4 * (j >> 3) + (jj & 3)];
+  const uint32_t mn = (mb >> (4 * (jj >> 2))) & 15u;
   const uint32_t dd = *reinterpret_cast<const uint32_t *>(u + DS4_DD_OFF + 4 * r);
   const float d = half_bits_to_float((uint16_t)(dd & 0xFFFF));
   const float dmin = half_bits_to_float((uint16_t)(dd >> 16));

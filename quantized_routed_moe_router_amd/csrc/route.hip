@@ -28,91 +28,146 @@ __device__ __forceinline__ void load4_as_double(const void *p, int64_t idx, doub
 }
 
 // ---------------------------------------------------------------- logits, T <= 16, sliced
-// Grid (E/4 expert groups) x (H/256 column slices): wave = one expert, lane =
-// 4 columns of the slice, every token.  Partial sums of a slice are reduced
-// over the 64 lanes in lane order through LDS and stored per slice in fp64;
-// the routing kernel adds the slices in slice order.  Workgroups of expert
-// group 0 also convert their slice of x to fp16 and form the 16-column sums.
+// Grid (E/4 expert groups) x (H/1024 column slices), 256 threads.  The slice
+// of x (T tokens x up to 1024 columns) is staged in LDS as fp32; wave = one
+// expert, lane = columns 4*lane + 256*i (i < 4).  Products of bf16/fp32
+// inputs are exact in fp64, so the per-token sums over the lanes (a
+// reduce-scatter butterfly) and over the slices (routing kernel, slice order)
+// give the fp64 dot product up to fp64 rounding.  Workgroups of expert group
+// 0 also convert their slice of x to fp16 and form the 16-column sums.
+constexpr int RSLICE = 1024;
+
 template <bool XB, bool WB>
 __global__ __launch_bounds__(256) void k_router_sliced(const void *__restrict__ x, const void *__restrict__ wr,
                                                        double *__restrict__ part, int T, int E, int H, XPrep xp,
                                                        bool do_x) {
-  __shared__ double red[4][16][65];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float xs[16 * RSLICE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e = blockIdx.x * 4 + wave;
   const int slice = blockIdx.y;
-  const int h = slice * 256 + 4 * lane;
-  double acc[16];
+  const int c0 = slice * RSLICE;
+  const int cw = min(RSLICE, H - c0);  // multiple of 256
+  // weights of this lane's columns (issued first)
+  double w[4][4];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) acc[t] = 0.0;
-  if (e < E) {
-    double w4[4];
-    load4_as_double<WB>(wr, (int64_t)e * H + h, w4);
-    double x4[16][4];
+  for (int i = 0; i < 4; ++i) {
+    if (e < E && 256 * i < cw) {
+      load4_as_double<WB>(wr, (int64_t)e * H + c0 + 256 * i + 4 * lane, w[i]);
+    } else {
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      if (t < T) load4_as_double<XB>(x, (int64_t)t * H + h, x4[t]);
+      for (int q = 0; q < 4; ++q) w[i][q] = 0.0;
+    }
+  }
+  // stage x[0:T, c0:c0+cw] as fp32: 16-byte loads, all in flight
+  {
+    constexpr int V = XB ? 8 : 4;  // elements per 16-byte load
+    constexpr int MAXL = 16 * RSLICE / V / 256;
+    const int per_row = cw / V;
+    const int nld = T * per_row;
+    u4 v[MAXL];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      if (t < T) {
-        acc[t] = fma(x4[t][0], w4[0], acc[t]);
-        acc[t] = fma(x4[t][1], w4[1], acc[t]);
-        acc[t] = fma(x4[t][2], w4[2], acc[t]);
-        acc[t] = fma(x4[t][3], w4[3], acc[t]);
+    for (int q = 0; q < MAXL; ++q) {
+      const int li = tid + 256 * q;
+      if (li < nld) {
+        const int t = li / per_row, c = (li - t * per_row) * V;
+        const char *src = reinterpret_cast<const char *>(x) + ((int64_t)t * H + c0 + c) * (XB ? 2 : 4);
+        v[q] = *reinterpret_cast<const u4 *>(src);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < MAXL; ++q) {
+      const int li = tid + 256 * q;
+      if (li < nld) {
+        const int t = li / per_row, c = (li - t * per_row) * V;
+        float *dst = xs + t * RSLICE + c;
+        if (XB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dst[2 * i] = bf16_bits_to_float((uint16_t)(v[q][i] & 0xFFFFu));
+            dst[2 * i + 1] = bf16_bits_to_float((uint16_t)(v[q][i] >> 16));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = __uint_as_float(v[q][i]);
+        }
       }
     }
   }
-#pragma unroll
-  for (int t = 0; t < 16; ++t)
-    if (t < T) red[wave][t][lane] = acc[t];
   __syncthreads();
-  if (lane < T && e < E) {
-    double v = 0.0;
-    for (int l = 0; l < 64; ++l) v += red[wave][lane][l];
-    part[((int64_t)slice * T + lane) * E + e] = v;
-  }
-  if (do_x && blockIdx.x == 0) {
-    const int t = threadIdx.x >> 4, j = threadIdx.x & 15;  // token, sub-block of this slice
+  double acc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    acc[t] = 0.0;
     if (t < T) {
-      const int64_t base = (int64_t)t * H + slice * 256 + 16 * j;
-      float v[16];
-      if (xp.x_bf16) {
-        const u4 a = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(x) + base);
-        const u4 b = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(x) + base + 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf16_bits_to_float((uint16_t)(a[i] & 0xFFFF));
-          v[2 * i + 1] = bf16_bits_to_float((uint16_t)(a[i] >> 16));
-          v[8 + 2 * i] = bf16_bits_to_float((uint16_t)(b[i] & 0xFFFF));
-          v[8 + 2 * i + 1] = bf16_bits_to_float((uint16_t)(b[i] >> 16));
-        }
-      } else {
-        const float *p = reinterpret_cast<const float *>(x) + base;
+      for (int i = 0; i < 4; ++i) {
+        if (256 * i < cw) {
+          const f4 xv = *reinterpret_cast<const f4 *>(xs + t * RSLICE + 256 * i + 4 * lane);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f4 a = *reinterpret_cast<const f4 *>(p + 4 * q);
-          v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
+          for (int q = 0; q < 4; ++q) acc[t] = fma((double)xv[q], w[i][q], acc[t]);
         }
       }
+    }
+  }
+  // reduce-scatter over the 64 lanes: after the halving steps lane l holds
+  // token ((l>>5)&1)*8 + ((l>>4)&1)*4 + ((l>>3)&1)*2 + ((l>>2)&1) summed over
+  // 16 lanes; two more steps complete the sum over all 64
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool up = (lane >> 5) & 1;
+    const double send = up ? acc[j] : acc[8 + j];
+    const double keep = up ? acc[8 + j] : acc[j];
+    acc[j] = keep + __shfl_xor(send, 32);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool up = (lane >> 4) & 1;
+    const double send = up ? acc[j] : acc[4 + j];
+    const double keep = up ? acc[4 + j] : acc[j];
+    acc[j] = keep + __shfl_xor(send, 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bool up = (lane >> 3) & 1;
+    const double send = up ? acc[j] : acc[2 + j];
+    const double keep = up ? acc[2 + j] : acc[j];
+    acc[j] = keep + __shfl_xor(send, 8);
+  }
+  {
+    const bool up = (lane >> 2) & 1;
+    const double send = up ? acc[0] : acc[1];
+    const double keep = up ? acc[1] : acc[0];
+    acc[0] = keep + __shfl_xor(send, 4);
+  }
+  acc[0] += __shfl_xor(acc[0], 2);
+  acc[0] += __shfl_xor(acc[0], 1);
+  const int tok = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+  if ((lane & 3) == 0 && tok < T && e < E) part[((int64_t)slice * T + tok) * E + e] = acc[0];
+  if (do_x && blockIdx.x == 0) {
+    // x slice -> fp16 and per-16-column sums of the fp16 values (hi + lo)
+    const int nsub = cw >> 4;
+    for (int q = tid; q < T * nsub; q += 256) {
+      const int t = q / nsub, j = q - t * nsub;
+      const float *src = xs + t * RSLICE + 16 * j;
       h8 o0, o1;
       float sum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        o0[i] = (half_t)v[i];
+        o0[i] = (half_t)src[i];
         sum += (float)o0[i];
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        o1[i] = (half_t)v[8 + i];
+        o1[i] = (half_t)src[8 + i];
         sum += (float)o1[i];
       }
+      const int64_t base = (int64_t)t * H + c0 + 16 * j;
       *reinterpret_cast<h8 *>(xp.x16 + base) = o0;
       *reinterpret_cast<h8 *>(xp.x16 + base + 8) = o1;
-      const int nsub = H >> 4;
-      const int jj = slice * 16 + j;
+      const int64_t sj = (int64_t)t * (H >> 4) + (c0 >> 4) + j;
       const half_t hi = (half_t)sum;
-      xp.xs_hi[(int64_t)t * nsub + jj] = hi;
-      xp.xs_lo[(int64_t)t * nsub + jj] = (half_t)(sum - (float)hi);
+      xp.xs_hi[sj] = hi;
+      xp.xs_lo[sj] = (half_t)(sum - (float)hi);
     }
   }
 }
@@ -471,146 +526,208 @@ __global__ __launch_bounds__(256) void k_place_chunks(int T, int E, int k, const
   }
 }
 
-// ---------------------------------------------------------------- permutation
-// Whole workgroup (1024 threads).  Counts by LDS integer atomics (order does
-// not matter for integers), exclusive scan by one wave, then a stable
-// placement in chunks of 1024 tokens: for each expert a bitmask of the chunk's
-// tokens that chose it; the rank of token t = number of set bits below t.
-__device__ void permute_block(const int32_t *__restrict__ idx, int T, int E, int k, RouteOut ro,
-                              int32_t *s_cnt, int32_t *s_base, int32_t *s_tbase, uint32_t *s_mask) {
-  const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
-  if (ro.zeros)
-    for (int i = tid; i < ro.nzeros; i += nthr) ro.zeros[i] = (half_t)0.0f;
-  for (int e = tid; e < E; e += nthr) s_cnt[e] = 0;
+// ---------------------------------------------------------------- routing, T <= 16
+// wave-wide max of a 32-bit value: DPP prefix maxima inside each 16-lane row,
+// then row broadcasts; lane 63 ends with the maximum.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// order-preserving 32-bit key of a logit: larger logit -> larger key; every
+// number maps to >= 0x007FFFFF, NaN to 1 (below every number), 0 = no expert
+__device__ __forceinline__ uint32_t logit_key(float l) {
+  if (l != l) return 1u;
+  uint32_t u = __float_as_uint(l);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_logit(uint32_t key) {
+  if (key == 1u) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Top-k of one token by one wave from its E logits in LDS: k rounds of
+// (wave max of the keys, lowest expert index among the lanes that hold it).
+// Lane j < k ends with rank j: expert, normalised weight.
+__device__ __forceinline__ void topk_wave(const float *__restrict__ lg, int E, int k, int &my_e, float &my_w) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? logit_key(lg[e]) : 0u;
+  }
+  my_e = 0;
+  float my_l = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t m = key[0] > key[1] ? key[0] : key[1];
+    const uint32_t m2 = key[2] > key[3] ? key[2] : key[3];
+    m = wave_max_u32(m > m2 ? m : m2);
+    // lowest e = lane + 64*i holding the maximum: smallest i, then lowest lane
+    int sel = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t b = __ballot(key[i] == m);
+      if (!found && b) {
+        sel = 64 * i + __ffsll((unsigned long long)b) - 1;
+        found = true;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == sel) key[i] = 0u;
+    if (lane == j) {
+      my_e = sel;
+      my_l = key_to_logit(m);
+    }
+  }
+  float sc = lane < k ? router_score(my_l) : 0.0f;
+  float S = sc;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+  my_w = sc / S;
+}
+
+// One workgroup, 1 <= T <= 16: slice sums + bias -> logits, top-k of token t
+// by wave t, then per expert the mask of tokens that chose it: counts,
+// offsets, the stable permutation (tokens ascending within an expert) and,
+// for the expert kernels, one tile per used expert in ascending order with
+// its token mask and per-token weights.
+__global__ __launch_bounds__(1024) void k_route_dec(const double *__restrict__ part, int nslice,
+                                                    const float *__restrict__ bias, float *__restrict__ logits, int T,
+                                                    int E, int k, RouteOut ro, DecTile *__restrict__ dt,
+                                                    int32_t *__restrict__ ntile) {
+  __shared__ float s_lg[16 * 256];
+  __shared__ int32_t s_idx[16 * 16];
+  __shared__ float s_w[16 * 16];
+  __shared__ uint32_t s_tm[256];
+  __shared__ int32_t s_off[256], s_tb[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = T * E;
+  if (tid < 256) s_tm[tid] = 0u;
+  {
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int s0 = 0; s0 < nslice; s0 += 4) {
+      double pv[4][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = tid + 1024 * q;
+          pv[q][u] = (i < n && s0 + u < nslice) ? part[(int64_t)(s0 + u) * n + i] : 0.0;
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s0 + u < nslice) v[q] += pv[q][u];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + 1024 * q;
+      if (i < n) {
+        double vv = v[q];
+        if (bias) vv += (double)bias[i % E];
+        const float l = (float)vv;
+        s_lg[i] = l;
+        logits[i] = l;
+      }
+    }
+  }
   __syncthreads();
-  const int64_t nA = (int64_t)T * k;
-  for (int64_t a = tid; a < nA; a += nthr) atomicAdd(&s_cnt[idx[a]], 1);
+  if (wave < T) {
+    int my_e;
+    float my_w;
+    topk_wave(s_lg + wave * E, E, k, my_e, my_w);
+    if (lane < k) {
+      const int a = wave * k + lane;
+      ro.idx[a] = my_e;
+      ro.w[a] = my_w;
+      s_idx[a] = my_e;
+      s_w[a] = my_w;
+    }
+  }
   __syncthreads();
-  if (tid < 64) {
-    // exclusive scans of counts and of tiles per expert; 4 experts per lane
-    const int lane = tid;
-    int c[4], nt[4], sc = 0, st = 0;
+  if (tid < T * k) atomicOr(&s_tm[s_idx[tid]], 1u << (tid / k));
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scans over experts (4 per lane) of counts and of used flags
+    int c[4], u[4], sc = 0, su = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
-      c[i] = e < E ? s_cnt[e] : 0;
-      nt[i] = (ro.tiles && c[i] > 0) ? (c[i] + ro.tile_n - 1) / ro.tile_n : 0;
+      const uint32_t tm = e < E ? s_tm[e] : 0u;
+      c[i] = __popc(tm);
+      u[i] = tm != 0u;
       sc += c[i];
-      st += nt[i];
+      su += u[i];
     }
-    int ic = sc, it = st;  // inclusive wave scans
+    int ic = sc, iu = su;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int oc = __shfl_up(ic, off), ot = __shfl_up(it, off);
+      const int oc = __shfl_up(ic, off), ou = __shfl_up(iu, off);
       if (lane >= off) {
         ic += oc;
-        it += ot;
+        iu += ou;
       }
     }
-    int rc = ic - sc, rt = it - st;
+    int rc = ic - sc, ru = iu - su;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
       if (e < E) {
-        s_base[e] = rc;
-        s_tbase[e] = rt;
+        s_off[e] = rc;
+        s_tb[e] = ru;
         ro.counts[e] = c[i];
         ro.offsets[e] = rc;
       }
       rc += c[i];
-      rt += nt[i];
+      ru += u[i];
     }
     if (lane == 63) {
       ro.offsets[E] = ic;
-      if (ro.ntiles) *ro.ntiles = it;
+      if (ntile) *ntile = iu;
     }
   }
   __syncthreads();
-  if (ro.tiles) {
-    for (int e = tid; e < E; e += nthr) {
-      const int c = s_cnt[e];
-      const int nt = (c + ro.tile_n - 1) / ro.tile_n;
-      for (int i = 0; i < nt; ++i) {
-        TileT tl;
-        tl.e = e;
-        tl.p0 = s_base[e] + i * ro.tile_n;
-        tl.n = min(ro.tile_n, c - i * ro.tile_n);
-        tl.pad = 0;
-        ro.tiles[s_tbase[e] + i] = tl;
+  if (dt && tid < E) {
+    const uint32_t tm = s_tm[tid];
+    if (tm) {
+      DecTile *d = dt + s_tb[tid];
+      d->e = tid;
+      d->tmask = tm;
+      d->pad0 = 0;
+      d->pad1 = 0;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        float wt = 0.0f;
+        if ((tm >> t) & 1u)
+          for (int j = 0; j < k; ++j)
+            if (s_idx[t * k + j] == tid) wt = s_w[t * k + j];
+        d->w[t] = wt;
       }
     }
   }
-  // stable placement, chunks of nthr tokens (nthr <= 1024, 32 words per expert)
-  const int words = nthr / 32;
-  for (int t0 = 0; t0 < T; t0 += nthr) {
-    for (int i = tid; i < E * words; i += nthr) s_mask[i] = 0u;
-    __syncthreads();
-    const int t = t0 + tid;
-    if (t < T)
-      for (int j = 0; j < k; ++j) atomicOr(&s_mask[idx[(int64_t)t * k + j] * words + (tid >> 5)], 1u << (tid & 31));
-    __syncthreads();
-    if (t < T) {
-      for (int j = 0; j < k; ++j) {
-        const int e = idx[(int64_t)t * k + j];
-        const uint32_t *m = s_mask + e * words;
-        int rank = __popc(m[tid >> 5] & ((1u << (tid & 31)) - 1u));
-        for (int w = 0; w < (tid >> 5); ++w) rank += __popc(m[w]);
-        const int p = s_base[e] + rank;
-        const int a = t * k + j;
-        ro.perm[p] = a;
-        if (ro.pos) ro.pos[a] = p;
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += nthr) {
-      int c = 0;
-      for (int w = 0; w < words; ++w) c += __popc(s_mask[e * words + w]);
-      s_base[e] += c;
-    }
-    __syncthreads();
+  if (tid < T * k) {
+    const int e = s_idx[tid], t = tid / k;
+    const int p = s_off[e] + __popc(s_tm[e] & ((1u << t) - 1u));
+    ro.perm[p] = tid;
+    if (ro.pos) ro.pos[tid] = p;
   }
-}
-
-// T <= 16: the whole block adds the slice partial sums of every (token,
-// expert) in slice order plus the bias (loads of all slices in flight at
-// once), then waves 0..T-1 route one token each from LDS, then the block
-// permutes.
-__global__ __launch_bounds__(1024) void k_route_small(const double *__restrict__ part, int nslice,
-                                                      const float *__restrict__ bias, float *__restrict__ logits,
-                                                      int T, int E, int k, RouteOut ro) {
-  __shared__ int32_t s_cnt[256], s_base[256], s_tbase[256];
-  __shared__ uint32_t s_mask[256 * 32];
-  __shared__ int32_t s_idx[16 * 16];
-  __shared__ float s_lg[16 * 256];
-  const int n = T * E;
-  for (int i = threadIdx.x; i < n; i += 1024) {
-    // slices in increasing order; loads issued 8 at a time ahead of the adds
-    double v = 0.0;
-    for (int q0 = 0; q0 < nslice; q0 += 8) {
-      double pv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pv[u] = (q0 + u < nslice) ? part[(int64_t)(q0 + u) * n + i] : 0.0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (q0 + u < nslice) v += pv[u];
-    }
-    const int e = i % E;
-    if (bias) v += (double)bias[e];
-    const float l = (float)v;
-    s_lg[i] = l;
-    logits[i] = l;
-  }
-  __syncthreads();
-  const int t = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (t < T) {
-    float lv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lv[q] = (lane + 64 * q < E) ? s_lg[t * E + lane + 64 * q] : 0.0f;
-    topk_select(lv, t, E, k, ro, s_idx + t * k);
-  }
-  __syncthreads();
-  permute_block(s_idx, T, E, k, ro, s_cnt, s_base, s_tbase, s_mask);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -632,6 +749,8 @@ hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool 
 
 int chunk_count(int T) { return (T + CHUNK - 1) / CHUNK; }
 
+int router_slices(int H) { return (H + RSLICE - 1) / RSLICE; }
+
 hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
                                 int32_t *ccnt, int32_t *base, int32_t *lrank, hipStream_t s, const Timing *tm_topk,
                                 const Timing *tm_perm) {
@@ -649,9 +768,9 @@ hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H,
   return hipGetLastError();
 }
 
-hipError_t launch_route_small(const double *part, int nslice, const float *bias, float *logits, int T, int E,
-                              int k, RouteOut ro, hipStream_t s, const Timing *tm) {
-  DS4_LAUNCH(tm, k_route_small, dim3(1), dim3(1024), 0, s, part, nslice, bias, logits, T, E, k, ro);
+hipError_t launch_route_dec(const double *part, int nslice, const float *bias, float *logits, int T, int E, int k,
+                            RouteOut ro, DecTile *dt, int32_t *ntile, hipStream_t s, const Timing *tm) {
+  DS4_LAUNCH(tm, k_route_dec, dim3(1), dim3(1024), 0, s, part, nslice, bias, logits, T, E, k, ro, dt, ntile);
   return hipGetLastError();
 }
 
@@ -659,7 +778,8 @@ template <bool XB, bool WB>
 static hipError_t router_sliced_t(const void *x, const void *wr, double *part, int T, int E, int H,
                                   const XPrep *xp, hipStream_t s, const Timing *tm) {
   XPrep xx = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
-  DS4_LAUNCH(tm, (k_router_sliced<XB, WB>), dim3((E + 3) / 4, H / 256), dim3(256), 0, s, x, wr, part, T, E, H, xx,
+  DS4_LAUNCH(tm, (k_router_sliced<XB, WB>), dim3((E + 3) / 4, router_slices(H)), dim3(256), 0, s, x, wr, part, T, E,
+             H, xx,
              xp != nullptr);
   return hipGetLastError();
 }
