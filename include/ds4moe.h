@@ -137,9 +137,10 @@ size_t ds4moe_packed_bytes(int64_t rows, int64_t cols);
  *   [0,1024)    2-bit codes, 16 bytes per MFMA lane (lane = 16*g + r, row r);
  *               dword u of lane (r,g) holds sub-block 4u+g of row r, element
  *               i at bits 4*(i%8) + 2*(i/8)
- *   [1024,1280) per row 16 bytes: halfword g of bytes 0-7 holds the scales of
- *               sub-blocks g, 4+g, 8+g, 12+g as nibbles 0..3; bytes 8-15
- *               hold the 16 mins as nibbles in sub-block order
+ *   [1024,1280) per row 16 bytes: bytes 2g and 2g+1 (g < 4) hold the scales
+ *               of sub-blocks g | 8+g<<4 and 4+g | 12+g<<4; bytes 8-11 and
+ *               12-15 hold the mins of sub-blocks 0-7 and 8-15, byte b of each
+ *               group holding sub-block b (low nibble) and b+4 (high nibble)
  *   [1280,1344) per row d (bits 0-15) and dmin (bits 16-31), binary16
  * The conversion is exact: no value is altered. */
 int ds4moe_pack_q2k(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, void *stream);
