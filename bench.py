@@ -22,6 +22,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+GRAPH_STEPS = 64               # at most this many layer calls per captured graph
 MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
 DEFAULTS = {  # workload: (steps, warmup, layer copies, token batches)
@@ -98,6 +99,7 @@ def run_workload(name: str, args) -> dict:
         else:
             B.ds4moe_forward_timed(mode, dl.dims, w, x, T, y, None, ws, ws.numel(), events, stream)
 
+    steps_eager = steps
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -105,38 +107,66 @@ def run_workload(name: str, args) -> dict:
     for i in range(steps):
         step(i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t1
+    elapsed_eager = time.perf_counter() - t1
+
+    # The timed loop: a HIP graph holding `glen` consecutive layer calls (the
+    # same rotation over layer copies and token batches), replayed; the library
+    # enqueues kernels only, so a capture holds the whole layer.
+    # (exactly `steps` calls: the graph length is the largest divisor of steps <= GRAPH_STEPS)
+    glen = 0 if args.no_graph else max(d for d in range(1, min(GRAPH_STEPS, steps) + 1) if steps % d == 0)
+    if glen:
+        reps = steps // glen
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(glen):
+                    w = layers[i % n_layers]
+                    x = xs[i % n_batches]
+                    fwd(dl.dims, w, x, T, y, None, ws, ws.numel(), cap)
+        torch.cuda.current_stream(dev).wait_stream(cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t1
+        del graph
+    else:
+        elapsed = elapsed_eager
 
     # second pass with per-kernel events stamped by each kernel's own dispatch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * B.N_TIMED_KERNELS)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * B.N_TIMED_KERNELS)] for _ in range(steps_eager)]
     for row in ev:  # torch creates the underlying hipEvent on first record
         for e in row:
             e.record(stream)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
-    for i in range(steps):
+    for i in range(steps_eager):
         step(i, ev[i])
     torch.cuda.synchronize()
     elapsed_ev = time.perf_counter() - t2
     stage_ms = {s: 0.0 for s in B.KERNEL_SLOTS}
     per_step_gateup = []
-    for i in range(steps):
+    for i in range(steps_eager):
         for j, s in enumerate(B.KERNEL_SLOTS):
             dt = ev[i][2 * j].elapsed_time(ev[i][2 * j + 1])
             stage_ms[s] += dt
             if s == "gateup":
                 per_step_gateup.append(dt)
-    stage_ms = {s: v / steps for s, v in stage_ms.items()}
+    stage_ms = {s: v / steps_eager for s, v in stage_ms.items()}
 
     H, I, E, k = wl.H, wl.I, wl.E, wl.k
     gu_bytes = dl.gu_bytes
     if mode == q.MODE_DECODE:
         # gate + up packed bytes of the experts each step touches
-        gu_total = sum(2 * gu_bytes * distinct[i % n_batches] for i in range(steps))
+        gu_total = sum(2 * gu_bytes * distinct[i % n_batches] for i in range(steps_eager))
         achieved = gu_total / (sum(per_step_gateup) * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_gateup", "algorithmic_bytes_per_launch": gu_total / steps}
+                "kernel": "k_gateup", "algorithmic_bytes_per_launch": gu_total / steps_eager}
         layer_bytes = np.mean([d * 3 * gu_bytes for d in distinct]) + E * H * 2 + T * H * (2 + 4)
         layer = {"bytes_per_step": float(layer_bytes),
                  "achieved_GBs": round(layer_bytes / (elapsed / steps) / 1e9, 1),
@@ -162,7 +192,9 @@ def run_workload(name: str, args) -> dict:
         "roofline": roof,
         "layer_roofline": layer,
         "kernel_ms": {s: round(v, 5) for s, v in stage_ms.items()},
-        "ms_per_step_with_kernel_events": round(elapsed_ev / steps * 1e3, 5),
+        "launch": f"hip graph of {glen} layer calls, replayed" if glen else "eager launches",
+        "ms_per_step_eager": round(elapsed_eager / steps_eager * 1e3, 5),
+        "ms_per_step_with_kernel_events": round(elapsed_ev / steps_eager * 1e3, 5),
         "setup_s": round(setup_s, 1),
     }
     if not args.no_cpu_baseline:
@@ -181,6 +213,7 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="rotated copies of the packed experts")
     ap.add_argument("--seed", type=int, default=20261203)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

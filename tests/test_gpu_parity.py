@@ -300,3 +300,45 @@ def test_full_route_only_matches_forward(full):
     rt = dl.route(dl.x_tensor(L.x))
     torch.cuda.synchronize()
     check_routing(rt, L, label="route-only prefill")
+
+
+# ------------------------------------------------------------------ graph capture
+
+
+@pytest.mark.parametrize("name,T", [("decode16", 16), ("decode1", 1), ("prefill", 300)])
+def test_graph_replay_matches_eager(full, name, T):
+    """A layer call captured in a HIP graph gives the eager result on every
+    replay, with other eager layer calls on the same workspace in between."""
+    q = _q()
+    L0, dl = full
+    L = synth.derive(L0, name, T=T)
+    L2 = synth.derive(L0, name, T=T, batch=1)
+    m = q.MODE_DECODE if name.startswith("decode") else q.MODE_PREFILL
+    fwd = q.ds4moe_forward_decode if m == q.MODE_DECODE else q.ds4moe_forward_prefill
+    x, x2 = dl.x_tensor(L.x), dl.x_tensor(L2.x)
+    ws = torch.empty(q.ds4moe_workspace_bytes(dl.dims, T, m), dtype=torch.uint8, device=dl.device)
+    y = torch.empty(T, L.wl.H, dtype=torch.float32, device=dl.device)
+    y2 = torch.empty_like(y)
+    w = dl.weights()
+    fwd(dl.dims, w, x, T, y, None, ws, ws.numel())
+    torch.cuda.synchronize()
+    ref = y.clone()
+    fwd(dl.dims, w, x2, T, y2, None, ws, ws.numel())
+    torch.cuda.synchronize()
+    ref2 = y2.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(dl.device)
+    s.wait_stream(torch.cuda.current_stream(dl.device))
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fwd(dl.dims, w, x, T, y, None, ws, ws.numel(), s)
+    torch.cuda.current_stream(dl.device).wait_stream(s)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), f"replay {rep}"
+        fwd(dl.dims, w, x2, T, y2, None, ws, ws.numel())
+        torch.cuda.synchronize()
+        assert torch.equal(y2.view(torch.int32), ref2.view(torch.int32)), f"eager after replay {rep}"
+    del g
