@@ -85,6 +85,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// 16 bytes per lane straight into LDS: lane l's bytes land at lds + 16*l
+// (lds wave-uniform); out-of-range lanes write zeros
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
+}
+
 __device__ __forceinline__ h8 buf_load_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

@@ -38,6 +38,12 @@ namespace ds4 {
 #ifndef DN_DEC_PD
 #define DN_DEC_PD 3
 #endif
+#ifndef GU_LDS_PD
+#define GU_LDS_PD 3
+#endif
+#ifndef DN_LDS_PD
+#define DN_LDS_PD 4
+#endif
 
 struct UnitRegs {
   u4 code;   // 4 raw dwords: sub-blocks g, 4+g, 8+g, 12+g of row r
@@ -586,6 +592,285 @@ __global__ __launch_bounds__(512) void k_down_dec(GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ small batches, T <= 4
+// Variants of the two kernels above for batches of at most four tokens: the
+// activations of each reduction step (x or h of the T tokens: 256 values and
+// the 16-column sums, 36 chunks of 16 bytes per token, padded to 37) come in
+// through one to three direct-to-LDS buffer loads per step instead of nine
+// 64-lane register loads, into a per-wave ring of PD LDS slots filled at the
+// same pipeline distance as the weights; the MFMA B fragments are read from
+// the slot.  Chunks of tokens that did not choose the tile's expert are out
+// of range and arrive as zeros.
+constexpr int XCH = 37;  // 16-byte chunks per token per step (36 + 1 pad)
+
+template <int NT>
+struct SlotLoads {
+  static constexpr int NI = (NT * XCH + 63) / 64;  // load instructions per step
+};
+
+// vmcnt(N) with the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int PD, int NT>
+__global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt) {
+  constexpr int NI = SlotLoads<NT>::NI;
+  constexpr int SLOT = 64 * 16 * NI;  // bytes per ring slot
+  __shared__ __attribute__((aligned(16))) char ring_lds[4 * PD * SLOT];
+  const int nrb = (n_rt + 1) >> 1;
+  const int tile_id = blockIdx.x / nrb;
+  const int rb = blockIdx.x - tile_id * nrb;
+  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int rt = 2 * rb + (wave >> 1), kh = wave & 1;
+  const int e = a.dtiles[tile_id].e;
+  const uint32_t tmask = a.dtiles[tile_id].tmask;
+  const int nsb = a.H >> 8;
+  const int half = (nsb + 1) >> 1;
+  const int sb0 = kh * half;
+  const int nit = max(0, min(nsb, sb0 + half) - sb0);
+  const uint32_t gub = (uint32_t)a.gu_bytes;
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gate + (size_t)e * a.gu_bytes, gub);
+  const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.up + (size_t)e * a.gu_bytes, gub);
+  const uint32_t roff = ((uint32_t)min(rt, n_rt - 1) * nsb + sb0) * DS4_UNIT_BYTES;
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
+  // chunk u = 64*q + lane of a slot: token u / XCH, chunk c = u % XCH
+  uint32_t src[NI], inc[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int u = 64 * q + lane;
+    const int t = u / XCH, c = u - t * XCH;
+    src[q] = DS4_OOB;
+    inc[q] = 0;
+    if (t < NT && c < 36 && ((tmask >> t) & 1u)) {
+      if (c < 32) {
+        src[q] = a.o_x16 + 2u * ((uint32_t)t * a.H + (uint32_t)sb0 * 256 + 8 * c);
+        inc[q] = 512;
+      } else {
+        const int cc = c - 32;
+        src[q] = ((cc >> 1) ? a.o_xs_lo : a.o_xs_hi) + 2u * ((uint32_t)t * (a.H >> 4) + sb0 * 16 + 8 * (cc & 1));
+        inc[q] = 32;
+      }
+    }
+  }
+  // B fragment of lane (r16, g): token r16 (columns r16 >= T read token 0 and are discarded)
+  const uint32_t brow = (uint32_t)(r16 < NT ? r16 : 0) * (XCH * 16);
+  char *ring = ring_lds + wave * (PD * SLOT);  // this wave's PD slots
+
+  struct Stage {
+    UnitRegs wg, wu;
+  };
+  Stage st[PD];
+  f4 yg = (f4){0.f, 0.f, 0.f, 0.f}, yu = yg;
+  auto load = [&](Stage &sg, int slot, int i) {
+    const bool in = i < nit;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier reads of this slot are done
+#pragma unroll
+    for (int q = 0; q < NI; ++q)
+      buf_load_lds16(ws, ring + slot * SLOT + 64 * 16 * q, in ? src[q] + inc[q] * (uint32_t)i : DS4_OOB);
+    const uint32_t wo = in ? roff + (uint32_t)i * DS4_UNIT_BYTES : DS4_OOB;
+    sg.wg = load_unit_buf(gr, wo, lane);
+    sg.wu = load_unit_buf(ur, wo, lane);
+  };
+  auto compute = [&](const Stage &sg, int slot) {
+    wait_vm<(PD - 1) * (NI + 6)>();  // this step's loads (LDS and registers) have landed
+    const char *base = ring + slot * SLOT + brow;
+    h8 b[9];
+#pragma unroll
+    for (int S = 0; S < 8; ++S)
+      b[S] = *reinterpret_cast<const h8 *>(base + 16 * (2 * (4 * (S >> 1) + g) + (S & 1)));
+    b[8] = *reinterpret_cast<const h8 *>(base + 16 * (32 + 2 * (g >> 1) + (g & 1)));
+    const UnitDecoded dg = decode_unit(sg.wg, g);
+    const UnitDecoded du = decode_unit(sg.wu, g);
+    f4 ag = (f4){0.f, 0.f, 0.f, 0.f}, au = ag;
+#define DEC_STEP(S)                                  \
+  ag = mfma16(step_frag<S>(sg.wg, dg), b[S], ag);    \
+  au = mfma16(step_frag<S>(sg.wu, du), b[S], au);
+    DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
+#undef DEC_STEP
+    const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
+    const f4 mg = mfma16(dg.mfrag, b[8], z);
+    const f4 mu = mfma16(du.mfrag, b[8], z);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      yg[q] = fmaf(dd_d(dg.dd[q]), ag[q], yg[q]);
+      yg[q] = fmaf(-dd_dmin(dg.dd[q]), mg[q], yg[q]);
+      yu[q] = fmaf(dd_d(du.dd[q]), au[q], yu[q]);
+      yu[q] = fmaf(-dd_dmin(du.dd[q]), mu[q], yu[q]);
+    }
+  };
+#pragma unroll
+  for (int sgi = 0; sgi < PD; ++sgi) load(st[sgi], sgi, sgi);
+  for (int i0 = 0; i0 < nit; i0 += PD) {
+#pragma unroll
+    for (int sgi = 0; sgi < PD; ++sgi) {
+      compute(st[sgi], sgi);
+      load(st[sgi], sgi, i0 + sgi + PD);
+    }
+  }
+
+  __shared__ f4 red[2][2][64];  // [row tile of the workgroup][gate, up]
+  const int rl = wave >> 1;
+  if (kh == 1) {
+    red[rl][0][lane] = yg;
+    red[rl][1][lane] = yu;
+  }
+  __syncthreads();
+  if (kh == 1 || rt >= n_rt) return;  // uniform per wave
+  const f4 pg = red[rl][0][lane], pu = red[rl][1][lane];
+  half_t hv[4];
+  float ssum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float gv = yg[q] + pg[q], uv = yu[q] + pu[q];
+    hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+    ssum += (float)hv[q];
+  }
+  ssum += __shfl_xor(ssum, 16);
+  ssum += __shfl_xor(ssum, 32);
+  if (r16 < a.T) {  // tokens that did not choose the expert get exact zeros
+    const size_t p = (size_t)tile_id * a.T + r16;
+    uint2 pk;
+    __builtin_memcpy(&pk, hv, 8);
+    *reinterpret_cast<uint2 *>(a.h + p * a.Ipad + rt * 16 + 4 * g) = pk;
+    if (g == 0) {
+      const int nj = a.Ipad >> 4;
+      const half_t hi = (half_t)ssum;
+      a.hs_hi[p * nj + rt] = hi;
+      a.hs_lo[p * nj + rt] = (half_t)(ssum - (float)hi);
+    }
+  }
+}
+
+// down fused with the combine (I a multiple of 256), activations through LDS
+template <int PD, int NT>
+__global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
+  constexpr int NI = SlotLoads<NT>::NI;
+  constexpr int SLOT = 64 * 16 * NI;
+  __shared__ __attribute__((aligned(16))) char ring_lds[8 * PD * SLOT];
+  const int rt = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int ntl = *a.ntiles;
+  const int nsb = a.Ipad >> 8;
+  const int nj = a.Ipad >> 4;
+  const int mt = wave < ntl ? (ntl - wave + 7) >> 3 : 0;  // tiles of this wave (<= 32)
+  const int nit = mt * nsb;
+  int e_l = 0;        // lane L: expert of this wave's L-th tile
+  uint32_t m_l = 0u;  // ... and its token mask
+  if (lane < mt) {
+    e_l = a.dtiles[wave + 8 * lane].e;
+    m_l = a.dtiles[wave + 8 * lane].tmask;
+  }
+  // wait for them here, before any weight load is in flight, so that the
+  // pipelined loop below never has to drain the load counter for them
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
+  // chunk u = 64*q + lane of a slot: token u / XCH, chunk c = u % XCH
+  // chunks c < 32: h[p][256*sb + 8c ...]; c = 32..35: sums hi/lo [p][16*sb + 8*(c&1) ...]
+  uint32_t cbase[NI], crow[NI], cstep[NI];
+  int ctok[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int u = 64 * q + lane;
+    const int t = u / XCH, c = u - t * XCH;
+    ctok[q] = (t < NT && c < 36) ? t : -1;
+    if (c < 32) {
+      cbase[q] = a.o_h + 2u * (8 * c);
+      crow[q] = 2u * a.Ipad;
+      cstep[q] = 512;
+    } else {
+      cbase[q] = (((c - 32) >> 1) ? a.o_hs_lo : a.o_hs_hi) + 2u * (8 * ((c - 32) & 1));
+      crow[q] = 2u * nj;
+      cstep[q] = 32;
+    }
+  }
+  const uint32_t brow = (uint32_t)(r16 < NT ? r16 : 0) * (XCH * 16);
+  char *ring = ring_lds + wave * (PD * SLOT);  // this wave's PD slots
+
+  struct Stage {
+    UnitRegs wd;
+    float wt;
+  };
+  Stage st[PD];
+  f4 y = (f4){0.f, 0.f, 0.f, 0.f};
+  int lt = 0, lsb = 0;  // tile and super-block of the next load
+  auto load = [&](Stage &sg, int slot) {
+    const bool in = lt < mt;
+    const int tile = min(wave + 8 * lt, ntl - 1);
+    const int e = __builtin_amdgcn_readlane(e_l, lt & 63);
+    const uint32_t tmask = in ? (uint32_t)__builtin_amdgcn_readlane((int)m_l, lt & 63) : 0u;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier reads of this slot are done
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int t = ctok[q];
+      const bool ok = t >= 0 && ((tmask >> t) & 1u);
+      const uint32_t p = (uint32_t)tile * a.T + t;
+      const uint32_t off = ok ? cbase[q] + crow[q] * p + cstep[q] * (uint32_t)lsb : DS4_OOB;
+      buf_load_lds16(ws, ring + slot * SLOT + 64 * 16 * q, off);
+    }
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.down + (size_t)e * a.d_bytes, (uint32_t)a.d_bytes);
+    sg.wd = load_unit_buf(wr, in ? ((uint32_t)rt * nsb + lsb) * DS4_UNIT_BYTES : DS4_OOB, lane);
+    sg.wt = a.dtiles[tile].w[r16];  // 0 for tokens that did not choose the expert
+    if (++lsb == nsb) {
+      lsb = 0;
+      ++lt;
+    }
+  };
+  auto compute = [&](const Stage &sg, int slot) {
+    wait_vm<(PD - 1) * (NI + 4)>();  // this step's loads (LDS and registers) have landed
+    const char *base = ring + slot * SLOT + brow;
+    h8 b[9];
+#pragma unroll
+    for (int S = 0; S < 8; ++S)
+      b[S] = *reinterpret_cast<const h8 *>(base + 16 * (2 * (4 * (S >> 1) + g) + (S & 1)));
+    b[8] = *reinterpret_cast<const h8 *>(base + 16 * (32 + 2 * (g >> 1) + (g & 1)));
+    const UnitDecoded dd = decode_unit(sg.wd, g);
+    f4 ac = (f4){0.f, 0.f, 0.f, 0.f};
+#define DEC_STEP(S) ac = mfma16(step_frag<S>(sg.wd, dd), b[S], ac);
+    DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
+#undef DEC_STEP
+    const f4 mm = mfma16(dd.mfrag, b[8], (f4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float v = fmaf(dd_d(dd.dd[q]), ac[q], -dd_dmin(dd.dd[q]) * mm[q]);
+      y[q] = fmaf(sg.wt, v, y[q]);
+    }
+  };
+#pragma unroll
+  for (int sgi = 0; sgi < PD; ++sgi) load(st[sgi], sgi);
+  for (int i0 = 0; i0 < nit; i0 += PD) {
+#pragma unroll
+    for (int sgi = 0; sgi < PD; ++sgi) {
+      compute(st[sgi], sgi);
+      load(st[sgi], sgi);
+    }
+  }
+  __shared__ f4 red[8][64];
+  red[wave][lane] = y;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 1; w < 8; ++w) {
+    const f4 p = red[w][lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] += p[q];
+  }
+  if (r16 < a.T) {
+    const size_t o = (size_t)r16 * a.H + rt * 16 + 4 * g;
+    if (a.ysh) {
+      const f4 v = *reinterpret_cast<const f4 *>(a.ysh + o);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] += v[q];
+    }
+    *reinterpret_cast<f4 *>(a.y + o) = y;
+  }
+}
+
 // ------------------------------------------------------------------ combine
 // y[t] = sum_j w[t,j] * Yp[pos(t,j)] in rank order, then + shared output.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ yp, const int32_t *__restrict__ pos,
@@ -760,11 +1045,28 @@ hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, hipStream_t s, co
   if (max_tiles <= 0) return hipSuccess;
   const int n_rt = a.I >> 4;
   const int nrb = (n_rt + 1) >> 1;
-  DS4_LAUNCH(tm, (k_gateup_dec<GU_DEC_PD>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(256), 0, s, a, n_rt);
+  const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
+  switch (a.T) {
+    case 1: DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, 1>), grid, dim3(256), 0, s, a, n_rt); break;
+    case 2: DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, 2>), grid, dim3(256), 0, s, a, n_rt); break;
+    case 3: DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, 3>), grid, dim3(256), 0, s, a, n_rt); break;
+    case 4: DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, 4>), grid, dim3(256), 0, s, a, n_rt); break;
+    default: DS4_LAUNCH(tm, (k_gateup_dec<GU_DEC_PD>), grid, dim3(256), 0, s, a, n_rt);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm) {
+  const dim3 grid((unsigned)(a.H >> 4));
+  if (a.I == a.Ipad && a.T <= 4) {
+    switch (a.T) {
+      case 1: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 1>), grid, dim3(512), 0, s, a); break;
+      case 2: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 2>), grid, dim3(512), 0, s, a); break;
+      case 3: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 3>), grid, dim3(512), 0, s, a); break;
+      default: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 4>), grid, dim3(512), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (a.I == a.Ipad)
     DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, false>), dim3((unsigned)(a.H >> 4)), dim3(512), 0, s, a);
   else
