@@ -136,34 +136,31 @@ __device__ __forceinline__ void gemm_load_a(UnitRegs (&u)[R][NM], const GemmCtx<
       u[r][m] = load_unit(c.W[m] + (size_t)rts[r] * c.rt_stride + (size_t)sb * DS4_UNIT_BYTES, lane);
 }
 
-// Activation staging: thread -> token row (tid/4)%64, chunk column tid%4;
-// with NW waves each thread stages 8*4/NW of the row's 32 chunks of 8 halves
-// (chunks lc + 4i), and threads of the first 256 also one chunk of sums
-// (lc: hi 0-7, hi 8-15, lo 0-7, lo 8-15).
-template <int NCH>
+// Activation staging: thread -> 16-byte chunk column sc = tid % 32 of token
+// rows tid/32 + SROWS*i (SROWS = threads/32), so 32 consecutive lanes move one
+// row's 512 bytes (contiguous in memory and conflict-free in LDS); sums:
+// thread -> row (tid%256)/4, quarter tid%4 (hi 0-7, hi 8-15, lo 0-7, lo 8-15).
+template <int NR>
 struct Stage {
-  u4 b[NCH];
+  u4 b[NR];
   u4 s;
 };
 
-template <int NCH, bool PADDED>
-__device__ __forceinline__ void stage_load(Stage<NCH> &st, const half_t *brow, const half_t *shi, const half_t *slo,
-                                           int sb, int lc, int part, int kreal, int jreal) {
+template <int NR, bool PADDED>
+__device__ __forceinline__ void stage_load(Stage<NR> &st, const half_t *const (&rowp)[NR], const half_t *sp, int sb,
+                                           int sc, int sq, int kreal, int jreal) {
+  const int col = sb * 256 + 8 * sc;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int col = sb * 256 + (lc + 4 * (part * NCH + i)) * 8;
-    st.b[i] = (!PADDED || col < kreal) ? *reinterpret_cast<const u4 *>(brow + col) : (u4){0u, 0u, 0u, 0u};
-  }
-  if (part != 0) return;
-  const int j0 = sb * 16 + 8 * (lc & 1);
-  const half_t *sp = (lc >> 1) ? slo : shi;
+  for (int i = 0; i < NR; ++i)
+    st.b[i] = (!PADDED || col < kreal) ? *reinterpret_cast<const u4 *>(rowp[i] + col) : (u4){0u, 0u, 0u, 0u};
   if (!PADDED) {
-    st.s = *reinterpret_cast<const u4 *>(sp + j0);
+    st.s = *reinterpret_cast<const u4 *>(sp + sb * 16);
     return;
   }
+  const int j0 = sb * 16 + 8 * (sq & 1);
   u4 v = (u4){0u, 0u, 0u, 0u};
   if (j0 < jreal) {
-    v = *reinterpret_cast<const u4 *>(sp + j0);
+    v = *reinterpret_cast<const u4 *>(sp + sb * 16);
     if (j0 + 8 > jreal) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -175,12 +172,12 @@ __device__ __forceinline__ void stage_load(Stage<NCH> &st, const half_t *brow, c
   st.s = v;
 }
 
-template <int NCH>
-__device__ __forceinline__ void stage_store(const Stage<NCH> &st, half_t *sB, half_t *sS, int lr, int lc, int part) {
+template <int NR, int SROWS>
+__device__ __forceinline__ void stage_store(const Stage<NR> &st, half_t *sB, half_t *sS, int sr0, int sc, int srow,
+                                            int sq) {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i)
-    *reinterpret_cast<u4 *>(sB + lr * SB_STRIDE + (lc + 4 * (part * NCH + i)) * 8) = st.b[i];
-  if (part == 0) *reinterpret_cast<u4 *>(sS + lr * SS_STRIDE + lc * 8) = st.s;
+  for (int i = 0; i < NR; ++i) *reinterpret_cast<u4 *>(sB + (sr0 + SROWS * i) * SB_STRIDE + 8 * sc) = st.b[i];
+  *reinterpret_cast<u4 *>(sS + srow * SS_STRIDE + 8 * sq) = st.s;
 }
 
 template <int NM, int R>
@@ -239,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   const int rb = blockIdx.x - tile_id * nrb;
   if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
   const TileT tl = a.tiles[tile_id];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   constexpr bool GU = NM == 2;
   const int K = GU ? a.H : a.Ipad;
@@ -252,23 +249,30 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
 #pragma unroll
   for (int r = 0; r < R; ++r) rts[r] = min(rt0 + r, n_rt - 1);
 
-  // activation rows staged by this thread
-  constexpr int NCH = 32 / NW;
-  const int lr = (tid >> 2) & 63, lc = tid & 3, part = tid >> 8;
-  const bool lvalid = lr < tl.n;
-  const half_t *brow, *shi, *slo;
-  if (GU) {
-    const int tok = a.perm[tl.p0 + (lvalid ? lr : 0)] / a.k;
-    brow = a.x16 + (size_t)tok * a.H;
-    shi = a.xs_hi + (size_t)tok * (a.H >> 4);
-    slo = a.xs_lo + (size_t)tok * (a.H >> 4);
-  } else {
-    const size_t p = (size_t)(tl.p0 + (lvalid ? lr : 0));
-    brow = a.h + p * a.Ipad;
-    shi = a.hs_hi + p * (a.Ipad >> 4);
-    slo = a.hs_lo + p * (a.Ipad >> 4);
+  // activation rows staged by this thread (rows without a token read zeros)
+  constexpr int SROWS = 64 * NW / 32, NR = 64 / SROWS;
+  const int sc = tid & 31, sr0 = tid >> 5;
+  const int srow = (tid & 255) >> 2, sq = tid & 3;
+  // source row of each staged row: token (gate/up) or assignment position (down);
+  // the lookups are issued together, rows past the tile clamp to its first row
+  int src[NR + 1];
+#pragma unroll
+  for (int i = 0; i <= NR; ++i) {
+    const int row = i < NR ? sr0 + SROWS * i : srow;
+    const int p = tl.p0 + (row < tl.n ? row : 0);
+    src[i] = GU ? a.perm[p] : p;
   }
-  if (!lvalid) brow = shi = slo = a.zeros;
+  const half_t *rowp[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const bool v = sr0 + SROWS * i < tl.n;
+    rowp[i] = !v ? a.zeros : GU ? a.x16 + (size_t)(src[i] / a.k) * a.H : a.h + (size_t)src[i] * a.Ipad;
+  }
+  const half_t *sp = a.zeros;
+  if (srow < tl.n) {
+    const size_t sbase = GU ? (size_t)(src[NR] / a.k) * (a.H >> 4) : (size_t)src[NR] * (a.Ipad >> 4);
+    sp = (GU ? ((sq >> 1) ? a.xs_lo : a.xs_hi) : ((sq >> 1) ? a.hs_lo : a.hs_hi)) + sbase + 8 * (sq & 1);
+  }
 
   GemmCtx<NM> c;
   c.nsb = nsb;
@@ -288,29 +292,31 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
 #pragma unroll
       for (int nt = 0; nt < GEMM_NT; ++nt) y[m][r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  Stage<NCH> st;
+  // every prefetch is issued unconditionally (the last super-block is
+  // reloaded at the end), so the load-counter waits are static
+  Stage<NR> st;
   UnitRegs ua[R][NM], ub[R][NM];
-  stage_load<NCH, PADDED>(st, brow, shi, slo, 0, lc, part, kreal, jreal);
+  stage_load<NR, PADDED>(st, rowp, sp, 0, sc, sq, kreal, jreal);
   gemm_load_a<NM, R>(ua, c, rts, 0, lane);
   for (int sb = 0; sb < nsb; sb += 2) {
     // even super-block: weights in ua, prefetch into ub
     __syncthreads();
-    stage_store<NCH>(st, sB, sS, lr, lc, part);
+    stage_store<NR, SROWS>(st, sB, sS, sr0, sc, srow, sq);
     __syncthreads();
-    if (sb + 1 < nsb) {
-      stage_load<NCH, PADDED>(st, brow, shi, slo, sb + 1, lc, part, kreal, jreal);
-      gemm_load_a<NM, R>(ub, c, rts, sb + 1, lane);
-    }
+    const int s1 = min(sb + 1, nsb - 1);
+    stage_load<NR, PADDED>(st, rowp, sp, s1, sc, sq, kreal, jreal);
+    gemm_load_a<NM, R>(ub, c, rts, s1, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
     gemm_compute_sb<NM, R>(ua, sB, sS, y, r16, g);
     if (sb + 1 >= nsb) break;
     // odd super-block: weights in ub, prefetch into ua
     __syncthreads();
-    stage_store<NCH>(st, sB, sS, lr, lc, part);
+    stage_store<NR, SROWS>(st, sB, sS, sr0, sc, srow, sq);
     __syncthreads();
-    if (sb + 2 < nsb) {
-      stage_load<NCH, PADDED>(st, brow, shi, slo, sb + 2, lc, part, kreal, jreal);
-      gemm_load_a<NM, R>(ua, c, rts, sb + 2, lane);
-    }
+    const int s2 = min(sb + 2, nsb - 1);
+    stage_load<NR, PADDED>(st, rowp, sp, s2, sc, sq, kreal, jreal);
+    gemm_load_a<NM, R>(ua, c, rts, s2, lane);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
     gemm_compute_sb<NM, R>(ub, sB, sS, y, r16, g);
   }
 
