@@ -14,6 +14,7 @@ Infinity Cache.  Prints one JSON line per workload (default: decode1).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,61 @@ DEFAULTS = {  # workload: (steps, warmup, layer copies, token batches)
     "prefill": (50, 5, 1, 4),
     "skewed": (20, 3, 1, 2),
 }
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "quantized_routed_moe_router_amd", "csrc")
+PROFILES = os.path.join(HERE, "profiles")
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources, so counter figures taken on other kernels are not reused."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def roofline_kernel(mode_decode: bool, T: int) -> str:
+    if not mode_decode:
+        return "k_moe_gemm"
+    return "k_gateup_dec_lds" if T <= 4 else "k_gateup_dec"
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None
+    when there is none or the HIP sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":", 1)[0] in ("source_sha256", "traffic_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                vals[k] = v.strip()
+    if vals.get("source_sha256") != source_hash() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def copy_calibration(mib: int, reps: int) -> dict:
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters to bytes (run it under rocprofv3 --pmc)."""
+    import torch
+    n = mib << 20
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_calibration": True, "bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": reps,
+            "source_sha256": source_hash()}
 
 
 def cpu_baseline(L, budget_s: float) -> dict:
@@ -160,13 +216,14 @@ def run_workload(name: str, args) -> dict:
 
     H, I, E, k = wl.H, wl.I, wl.E, wl.k
     gu_bytes = dl.gu_bytes
+    rk = roofline_kernel(mode == q.MODE_DECODE, T)
     if mode == q.MODE_DECODE:
         # gate + up packed bytes of the experts each step touches
         gu_total = sum(2 * gu_bytes * distinct[i % n_batches] for i in range(steps_eager))
         achieved = gu_total / (sum(per_step_gateup) * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_gateup", "algorithmic_bytes_per_launch": gu_total / steps_eager}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(rk, name),
+                "kernel": rk, "algorithmic_bytes_per_launch": gu_total / steps_eager}
         layer_bytes = np.mean([d * 3 * gu_bytes for d in distinct]) + E * H * 2 + T * H * (2 + 4)
         layer = {"bytes_per_step": float(layer_bytes),
                  "achieved_GBs": round(layer_bytes / (elapsed / steps) / 1e9, 1),
@@ -175,8 +232,8 @@ def run_workload(name: str, args) -> dict:
         flops = 2.0 * T * k * 2 * H * I
         achieved = flops / (stage_ms["gateup"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": None,
-                "kernel": "k_gateup", "algorithmic_flops_per_launch": flops}
+                "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": measured_traffic(rk, name),
+                "kernel": rk + " (gate/up + SwiGLU)", "algorithmic_flops_per_launch": flops}
         lf = 2.0 * T * k * 3 * H * I + (2.0 * T * 3 * H * wl.Is if wl.Is else 0.0)
         layer = {"flops_per_step": lf, "achieved_TFs": round(lf / (elapsed / steps) / 1e12, 2),
                  "frac": round(lf / (elapsed / steps) / 1e12 / MFMA_F16_PEAK_TFS, 4)}
@@ -215,11 +272,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer is benchmarked on a single MI355X "
               "(no sharding, no collectives); run it without --gpus or with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(args.copy_calibration, args.steps or 10)), flush=True)
+        return
     names = [n for n in DEFAULTS if n != "tiny"] if args.workload == "all" else [args.workload]
     for n in names:
         print(json.dumps(run_workload(n, args)), flush=True)
