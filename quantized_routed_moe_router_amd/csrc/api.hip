@@ -203,11 +203,16 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   DecTile *dtiles = nullptr;
   if (dec) dtiles = at<DecTile>(ws, L.tiles);
   int32_t *ntiles = at<int32_t>(ws, L.ntiles);
+  // decode with T <= 4: the gate/up kernel routes the batch itself
+  const bool fused_route = dec && L.sliced && T <= 4;
+  DecRoute rr{at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, d.n_experts, d.top_k, ro,
+              dtiles, ntiles};
   if (L.sliced) {
     TRY(launch_router_sliced(x, xb, w->router_w, wb, at<double>(ws, L.part), T, d.n_experts, d.hidden, &xp, s,
                              tm(SL_ROUTER)));
-    TRY(launch_route_dec(at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, T, d.n_experts,
-                         d.top_k, ro, dtiles, ntiles, s, tm(SL_ROUTE)));
+    if (!fused_route)
+      TRY(launch_route_dec(at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, T,
+                           d.n_experts, d.top_k, ro, dtiles, ntiles, s, tm(SL_ROUTE)));
   } else {
     TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s,
                             tm(SL_ROUTER)));
@@ -260,7 +265,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     return DS4MOE_OK;
   };
   if (dec) {
-    TRY(launch_gateup_dec(ga, L.max_tiles, s, tm(SL_GATEUP)));
+    TRY(launch_gateup_dec(ga, L.max_tiles, fused_route ? &rr : nullptr, s, tm(SL_GATEUP)));
     st = shared();
     if (st) return st;
     ga.ysh = ysh;

@@ -16,6 +16,7 @@
 // lane's 16-byte code vector holds 4 whole sub-blocks.
 #include "common.h"
 #include "launch.h"
+#include "route_dev.h"
 
 namespace ds4 {
 
@@ -621,20 +622,46 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int PD, int NT>
-__global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt) {
+// ROUTE: the workgroup first routes the batch itself (route_small_block on
+// the router's partial sums, one wave per token; the LDS of that step is the
+// ring's, before the ring is used) and takes the tile_id-th used expert;
+// workgroup 0 writes the routing outputs and the tiles for the down kernel.
+template <int PD, int NT, bool ROUTE>
+__global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, DecRoute rr) {
   constexpr int NI = SlotLoads<NT>::NI;
   constexpr int SLOT = 64 * 16 * NI;  // bytes per ring slot
   __shared__ __attribute__((aligned(16))) char ring_lds[4 * PD * SLOT];
   const int nrb = (n_rt + 1) >> 1;
   const int tile_id = blockIdx.x / nrb;
   const int rb = blockIdx.x - tile_id * nrb;
-  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int e;
+  uint32_t tmask;
+  if constexpr (ROUTE) {
+    static_assert(sizeof(RouteLds<4>) <= sizeof(ring_lds), "routing LDS must fit in the ring");
+    RouteLds<4> &L = *reinterpret_cast<RouteLds<4> *>(ring_lds);
+    route_small_block<256, 4>(L, rr.part, rr.nslice, rr.bias, rr.logits, a.T, rr.E, rr.k, rr.ro, rr.dt, rr.ntile,
+                              blockIdx.x == 0);
+    if (tile_id >= L.ntile) return;  // uniform over the workgroup
+    // the used expert whose tile index is tile_id (lowest e among equal tb: the used one)
+    int sel = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = lane + 64 * i;
+      const bool hit = ee < rr.E && L.tm[ee] != 0u && L.tb[ee] == tile_id;
+      const uint64_t b = __ballot(hit);
+      if (sel < 0 && b) sel = 64 * i + __ffsll((unsigned long long)b) - 1;
+    }
+    e = sel;
+    tmask = L.tm[e];
+    __syncthreads();  // every wave has read the routing before the ring is filled
+  } else {
+    if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
+    e = a.dtiles[tile_id].e;
+    tmask = a.dtiles[tile_id].tmask;
+  }
   const int r16 = lane & 15, g = lane >> 4;
   const int rt = 2 * rb + (wave >> 1), kh = wave & 1;
-  const int e = a.dtiles[tile_id].e;
-  const uint32_t tmask = a.dtiles[tile_id].tmask;
   const int nsb = a.H >> 8;
   const int half = (nsb + 1) >> 1;
   const int sb0 = kh * half;
@@ -1047,16 +1074,27 @@ hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Ti
 }
 
 // Small batches (T <= 16).
-hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
+template <int NT>
+static void gateup_dec_lds(const GemmArgs &a, int n_rt, const DecRoute *rr, dim3 grid, hipStream_t s,
+                           const Timing *tm) {
+  if (rr)
+    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, true>), grid, dim3(256), 0, s, a, n_rt, *rr);
+  else
+    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, false>), grid, dim3(256), 0, s, a, n_rt, DecRoute{});
+}
+
+hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, const DecRoute *rr, hipStream_t s,
+                             const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
+  if (rr && (a.T > 4 || rr->E > 256 || rr->k > 16)) return hipErrorInvalidValue;
   const int n_rt = a.I >> 4;
   const int nrb = (n_rt + 1) >> 1;
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
   switch (a.T) {
-    case 1: DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, 1>), grid, dim3(256), 0, s, a, n_rt); break;
-    case 2: DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, 2>), grid, dim3(256), 0, s, a, n_rt); break;
-    case 3: DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, 3>), grid, dim3(256), 0, s, a, n_rt); break;
-    case 4: DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, 4>), grid, dim3(256), 0, s, a, n_rt); break;
+    case 1: gateup_dec_lds<1>(a, n_rt, rr, grid, s, tm); break;
+    case 2: gateup_dec_lds<2>(a, n_rt, rr, grid, s, tm); break;
+    case 3: gateup_dec_lds<3>(a, n_rt, rr, grid, s, tm); break;
+    case 4: gateup_dec_lds<4>(a, n_rt, rr, grid, s, tm); break;
     default: DS4_LAUNCH(tm, (k_gateup_dec<GU_DEC_PD>), grid, dim3(256), 0, s, a, n_rt);
   }
   return hipGetLastError();

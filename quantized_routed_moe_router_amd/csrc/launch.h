@@ -97,8 +97,25 @@ hipError_t launch_route_dec(const double *part, int nslice, const float *bias, f
 // grouped GEMMs over the tile list (max_tiles = grid bound)
 hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
 hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
-// small batches: gate/up over the DecTile list, and down fused with the combine (writes y)
-hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
+// Routing folded into the small-batch gate/up kernel (T <= 4): every
+// workgroup routes the batch from the router's partial sums for itself;
+// workgroup 0 also writes the routing outputs and the DecTile list.
+struct DecRoute {
+  const double *part;  // [nslice][T][E]
+  int nslice;
+  const float *bias;   // [E] or nullptr
+  float *logits;       // [T,E]
+  int E, k;
+  RouteOut ro;
+  DecTile *dt;
+  int32_t *ntile;
+};
+
+// small batches: gate/up over the DecTile list (rr != nullptr: T <= 4 and
+// the routing is done by the kernel itself), and down fused with the combine
+// (writes y)
+hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, const DecRoute *rr, hipStream_t s,
+                             const Timing *tm = nullptr);
 hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm = nullptr);
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,
                           int k, int H, hipStream_t s, const Timing *tm = nullptr);

@@ -1,15 +1,11 @@
 // Router: fp64-accumulated logits, sqrt(softplus) scores, top-k by wavefront
 // reductions, weight normalisation, activation preparation, and the
-// token-to-expert histogram / scan / stable permutation.
-//
-// Score: the router numeric test described on the opensource-hub.com
-// "antirez/ds4" page (FAQ #1) shows log(1 + exp(x)) in fp32 losing precision
-// near logit -12; the fix evaluates log1p by a four-term series when
-// exp(x) < 1/32, with the series input clamped.  Here softplus(l) is
-// max(l,0) + log1p(u), u = exp(-|l|) <= 1, which is the same thing for l <= 0
-// and never overflows for large l.
+// token-to-expert histogram / scan / stable permutation.  The score
+// (sqrt(softplus) with the stable log1p series) and the small-batch routing
+// are in route_dev.h.
 #include "common.h"
 #include "launch.h"
+#include "route_dev.h"
 
 namespace ds4 {
 
@@ -242,18 +238,6 @@ __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x,
       if (t < T) logits[(int64_t)t * E + e] = (float)(acc[n][i] + b);
     }
   }
-}
-
-// ---------------------------------------------------------------- score
-// s = sqrt(max(l,0) + log1p(u)), u = exp(-|l|); log1p(u) by the series
-// u - u^2/2 + u^3/3 - u^4/4 for u < 1/32 (series input clamped to 1/32),
-// log(1 + u) otherwise.  Max relative error vs. the exact value < 3e-6.
-__device__ __forceinline__ float router_score(float l) {
-  const float u = expf(-fabsf(l));
-  const float uc = fminf(u, 0.03125f);
-  const float ser = uc * (1.0f - uc * (0.5f - uc * (0.33333334f - uc * 0.25f)));
-  const float lp = (u < 0.03125f) ? ser : logf(1.0f + u);
-  return sqrtf(fmaxf(l, 0.0f) + lp);
 }
 
 // order-preserving key: larger logit first, then lower expert index; NaN last
@@ -527,207 +511,14 @@ __global__ __launch_bounds__(256) void k_place_chunks(int T, int E, int k, const
 }
 
 // ---------------------------------------------------------------- routing, T <= 16
-// wave-wide max of a 32-bit value: DPP prefix maxima inside each 16-lane row,
-// then row broadcasts; lane 63 ends with the maximum.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
-  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
-  return o > v ? o : v;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = dpp_max_step<0x111, 0xF>(v);  // row_shr:1
-  v = dpp_max_step<0x112, 0xF>(v);  // row_shr:2
-  v = dpp_max_step<0x114, 0xF>(v);  // row_shr:4
-  v = dpp_max_step<0x118, 0xF>(v);  // row_shr:8
-  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// order-preserving 32-bit key of a logit: larger logit -> larger key; every
-// number maps to >= 0x007FFFFF, NaN to 1 (below every number), 0 = no expert
-__device__ __forceinline__ uint32_t logit_key(float l) {
-  if (l != l) return 1u;
-  uint32_t u = __float_as_uint(l);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_to_logit(uint32_t key) {
-  if (key == 1u) return __uint_as_float(0x7FC00000u);
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
-// Top-k of one token by one wave from its E logits in LDS: k rounds of
-// (wave max of the keys, lowest expert index among the lanes that hold it).
-// Lane j < k ends with rank j: expert, normalised weight.
-__device__ __forceinline__ void topk_wave(const float *__restrict__ lg, int E, int k, int &my_e, float &my_w) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? logit_key(lg[e]) : 0u;
-  }
-  my_e = 0;
-  float my_l = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint32_t m = key[0] > key[1] ? key[0] : key[1];
-    const uint32_t m2 = key[2] > key[3] ? key[2] : key[3];
-    m = wave_max_u32(m > m2 ? m : m2);
-    // lowest e = lane + 64*i holding the maximum: smallest i, then lowest lane
-    int sel = 0;
-    bool found = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t b = __ballot(key[i] == m);
-      if (!found && b) {
-        sel = 64 * i + __ffsll((unsigned long long)b) - 1;
-        found = true;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == sel) key[i] = 0u;
-    if (lane == j) {
-      my_e = sel;
-      my_l = key_to_logit(m);
-    }
-  }
-  float sc = lane < k ? router_score(my_l) : 0.0f;
-  float S = sc;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
-  my_w = sc / S;
-}
-
-// One workgroup, 1 <= T <= 16: slice sums + bias -> logits, top-k of token t
-// by wave t, then per expert the mask of tokens that chose it: counts,
-// offsets, the stable permutation (tokens ascending within an expert) and,
-// for the expert kernels, one tile per used expert in ascending order with
-// its token mask and per-token weights.
+// One workgroup: slice sums + bias -> logits, top-k of token t by wave t, then
+// counts, offsets, the stable permutation and the small-batch tiles.
 __global__ __launch_bounds__(1024) void k_route_dec(const double *__restrict__ part, int nslice,
                                                     const float *__restrict__ bias, float *__restrict__ logits, int T,
                                                     int E, int k, RouteOut ro, DecTile *__restrict__ dt,
                                                     int32_t *__restrict__ ntile) {
-  __shared__ float s_lg[16 * 256];
-  __shared__ int32_t s_idx[16 * 16];
-  __shared__ float s_w[16 * 16];
-  __shared__ uint32_t s_tm[256];
-  __shared__ int32_t s_off[256], s_tb[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = T * E;
-  if (tid < 256) s_tm[tid] = 0u;
-  {
-    double v[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int s0 = 0; s0 < nslice; s0 += 4) {
-      double pv[4][4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = tid + 1024 * q;
-          pv[q][u] = (i < n && s0 + u < nslice) ? part[(int64_t)(s0 + u) * n + i] : 0.0;
-        }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (s0 + u < nslice) v[q] += pv[q][u];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = tid + 1024 * q;
-      if (i < n) {
-        double vv = v[q];
-        if (bias) vv += (double)bias[i % E];
-        const float l = (float)vv;
-        s_lg[i] = l;
-        logits[i] = l;
-      }
-    }
-  }
-  __syncthreads();
-  if (wave < T) {
-    int my_e;
-    float my_w;
-    topk_wave(s_lg + wave * E, E, k, my_e, my_w);
-    if (lane < k) {
-      const int a = wave * k + lane;
-      ro.idx[a] = my_e;
-      ro.w[a] = my_w;
-      s_idx[a] = my_e;
-      s_w[a] = my_w;
-    }
-  }
-  __syncthreads();
-  if (tid < T * k) atomicOr(&s_tm[s_idx[tid]], 1u << (tid / k));
-  __syncthreads();
-  if (wave == 0) {
-    // exclusive scans over experts (4 per lane) of counts and of used flags
-    int c[4], u[4], sc = 0, su = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * lane + i;
-      const uint32_t tm = e < E ? s_tm[e] : 0u;
-      c[i] = __popc(tm);
-      u[i] = tm != 0u;
-      sc += c[i];
-      su += u[i];
-    }
-    int ic = sc, iu = su;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int oc = __shfl_up(ic, off), ou = __shfl_up(iu, off);
-      if (lane >= off) {
-        ic += oc;
-        iu += ou;
-      }
-    }
-    int rc = ic - sc, ru = iu - su;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * lane + i;
-      if (e < E) {
-        s_off[e] = rc;
-        s_tb[e] = ru;
-        ro.counts[e] = c[i];
-        ro.offsets[e] = rc;
-      }
-      rc += c[i];
-      ru += u[i];
-    }
-    if (lane == 63) {
-      ro.offsets[E] = ic;
-      if (ntile) *ntile = iu;
-    }
-  }
-  __syncthreads();
-  if (dt && tid < E) {
-    const uint32_t tm = s_tm[tid];
-    if (tm) {
-      DecTile *d = dt + s_tb[tid];
-      d->e = tid;
-      d->tmask = tm;
-      d->pad0 = 0;
-      d->pad1 = 0;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        float wt = 0.0f;
-        if ((tm >> t) & 1u)
-          for (int j = 0; j < k; ++j)
-            if (s_idx[t * k + j] == tid) wt = s_w[t * k + j];
-        d->w[t] = wt;
-      }
-    }
-  }
-  if (tid < T * k) {
-    const int e = s_idx[tid], t = tid / k;
-    const int p = s_off[e] + __popc(s_tm[e] & ((1u << t) - 1u));
-    ro.perm[p] = tid;
-    if (ro.pos) ro.pos[tid] = p;
-  }
+  __shared__ RouteLds<16> L;
+  route_small_block<1024, 16>(L, part, nslice, bias, logits, T, E, k, ro, dt, ntile, true);
 }
 
 // ---------------------------------------------------------------- launchers

@@ -167,6 +167,42 @@ def test_tiny_ragged_prefill(tiny, T):
     assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 9, 16])
+def test_tiny_ragged_decode(tiny, T):
+    """Decode at every batch-size class: T <= 4 routes inside the gate/up
+    kernel (one template per T), 5..16 through the routing kernel."""
+    q = _q()
+    L0, dl = tiny
+    L = synth.make_layer("tiny", T=T)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"ragged decode T={T}")
+    ref, _, _ = oracle.layer_inputs(L)
+    assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_tiny_decode_all_tokens_one_expert(tiny, T):
+    """Decode with every token sending its first choice to expert 3."""
+    q = _q()
+    L0, dl0 = tiny
+    L = synth.make_layer("tiny", T=T)
+    bias = np.zeros(L.wl.E, np.float32)
+    bias[3] = 100.0
+    L.router_bias = bias
+    dl = q.DeviceLayer(L.wl.H, L.wl.I, L.wl.E, L.wl.k, 0, q.DS4MOE_F32, q.DS4MOE_F32)
+    dl.set_router(L.router_w, bias)
+    dl.gate, dl.up, dl.down = dl0.gate, dl0.up, dl0.down
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE, routing=bufs)
+    torch.cuda.synchronize()
+    idx = check_routing(bufs, L, label=f"decode one-expert T={T}")
+    assert np.all(idx[:, 0] == 3)
+    ref, _, _ = oracle.layer_inputs(L)
+    assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
+
+
 def test_tiny_all_tokens_one_expert(tiny):
     """A large bias on expert 3 sends every token there (several tiles), most
     experts get none."""
@@ -190,16 +226,17 @@ def test_tiny_all_tokens_one_expert(tiny):
         assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
 
 
-@pytest.mark.parametrize("k,E", [(1, 8), (8, 8)])
-def test_tiny_topk_extremes(k, E):
+@pytest.mark.parametrize("k,E,T,mode", [(1, 8, 33, "prefill"), (8, 8, 33, "prefill"), (1, 8, 4, "decode"),
+                                          (8, 8, 4, "decode"), (8, 8, 12, "decode")])
+def test_tiny_topk_extremes(k, E, T, mode):
     """k = 1 (weight exactly 1) and k = E (every expert selected)."""
     q = _q()
-    wl = synth.Workload("tiny_k", 0, T=33, H=256, E=E, I=128, k=k, x_dtype="f32", router_dtype="f32",
+    wl = synth.Workload("tiny_k", 0, T=T, H=256, E=E, I=128, k=k, x_dtype="f32", router_dtype="f32",
                         router_sigma=0.05, layer_id=0)
     L = synth.make_layer(wl)
     dl = q.from_layer_inputs(L)
     bufs = dl.routing_buffers(L.T)
-    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE if mode == "decode" else q.MODE_PREFILL, routing=bufs)
     torch.cuda.synchronize()
     check_routing(bufs, L, label=f"k={k}")
     if k == 1:
@@ -243,6 +280,22 @@ def _full_case(full, name, mode, sample=None, shared=None):
 
 def test_full_decode1(full):
     _full_case(full, "decode1", "decode")
+
+
+@pytest.mark.parametrize("T", [2, 4, 7])
+def test_full_decode_small_batches(full, T):
+    """Full-size decode at batch sizes between the two decode workloads."""
+    q = _q()
+    L0, dl = full
+    L = synth.derive(L0, "decode16", T=T)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"decode T={T}")
+    ref, _, _ = oracle.layer_inputs(L)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"decode T={T}: per-token rel err {err:.3e}")
+    assert err <= TOL_Y
 
 
 def test_full_decode16(full):
