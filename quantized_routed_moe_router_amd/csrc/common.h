@@ -91,6 +91,13 @@ __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void *l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
 }
 
+// vmcnt(N) with the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 __device__ __forceinline__ h8 buf_load_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

@@ -369,6 +369,239 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   }
 }
 
+// ------------------------------------------------------------------ prefill grouped GEMM, wide tiles
+// Workgroup = one tile of up to 96 tokens x (8 waves * R * 16) rows of NM
+// packed matrices.  Per super-block every token row of the tile (256 fp16
+// activations and the 32 halves of their 16-column sums, hi then lo: 36
+// chunks of 16 bytes, plus one pad chunk so that rows start on different
+// banks) arrives through direct-to-LDS buffer loads into one of two ring
+// slots; chunks of rows past the tile's tokens are out of range and arrive as
+// zeros.  One barrier per super-block: after it every wave's loads of this
+// super-block have landed and every wave has finished reading the other slot,
+// which then takes the next super-block's activations while this one is
+// multiplied (the packed weights of the next super-block load into the
+// other register set meanwhile).  The multiply is instantiated for the tile's
+// number of live 16-token n-tiles, so partial tiles issue no dead MFMAs.
+constexpr int PT_NTM = 6;                                          // n-tiles per tile (96 tokens)
+constexpr int PT_CH = 37;                                          // chunks per token row
+constexpr int PT_NW = 8;                                           // waves per workgroup
+constexpr int PT_SLOT_CH = ((PT_NTM * 16 * PT_CH + 64 * PT_NW - 1) / (64 * PT_NW)) * (64 * PT_NW);
+constexpr int PT_LPW = PT_SLOT_CH / (64 * PT_NW);                  // load instructions per wave per slot
+constexpr int PT_SLOT_BYTES = PT_SLOT_CH * 16;
+static_assert(PT_LPW * 64 * PT_NW == PT_SLOT_CH, "slot chunks");
+
+// chunk of the 8 activations a lane (group g) feeds at step S (see step_col)
+template <int S>
+__device__ __forceinline__ int step_chunk(int g) {
+  return 2 * (4 * (S >> 1) + g) + (S & 1);
+}
+
+template <int NM, int R, int NTV>
+__device__ __forceinline__ void pt_compute_sb(const UnitRegs (&u)[R][NM], const char *slot, f4 (&y)[NM][R][NTV],
+                                              int r16, int g) {
+  UnitDecoded dc[R][NM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) dc[r][m] = decode_unit(u[r][m], g);
+  f4 acc[NM][R][NTV];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) acc[m][r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+  const char *rowb = slot + r16 * (PT_CH * 16);
+#define PT_STEP(S)                                                                            \
+  {                                                                                           \
+    h8 b[NTV];                                                                                \
+    _Pragma("unroll") for (int nt = 0; nt < NTV; ++nt) b[nt] =                                \
+        *reinterpret_cast<const h8 *>(rowb + (16 * nt * PT_CH + step_chunk<S>(g)) * 16);       \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                           \
+      _Pragma("unroll") for (int m = 0; m < NM; ++m) {                                        \
+        const h8 A = step_frag<S>(u[r][m], dc[r][m]);                                         \
+        _Pragma("unroll") for (int nt = 0; nt < NTV; ++nt) acc[m][r][nt] =                    \
+            mfma16(A, b[nt], acc[m][r][nt]);                                                  \
+      }                                                                                       \
+    }                                                                                         \
+  }
+  PT_STEP(0) PT_STEP(1) PT_STEP(2) PT_STEP(3) PT_STEP(4) PT_STEP(5) PT_STEP(6) PT_STEP(7)
+#undef PT_STEP
+  h8 bm[NTV];
+#pragma unroll
+  for (int nt = 0; nt < NTV; ++nt) bm[nt] = *reinterpret_cast<const h8 *>(rowb + (16 * nt * PT_CH + 32 + g) * 16);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
+        const f4 mm = mfma16(dc[r][m].mfrag, bm[nt], (f4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          y[m][r][nt][q] = fmaf(dd_d(dc[r][m].dd[q]), acc[m][r][nt][q], y[m][r][nt][q]);
+          y[m][r][nt][q] = fmaf(-dd_dmin(dc[r][m].dd[q]), mm[q], y[m][r][nt][q]);
+        }
+      }
+}
+
+template <int NM, int R, int NTV>
+__device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, const TileT &tl, int rb, char *ring) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  constexpr bool GU = NM == 2;
+  const int K = GU ? a.H : a.Ipad;
+  const int nsb = K >> 8;
+  const int n_rt = (GU ? a.I : a.H) >> 4;
+  const int rt0 = (rb * PT_NW + wave) * R;
+  int rts[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rts[r] = min(rt0 + r, n_rt - 1);
+
+  // this lane's chunk of each of the wave's slot loads: token row u / PT_CH,
+  // chunk u % PT_CH; the source row lookups are issued together
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(xa.base, xa.len);
+  uint32_t src[PT_LPW], inc[PT_LPW];
+  int srow[PT_LPW];
+#pragma unroll
+  for (int q = 0; q < PT_LPW; ++q) {
+    const int u = 64 * (PT_LPW * wave + q) + lane;
+    const int row = u / PT_CH;
+    srow[q] = tl.p0 + (row < tl.n ? row : 0);
+    if (GU) srow[q] = a.perm[srow[q]];
+  }
+#pragma unroll
+  for (int q = 0; q < PT_LPW; ++q) {
+    const int u = 64 * (PT_LPW * wave + q) + lane;
+    const int row = u / PT_CH, c = u - row * PT_CH;
+    const uint32_t sr = (uint32_t)(GU ? srow[q] / a.k : srow[q]);
+    src[q] = DS4_OOB;
+    inc[q] = 0;
+    if (row < tl.n && c < 36) {
+      if (c < 32) {
+        src[q] = sr * xa.row_bytes + 16u * c;
+        inc[q] = 512;
+      } else {
+        const int cc = c - 32;
+        src[q] = ((cc >> 1) ? xa.o_slo : xa.o_shi) + sr * xa.srow_bytes + 16u * (cc & 1);
+        inc[q] = 32;
+      }
+    }
+  }
+  auto issue = [&](int slot, int sb) {
+    char *dst = ring + slot * PT_SLOT_BYTES + (PT_LPW * wave) * 1024;
+#pragma unroll
+    for (int q = 0; q < PT_LPW; ++q) buf_load_lds16(xr, dst + 1024 * q, src[q] + inc[q] * (uint32_t)sb);
+  };
+
+  GemmCtx<NM> c;
+  c.nsb = nsb;
+  c.rt_stride = (size_t)nsb * DS4_UNIT_BYTES;
+  if (GU) {
+    c.W[0] = a.gate + (size_t)tl.e * a.gu_bytes;
+    c.W[NM - 1] = a.up + (size_t)tl.e * a.gu_bytes;
+  } else {
+    c.W[0] = a.down + (size_t)tl.e * a.d_bytes;
+  }
+
+  f4 y[NM][R][NTV];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) y[m][r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  UnitRegs ua[R][NM], ub[R][NM];
+  issue(0, 0);
+  gemm_load_a<NM, R>(ua, c, rts, 0, lane);
+  for (int sb = 0; sb < nsb; sb += 2) {
+    // even super-block: slot 0, weights in ua; the next goes to slot 1 / ub
+    wait_vm<0>();
+    __syncthreads();
+    if (sb + 1 < nsb) {
+      issue(1, sb + 1);
+      gemm_load_a<NM, R>(ub, c, rts, sb + 1, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pt_compute_sb<NM, R, NTV>(ua, ring, y, r16, g);
+    if (sb + 1 >= nsb) break;
+    // odd super-block: slot 1, weights in ub
+    wait_vm<0>();
+    __syncthreads();
+    if (sb + 2 < nsb) {
+      issue(0, sb + 2);
+      gemm_load_a<NM, R>(ua, c, rts, sb + 2, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pt_compute_sb<NM, R, NTV>(ub, ring + PT_SLOT_BYTES, y, r16, g);
+  }
+
+  if (rt0 >= n_rt) return;
+  if (GU) {
+    const int nj = a.Ipad >> 4;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool rv = rt0 + r < n_rt;
+      const int row0 = (rt0 + r) * 16 + 4 * g;
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
+        const int col = 16 * nt + r16;
+        const bool valid = col < tl.n;
+        half_t hv[4];
+        float ssum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float gv = y[0][r][nt][q], uv = y[NM - 1][r][nt][q];
+          hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+          ssum += (float)hv[q];
+        }
+        ssum += __shfl_xor(ssum, 16);
+        ssum += __shfl_xor(ssum, 32);
+        if (valid && rv) {
+          const size_t p = (size_t)(tl.p0 + col);
+          uint2 pk;
+          __builtin_memcpy(&pk, hv, 8);
+          *reinterpret_cast<uint2 *>(a.h + p * a.Ipad + row0) = pk;
+          if (g == 0) {
+            const half_t hi = (half_t)ssum;
+            a.hs_hi[p * nj + rt0 + r] = hi;
+            a.hs_lo[p * nj + rt0 + r] = (half_t)(ssum - (float)hi);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (rt0 + r >= n_rt) continue;
+      const int row0 = (rt0 + r) * 16 + 4 * g;
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
+        const int col = 16 * nt + r16;
+        if (col < tl.n) *reinterpret_cast<f4 *>(a.yp + (size_t)(tl.p0 + col) * a.H + row0) = y[0][r][nt];
+      }
+    }
+  }
+}
+
+template <int NM, int R>
+__global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAct xa, int nrb) {
+  __shared__ __attribute__((aligned(16))) char ring[2 * PT_SLOT_BYTES];
+  const int tile_id = blockIdx.x / nrb;
+  const int rb = blockIdx.x - tile_id * nrb;
+  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
+  const TileT tl = a.tiles[tile_id];
+  switch ((tl.n + 15) >> 4) {  // 1..PT_NTM, uniform
+    case 1: pt_tile<NM, R, 1>(a, xa, tl, rb, ring); break;
+    case 2: pt_tile<NM, R, 2>(a, xa, tl, rb, ring); break;
+    case 3: pt_tile<NM, R, 3>(a, xa, tl, rb, ring); break;
+    case 4: pt_tile<NM, R, 4>(a, xa, tl, rb, ring); break;
+    case 5: pt_tile<NM, R, 5>(a, xa, tl, rb, ring); break;
+    default: pt_tile<NM, R, 6>(a, xa, tl, rb, ring); break;
+  }
+}
+
 // ------------------------------------------------------------------ small batches
 // T <= 16 tokens: token t is MFMA column t of every tile (a zero column where
 // the token did not choose the tile's expert), so h and y are indexed by
@@ -615,12 +848,6 @@ struct SlotLoads {
   static constexpr int NI = (NT * XCH + 63) / 64;  // load instructions per step
 };
 
-// vmcnt(N) with the other counters left alone
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // ROUTE: the workgroup first routes the batch itself (route_small_block on
 // the router's partial sums, one wave per token; the LDS of that step is the
@@ -1050,8 +1277,33 @@ __global__ __launch_bounds__(256) void k_shared_down(const uint16_t *__restrict_
 
 // ------------------------------------------------------------------ launchers
 // Prefill: four n-tiles (64 tokens) per workgroup.
+// Activations of the wide-tile GEMMs: one buffer window from the activation
+// rows to the end of their hi/lo sums (false if it does not fit 2 GiB).
+static bool act_window(const void *rows, const void *s_hi, const void *s_lo, int64_t nrows, int K, GemmAct &xa) {
+  const uint8_t *b = (const uint8_t *)rows;
+  const int64_t ohi = (const uint8_t *)s_hi - b, olo = (const uint8_t *)s_lo - b;
+  const int64_t sbytes = nrows * (int64_t)(K / 16) * 2;
+  const int64_t end = (ohi > olo ? ohi : olo) + sbytes;
+  if (ohi < nrows * (int64_t)K * 2 || olo < nrows * (int64_t)K * 2 || end > (int64_t)0x80000000LL) return false;
+  xa.base = b;
+  xa.len = (uint32_t)end;
+  xa.o_shi = (uint32_t)ohi;
+  xa.o_slo = (uint32_t)olo;
+  xa.row_bytes = (uint32_t)K * 2;
+  xa.srow_bytes = (uint32_t)(K / 16) * 2;
+  return true;
+}
+
 hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
+  if (a.tile_n > 64) {
+    GemmAct xa;
+    if (a.tile_n > 16 * PT_NTM || !act_window(a.x16, a.xs_hi, a.xs_lo, a.T, a.H, xa)) return hipErrorInvalidValue;
+    const int nrb = (a.I + 16 * PT_NW - 1) / (16 * PT_NW);
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW), 0, s, a,
+               xa, nrb);
+    return hipGetLastError();
+  }
   constexpr int R = GEMM_R_GU, NW = GEMM_NW_GU;
   const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.I + rows_per_wg - 1) / rows_per_wg;
@@ -1062,6 +1314,7 @@ hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const 
 
 hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
+  if (a.tile_n > 64) return hipErrorInvalidValue;  // down takes 64-token tiles
   constexpr int R = GEMM_R_DN, NW = GEMM_NW_DN;
   const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.H + rows_per_wg - 1) / rows_per_wg;

@@ -46,8 +46,20 @@ struct RouteOut {
   TileT *tiles;        // [max_tiles] (nullable)
   int32_t *ntiles;     // [1]       (nullable)
   int tile_n;          // tokens per tile
+  TileT *tiles2;       // second list with tile_n2 tokens per tile (nullable)
+  int32_t *ntiles2;    // [1]       (nullable)
+  int tile_n2;
   _Float16 *zeros;     // cleared here each call: read by GEMM lanes with no token
   int nzeros;          // halves
+};
+
+// Activations of a wide-tile grouped GEMM through one buffer window: rows of
+// K fp16 values, then their per-16 sums (hi, lo) at byte offsets o_shi, o_slo.
+struct GemmAct {
+  const uint8_t *base;
+  uint32_t len;
+  uint32_t o_shi, o_slo;
+  uint32_t row_bytes, srow_bytes;
 };
 
 struct GemmArgs {
@@ -68,6 +80,7 @@ struct GemmArgs {
   uint32_t o_x16, o_xs_hi, o_xs_lo, o_h, o_hs_hi, o_hs_lo;
   const DecTile *dtiles;
   int T;
+  int tile_n;                        // tokens per prefill tile (> 64: wide-tile GEMMs)
   const float *ysh;                  // [T,H] shared-expert output or nullptr
   float *y;                          // [T,H]
 };
@@ -94,7 +107,10 @@ hipError_t launch_router_sliced(const void *x, bool x_bf16, const void *wr, bool
 hipError_t launch_route_dec(const double *part, int nslice, const float *bias, float *logits, int T, int E, int k,
                             RouteOut ro, DecTile *dt, int32_t *ntile, hipStream_t s, const Timing *tm = nullptr);
 
-// grouped GEMMs over the tile list (max_tiles = grid bound)
+// grouped GEMMs over the tile list (max_tiles = grid bound); with tiles of
+// more than 64 tokens gate/up takes the wide-tile kernel (its activation
+// window, x16 through the end of its sums, must fit 2 GiB); down always
+// takes tiles of at most 64 tokens (the routing's second list)
 hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
 hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
 // Routing folded into the small-batch gate/up kernel (T <= 4): every

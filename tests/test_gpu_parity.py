@@ -245,6 +245,49 @@ def test_tiny_topk_extremes(k, E, T, mode):
     assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
 
 
+def _mid_workload(T, E=8, k=2):
+    # I a multiple of 256: the prefill GEMMs take 96-token tiles
+    return synth.Workload("mid", 0, T=T, H=512, E=E, I=256, k=k, x_dtype="f32", router_dtype="f32",
+                          router_sigma=0.05, layer_id=0)
+
+
+@pytest.mark.parametrize("T", [1, 17, 48, 97, 300, 1000])
+def test_mid_wide_tiles_prefill(T):
+    """Prefill with 96-token tiles: one partial n-tile, several tiles per
+    expert and ragged last tiles."""
+    q = _q()
+    L = synth.make_layer(_mid_workload(T))
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"mid T={T}")
+    ref, _, _ = oracle.layer_inputs(L)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"mid T={T}: per-token rel err {err:.3e}")
+    assert err <= TOL_Y
+
+
+def test_mid_wide_tiles_one_expert():
+    """Every token's first choice is expert 5: 300 tokens in tiles of 96, 96,
+    96 and 12 for that expert, the other experts share the second choices."""
+    q = _q()
+    T = 300
+    L = synth.make_layer(_mid_workload(T))
+    bias = np.zeros(L.wl.E, np.float32)
+    bias[5] = 100.0
+    L.router_bias = bias
+    dl = q.from_layer_inputs(L)
+    dl.set_router(L.router_w, bias)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    idx = check_routing(bufs, L, label="mid one-expert")
+    assert np.all(idx[:, 0] == 5)
+    ref, _, _ = oracle.layer_inputs(L)
+    assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
+
+
 def test_prefill_zero_tokens_is_noop(tiny):
     q = _q()
     L, dl = tiny
