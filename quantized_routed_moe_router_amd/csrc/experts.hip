@@ -1275,6 +1275,126 @@ __global__ __launch_bounds__(256) void k_shared_down(const uint16_t *__restrict_
   }
 }
 
+// ------------------------------------------------------------------ shared expert, larger batches
+// Dense C[rows, tokens] = W[rows, K] (bf16) x X[tokens, K]^T (fp16), fp32
+// accumulation.  Workgroup = 4 waves, tile of 256 weight rows x 128 tokens;
+// per K-chunk of 32 the weight rows (converted to fp16 once, while staging)
+// and the token rows go to LDS through registers that are loaded one chunk
+// ahead, double-buffered, one barrier per chunk.  Wave (wr, wc) holds 8
+// row n-tiles x 4 token n-tiles of 16x16 accumulators, so every LDS fragment
+// feeds 4 or 8 MFMAs.  GU: the tile's rows are 128 gate rows and the same
+// 128 up rows, a wave takes 64 of each, and the epilogue writes
+// h = silu(gate)*up (fp16); otherwise the rows are 256 down rows, 128 per
+// wave, and the epilogue writes fp32.  Rows past `rows` and tokens past T
+// are zero-filled and not written.
+constexpr int DG_KC = 32;            // K per chunk
+constexpr int DG_LD = 40;            // halves per LDS row (32 + pad: 5 chunks of 16 bytes)
+constexpr int DG_ROWS = 256, DG_TOK = 128;
+
+template <bool GU>
+__global__ __launch_bounds__(256) void k_dense_gemm(const uint16_t *__restrict__ wa, const uint16_t *__restrict__ wb,
+                                                    const half_t *__restrict__ x, void *__restrict__ out, int T,
+                                                    int K, int rows) {
+  __shared__ __attribute__((aligned(16))) half_t sA[2][DG_ROWS * DG_LD];
+  __shared__ __attribute__((aligned(16))) half_t sX[2][DG_TOK * DG_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int row0 = blockIdx.x * (GU ? DG_ROWS / 2 : DG_ROWS);
+  const int t0 = blockIdx.y * DG_TOK;
+
+  // staging: thread tid loads 64 bytes (32 k) of LDS row tid of A and 32
+  // bytes of token row tid/2 of X
+  const int arow = tid;
+  const int wrow = GU ? row0 + (arow & 127) : row0 + arow;
+  const bool aval = wrow < rows;
+  const uint16_t *asrc = (GU && arow >= 128 ? wb : wa) + (size_t)(aval ? wrow : 0) * K;
+  const int xt = tid >> 1, xh = tid & 1;
+  const bool xval = t0 + xt < T;
+  const half_t *xsrc = x + (size_t)(xval ? t0 + xt : 0) * K + 16 * xh;
+  u4 ra[4], rx[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ra[i] = aval ? *reinterpret_cast<const u4 *>(asrc + k0 + 8 * i) : (u4){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      rx[i] = xval ? *reinterpret_cast<const u4 *>(xsrc + k0 + 8 * i) : (u4){0u, 0u, 0u, 0u};
+  };
+  auto store = [&](int b) {
+    half_t *da = sA[b] + arow * DG_LD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<h8 *>(da + 8 * i) = bf16x8_to_h8(ra[i]);
+    half_t *dx = sX[b] + xt * DG_LD + 16 * xh;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u4 *>(dx + 8 * i) = rx[i];
+  };
+
+  // this wave's A fragments: LDS rows of row n-tile i
+  int arow_base[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    arow_base[i] = GU ? (i < 4 ? 64 * wr + 16 * i : 128 + 64 * wr + 16 * (i - 4)) : 128 * wr + 16 * i;
+
+  f4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / DG_KC;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nk; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nk) load((c + 1) * DG_KC);
+    h8 bx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bx[j] = *reinterpret_cast<const h8 *>(sX[b] + (64 * wc + 16 * j + r16) * DG_LD + 8 * g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const h8 av = *reinterpret_cast<const h8 *>(sA[b] + (arow_base[i] + r16) * DG_LD + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(av, bx[j], acc[i][j]);
+    }
+    if (c + 1 < nk) store(b ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: accumulator (i, j) lane (r16, g) = row n-tile i rows 4g..4g+3, token 16j + r16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + 64 * wc + 16 * j + r16;
+    if (t >= T) continue;
+    if (GU) {
+      half_t *hs = reinterpret_cast<half_t *>(out);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = row0 + 64 * wr + 16 * i + 4 * g;
+        if (row >= rows) continue;
+        half_t hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float gv = acc[i][j][q], uv = acc[4 + i][j][q];
+          hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+        }
+        uint2 pk;
+        __builtin_memcpy(&pk, hv, 8);
+        *reinterpret_cast<uint2 *>(hs + (size_t)t * rows + row) = pk;
+      }
+    } else {
+      float *y = reinterpret_cast<float *>(out);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = row0 + 128 * wr + 16 * i + 4 * g;
+        if (row < rows) *reinterpret_cast<f4 *>(y + (size_t)t * rows + row) = acc[i][j];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 // Prefill: four n-tiles (64 tokens) per workgroup.
 // Activations of the wide-tile GEMMs: one buffer window from the activation
@@ -1381,6 +1501,11 @@ hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, c
 hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, _Float16 *hs, int T,
                                 int H, int Is, hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
+  if (T > 64) {
+    const dim3 grid((Is + DG_ROWS / 2 - 1) / (DG_ROWS / 2), (T + DG_TOK - 1) / DG_TOK);
+    DS4_LAUNCH(tm, (k_dense_gemm<true>), grid, dim3(256), 0, s, wg, wu, x16, hs, T, H, Is);
+    return hipGetLastError();
+  }
   constexpr int R = 1, NT = 4;
   const dim3 grid((Is + 16 * R * WAVES - 1) / (16 * R * WAVES), (T + 16 * NT - 1) / (16 * NT));
   DS4_LAUNCH(tm, (k_shared_gateup<R, NT>), grid, dim3(256), 0, s, wg, wu, x16, hs, T, H, Is);
@@ -1390,6 +1515,11 @@ hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _F
 hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, float *ysh, int T, int H, int Is,
                               hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
+  if (T > 64) {
+    const dim3 grid((H + DG_ROWS - 1) / DG_ROWS, (T + DG_TOK - 1) / DG_TOK);
+    DS4_LAUNCH(tm, (k_dense_gemm<false>), grid, dim3(256), 0, s, wd, nullptr, hs, ysh, T, Is, H);
+    return hipGetLastError();
+  }
   constexpr int R = 1, NT = 4;
   const dim3 grid((H + 16 * R * WAVES - 1) / (16 * R * WAVES), (T + 16 * NT - 1) / (16 * NT));
   DS4_LAUNCH(tm, (k_shared_down<R, NT>), grid, dim3(256), 0, s, wd, hs, ysh, T, H, Is);

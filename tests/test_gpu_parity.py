@@ -268,6 +268,26 @@ def test_mid_wide_tiles_prefill(T):
     assert err <= TOL_Y
 
 
+@pytest.mark.parametrize("T,Is", [(20, 96), (200, 96), (300, 256)])
+def test_mid_shared_expert_prefill(T, Is):
+    """Routed layer plus a bf16 shared expert: T <= 64 on the per-wave kernels,
+    larger T on the LDS-tiled GEMMs, with shared rows (Is = 96) and tokens
+    that do not fill the last tile."""
+    q = _q()
+    wl = synth.Workload("mid_sh", 0, T=T, H=512, E=8, I=256, k=2, Is=Is, x_dtype="bf16", router_dtype="bf16",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"mid shared T={T}")
+    ref, _, _ = oracle.layer_inputs(L)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"mid shared T={T} Is={Is}: per-token rel err {err:.3e}")
+    assert err <= TOL_Y
+
+
 def test_mid_wide_tiles_one_expert():
     """Every token's first choice is expert 5: 300 tokens in tiles of 96, 96,
     96 and 12 for that expert, the other experts share the second choices."""
