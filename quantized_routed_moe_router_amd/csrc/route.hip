@@ -180,152 +180,99 @@ template <bool XB, bool WB>
 __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x, const void *__restrict__ wr,
                                                      const float *__restrict__ bias, float *__restrict__ logits,
                                                      int T, int E, int H) {
-  __shared__ float xs[32][68];  // [k][token]
-  __shared__ float ws[32][68];  // [k][expert]
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  // tile: 32 tokens x 64 experts; wave (tw, ew) = 16 tokens x 32 experts.
+  // K-chunks of 32, staged in LDS as fp32 ([k][token], [k][expert]) from raw
+  // registers loaded one chunk ahead; double-buffered, one barrier per chunk.
+  __shared__ float xs[2][32][36];
+  __shared__ float ws[2][32][68];
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  d4 acc[4];
+  const int tw = wave & 1, ew = wave >> 1;
+  d4 acc[2];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = (d4){0.0, 0.0, 0.0, 0.0};
-  const int lrow = tid >> 2, lk = (tid & 3) * 8;
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    {
-      double v[8];
-      const int t = t0 + lrow;
-      if (t < T) {
-        load4_as_double<XB>(x, (int64_t)t * H + k0 + lk, v);
-        load4_as_double<XB>(x, (int64_t)t * H + k0 + lk + 4, v + 4);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xs[lk + i][lrow] = (float)v[i];
-      const int e = e0 + lrow;
-      if (e < E) {
-        load4_as_double<WB>(wr, (int64_t)e * H + k0 + lk, v);
-        load4_as_double<WB>(wr, (int64_t)e * H + k0 + lk + 4, v + 4);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ws[lk + i][lrow] = (float)v[i];
+  for (int n = 0; n < 2; ++n) acc[n] = (d4){0.0, 0.0, 0.0, 0.0};
+  // staging: x token tid/8, k (tid%8)*4 (4 values); w expert tid/4, k (tid%4)*8 (8 values)
+  const int xt = tid >> 3, xk = (tid & 7) * 4;
+  const int we = tid >> 2, wk = (tid & 3) * 8;
+  const bool xv = t0 + xt < T, wv = e0 + we < E;
+  const int64_t xoff = (int64_t)(xv ? t0 + xt : 0) * H + xk;
+  const int64_t woff = (int64_t)(wv ? e0 + we : 0) * H + wk;
+  u4 rx, rw0, rw1;  // raw bits: bf16 x uses rx.xy, bf16 w uses rw0; fp32 uses all
+  auto load = [&](int k0) {
+    if (XB) {
+      const u2 v = xv ? *reinterpret_cast<const u2 *>(reinterpret_cast<const uint16_t *>(x) + xoff + k0) : (u2){0u, 0u};
+      rx = (u4){v.x, v.y, 0u, 0u};
+    } else {
+      rx = xv ? *reinterpret_cast<const u4 *>(reinterpret_cast<const float *>(x) + xoff + k0) : (u4){0u, 0u, 0u, 0u};
     }
-    __syncthreads();
+    if (WB) {
+      rw0 = wv ? *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(wr) + woff + k0) : (u4){0u, 0u, 0u, 0u};
+    } else {
+      const float *p = reinterpret_cast<const float *>(wr) + woff + k0;
+      rw0 = wv ? *reinterpret_cast<const u4 *>(p) : (u4){0u, 0u, 0u, 0u};
+      rw1 = wv ? *reinterpret_cast<const u4 *>(p + 4) : (u4){0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int b) {
+    float xf[4], wf[8];
+    if (XB) {
+      xf[0] = bf16_bits_to_float((uint16_t)(rx.x & 0xFFFFu));
+      xf[1] = bf16_bits_to_float((uint16_t)(rx.x >> 16));
+      xf[2] = bf16_bits_to_float((uint16_t)(rx.y & 0xFFFFu));
+      xf[3] = bf16_bits_to_float((uint16_t)(rx.y >> 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xf[i] = __uint_as_float(rx[i]);
+    }
+    if (WB) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wf[2 * i] = bf16_bits_to_float((uint16_t)(rw0[i] & 0xFFFFu));
+        wf[2 * i + 1] = bf16_bits_to_float((uint16_t)(rw0[i] >> 16));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wf[i] = __uint_as_float(rw0[i]);
+        wf[4 + i] = __uint_as_float(rw1[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xs[b][xk + i][xt] = xf[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ws[b][wk + i][we] = wf[i];
+  };
+  const int nk = H / 32;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nk; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nk) load((c + 1) * 32);
 #pragma unroll
     for (int kk = 0; kk < 32; kk += 4) {
-      const double a = (double)xs[kk + g][16 * wave + r16];
+      const double av = (double)xs[b][kk + g][16 * tw + r16];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const double b = (double)ws[kk + g][16 * n + r16];
-        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[n], 0, 0, 0);
+      for (int n = 0; n < 2; ++n) {
+        const double bv = (double)ws[b][kk + g][32 * ew + 16 * n + r16];
+        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[n], 0, 0, 0);
       }
     }
+    if (c + 1 < nk) store(b ^ 1);
     __syncthreads();
   }
   // D (fp64 16x16x4): lane holds rows (tokens) g, g+4, g+8, g+12 of the wave's 16,
   // column (expert) r16
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int e = e0 + 16 * n + r16;
+  for (int n = 0; n < 2; ++n) {
+    const int e = e0 + 32 * ew + 16 * n + r16;
     if (e >= E) continue;
-    const double b = bias ? (double)bias[e] : 0.0;
+    const double bb = bias ? (double)bias[e] : 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * wave + g + 4 * i;
-      if (t < T) logits[(int64_t)t * E + e] = (float)(acc[n][i] + b);
-    }
-  }
-}
-
-// order-preserving key: larger logit first, then lower expert index; NaN last
-__device__ __forceinline__ uint64_t rank_key(float l, int e) {
-  uint32_t u = __float_as_uint(l);
-  uint32_t ord;
-  if (l != l) {
-    ord = 0u;
-  } else {
-    if (u == 0x80000000u) u = 0u;  // -0 == +0
-    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
-  if (ord == 0u) return __uint_as_float(0x7FC00000u);
-  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-  return __uint_as_float(u);
-}
-
-// max with the value DPP-shifted right by N lanes inside each 16-lane row
-// (lanes with no source keep their own value)
-template <int N>
-__device__ __forceinline__ uint64_t dpp_max_shr(uint64_t v) {
-  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, 0x110 | N, 0xF, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, 0x110 | N, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > v ? o : v;
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// wave-wide max: row prefix maxima by DPP, then the four row maxima
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_shr<1>(v);
-  v = dpp_max_shr<2>(v);
-  v = dpp_max_shr<4>(v);
-  v = dpp_max_shr<8>(v);
-  uint64_t m = readlane_u64(v, 15);
-  const uint64_t m1 = readlane_u64(v, 31), m2 = readlane_u64(v, 47), m3 = readlane_u64(v, 63);
-  m = m1 > m ? m1 : m;
-  m = m2 > m ? m2 : m;
-  m = m3 > m ? m3 : m;
-  return m;
-}
-
-// Top-k of one token by one wave from the logits of experts lane + 64*i held
-// in registers; lane j < k writes rank j (index and normalised weight) to
-// global memory and, if s_row is given, the index to s_row[j] (LDS) as well.
-__device__ void topk_select(const float lv[4], int t, int E, int k, RouteOut ro, int32_t *s_row) {
-  const int lane = threadIdx.x & 63;
-  uint64_t keys[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    keys[i] = e < E ? rank_key(lv[i], e) : 0ull;  // live keys are never 0
-  }
-  float sel_l[16];
-  int sel_e[16];
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) best = keys[i] > best ? keys[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (keys[i] == best) keys[i] = 0ull;  // keys are unique: removes the winner
-    sel_e[j] = e;
-    sel_l[j] = key_logit(best);
-  }
-  float sc[16], S = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    sc[j] = router_score(sel_l[j]);
-    S += sc[j];
-  }
-  for (int j = 0; j < k; ++j) {
-    if (lane == j) {
-      ro.idx[(int64_t)t * k + j] = sel_e[j];
-      ro.w[(int64_t)t * k + j] = sc[j] / S;
-      if (s_row) s_row[j] = sel_e[j];
+      const int t = t0 + 16 * tw + g + 4 * i;
+      if (t < T) logits[(int64_t)t * E + e] = (float)(acc[n][i] + bb);
     }
   }
 }
@@ -382,39 +329,69 @@ __device__ void xprep_token(int t, int H, const void *xptr, bool x_bf16, _Float1
 // the chunk's assignments to the same expert (earlier tokens first).
 constexpr int CHUNK = 64;
 
-__global__ __launch_bounds__(256) void k_topk_chunk(const float *__restrict__ logits, int T, int E, int k, int H,
-                                                    XPrep xp, bool do_x, RouteOut ro, int32_t *__restrict__ ccnt,
-                                                    int32_t *__restrict__ lrank) {
+// One workgroup of 16 waves per chunk of 64 tokens; wave w takes tokens
+// 4w..4w+3 of the chunk: their logits are loaded together, staged in the
+// wave's LDS row and ranked by topk_wave; then the per-expert token masks of
+// the chunk give its counts and each assignment's rank inside the chunk.
+__global__ __launch_bounds__(1024) void k_topk_chunk(const float *__restrict__ logits, int T, int E, int k, int H,
+                                                     XPrep xp, bool do_x, RouteOut ro, int32_t *__restrict__ ccnt,
+                                                     int32_t *__restrict__ lrank) {
   __shared__ int32_t s_idx[CHUNK * 16];
   __shared__ uint32_t s_mask[256 * 2];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float s_lg[16][256];
+  __shared__ uint64_t s_sel[16][128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = blockIdx.x * CHUNK;
-  for (int i = threadIdx.x; i < E * 2; i += 256) s_mask[i] = 0u;
-  for (int q = 0; q < CHUNK / 4; ++q) {
-    const int tl = 16 * wave + q;
-    const int t = c0 + tl;
-    if (t >= T) break;
-    float lv[4];
+  for (int i = tid; i < E * 2; i += 1024) s_mask[i] = 0u;
+  float lv[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lv[i] = (lane + 64 * i < E) ? logits[(int64_t)t * E + lane + 64 * i] : 0.0f;
-    topk_select(lv, t, E, k, ro, s_idx + tl * k);
-    if (do_x) xprep_token(t, H, xp.x, xp.x_bf16, xp.x16, xp.xs_hi, xp.xs_lo);
+  for (int q = 0; q < 4; ++q) {
+    const int t = c0 + 4 * wave + q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      lv[q][i] = (t < T && e < E) ? logits[(int64_t)t * E + e] : 0.0f;
+    }
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int tl = 4 * wave + q;
+    const int t = c0 + tl;
+    if (t >= T) break;  // uniform per wave
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_lg[wave][4 * lane + i] = lv[q][i];
+    wave_lds_order();
+    int my_e;
+    float my_w;
+    topk_wave(s_lg[wave], E, k, my_e, my_w, s_sel[wave]);
+    if (lane < k) {
+      ro.idx[(int64_t)t * k + lane] = my_e;
+      ro.w[(int64_t)t * k + lane] = my_w;
+      s_idx[tl * k + lane] = my_e;
+    }
+    wave_lds_order();
+  }
+  if (do_x)
+    for (int q = 0; q < 4; ++q) {
+      const int t = c0 + 4 * wave + q;
+      if (t >= T) break;
+      xprep_token(t, H, xp.x, xp.x_bf16, xp.x16, xp.xs_hi, xp.xs_lo);
+    }
   __syncthreads();
   const int nt = min(CHUNK, T - c0);
-  for (int a = threadIdx.x; a < nt * k; a += 256) {
+  for (int a = tid; a < nt * k; a += 1024) {
     const int tl = a / k;
     atomicOr(&s_mask[s_idx[a] * 2 + (tl >> 5)], 1u << (tl & 31));
   }
   __syncthreads();
-  for (int a = threadIdx.x; a < nt * k; a += 256) {
+  for (int a = tid; a < nt * k; a += 1024) {
     const int tl = a / k;
     const uint32_t *m = s_mask + s_idx[a] * 2;
     int r = __popc(m[tl >> 5] & ((1u << (tl & 31)) - 1u));
     if (tl >= 32) r += __popc(m[0]);
     lrank[(int64_t)c0 * k + a] = r;
   }
-  for (int e = threadIdx.x; e < E; e += 256)
+  for (int e = tid; e < E; e += 1024)
     ccnt[(int64_t)blockIdx.x * E + e] = __popc(s_mask[2 * e]) + __popc(s_mask[2 * e + 1]);
 }
 
@@ -543,7 +520,7 @@ __global__ __launch_bounds__(1024) void k_route_dec(const double *__restrict__ p
 template <bool XB, bool WB>
 static hipError_t router_tiled_t(const void *x, const void *wr, const float *bias, float *logits, int T, int E,
                                  int H, hipStream_t s, const Timing *tm) {
-  DS4_LAUNCH(tm, (k_router_mfma<XB, WB>), dim3((T + 63) / 64, (E + 63) / 64), dim3(256), 0, s, x, wr, bias,
+  DS4_LAUNCH(tm, (k_router_mfma<XB, WB>), dim3((T + 31) / 32, (E + 63) / 64), dim3(256), 0, s, x, wr, bias,
              logits, T, E, H);
   return hipGetLastError();
 }
@@ -565,7 +542,7 @@ hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H,
                                 const Timing *tm_perm) {
   const int nchunk = chunk_count(T);
   XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
-  DS4_LAUNCH(tm_topk, k_topk_chunk, dim3(nchunk), dim3(256), 0, s, logits, T, E, k, H, x, xp != nullptr, ro, ccnt,
+  DS4_LAUNCH(tm_topk, k_topk_chunk, dim3(nchunk), dim3(1024), 0, s, logits, T, E, k, H, x, xp != nullptr, ro, ccnt,
              lrank);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
