@@ -39,8 +39,6 @@ struct Layout {
   int nzeros;
   size_t total;
   int tile_n, max_tiles, Ipad;
-  int max_tiles2;  // 64-token tiles of the down GEMM when tile_n > 64, else 0
-  size_t tiles2, ntiles2;
   bool sliced;  // T <= 16 routing (sliced router + one-workgroup routing); else the chunked path
 };
 
@@ -60,12 +58,13 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
   L.Ipad = d.inter % 256 ? 256 : d.inter;
   L.tile_n = mode == DS4MOE_MODE_PREFILL ? kTilePrefill : kTileDecode;
   if (mode == DS4MOE_MODE_PREFILL && d.inter % 256 == 0) {
-    // wide tiles when the gate/up activation window (x16 and its hi/lo sums,
-    // contiguous below) fits 2 GiB
+    // wide tiles when the activation windows (x16 or h and their hi/lo sums,
+    // contiguous below) fit 2 GiB
     const int64_t xw = (int64_t)align256(2 * T * H) + (int64_t)align256(2 * T * (H / 16)) + 2 * T * (H / 16);
-    if (xw <= ((int64_t)1 << 31)) L.tile_n = kTilePrefillWide;
+    const int64_t hw = (int64_t)align256(2 * A * L.Ipad) + (int64_t)align256(2 * A * (L.Ipad / 16)) +
+                       2 * A * (L.Ipad / 16);
+    if (xw <= ((int64_t)1 << 31) && hw <= ((int64_t)1 << 31)) L.tile_n = kTilePrefillWide;
   }
-  L.max_tiles2 = L.tile_n > kTilePrefill ? (int)(A / kTilePrefill + (A < E ? A : E)) : 0;
   L.max_tiles = mode == DS4MOE_MODE_DECODE ? (int)(A < E ? A : E) : (int)(A / L.tile_n + (A < E ? A : E));
   L.logits = take(sizeof(float) * T * E);
   L.part = L.sliced ? take(sizeof(double) * router_slices((int)H) * T * E) : 0;
@@ -94,10 +93,6 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
       L.tiles = take(sizeof(DecTile) * (size_t)L.max_tiles);
     } else {
       L.tiles = take(sizeof(TileT) * (size_t)L.max_tiles);
-      if (L.max_tiles2) {
-        L.tiles2 = take(sizeof(TileT) * (size_t)L.max_tiles2);
-        L.ntiles2 = take(16);
-      }
       L.pos = take(sizeof(int32_t) * A);
       L.yp = take(sizeof(float) * A * H);
       L.nzeros = (int)(H > L.Ipad ? H : L.Ipad);
@@ -206,17 +201,11 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
 
   XPrep xp{x, xb, at<_Float16>(ws, L.x16), at<_Float16>(ws, L.xs_hi), at<_Float16>(ws, L.xs_lo)};
   const bool dec = mode == DS4MOE_MODE_DECODE;
-  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, L.tile_n, nullptr, nullptr, 0,
-              nullptr, 0};
+  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, L.tile_n, nullptr, 0};
   if (!dec) {
     ro.pos = at<int32_t>(ws, L.pos);
     ro.tiles = at<TileT>(ws, L.tiles);
     ro.ntiles = at<int32_t>(ws, L.ntiles);
-    if (L.max_tiles2) {  // down takes 64-token tiles
-      ro.tiles2 = at<TileT>(ws, L.tiles2);
-      ro.ntiles2 = at<int32_t>(ws, L.ntiles2);
-      ro.tile_n2 = kTilePrefill;
-    }
     ro.zeros = at<_Float16>(ws, L.zeros);
     ro.nzeros = L.nzeros;
   }
@@ -293,13 +282,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     TRY(launch_down_combine_dec(ga, s, tm(SL_DOWN)));
   } else {
     TRY(launch_gateup(ga, L.max_tiles, s, tm(SL_GATEUP)));
-    GemmArgs gd = ga;
-    if (L.max_tiles2) {
-      gd.tiles = ro.tiles2;
-      gd.ntiles = ro.ntiles2;
-      gd.tile_n = kTilePrefill;
-    }
-    TRY(launch_down(gd, L.max_tiles2 ? L.max_tiles2 : L.max_tiles, s, tm(SL_DOWN)));
+    TRY(launch_down(ga, L.max_tiles, s, tm(SL_DOWN)));
     st = shared();
     if (st) return st;
     TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s, tm(SL_COMBINE)));
@@ -377,8 +360,7 @@ int ds4moe_route(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x
   hipStream_t s = (hipStream_t)stream;
   const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
   const Ptrs p = routing_ptrs(ws, L, out);
-  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, kTileDecode, nullptr, nullptr, 0,
-              nullptr, 0};
+  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, kTileDecode, nullptr, 0};
   if (L.sliced) {
     TRY(launch_router_sliced(x, xb, w->router_w, wb, at<double>(ws, L.part), T, d.n_experts, d.hidden, nullptr,
                              s));

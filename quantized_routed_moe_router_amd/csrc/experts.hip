@@ -585,13 +585,21 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
   }
 }
 
-template <int NM, int R>
+// ALL: every tile takes the PT_NTM-n-tile multiply (one instance; empty
+// n-tiles multiply zeros).  The down projection uses it: a build with one
+// instance per n-tile count and two row tiles per wave gave wrong values in
+// its last n-tile, which the single instance does not.
+template <int NM, int R, bool ALL>
 __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAct xa, int nrb) {
   __shared__ __attribute__((aligned(16))) char ring[2 * PT_SLOT_BYTES];
   const int tile_id = blockIdx.x / nrb;
   const int rb = blockIdx.x - tile_id * nrb;
   if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
   const TileT tl = a.tiles[tile_id];
+  if (ALL) {
+    pt_tile<NM, R, PT_NTM>(a, xa, tl, rb, ring);
+    return;
+  }
   switch ((tl.n + 15) >> 4) {  // 1..PT_NTM, uniform
     case 1: pt_tile<NM, R, 1>(a, xa, tl, rb, ring); break;
     case 2: pt_tile<NM, R, 2>(a, xa, tl, rb, ring); break;
@@ -1420,8 +1428,8 @@ hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const 
     GemmAct xa;
     if (a.tile_n > 16 * PT_NTM || !act_window(a.x16, a.xs_hi, a.xs_lo, a.T, a.H, xa)) return hipErrorInvalidValue;
     const int nrb = (a.I + 16 * PT_NW - 1) / (16 * PT_NW);
-    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW), 0, s, a,
-               xa, nrb);
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1, false>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW), 0,
+               s, a, xa, nrb);
     return hipGetLastError();
   }
   constexpr int R = GEMM_R_GU, NW = GEMM_NW_GU;
@@ -1434,7 +1442,16 @@ hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const 
 
 hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
-  if (a.tile_n > 64) return hipErrorInvalidValue;  // down takes 64-token tiles
+  if (a.tile_n > 64) {
+    GemmAct xa;
+    if (a.tile_n > 16 * PT_NTM || a.I != a.Ipad ||
+        !act_window(a.h, a.hs_hi, a.hs_lo, (int64_t)a.T * a.k, a.Ipad, xa))
+      return hipErrorInvalidValue;
+    const int nrb = (a.H + 32 * PT_NW - 1) / (32 * PT_NW);
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<1, 2, true>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW), 0, s,
+               a, xa, nrb);
+    return hipGetLastError();
+  }
   constexpr int R = GEMM_R_DN, NW = GEMM_NW_DN;
   const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.H + rows_per_wg - 1) / rows_per_wg;

@@ -46,9 +46,6 @@ struct RouteOut {
   TileT *tiles;        // [max_tiles] (nullable)
   int32_t *ntiles;     // [1]       (nullable)
   int tile_n;          // tokens per tile
-  TileT *tiles2;       // second list with tile_n2 tokens per tile (nullable)
-  int32_t *ntiles2;    // [1]       (nullable)
-  int tile_n2;
   _Float16 *zeros;     // cleared here each call: read by GEMM lanes with no token
   int nzeros;          // halves
 };
@@ -107,10 +104,9 @@ hipError_t launch_router_sliced(const void *x, bool x_bf16, const void *wr, bool
 hipError_t launch_route_dec(const double *part, int nslice, const float *bias, float *logits, int T, int E, int k,
                             RouteOut ro, DecTile *dt, int32_t *ntile, hipStream_t s, const Timing *tm = nullptr);
 
-// grouped GEMMs over the tile list (max_tiles = grid bound); with tiles of
-// more than 64 tokens gate/up takes the wide-tile kernel (its activation
-// window, x16 through the end of its sums, must fit 2 GiB); down always
-// takes tiles of at most 64 tokens (the routing's second list)
+// grouped GEMMs over the tile list (max_tiles = grid bound); tiles of more
+// than 64 tokens take the wide-tile kernels, whose activation windows (x16 or
+// h through the end of their sums) must fit 2 GiB
 hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
 hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm = nullptr);
 // Routing folded into the small-batch gate/up kernel (T <= 4): every

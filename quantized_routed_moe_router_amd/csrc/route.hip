@@ -400,7 +400,7 @@ __global__ __launch_bounds__(1024) void k_topk_chunk(const float *__restrict__ l
 __global__ __launch_bounds__(1024) void k_scan_chunks(int T, int E, int k, int nchunk,
                                                       const int32_t *__restrict__ ccnt, int32_t *__restrict__ base,
                                                       RouteOut ro) {
-  __shared__ int32_t s_cnt[256], s_off[256], s_tb[256], s_tb2[256];
+  __shared__ int32_t s_cnt[256], s_off[256], s_tb[256];
   const int tid = threadIdx.x;
   if (ro.zeros)
     for (int i = tid; i < ro.nzeros; i += 1024) ro.zeros[i] = (half_t)0.0f;
@@ -422,46 +422,40 @@ __global__ __launch_bounds__(1024) void k_scan_chunks(int T, int E, int k, int n
   __syncthreads();
   if (tid < 64) {
     const int lane = tid;
-    int c[4], nt[4], nt2[4], sc = 0, st = 0, st2 = 0;
+    int c[4], nt[4], sc = 0, st = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
       c[i] = e < E ? s_cnt[e] : 0;
       nt[i] = (ro.tiles && c[i] > 0) ? (c[i] + ro.tile_n - 1) / ro.tile_n : 0;
-      nt2[i] = (ro.tiles2 && c[i] > 0) ? (c[i] + ro.tile_n2 - 1) / ro.tile_n2 : 0;
       sc += c[i];
       st += nt[i];
-      st2 += nt2[i];
     }
-    int ic = sc, it = st, it2 = st2;
+    int ic = sc, it = st;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int oc = __shfl_up(ic, off), ot = __shfl_up(it, off), ot2 = __shfl_up(it2, off);
+      const int oc = __shfl_up(ic, off), ot = __shfl_up(it, off);
       if (lane >= off) {
         ic += oc;
         it += ot;
-        it2 += ot2;
       }
     }
-    int rc = ic - sc, rt = it - st, rt2 = it2 - st2;
+    int rc = ic - sc, rt = it - st;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
       if (e < E) {
         s_off[e] = rc;
         s_tb[e] = rt;
-        s_tb2[e] = rt2;
         ro.counts[e] = c[i];
         ro.offsets[e] = rc;
       }
       rc += c[i];
       rt += nt[i];
-      rt2 += nt2[i];
     }
     if (lane == 63) {
       ro.offsets[E] = ic;
       if (ro.ntiles) *ro.ntiles = it;
-      if (ro.ntiles2) *ro.ntiles2 = it2;
     }
   }
   __syncthreads();
@@ -475,18 +469,6 @@ __global__ __launch_bounds__(1024) void k_scan_chunks(int T, int E, int k, int n
       tl.n = min(ro.tile_n, c - i * ro.tile_n);
       tl.pad = 0;
       ro.tiles[s_tb[e] + i] = tl;
-    }
-  }
-  for (int e = tid; e < E && ro.tiles2; e += 1024) {
-    const int c = s_cnt[e];
-    const int nt = (c + ro.tile_n2 - 1) / ro.tile_n2;
-    for (int i = 0; i < nt; ++i) {
-      TileT tl;
-      tl.e = e;
-      tl.p0 = s_off[e] + i * ro.tile_n2;
-      tl.n = min(ro.tile_n2, c - i * ro.tile_n2);
-      tl.pad = 0;
-      ro.tiles2[s_tb2[e] + i] = tl;
     }
   }
 }
