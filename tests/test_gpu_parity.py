@@ -308,6 +308,52 @@ def test_mid_wide_tiles_one_expert():
     assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
 
 
+@pytest.mark.parametrize("T,mode", [(5, "decode"), (16, "decode"), (40, "prefill")])
+def test_k16_e256_limits(T, mode):
+    """The largest top-k (16) over the largest expert count (256)."""
+    q = _q()
+    wl = synth.Workload("lim", 0, T=T, H=256, E=256, I=128, k=16, x_dtype="f32", router_dtype="f32",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE if mode == "decode" else q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"k16 {mode} T={T}")
+    ref, _, _ = oracle.layer_inputs(L)
+    assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
+
+
+@pytest.mark.parametrize("T,mode", [(3, "decode"), (12, "decode"), (70, "prefill")])
+def test_nan_token_keeps_others(T, mode):
+    """A NaN in one token's activations (out of contract): its logits are NaN,
+    it selects experts 0..k-1 (NaN ranks last, ties to the lower index), the
+    routing stays a valid permutation, and every other token is unaffected."""
+    q = _q()
+    L = synth.make_layer("tiny", T=T)
+    bad = T // 2
+    L.x = L.x.copy()
+    L.x[bad, 5] = np.nan
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE if mode == "decode" else q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    k, E = L.wl.k, L.wl.E
+    idx = bufs["topk_idx"].cpu().numpy()
+    assert np.array_equal(idx[bad], np.arange(k))
+    lg = bufs["logits"].cpu().numpy()
+    assert np.all(np.isnan(lg[bad]))
+    counts, offsets, perm = oracle.permute(idx, E)
+    assert np.array_equal(bufs["counts"].cpu().numpy(), counts)
+    assert np.array_equal(bufs["perm"].cpu().numpy(), perm)
+    good = [t for t in range(T) if t != bad]
+    ref, ridx, _ = oracle.layer_inputs(L, tokens=good)
+    assert np.array_equal(ridx, idx[good])
+    ref_lg = oracle.logits(L.x[good].astype(np.float32), L.router_w, L.router_bias)
+    assert np.array_equal(lg[good].view(np.uint32), ref_lg.view(np.uint32))
+    assert per_token_err(y.cpu().numpy()[good], ref) <= TOL_Y
+
+
 def test_prefill_zero_tokens_is_noop(tiny):
     q = _q()
     L, dl = tiny
