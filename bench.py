@@ -91,21 +91,59 @@ def copy_calibration(mib: int, reps: int) -> dict:
 
 
 def cpu_baseline(L, budget_s: float) -> dict:
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    small batches are repeated over fresh token batches of the workload,
+    large ones are taken in growing token prefixes, until about budget_s of
+    CPU time has been spent."""
     import oracle
-    import synth  # noqa: F401
-    T = L.T
+    import synth
+    T, wl = L.T, L.wl
+    done, spent, what = 0, 0.0, ""
+    if T <= 16:
+        b = 0
+        while spent < budget_s and b < 4096:
+            Lb = L if b == 0 else synth.derive(L, wl, batch=b)
+            t0 = time.perf_counter()
+            oracle.layer_inputs(Lb)
+            spent += time.perf_counter() - t0
+            done += T
+            b += 1
+        what = f"{b} token batches of {T} (batch 0 the benchmarked one, then fresh draws of the same recipe)"
+    else:
+        n = 1
+        while True:
+            t0 = time.perf_counter()
+            oracle.layer_inputs(L, tokens=list(range(n)))
+            dt = time.perf_counter() - t0
+            if dt >= budget_s or n >= T:
+                break
+            n = min(T, max(n + 1, int(n * min(8.0, 1.2 * budget_s / max(dt, 1e-3)))))
+        done, spent = n, dt
+        what = f"first {n} of the {T} tokens of one batch"
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": done / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{L.wl.name}: {what}, full layer (fp64 C, OpenMP), {spent:.1f} s", "cpu_model": model}
+
+
+def library_gemm_reference(n: int = 8192, reps: int = 10) -> dict:
+    """Context for the MFMA fraction: a dense fp16 GEMM through the vendor
+    library (torch.matmul), n x n x n, on the same GPU."""
+    import torch
+    a = torch.randn(n, n, dtype=torch.float16, device="cuda:0")
+    b = torch.randn(n, n, dtype=torch.float16, device="cuda:0")
+    torch.matmul(a, b)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    oracle.layer_inputs(L, tokens=[0])
-    one = time.perf_counter() - t0
-    n = int(max(1, min(T, budget_s / max(one, 1e-3))))
-    toks = list(range(n))
-    t0 = time.perf_counter()
-    oracle.layer_inputs(L, tokens=toks)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {n} of the {T} tokens of one {L.wl.name} batch, full layer "
-                      f"(fp64 C, OpenMP), {dt:.1f} s"}
+    for _ in range(reps):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return {"shape": f"{n}x{n}x{n} fp16", "TFLOP/s": round(2.0 * n ** 3 / dt / 1e12, 1)}
 
 
 def run_workload(name: str, args) -> dict:
@@ -189,9 +227,31 @@ def run_workload(name: str, args) -> dict:
             graph.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t1
+        # spread: a second pass of the same replays with an event between
+        # replays (outside the timed region); per-step time of each replay
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        marks[0].record()
+        for r in range(reps):
+            graph.replay()
+            marks[r + 1].record()
+        torch.cuda.synchronize()
+        rep_ms = np.array([marks[r].elapsed_time(marks[r + 1]) / glen for r in range(reps)])
+        pct = {f"p{q}": round(float(np.percentile(rep_ms, q)), 5) for q in (10, 50, 90)}
+        pct["over"] = f"{reps} replays of {glen} steps"
         del graph
+        if reps < 10:  # too few replays: eager steps, an event between steps
+            marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            marks[0].record()
+            for i in range(steps):
+                step(i)
+                marks[i + 1].record()
+            torch.cuda.synchronize()
+            st_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+            pct = {f"p{q}": round(float(np.percentile(st_ms, q)), 5) for q in (10, 50, 90)}
+            pct["over"] = f"{steps} eager steps"
     else:
         elapsed = elapsed_eager
+        pct = None
 
     # second pass with per-kernel events stamped by each kernel's own dispatch
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * B.N_TIMED_KERNELS)] for _ in range(steps_eager)]
@@ -250,10 +310,13 @@ def run_workload(name: str, args) -> dict:
         "layer_roofline": layer,
         "kernel_ms": {s: round(v, 5) for s, v in stage_ms.items()},
         "launch": f"hip graph of {glen} layer calls, replayed" if glen else "eager launches",
+        "ms_per_step_percentiles": pct,
         "ms_per_step_eager": round(elapsed_eager / steps_eager * 1e3, 5),
         "ms_per_step_with_kernel_events": round(elapsed_ev / steps_eager * 1e3, 5),
         "setup_s": round(setup_s, 1),
     }
+    if mode != q.MODE_DECODE and not args.no_gemm_reference:
+        out["roofline"]["library_fp16_gemm_reference"] = library_gemm_reference()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
     del copies, xs, dl
@@ -272,6 +335,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the library fp16 GEMM reference run (prefill workloads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
     args = ap.parse_args()
