@@ -54,6 +54,10 @@ def lib():
         L.oracle_topk.argtypes = [P, I64, I64, I64, P, P, P]
         L.oracle_permute.argtypes = [P, I64, I64, I64, P, P, P]
         L.oracle_layer.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, I64, P, P, P, P, P, P]
+        L.oracle_dequant_f64_bits.argtypes = [P, I64, ctypes.c_int, P]
+        L.oracle_dequant_f32_bits.argtypes = [P, I64, ctypes.c_int, P]
+        L.oracle_layer_bits.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, ctypes.c_int, I64, P, P, P, P,
+                                        P, P]
         L.oracle_layer.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -68,19 +72,25 @@ def _p(a):
     return ctypes.c_void_p(0) if a is None else ctypes.c_void_p(a.ctypes.data)
 
 
-def dequant_f64(blocks: np.ndarray) -> np.ndarray:
+def block_bytes(bits: int = 2) -> int:
+    """Bytes of one block of 256 weights with 2- or 4-bit codes."""
+    assert bits in (2, 4)
+    return 16 + 32 * bits + 4
+
+
+def dequant_f64(blocks: np.ndarray, bits: int = 2) -> np.ndarray:
     b = _c(blocks, np.uint8).reshape(-1)
-    nb = b.size // 84
+    nb = b.size // block_bytes(bits)
     out = np.empty(nb * 256, dtype=np.float64)
-    lib().oracle_dequant_f64(_p(b), nb, _p(out))
+    lib().oracle_dequant_f64_bits(_p(b), nb, bits, _p(out))
     return out
 
 
-def dequant_f32(blocks: np.ndarray) -> np.ndarray:
+def dequant_f32(blocks: np.ndarray, bits: int = 2) -> np.ndarray:
     b = _c(blocks, np.uint8).reshape(-1)
-    nb = b.size // 84
+    nb = b.size // block_bytes(bits)
     out = np.empty(nb * 256, dtype=np.float32)
-    lib().oracle_dequant_f32(_p(b), nb, _p(out))
+    lib().oracle_dequant_f32_bits(_p(b), nb, bits, _p(out))
     return out
 
 
@@ -128,7 +138,7 @@ def permute(idx: np.ndarray, E: int):
     return counts, offsets, perm
 
 
-def layer(x, wr, bias, gate, up, down, H, I, E, k, sh_gate=None, sh_up=None, sh_down=None):
+def layer(x, wr, bias, gate, up, down, H, I, E, k, sh_gate=None, sh_up=None, sh_down=None, bits=2):
     """Whole layer.  x [T,H] and wr [E,H] as fp32 values; gate/up/down canonical
     blocks [E, nbytes]; shared weights as fp32 values or None.
     Returns (y fp32 [T,H], idx int32 [T,k], w fp32 [T,k])."""
@@ -145,8 +155,8 @@ def layer(x, wr, bias, gate, up, down, H, I, E, k, sh_gate=None, sh_up=None, sh_
     y = np.empty((T, H), dtype=np.float32)
     idx = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float32)
-    rc = lib().oracle_layer(_p(x), T, H, I, E, k, _p(wr), _p(b), _p(g), _p(u), _p(d), Is,
-                            _p(sg), _p(su), _p(sd), _p(y), _p(idx), _p(w))
+    rc = lib().oracle_layer_bits(_p(x), T, H, I, E, k, _p(wr), _p(b), _p(g), _p(u), _p(d), bits, Is,
+                                 _p(sg), _p(su), _p(sd), _p(y), _p(idx), _p(w))
     if rc != 0:
         raise MemoryError("oracle_layer failed to allocate")
     return y, idx, w
@@ -167,7 +177,7 @@ def layer_inputs(L, tokens=None):
     sh = (None, None, None)
     if L.sh_gate is not None:
         sh = (bf16_to_f32(L.sh_gate), bf16_to_f32(L.sh_up), bf16_to_f32(L.sh_down))
-    return layer(x, wr, L.router_bias, L.gate, L.up, L.down, wl.H, wl.I, wl.E, wl.k, *sh)
+    return layer(x, wr, L.router_bias, L.gate, L.up, L.down, wl.H, wl.I, wl.E, wl.k, *sh, bits=wl.bits)
 
 
 def num_threads() -> int:

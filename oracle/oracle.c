@@ -28,6 +28,10 @@
  * reason in the design notes):
  *   - block byte order: scales[16] @0, qs[64] @16, d @80, dmin @82 (84 bytes);
  *   - code order: weight i of a block -> byte 16+i/4, bits 2*(i%4);
+ *   - the 4-bit variant of the routed experts (the q2/q4 mix on the [models]
+ *     page keeps some layers at 4 bits; no page gives a 4-bit block): the same
+ *     block with 4-bit codes, weight i -> byte 16+i/2, bits 4*(i%2), d @144,
+ *     dmin @146 (148 bytes), w = d*scale*q - dmin*min with q in 0..15;
  *   - blocks tile the row-major flattened tensor (a block may span rows);
  *   - router logit = round-to-fp32 of the fp64 sum over h of x*W plus bias;
  *   - selection ranks logits (sqrt(softplus) is strictly increasing), ties
@@ -54,29 +58,44 @@ static double half_to_double(uint16_t h) {
   return sign ? -v : v;
 }
 
-/* Value of weight i (0..255) of one canonical block, exact in double: every
- * product has at most 17 significant bits and the difference of two such
- * numbers of the binary16 range fits in 53 bits. [workload] */
-static double block_weight(const uint8_t *blk, int i) {
+/* Bytes of one block of 256 weights with `bits`-bit codes (2 or 4). */
+static int64_t block_bytes(int bits) { return 16 + 32 * bits + 4; }
+
+/* Value of weight i (0..255) of one canonical block with `bits`-bit codes,
+ * exact in double: every product has at most 19 significant bits and the
+ * difference of two such numbers of the binary16 range fits in 53 bits.
+ * [workload] */
+static double block_weight(const uint8_t *blk, int i, int bits) {
+  const int per_byte = 8 / bits, nb = (int)block_bytes(bits);
   int j = i / 16;                                  /* sub-block */
   int sc = blk[j] & 0x0F;                          /* low nibble: scale */
   int mn = blk[j] >> 4;                            /* high nibble: min  */
-  int q = (blk[16 + i / 4] >> (2 * (i % 4))) & 3;  /* 2-bit code        */
-  double d = half_to_double((uint16_t)(blk[80] | (blk[81] << 8)));
-  double dmin = half_to_double((uint16_t)(blk[82] | (blk[83] << 8)));
+  int q = (blk[16 + i / per_byte] >> (bits * (i % per_byte))) & ((1 << bits) - 1);
+  double d = half_to_double((uint16_t)(blk[nb - 4] | (blk[nb - 3] << 8)));
+  double dmin = half_to_double((uint16_t)(blk[nb - 2] | (blk[nb - 1] << 8)));
   return d * sc * q - dmin * mn;
 }
 
 /* Dequantize n blocks (256 weights each) to doubles. */
-void oracle_dequant_f64(const uint8_t *blocks, int64_t nblocks, double *out) {
+void oracle_dequant_f64_bits(const uint8_t *blocks, int64_t nblocks, int bits, double *out) {
+  const int64_t nb = block_bytes(bits);
   for (int64_t b = 0; b < nblocks; ++b)
-    for (int i = 0; i < 256; ++i) out[b * 256 + i] = block_weight(blocks + 84 * b, i);
+    for (int i = 0; i < 256; ++i) out[b * 256 + i] = block_weight(blocks + nb * b, i, bits);
 }
 
 /* Dequantize n blocks to fp32: the exact value rounded once to nearest. */
-void oracle_dequant_f32(const uint8_t *blocks, int64_t nblocks, float *out) {
+void oracle_dequant_f32_bits(const uint8_t *blocks, int64_t nblocks, int bits, float *out) {
+  const int64_t nb = block_bytes(bits);
   for (int64_t b = 0; b < nblocks; ++b)
-    for (int i = 0; i < 256; ++i) out[b * 256 + i] = (float)block_weight(blocks + 84 * b, i);
+    for (int i = 0; i < 256; ++i) out[b * 256 + i] = (float)block_weight(blocks + nb * b, i, bits);
+}
+
+void oracle_dequant_f64(const uint8_t *blocks, int64_t nblocks, double *out) {
+  oracle_dequant_f64_bits(blocks, nblocks, 2, out);
+}
+
+void oracle_dequant_f32(const uint8_t *blocks, int64_t nblocks, float *out) {
+  oracle_dequant_f32_bits(blocks, nblocks, 2, out);
 }
 
 /* Router logits, l[t,e] = fp32( sum_h x[t,h]*W[e,h] + b[e] ), the sum
@@ -194,10 +213,10 @@ static void swiglu_ffn(const double *Wg, const double *Wu, const double *Wd, con
  * Each routed expert is dequantized once and applied to each of its tokens
  * separately; every token's FFN is computed densely and independently.
  */
-int oracle_layer(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,
-                 const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down, int64_t Is,
-                 const float *sh_gate, const float *sh_up, const float *sh_down, float *y, int32_t *idx_out,
-                 float *w_out) {
+int oracle_layer_bits(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,
+                      const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down, int bits,
+                      int64_t Is, const float *sh_gate, const float *sh_up, const float *sh_down, float *y,
+                      int32_t *idx_out, float *w_out) {
   if (T <= 0) return 0;
   float *logits = (float *)malloc(sizeof(float) * (size_t)(T * E));
   int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * k));
@@ -219,9 +238,10 @@ int oracle_layer(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int
     double *Wd = (double *)malloc(sizeof(double) * (size_t)(H * I));
     double *xt = (double *)malloc(sizeof(double) * (size_t)H);
     double *hb = (double *)malloc(sizeof(double) * (size_t)I);
-    oracle_dequant_f64(gate + e * mat_blocks * 84, mat_blocks, Wg);
-    oracle_dequant_f64(up + e * mat_blocks * 84, mat_blocks, Wu);
-    oracle_dequant_f64(down + e * mat_blocks * 84, mat_blocks, Wd);
+    const int64_t mat_bytes = mat_blocks * block_bytes(bits);
+    oracle_dequant_f64_bits(gate + e * mat_bytes, mat_blocks, bits, Wg);
+    oracle_dequant_f64_bits(up + e * mat_bytes, mat_blocks, bits, Wu);
+    oracle_dequant_f64_bits(down + e * mat_bytes, mat_blocks, bits, Wd);
     for (int64_t a = 0; a < T * k; ++a) {
       if (idx[a] != e) continue;
       int64_t t = a / k;
@@ -260,6 +280,14 @@ int oracle_layer(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int
   free(Sg); free(Su); free(Sd);
   free(logits); free(idx); free(w); free(wd); free(Y);
   return 0;
+}
+
+int oracle_layer(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,
+                 const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down, int64_t Is,
+                 const float *sh_gate, const float *sh_up, const float *sh_down, float *y, int32_t *idx_out,
+                 float *w_out) {
+  return oracle_layer_bits(x, T, H, I, E, k, wr, bias, gate, up, down, 2, Is, sh_gate, sh_up, sh_down, y, idx_out,
+                           w_out);
 }
 
 int oracle_num_threads(void) {

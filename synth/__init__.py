@@ -63,6 +63,9 @@ def lib():
         L.synth_quantize.argtypes = [P, ctypes.c_int64, P]
         L.synth_q2k_matrices.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_double, P]
+        L.synth_qk_matrices.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_double, ctypes.c_int, P]
+        L.synth_quantize_bits.argtypes = [P, ctypes.c_int64, ctypes.c_int, P]
         L.synth_u32.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, P]
         L.synth_num_threads.restype = ctypes.c_int
         _lib = L
@@ -106,26 +109,39 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def quantize_blocks(w: np.ndarray) -> np.ndarray:
+def block_bytes(bits: int = 2) -> int:
+    """Bytes of one canonical block of 256 weights with 2- or 4-bit codes."""
+    assert bits in (2, 4)
+    return 16 + 32 * bits + 4
+
+
+def quantize_blocks(w: np.ndarray, bits: int = 2) -> np.ndarray:
     """RTN-quantize fp32 weights (size multiple of 256, row-major) to canonical blocks."""
     w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
     assert w.size % BLOCK_WEIGHTS == 0
     nb = w.size // BLOCK_WEIGHTS
-    out = np.empty(nb * BLOCK_BYTES, dtype=np.uint8)
-    lib().synth_quantize(_ptr(w), nb, _ptr(out))
+    out = np.empty(nb * block_bytes(bits), dtype=np.uint8)
+    lib().synth_quantize_bits(_ptr(w), nb, bits, _ptr(out))
+    return out
+
+
+def qk_matrices(seed: int, stream_base: int, n_mats: int, rows: int, cols: int, sigma: float,
+                bits: int = 2) -> np.ndarray:
+    """n_mats matrices [rows, cols] of N(0,sigma) weights quantized to canonical
+    blocks with `bits`-bit codes.
+
+    Returns uint8 [n_mats, rows*cols/256*block_bytes(bits)]; matrix e is stream stream_base+e.
+    """
+    assert (rows * cols) % BLOCK_WEIGHTS == 0
+    per = rows * cols // BLOCK_WEIGHTS * block_bytes(bits)
+    out = np.empty((n_mats, per), dtype=np.uint8)
+    lib().synth_qk_matrices(seed, stream_base, n_mats, rows, cols, sigma, bits, _ptr(out))
     return out
 
 
 def q2k_matrices(seed: int, stream_base: int, n_mats: int, rows: int, cols: int, sigma: float) -> np.ndarray:
-    """n_mats matrices [rows, cols] of N(0,sigma) weights quantized to canonical blocks.
-
-    Returns uint8 [n_mats, rows*cols/256*84]; matrix e is stream stream_base+e.
-    """
-    assert (rows * cols) % BLOCK_WEIGHTS == 0
-    per = rows * cols // BLOCK_WEIGHTS * BLOCK_BYTES
-    out = np.empty((n_mats, per), dtype=np.uint8)
-    lib().synth_q2k_matrices(seed, stream_base, n_mats, rows, cols, sigma, _ptr(out))
-    return out
+    """2-bit blocks (84 bytes per 256 weights); see qk_matrices."""
+    return qk_matrices(seed, stream_base, n_mats, rows, cols, sigma, 2)
 
 
 def u32(seed: int, stream: int, n: int) -> np.ndarray:
@@ -157,6 +173,7 @@ class Workload:
     zipf_scale: float = 0.75
     layer_id: int = 1              # weight streams: workloads of one shape share a layer
     description: str = ""
+    bits: int = 2                  # routed-expert code width: 2 (84-byte blocks) or 4 (148-byte blocks)
 
 
 WORKLOADS = {
@@ -170,6 +187,11 @@ WORKLOADS = {
                         description="prefill chunk of 2048 tokens"),
     "skewed": Workload("skewed", 4, T=8192, H=4096, E=256, I=2048, k=8, Is=2048, zipf_s=1.1,
                        description="long prefill, Zipf-skewed routing, bf16 shared expert"),
+    # the same decode and prefill shapes with 4-bit routed experts (own layer)
+    "decode1_q4": Workload("decode1_q4", 5, T=1, H=4096, E=256, I=2048, k=8, layer_id=2, bits=4,
+                           description="decode, one token, 4-bit routed experts"),
+    "prefill_q4": Workload("prefill_q4", 6, T=2048, H=4096, E=256, I=2048, k=8, layer_id=2, bits=4,
+                           description="prefill chunk of 2048 tokens, 4-bit routed experts"),
 }
 
 
@@ -233,9 +255,9 @@ def make_layer(wl: Workload | str, seed: int = DEFAULT_SEED, T: int | None = Non
         rw = f32_to_bf16_bits(rw)
     bias = zipf_bias(wl, seed) if wl.zipf_s else None
     if experts:
-        gate = q2k_matrices(seed, stream_id(lid, K_GATE), E, I, H, wl.w_sigma)
-        up = q2k_matrices(seed, stream_id(lid, K_UP), E, I, H, wl.w_sigma)
-        down = q2k_matrices(seed, stream_id(lid, K_DOWN), E, H, I, wl.w_sigma)
+        gate = qk_matrices(seed, stream_id(lid, K_GATE), E, I, H, wl.w_sigma, wl.bits)
+        up = qk_matrices(seed, stream_id(lid, K_UP), E, I, H, wl.w_sigma, wl.bits)
+        down = qk_matrices(seed, stream_id(lid, K_DOWN), E, H, I, wl.w_sigma, wl.bits)
     else:
         gate = up = down = None
     shg = shu = shd = None
@@ -253,7 +275,7 @@ def derive(base: LayerInputs, wl: Workload | str, T: int | None = None, batch: i
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
     b = base.wl
-    assert (wl.H, wl.E, wl.I, wl.layer_id) == (b.H, b.E, b.I, b.layer_id)
+    assert (wl.H, wl.E, wl.I, wl.layer_id, wl.bits) == (b.H, b.E, b.I, b.layer_id, b.bits)
     T = wl.T if T is None else T
     shared = make_layer(wl, base.seed, T=1, experts=False) if (wl.Is or wl.zipf_s) else None
     return LayerInputs(wl, base.seed, T, make_x(wl, base.seed, T, batch), base.router_w,

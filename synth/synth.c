@@ -145,8 +145,16 @@ static float f16_to_f32(uint16_t h) {
 
 static inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-/* Quantize 256 fp32 weights into one canonical 84-byte block (RTN). */
-void synth_quantize_block(const float *w, uint8_t *blk) {
+/* Bytes of one canonical block of 256 weights with `bits`-bit codes (2 or 4):
+ * scales[16], codes (256*bits/8 bytes), d, dmin. */
+static inline int block_bytes(int bits) { return 16 + 32 * bits + 4; }
+
+/* Quantize 256 fp32 weights into one canonical block (RTN), 2- or 4-bit
+ * codes: per sub-block of 16 the range [min(0, min w), max w] is split into
+ * 2^bits - 1 steps of d*sc, the offset is dmin*m; code i sits at byte
+ * 16 + i*bits/8, lowest bits first. */
+void synth_quantize_block_bits(const float *w, uint8_t *blk, int bits) {
+  const int levels = (1 << bits) - 1, per_byte = 8 / bits, nb = block_bytes(bits);
   float scf[16], mnv[16];
   float max_scf = 0.f, max_mn = 0.f;
   for (int j = 0; j < 16; ++j) {
@@ -156,7 +164,7 @@ void synth_quantize_block(const float *w, uint8_t *blk) {
       if (v < mn) mn = v;
       if (v > mx) mx = v;
     }
-    scf[j] = (mx - mn) / 3.0f;
+    scf[j] = (mx - mn) / (float)levels;
     mnv[j] = -mn; /* >= 0 */
     if (scf[j] > max_scf) max_scf = scf[j];
     if (mnv[j] > max_mn) max_mn = mnv[j];
@@ -164,40 +172,47 @@ void synth_quantize_block(const float *w, uint8_t *blk) {
   uint16_t d_bits = f32_to_f16(max_scf / 15.0f);
   uint16_t dmin_bits = f32_to_f16(max_mn / 15.0f);
   float d = f16_to_f32(d_bits), dmin = f16_to_f32(dmin_bits);
-  memset(blk, 0, 84);
+  memset(blk, 0, (size_t)nb);
   for (int j = 0; j < 16; ++j) {
     int sc = d > 0.f ? clampi((int)lrintf(scf[j] / d), 0, 15) : 0;
     int m = dmin > 0.f ? clampi((int)lrintf(mnv[j] / dmin), 0, 15) : 0;
     blk[j] = (uint8_t)(sc | (m << 4));
     float step = d * (float)sc, off = dmin * (float)m;
     for (int i = 0; i < 16; ++i) {
-      int q = step > 0.f ? clampi((int)lrintf((w[16 * j + i] + off) / step), 0, 3) : 0;
+      int q = step > 0.f ? clampi((int)lrintf((w[16 * j + i] + off) / step), 0, levels) : 0;
       int idx = 16 * j + i;
-      blk[16 + idx / 4] |= (uint8_t)(q << (2 * (idx % 4)));
+      blk[16 + idx / per_byte] |= (uint8_t)(q << (bits * (idx % per_byte)));
     }
   }
-  blk[80] = (uint8_t)(d_bits & 0xFF);
-  blk[81] = (uint8_t)(d_bits >> 8);
-  blk[82] = (uint8_t)(dmin_bits & 0xFF);
-  blk[83] = (uint8_t)(dmin_bits >> 8);
+  blk[nb - 4] = (uint8_t)(d_bits & 0xFF);
+  blk[nb - 3] = (uint8_t)(d_bits >> 8);
+  blk[nb - 2] = (uint8_t)(dmin_bits & 0xFF);
+  blk[nb - 1] = (uint8_t)(dmin_bits >> 8);
 }
+
+/* Quantize 256 fp32 weights into one canonical 84-byte 2-bit block (RTN). */
+void synth_quantize_block(const float *w, uint8_t *blk) { synth_quantize_block_bits(w, blk, 2); }
 
 /* Quantize n_blocks*256 fp32 weights (row-major flattened) to blocks. */
-void synth_quantize(const float *w, int64_t n_blocks, uint8_t *out) {
+void synth_quantize_bits(const float *w, int64_t n_blocks, int bits, uint8_t *out) {
+  const int nb = block_bytes(bits);
 #pragma omp parallel for schedule(static)
-  for (int64_t b = 0; b < n_blocks; ++b) synth_quantize_block(w + 256 * b, out + 84 * b);
+  for (int64_t b = 0; b < n_blocks; ++b) synth_quantize_block_bits(w + 256 * b, out + nb * b, bits);
 }
 
+void synth_quantize(const float *w, int64_t n_blocks, uint8_t *out) { synth_quantize_bits(w, n_blocks, 2, out); }
+
 /*
- * Generate and quantize `n_mats` matrices of rows*cols weights N(0, sigma).
- * Matrix e (e = 0..n_mats-1) uses stream (stream_base + e); the whole
- * matrix is one stream, so (seed, stream) fixes its bytes regardless of how
- * many matrices are generated together.
+ * Generate and quantize `n_mats` matrices of rows*cols weights N(0, sigma)
+ * to `bits`-bit blocks.  Matrix e (e = 0..n_mats-1) uses stream
+ * (stream_base + e); the whole matrix is one stream, so (seed, stream) fixes
+ * its bytes regardless of how many matrices are generated together.
  */
-void synth_q2k_matrices(uint64_t seed, uint32_t stream_base, int64_t n_mats, int64_t rows, int64_t cols,
-                        double sigma, uint8_t *out) {
+void synth_qk_matrices(uint64_t seed, uint32_t stream_base, int64_t n_mats, int64_t rows, int64_t cols,
+                       double sigma, int bits, uint8_t *out) {
   int64_t per = rows * cols;      /* weights per matrix, multiple of 256 */
   int64_t nblk = per / 256;
+  const int nb = block_bytes(bits);
   const int64_t CH = 64;          /* blocks per work item */
   int64_t chunks = (nblk + CH - 1) / CH;
 #pragma omp parallel
@@ -214,13 +229,17 @@ void synth_q2k_matrices(uint64_t seed, uint32_t stream_base, int64_t n_mats, int
           for (int j = 0; j < 4; ++j) buf[i - i0 + j] = (float)(sigma * z[j]);
         }
         for (int64_t b = b0; b < b1; ++b)
-          synth_quantize_block(buf + (b - b0) * 256, out + (e * nblk + b) * 84);
+          synth_quantize_block_bits(buf + (b - b0) * 256, out + (e * nblk + b) * nb, bits);
       }
     }
   }
 }
 
-/* Uniform 32-bit words (for seeded permutations), element i of the stream. */
+void synth_q2k_matrices(uint64_t seed, uint32_t stream_base, int64_t n_mats, int64_t rows, int64_t cols,
+                        double sigma, uint8_t *out) {
+  synth_qk_matrices(seed, stream_base, n_mats, rows, cols, sigma, 2, out);
+}
+
 void synth_u32(uint64_t seed, uint32_t stream, int64_t n, uint32_t *out) {
   for (int64_t blk = 0; blk < (n + 3) / 4; ++blk) {
     uint32_t c[4] = {(uint32_t)blk, (uint32_t)((uint64_t)blk >> 32), stream, 0xC0FFEE00u};
