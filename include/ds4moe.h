@@ -5,7 +5,10 @@
  * in asymmetric 2-bit super-blocks while the router and the shared expert stay
  * at higher precision (ds4 README, "Models" section, as translated on
  * molayo1419.me: only the routed MoE experts are quantized; routing, shared
- * experts and projections are left alone).  Per token t the layer computes
+ * experts and projections are left alone).  The same layer also runs on
+ * routed experts with 4-bit codes in the same super-block (the higher-quality
+ * weight option the README lists beside the 2-bit one).  Per token t the
+ * layer computes
  *
  *   l[t,e] = fp32( sum_h x[t,h] * Wr[e,h] + b[e] )      (fp64 accumulation)
  *   s      = sqrt(softplus(l)), softplus evaluated in the stable form
@@ -65,7 +68,8 @@ typedef enum { DS4MOE_MODE_ROUTE = 0, DS4MOE_MODE_DECODE = 1, DS4MOE_MODE_PREFIL
  *   top_k         k: 1..16
  *   shared_inter  Is: 0 (no shared expert) or a multiple of 32
  *   x_dtype       dtype of x: DS4MOE_F32 or DS4MOE_BF16
- *   router_dtype  dtype of Wr: DS4MOE_F32 or DS4MOE_BF16 */
+ *   router_dtype  dtype of Wr: DS4MOE_F32 or DS4MOE_BF16
+ *   expert_bits   code width of the packed routed experts: 2 or 4 */
 typedef struct {
   int32_t hidden;
   int32_t inter;
@@ -74,15 +78,18 @@ typedef struct {
   int32_t shared_inter;
   int32_t x_dtype;
   int32_t router_dtype;
+  int32_t expert_bits;
 } ds4moe_dims;
 
 /* Weights (host struct of device pointers).
  *   router_w   [E,H] row-major, router_dtype
  *   router_bias [E] fp32, or NULL: added to the logit, so it moves both the
  *              selection and the weights
- *   gate, up   E packed matrices W[I,H] each (ds4moe_pack_q2k layout),
- *              expert e at byte offset e * ds4moe_packed_bytes(I, H)
- *   down       E packed matrices W[H,I], expert e at e * ds4moe_packed_bytes(H, I)
+ *   gate, up   E packed matrices W[I,H] each (ds4moe_pack layout with
+ *              dims->expert_bits), expert e at byte offset
+ *              e * ds4moe_packed_bytes_bits(I, H, expert_bits)
+ *   down       E packed matrices W[H,I], expert e at
+ *              e * ds4moe_packed_bytes_bits(H, I, expert_bits)
  *   sh_gate, sh_up  [Is,H] bf16 row-major; sh_down [H,Is] bf16; all NULL
  *              when shared_inter == 0.  The shared expert is computed with
  *              fp16 operands: its weights must lie inside the binary16 range. */
@@ -116,9 +123,14 @@ typedef struct {
 } ds4moe_routing;
 
 /* Bytes of one packed matrix of `rows` x `cols` weights (cols = reduction
- * length).  Same byte count as the canonical blocks (84 bytes per 256
- * weights, 2.625 bits per weight) when cols is a multiple of 256; a divisor
- * of 256 is padded to 256.  Returns 0 for an unsupported shape. */
+ * length) with `bits`-bit codes (2 or 4).  Same byte count as the canonical
+ * blocks (84 bytes per 256 weights, 2.625 bits per weight, with 2-bit codes;
+ * 148 bytes, 4.625 bits per weight, with 4-bit codes) when cols is a multiple
+ * of 256; a divisor of 256 is padded to 256.  Returns 0 for an unsupported
+ * shape or width (rows, cols above 2^31 included). */
+size_t ds4moe_packed_bytes_bits(int64_t rows, int64_t cols, int32_t bits);
+
+/* ds4moe_packed_bytes_bits(rows, cols, 2). */
 size_t ds4moe_packed_bytes(int64_t rows, int64_t cols);
 
 /* Repack canonical super-blocks into the HBM layout the GEMV/GEMM kernels
@@ -142,13 +154,39 @@ size_t ds4moe_packed_bytes(int64_t rows, int64_t cols);
  *               12-15 hold the mins of sub-blocks 0-7 and 8-15, byte b of each
  *               group holding sub-block b (low nibble) and b+4 (high nibble)
  *   [1280,1344) per row d (bits 0-15) and dmin (bits 16-31), binary16
- * The conversion is exact: no value is altered. */
+ * The conversion is exact: no value is altered.  Same as ds4moe_pack with
+ * bits = 2. */
 int ds4moe_pack_q2k(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, void *stream);
+
+/* Repack canonical super-blocks with `bits`-bit codes (2 or 4).
+ * bits = 2: the blocks and units of ds4moe_pack_q2k.
+ * bits = 4: canonical blocks of 148 bytes: scales[16] @0 as above, qs[128]
+ *   @16 (weight i at byte i/2, bits 4*(i%2)), d @144, dmin @146; w =
+ *   d*scale*q - dmin*min with q in 0..15.  Units of 16 rows x 256 columns,
+ *   2368 bytes each, at ((row_tile * nchunks) + col_chunk) * 2368:
+ *   [0,2048)    two code planes of 1024 bytes, 16 bytes per MFMA lane
+ *               (lane = 16*g + r, row r) in each: dword 4p+v of lane (r,g)
+ *               lies in plane p at 16*lane + 4*v; dword 2u+h holds elements
+ *               8h..8h+7 of sub-block 4u+g of row r, element 8h+e in the
+ *               nibble 2e (e < 4) or 2(e-4)+1 (e >= 4)
+ *   [2048,2304) scales and mins per row, as in the 2-bit unit
+ *   [2304,2368) per row d | dmin<<16, as in the 2-bit unit
+ * Arguments, alignment and status codes as ds4moe_pack_q2k; also
+ * DS4MOE_ERR_SHAPE for a width other than 2 or 4, or 2^39 padded weights or
+ * more in all.  Exact. */
+int ds4moe_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, int32_t bits,
+                void *stream);
 
 /* Dequantize packed matrices to fp32, row-major [n_mats, rows, cols]:
  * w = d*scale*q - dmin*min, every product exact, one rounding (bitwise equal
- * to the correctly rounded value of the block's definition). */
+ * to the correctly rounded value of the block's definition).  Same as
+ * ds4moe_dequant with bits = 2. */
 int ds4moe_dequant_q2k(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, void *stream);
+
+/* ds4moe_dequant_q2k for units with `bits`-bit codes (2 or 4); products of
+ * at most 19 significant bits with 4-bit codes, still one rounding. */
+int ds4moe_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, int32_t bits,
+                   void *stream);
 
 /* Workspace bytes needed by a call with `T` tokens in `mode`
  * (ds4moe_mode).  Returns 0 if dims is NULL or invalid. */

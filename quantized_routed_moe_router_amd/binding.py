@@ -27,7 +27,8 @@ DS4MOE_F32 = 0
 DS4MOE_BF16 = 1
 MODE_ROUTE, MODE_DECODE, MODE_PREFILL = 0, 1, 2
 
-EXPORTED = ("ds4moe_packed_bytes", "ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_workspace_bytes",
+EXPORTED = ("ds4moe_packed_bytes", "ds4moe_packed_bytes_bits", "ds4moe_pack_q2k", "ds4moe_pack",
+            "ds4moe_dequant_q2k", "ds4moe_dequant", "ds4moe_workspace_bytes",
             "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_status_str",
             "ds4moe_version", "ds4moe_forward_timed")
 N_TIMED_KERNELS = 8
@@ -37,7 +38,7 @@ KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup",
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
-                ("router_dtype", ctypes.c_int32)]
+                ("router_dtype", ctypes.c_int32), ("expert_bits", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -68,8 +69,12 @@ def lib() -> ctypes.CDLL:
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         L.ds4moe_packed_bytes.argtypes = [I64, I64]
         L.ds4moe_packed_bytes.restype = ctypes.c_size_t
+        L.ds4moe_packed_bytes_bits.argtypes = [I64, I64, I32]
+        L.ds4moe_packed_bytes_bits.restype = ctypes.c_size_t
         L.ds4moe_pack_q2k.argtypes = [P, P, I64, I64, I64, P]
         L.ds4moe_dequant_q2k.argtypes = [P, P, I64, I64, I64, P]
+        L.ds4moe_pack.argtypes = [P, P, I64, I64, I64, I32, P]
+        L.ds4moe_dequant.argtypes = [P, P, I64, I64, I64, I32, P]
         L.ds4moe_workspace_bytes.argtypes = [P, I32, I32]
         L.ds4moe_workspace_bytes.restype = ctypes.c_size_t
         L.ds4moe_route.argtypes = [P, P, P, I32, P, P, ctypes.c_size_t, P]
@@ -79,7 +84,8 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_status_str.argtypes = [ctypes.c_int]
         L.ds4moe_status_str.restype = ctypes.c_char_p
         L.ds4moe_version.restype = ctypes.c_int
-        for fn in ("ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_route", "ds4moe_forward_decode",
+        for fn in ("ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_pack", "ds4moe_dequant", "ds4moe_route",
+                   "ds4moe_forward_decode",
                    "ds4moe_forward_prefill", "ds4moe_forward_timed"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -111,8 +117,8 @@ def _check(status: int, what: str) -> None:
         raise Ds4MoeError(status, what)
 
 
-def make_dims(H, I, E, k, Is=0, x_dtype=DS4MOE_BF16, router_dtype=DS4MOE_BF16) -> Dims:
-    return Dims(H, I, E, k, Is, x_dtype, router_dtype)
+def make_dims(H, I, E, k, Is=0, x_dtype=DS4MOE_BF16, router_dtype=DS4MOE_BF16, expert_bits=2) -> Dims:
+    return Dims(H, I, E, k, Is, x_dtype, router_dtype, expert_bits)
 
 
 def make_weights(router_w, gate, up, down, router_bias=None, sh_gate=None, sh_up=None, sh_down=None) -> Weights:
@@ -130,12 +136,24 @@ def ds4moe_packed_bytes(rows: int, cols: int) -> int:
     return int(lib().ds4moe_packed_bytes(rows, cols))
 
 
+def ds4moe_packed_bytes_bits(rows: int, cols: int, bits: int) -> int:
+    return int(lib().ds4moe_packed_bytes_bits(rows, cols, bits))
+
+
 def ds4moe_pack_q2k(dst, canonical, n_mats: int, rows: int, cols: int, stream=None) -> None:
     _check(lib().ds4moe_pack_q2k(_ptr(dst), _ptr(canonical), n_mats, rows, cols, _stream(stream)), "pack_q2k")
 
 
 def ds4moe_dequant_q2k(dst, packed, n_mats: int, rows: int, cols: int, stream=None) -> None:
     _check(lib().ds4moe_dequant_q2k(_ptr(dst), _ptr(packed), n_mats, rows, cols, _stream(stream)), "dequant_q2k")
+
+
+def ds4moe_pack(dst, canonical, n_mats: int, rows: int, cols: int, bits: int, stream=None) -> None:
+    _check(lib().ds4moe_pack(_ptr(dst), _ptr(canonical), n_mats, rows, cols, bits, _stream(stream)), "pack")
+
+
+def ds4moe_dequant(dst, packed, n_mats: int, rows: int, cols: int, bits: int, stream=None) -> None:
+    _check(lib().ds4moe_dequant(_ptr(dst), _ptr(packed), n_mats, rows, cols, bits, _stream(stream)), "dequant")
 
 
 def ds4moe_workspace_bytes(dims: Dims, T: int, mode: int) -> int:

@@ -30,6 +30,7 @@ int validate_dims(const ds4moe_dims *d) {
   if (d->top_k < 1 || d->top_k > 16) return DS4MOE_ERR_SHAPE;
   if (d->n_experts < d->top_k || d->n_experts > 256) return DS4MOE_ERR_SHAPE;
   if (d->shared_inter < 0 || d->shared_inter > 65536 || d->shared_inter % 32) return DS4MOE_ERR_SHAPE;
+  if (d->expert_bits != 2 && d->expert_bits != 4) return DS4MOE_ERR_SHAPE;
   return DS4MOE_OK;
 }
 
@@ -233,8 +234,9 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.gate = (const uint8_t *)w->gate;
   ga.up = (const uint8_t *)w->up;
   ga.down = (const uint8_t *)w->down;
-  ga.gu_bytes = ds4moe_packed_bytes(d.inter, d.hidden);
-  ga.d_bytes = ds4moe_packed_bytes(d.hidden, d.inter);
+  ga.gu_bytes = ds4moe_packed_bytes_bits(d.inter, d.hidden, d.expert_bits);
+  ga.d_bytes = ds4moe_packed_bytes_bits(d.hidden, d.inter, d.expert_bits);
+  ga.bits = d.expert_bits;
   ga.tiles = ro.tiles;
   ga.ntiles = ntiles;
   ga.perm = p.perm;
@@ -297,6 +299,13 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   return DS4MOE_OK;
 }
 
+// grid bounds of the pack (one workgroup per unit) and dequant (one thread
+// per weight) launches: fewer than 2^39 padded weights in all
+bool fits_grid(int64_t n_mats, int64_t rows, int64_t cols) {
+  const int64_t per = rows * ((cols + 255) / 256) * 256;
+  return n_mats <= (((int64_t)1 << 39) - 1) / per;
+}
+
 }  // namespace
 
 extern "C" {
@@ -317,29 +326,43 @@ const char *ds4moe_status_str(int status) {
 
 int ds4moe_version(void) { return kVersion; }
 
-size_t ds4moe_packed_bytes(int64_t rows, int64_t cols) {
+size_t ds4moe_packed_bytes_bits(int64_t rows, int64_t cols, int32_t bits) {
+  if (bits != 2 && bits != 4) return 0;
   if (rows <= 0 || cols <= 0 || rows % 16 || cols % 16) return 0;
   if (cols % 256 && 256 % cols) return 0;
+  if (rows > ((int64_t)1 << 31) || cols > ((int64_t)1 << 31)) return 0;
   const int64_t nchunks = (cols + 255) / 256;
-  return (size_t)(rows / 16) * (size_t)nchunks * 1344u;
+  return (size_t)(rows / 16) * (size_t)nchunks * (bits == 4 ? 2368u : 1344u);
 }
 
-int ds4moe_pack_q2k(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, void *stream) {
+size_t ds4moe_packed_bytes(int64_t rows, int64_t cols) { return ds4moe_packed_bytes_bits(rows, cols, 2); }
+
+int ds4moe_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, int32_t bits,
+                void *stream) {
   if (n_mats < 0) return DS4MOE_ERR_SHAPE;
-  if (!ds4moe_packed_bytes(rows, cols)) return DS4MOE_ERR_SHAPE;
+  if (!ds4moe_packed_bytes_bits(rows, cols, bits) || !fits_grid(n_mats, rows, cols)) return DS4MOE_ERR_SHAPE;
   if (n_mats == 0) return DS4MOE_OK;
   if (!dst || !canonical) return DS4MOE_ERR_NULL;
   if (!aligned(dst, 16)) return DS4MOE_ERR_ALIGN;
-  return hip_status(launch_pack(dst, canonical, n_mats, rows, cols, (hipStream_t)stream));
+  return hip_status(launch_pack(dst, canonical, n_mats, rows, cols, bits, (hipStream_t)stream));
 }
 
-int ds4moe_dequant_q2k(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, void *stream) {
+int ds4moe_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, int32_t bits,
+                   void *stream) {
   if (n_mats < 0) return DS4MOE_ERR_SHAPE;
-  if (!ds4moe_packed_bytes(rows, cols)) return DS4MOE_ERR_SHAPE;
+  if (!ds4moe_packed_bytes_bits(rows, cols, bits) || !fits_grid(n_mats, rows, cols)) return DS4MOE_ERR_SHAPE;
   if (n_mats == 0) return DS4MOE_OK;
   if (!dst || !packed) return DS4MOE_ERR_NULL;
   if (!aligned(dst, 4) || !aligned(packed, 16)) return DS4MOE_ERR_ALIGN;
-  return hip_status(launch_dequant(dst, packed, n_mats, rows, cols, (hipStream_t)stream));
+  return hip_status(launch_dequant(dst, packed, n_mats, rows, cols, bits, (hipStream_t)stream));
+}
+
+int ds4moe_pack_q2k(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, void *stream) {
+  return ds4moe_pack(dst, canonical, n_mats, rows, cols, 2, stream);
+}
+
+int ds4moe_dequant_q2k(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, void *stream) {
+  return ds4moe_dequant(dst, packed, n_mats, rows, cols, 2, stream);
 }
 
 size_t ds4moe_workspace_bytes(const ds4moe_dims *dims, int32_t T, int32_t mode) {

@@ -11,9 +11,27 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 // Packed expert layout: one unit = 16 rows x 256 reduction columns.
-#define DS4_UNIT_BYTES 1344
-#define DS4_SCALE_OFF 1024
-#define DS4_DD_OFF 1280
+// Unit of B-bit codes (B = 2 or 4): B/2 code planes of 1024 bytes (16 bytes
+// per MFMA lane each), then 16 bytes of scales and mins per row, then
+// d | dmin<<16 per row.  The scale, min and d layouts do not depend on B.
+template <int B>
+struct Unit;
+template <>
+struct Unit<2> {
+  static constexpr uint32_t BYTES = 1344, SCALE_OFF = 1024, DD_OFF = 1280;
+  static constexpr int LOADS = 3;  // 16-byte loads per lane per unit
+};
+template <>
+struct Unit<4> {
+  static constexpr uint32_t BYTES = 2368, SCALE_OFF = 2048, DD_OFF = 2304;
+  static constexpr int LOADS = 4;
+};
+
+// canonical block of 256 weights with B-bit codes: scales[16], codes, d, dmin
+template <int B>
+constexpr int canon_block_bytes() {
+  return 16 + 32 * B + 4;
+}
 
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
@@ -55,6 +73,16 @@ __device__ __forceinline__ h8 dequant_frag(uint32_t raw, h2 sc2) {
 // exactly (exponent field 0 or 1), so scale 512 gives the small integer b.
 // HI picks the upper 16 bits of `w`; the low byte lands in element 0.
 #define CVT_FP8(w, HI) __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((w), 512.0f, (HI))
+
+// A-operand fragment of one MFMA step with 4-bit codes: the dword holds the
+// step's 8 codes, element e in nibble 2e (e < 4) or 2(e-4)+1 (e >= 4), so the
+// low nibbles of its bytes are elements 0-3 and the high nibbles 4-7; each
+// code (<= 15) converts exactly and sc*q (<= 225) is exact in fp16.
+__device__ __forceinline__ h8 dequant_frag4(uint32_t raw, h2 sc2) {
+  const uint32_t lo = raw & 0x0F0F0F0Fu, hi = (raw >> 4) & 0x0F0F0F0Fu;
+  return cat8(CVT_FP8(lo, false) * sc2, CVT_FP8(lo, true) * sc2, CVT_FP8(hi, false) * sc2,
+              CVT_FP8(hi, true) * sc2);
+}
 
 __device__ __forceinline__ h2 splat_h2(float v) {
   h2 r;

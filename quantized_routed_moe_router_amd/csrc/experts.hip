@@ -10,10 +10,14 @@
 // (x, or h between the two projections) round.  The min term is one extra
 // 16x16x32 MFMA per super-block with X split into fp16 hi + lo.
 //
+// The same holds for 4-bit codes (sc*q <= 225).
+//
 // MFMA v_mfma_f32_16x16x32_f16, lane l = 16*g + r:
 //   A: row r, 8 k's;  B: column r (token), the same 8 k's;  D: rows 4g..4g+3, column r.
 // Per super-block the 8 steps s cover sub-block 4*(s/2) + g, half s%2, so a
-// lane's 16-byte code vector holds 4 whole sub-blocks.
+// lane's code vectors (16 bytes with 2-bit codes, 2 x 16 with 4-bit codes)
+// hold 4 whole sub-blocks.  Every kernel is instantiated for both code widths
+// B; only the unit size, the code loads and the fragment decode differ.
 #include "common.h"
 #include "launch.h"
 #include "route_dev.h"
@@ -46,27 +50,39 @@ namespace ds4 {
 #define DN_LDS_PD 4
 #endif
 
+// One lane's share of a packed unit.  Code plane p (1024 bytes at 1024*p)
+// holds dwords 4p..4p+3 of every lane, 16 bytes per lane, so each plane is one
+// fully coalesced load; dword S of a lane feeds MFMA step S with 4-bit codes,
+// dword S/2 (both halves) with 2-bit codes.
+template <int B>
 struct UnitRegs {
-  u4 code;   // 4 raw dwords: sub-blocks g, 4+g, 8+g, 12+g of row r
-  u4 scale;  // row r: scale halfwords (bytes 0-7), min nibbles (bytes 8-15)
-  u4 dd;     // rows 4g..4g+3: d | dmin<<16
+  u4 code[B / 2];  // raw code dwords of sub-blocks g, 4+g, 8+g, 12+g of row r
+  u4 scale;        // row r: scale halfwords (bytes 0-7), min nibbles (bytes 8-15)
+  u4 dd;           // rows 4g..4g+3: d | dmin<<16
 };
 
-__device__ __forceinline__ UnitRegs load_unit(const uint8_t *__restrict__ unit, int lane) {
-  UnitRegs u;
-  u.code = *reinterpret_cast<const u4 *>(unit + 16 * lane);
-  u.scale = *reinterpret_cast<const u4 *>(unit + DS4_SCALE_OFF + 16 * (lane & 15));
-  u.dd = *reinterpret_cast<const u4 *>(unit + DS4_DD_OFF + 16 * (lane >> 4));
+template <int B>
+__device__ __forceinline__ UnitRegs<B> load_unit(const uint8_t *__restrict__ unit, int lane) {
+  UnitRegs<B> u;
+#pragma unroll
+  for (int p = 0; p < B / 2; ++p) u.code[p] = *reinterpret_cast<const u4 *>(unit + 1024 * p + 16 * lane);
+  u.scale = *reinterpret_cast<const u4 *>(unit + Unit<B>::SCALE_OFF + 16 * (lane & 15));
+  u.dd = *reinterpret_cast<const u4 *>(unit + Unit<B>::DD_OFF + 16 * (lane >> 4));
   return u;
 }
 
 // The same unit through a buffer descriptor (offset out of range: all zeros,
 // which decode to zero weights).
-__device__ __forceinline__ UnitRegs load_unit_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, int lane) {
-  UnitRegs u;
-  u.code = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * lane, 0, 0));
-  u.scale = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off + DS4_SCALE_OFF + 16 * (lane & 15), 0, 0));
-  u.dd = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off + DS4_DD_OFF + 16 * (lane >> 4), 0, 0));
+template <int B>
+__device__ __forceinline__ UnitRegs<B> load_unit_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, int lane) {
+  UnitRegs<B> u;
+#pragma unroll
+  for (int p = 0; p < B / 2; ++p)
+    u.code[p] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 1024 * p + 16 * lane, 0, 0));
+  u.scale = __builtin_bit_cast(
+      u4, __builtin_amdgcn_raw_buffer_load_b128(r, off + Unit<B>::SCALE_OFF + 16 * (lane & 15), 0, 0));
+  u.dd = __builtin_bit_cast(u4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off + Unit<B>::DD_OFF + 16 * (lane >> 4), 0, 0));
   return u;
 }
 
@@ -79,7 +95,8 @@ struct UnitDecoded {
 __device__ __forceinline__ float dd_d(uint32_t v) { return half_bits_to_float((uint16_t)(v & 0xFFFFu)); }
 __device__ __forceinline__ float dd_dmin(uint32_t v) { return half_bits_to_float((uint16_t)(v >> 16)); }
 
-__device__ __forceinline__ UnitDecoded decode_unit(const UnitRegs &u, int g) {
+template <int B>
+__device__ __forceinline__ UnitDecoded decode_unit(const UnitRegs<B> &u, int g) {
   UnitDecoded o;
   const uint32_t sw = (g < 2) ? u.scale.x : u.scale.y;
   const uint32_t hw = (g & 1) ? (sw >> 16) : sw;
@@ -93,14 +110,15 @@ __device__ __forceinline__ UnitDecoded decode_unit(const UnitRegs &u, int g) {
   return o;
 }
 
-template <int S>
-__device__ __forceinline__ h8 step_frag(const UnitRegs &u, const UnitDecoded &dc) {
+template <int S, int B>
+__device__ __forceinline__ h8 step_frag(const UnitRegs<B> &u, const UnitDecoded &dc) {
   constexpr int Q = S >> 1;  // sub-block 4*Q + g
   const h2 pair = (Q < 2) ? dc.sc01 : dc.sc23;
   h2 sc2;
   sc2[0] = pair[Q & 1];
   sc2[1] = pair[Q & 1];
-  return dequant_frag<(S & 1)>(u.code[Q], sc2);
+  if constexpr (B == 2) return dequant_frag<(S & 1)>(u.code[0][Q], sc2);
+  else return dequant_frag4(u.code[S >> 2][S & 3], sc2);
 }
 
 // offset of the 8 activations a lane (group g) feeds at step S of a super-block
@@ -127,14 +145,14 @@ struct GemmCtx {
   size_t rt_stride;                   // bytes between consecutive row tiles
 };
 
-template <int NM, int R>
-__device__ __forceinline__ void gemm_load_a(UnitRegs (&u)[R][NM], const GemmCtx<NM> &c, const int (&rts)[R], int sb,
-                                            int lane) {
+template <int NM, int R, int B>
+__device__ __forceinline__ void gemm_load_a(UnitRegs<B> (&u)[R][NM], const GemmCtx<NM> &c, const int (&rts)[R],
+                                            int sb, int lane) {
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < NM; ++m)
-      u[r][m] = load_unit(c.W[m] + (size_t)rts[r] * c.rt_stride + (size_t)sb * DS4_UNIT_BYTES, lane);
+      u[r][m] = load_unit<B>(c.W[m] + (size_t)rts[r] * c.rt_stride + (size_t)sb * Unit<B>::BYTES, lane);
 }
 
 // Activation staging: thread -> 16-byte chunk column sc = tid % 32 of token
@@ -181,8 +199,8 @@ __device__ __forceinline__ void stage_store(const Stage<NR> &st, half_t *sB, hal
   *reinterpret_cast<u4 *>(sS + srow * SS_STRIDE + 8 * sq) = st.s;
 }
 
-template <int NM, int R>
-__device__ __forceinline__ void gemm_compute_sb(const UnitRegs (&u)[R][NM], const half_t *sB, const half_t *sS,
+template <int NM, int R, int B>
+__device__ __forceinline__ void gemm_compute_sb(const UnitRegs<B> (&u)[R][NM], const half_t *sB, const half_t *sS,
                                                 f4 (&y)[NM][R][GEMM_NT], int r16, int g) {
   UnitDecoded dc[R][NM];
 #pragma unroll
@@ -203,7 +221,7 @@ __device__ __forceinline__ void gemm_compute_sb(const UnitRegs (&u)[R][NM], cons
         load_h8(sB + (16 * nt + r16) * SB_STRIDE + step_col<S>(g));                           \
     _Pragma("unroll") for (int r = 0; r < R; ++r) {                                           \
       _Pragma("unroll") for (int m = 0; m < NM; ++m) {                                        \
-        const h8 A = step_frag<S>(u[r][m], dc[r][m]);                                         \
+        const h8 A = step_frag<S, B>(u[r][m], dc[r][m]);                                      \
         _Pragma("unroll") for (int nt = 0; nt < GEMM_NT; ++nt) acc[m][r][nt] =                \
             mfma16(A, b[nt], acc[m][r][nt]);                                                  \
       }                                                                                       \
@@ -229,7 +247,7 @@ __device__ __forceinline__ void gemm_compute_sb(const UnitRegs (&u)[R][NM], cons
       }
 }
 
-template <int NM, int R, int NW, bool PADDED>
+template <int NM, int R, int NW, bool PADDED, int B>
 __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   __shared__ __attribute__((aligned(16))) half_t sB[64 * SB_STRIDE];
   __shared__ __attribute__((aligned(16))) half_t sS[64 * SS_STRIDE];
@@ -277,7 +295,7 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
 
   GemmCtx<NM> c;
   c.nsb = nsb;
-  c.rt_stride = (size_t)nsb * DS4_UNIT_BYTES;
+  c.rt_stride = (size_t)nsb * Unit<B>::BYTES;
   if (GU) {
     c.W[0] = a.gate + (size_t)tl.e * a.gu_bytes;
     c.W[NM - 1] = a.up + (size_t)tl.e * a.gu_bytes;
@@ -296,9 +314,9 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   // every prefetch is issued unconditionally (the last super-block is
   // reloaded at the end), so the load-counter waits are static
   Stage<NR> st;
-  UnitRegs ua[R][NM], ub[R][NM];
+  UnitRegs<B> ua[R][NM], ub[R][NM];
   stage_load<NR, PADDED>(st, rowp, sp, 0, sc, sq, kreal, jreal);
-  gemm_load_a<NM, R>(ua, c, rts, 0, lane);
+  gemm_load_a<NM, R, B>(ua, c, rts, 0, lane);
   for (int sb = 0; sb < nsb; sb += 2) {
     // even super-block: weights in ua, prefetch into ub
     __syncthreads();
@@ -306,9 +324,9 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
     __syncthreads();
     const int s1 = min(sb + 1, nsb - 1);
     stage_load<NR, PADDED>(st, rowp, sp, s1, sc, sq, kreal, jreal);
-    gemm_load_a<NM, R>(ub, c, rts, s1, lane);
+    gemm_load_a<NM, R, B>(ub, c, rts, s1, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-    gemm_compute_sb<NM, R>(ua, sB, sS, y, r16, g);
+    gemm_compute_sb<NM, R, B>(ua, sB, sS, y, r16, g);
     if (sb + 1 >= nsb) break;
     // odd super-block: weights in ub, prefetch into ua
     __syncthreads();
@@ -316,9 +334,9 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
     __syncthreads();
     const int s2 = min(sb + 2, nsb - 1);
     stage_load<NR, PADDED>(st, rowp, sp, s2, sc, sq, kreal, jreal);
-    gemm_load_a<NM, R>(ua, c, rts, s2, lane);
+    gemm_load_a<NM, R, B>(ua, c, rts, s2, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-    gemm_compute_sb<NM, R>(ub, sB, sS, y, r16, g);
+    gemm_compute_sb<NM, R, B>(ub, sB, sS, y, r16, g);
   }
 
   if (rt0 >= n_rt) return;
@@ -396,8 +414,8 @@ __device__ __forceinline__ int step_chunk(int g) {
   return 2 * (4 * (S >> 1) + g) + (S & 1);
 }
 
-template <int NM, int R, int NTV>
-__device__ __forceinline__ void pt_compute_sb(const UnitRegs (&u)[R][NM], const char *slot, f4 (&y)[NM][R][NTV],
+template <int NM, int R, int NTV, int B>
+__device__ __forceinline__ void pt_compute_sb(const UnitRegs<B> (&u)[R][NM], const char *slot, f4 (&y)[NM][R][NTV],
                                               int r16, int g) {
   UnitDecoded dc[R][NM];
 #pragma unroll
@@ -419,7 +437,7 @@ __device__ __forceinline__ void pt_compute_sb(const UnitRegs (&u)[R][NM], const 
         *reinterpret_cast<const h8 *>(rowb + (16 * nt * PT_CH + step_chunk<S>(g)) * 16);       \
     _Pragma("unroll") for (int r = 0; r < R; ++r) {                                           \
       _Pragma("unroll") for (int m = 0; m < NM; ++m) {                                        \
-        const h8 A = step_frag<S>(u[r][m], dc[r][m]);                                         \
+        const h8 A = step_frag<S, B>(u[r][m], dc[r][m]);                                      \
         _Pragma("unroll") for (int nt = 0; nt < NTV; ++nt) acc[m][r][nt] =                    \
             mfma16(A, b[nt], acc[m][r][nt]);                                                  \
       }                                                                                       \
@@ -445,7 +463,7 @@ __device__ __forceinline__ void pt_compute_sb(const UnitRegs (&u)[R][NM], const 
       }
 }
 
-template <int NM, int R, int NTV>
+template <int NM, int R, int NTV, int B>
 __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, const TileT &tl, int rb, char *ring) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -496,7 +514,7 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
 
   GemmCtx<NM> c;
   c.nsb = nsb;
-  c.rt_stride = (size_t)nsb * DS4_UNIT_BYTES;
+  c.rt_stride = (size_t)nsb * Unit<B>::BYTES;
   if (GU) {
     c.W[0] = a.gate + (size_t)tl.e * a.gu_bytes;
     c.W[NM - 1] = a.up + (size_t)tl.e * a.gu_bytes;
@@ -512,29 +530,29 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt) y[m][r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  UnitRegs ua[R][NM], ub[R][NM];
+  UnitRegs<B> ua[R][NM], ub[R][NM];
   issue(0, 0);
-  gemm_load_a<NM, R>(ua, c, rts, 0, lane);
+  gemm_load_a<NM, R, B>(ua, c, rts, 0, lane);
   for (int sb = 0; sb < nsb; sb += 2) {
     // even super-block: slot 0, weights in ua; the next goes to slot 1 / ub
     wait_vm<0>();
     __syncthreads();
     if (sb + 1 < nsb) {
       issue(1, sb + 1);
-      gemm_load_a<NM, R>(ub, c, rts, sb + 1, lane);
+      gemm_load_a<NM, R, B>(ub, c, rts, sb + 1, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
-    pt_compute_sb<NM, R, NTV>(ua, ring, y, r16, g);
+    pt_compute_sb<NM, R, NTV, B>(ua, ring, y, r16, g);
     if (sb + 1 >= nsb) break;
     // odd super-block: slot 1, weights in ub
     wait_vm<0>();
     __syncthreads();
     if (sb + 2 < nsb) {
       issue(0, sb + 2);
-      gemm_load_a<NM, R>(ua, c, rts, sb + 2, lane);
+      gemm_load_a<NM, R, B>(ua, c, rts, sb + 2, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
-    pt_compute_sb<NM, R, NTV>(ub, ring + PT_SLOT_BYTES, y, r16, g);
+    pt_compute_sb<NM, R, NTV, B>(ub, ring + PT_SLOT_BYTES, y, r16, g);
   }
 
   if (rt0 >= n_rt) return;
@@ -589,7 +607,7 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
 // n-tiles multiply zeros).  The down projection uses it: a build with one
 // instance per n-tile count and two row tiles per wave gave wrong values in
 // its last n-tile, which the single instance does not.
-template <int NM, int R, bool ALL>
+template <int NM, int R, bool ALL, int B>
 __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAct xa, int nrb) {
   __shared__ __attribute__((aligned(16))) char ring[2 * PT_SLOT_BYTES];
   const int tile_id = blockIdx.x / nrb;
@@ -597,16 +615,16 @@ __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAc
   if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
   const TileT tl = a.tiles[tile_id];
   if (ALL) {
-    pt_tile<NM, R, PT_NTM>(a, xa, tl, rb, ring);
+    pt_tile<NM, R, PT_NTM, B>(a, xa, tl, rb, ring);
     return;
   }
   switch ((tl.n + 15) >> 4) {  // 1..PT_NTM, uniform
-    case 1: pt_tile<NM, R, 1>(a, xa, tl, rb, ring); break;
-    case 2: pt_tile<NM, R, 2>(a, xa, tl, rb, ring); break;
-    case 3: pt_tile<NM, R, 3>(a, xa, tl, rb, ring); break;
-    case 4: pt_tile<NM, R, 4>(a, xa, tl, rb, ring); break;
-    case 5: pt_tile<NM, R, 5>(a, xa, tl, rb, ring); break;
-    default: pt_tile<NM, R, 6>(a, xa, tl, rb, ring); break;
+    case 1: pt_tile<NM, R, 1, B>(a, xa, tl, rb, ring); break;
+    case 2: pt_tile<NM, R, 2, B>(a, xa, tl, rb, ring); break;
+    case 3: pt_tile<NM, R, 3, B>(a, xa, tl, rb, ring); break;
+    case 4: pt_tile<NM, R, 4, B>(a, xa, tl, rb, ring); break;
+    case 5: pt_tile<NM, R, 5, B>(a, xa, tl, rb, ring); break;
+    default: pt_tile<NM, R, 6, B>(a, xa, tl, rb, ring); break;
   }
 }
 
@@ -619,7 +637,7 @@ __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAc
 
 // gate/up + SwiGLU.  Workgroup = one tile x two 16-row tiles; wave = (row
 // tile, half of the reduction); the halves meet in LDS (lower half first).
-template <int PD>
+template <int PD, int B>
 __global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
   const int nrb = (n_rt + 1) >> 1;
   const int tile_id = blockIdx.x / nrb;
@@ -638,7 +656,7 @@ __global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
   const uint32_t gub = (uint32_t)a.gu_bytes;
   const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gate + (size_t)e * a.gu_bytes, gub);
   const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.up + (size_t)e * a.gu_bytes, gub);
-  const uint32_t roff = ((uint32_t)min(rt, n_rt - 1) * nsb + sb0) * DS4_UNIT_BYTES;
+  const uint32_t roff = ((uint32_t)min(rt, n_rt - 1) * nsb + sb0) * Unit<B>::BYTES;
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
   // byte offsets of this lane's activations (out of range: zeros)
   const uint32_t xoff =
@@ -648,7 +666,7 @@ __global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
             : DS4_OOB;
 
   struct Stage {
-    UnitRegs wg, wu;
+    UnitRegs<B> wg, wu;
     h8 b[9];
   };
   Stage st[PD];
@@ -657,9 +675,9 @@ __global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
   // load counter waits are static and the pipeline never drains
   auto load = [&](Stage &sg, int i) {
     const bool in = i < nit;
-    const uint32_t wo = in ? roff + (uint32_t)i * DS4_UNIT_BYTES : DS4_OOB;
-    sg.wg = load_unit_buf(gr, wo, lane);
-    sg.wu = load_unit_buf(ur, wo, lane);
+    const uint32_t wo = in ? roff + (uint32_t)i * Unit<B>::BYTES : DS4_OOB;
+    sg.wg = load_unit_buf<B>(gr, wo, lane);
+    sg.wu = load_unit_buf<B>(ur, wo, lane);
     const uint32_t xo = in ? xoff + 512u * i : DS4_OOB;
     const uint32_t so = in ? xsoff + 32u * i : DS4_OOB;
 #pragma unroll
@@ -671,8 +689,8 @@ __global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
     const UnitDecoded du = decode_unit(sg.wu, g);
     f4 ag = (f4){0.f, 0.f, 0.f, 0.f}, au = ag;
 #define DEC_STEP(S)                                    \
-  ag = mfma16(step_frag<S>(sg.wg, dg), sg.b[S], ag);   \
-  au = mfma16(step_frag<S>(sg.wu, du), sg.b[S], au);
+  ag = mfma16(step_frag<S, B>(sg.wg, dg), sg.b[S], ag);   \
+  au = mfma16(step_frag<S, B>(sg.wu, du), sg.b[S], au);
     DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
 #undef DEC_STEP
     const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
@@ -733,7 +751,7 @@ __global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
 // wave w takes tiles w, w+8, ... (experts ascending), scales each tile's
 // contribution to token t by the token's routing weight, and the eight
 // partial sums are added in wave order, then the shared-expert output.
-template <int PD, bool PADDED>
+template <int PD, bool PADDED, int B>
 __global__ __launch_bounds__(512) void k_down_dec(GemmArgs a) {
   const int rt = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -756,7 +774,7 @@ __global__ __launch_bounds__(512) void k_down_dec(GemmArgs a) {
   const uint32_t hs_base = ((g >> 1) ? a.o_hs_lo : a.o_hs_hi) + 2u * (8 * (g & 1));
 
   struct Stage {
-    UnitRegs wd;
+    UnitRegs<B> wd;
     h8 b[9];
     float wt;
   };
@@ -771,7 +789,7 @@ __global__ __launch_bounds__(512) void k_down_dec(GemmArgs a) {
     const int e = __builtin_amdgcn_readlane(e_l, lt & 63);
     const uint32_t tmask = in ? (uint32_t)__builtin_amdgcn_readlane((int)m_l, lt & 63) : 0u;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.down + (size_t)e * a.d_bytes, (uint32_t)a.d_bytes);
-    sg.wd = load_unit_buf(wr, in ? ((uint32_t)rt * nsb + lsb) * DS4_UNIT_BYTES : DS4_OOB, lane);
+    sg.wd = load_unit_buf<B>(wr, in ? ((uint32_t)rt * nsb + lsb) * Unit<B>::BYTES : DS4_OOB, lane);
     // h of token r16 if it chose the expert (zeros otherwise, weight 0)
     const bool routed = (tmask >> r16) & 1u;  // implies r16 < T
     const uint32_t p = (uint32_t)tile * a.T + r16;
@@ -800,7 +818,7 @@ __global__ __launch_bounds__(512) void k_down_dec(GemmArgs a) {
   auto compute = [&](const Stage &sg) {
     const UnitDecoded dd = decode_unit(sg.wd, g);
     f4 ac = (f4){0.f, 0.f, 0.f, 0.f};
-#define DEC_STEP(S) ac = mfma16(step_frag<S>(sg.wd, dd), sg.b[S], ac);
+#define DEC_STEP(S) ac = mfma16(step_frag<S, B>(sg.wd, dd), sg.b[S], ac);
     DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
 #undef DEC_STEP
     const f4 mm = mfma16(dd.mfrag, sg.b[8], (f4){0.f, 0.f, 0.f, 0.f});
@@ -861,7 +879,7 @@ struct SlotLoads {
 // the router's partial sums, one wave per token; the LDS of that step is the
 // ring's, before the ring is used) and takes the tile_id-th used expert;
 // workgroup 0 writes the routing outputs and the tiles for the down kernel.
-template <int PD, int NT, bool ROUTE>
+template <int PD, int NT, bool ROUTE, int B>
 __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, DecRoute rr) {
   constexpr int NI = SlotLoads<NT>::NI;
   constexpr int SLOT = 64 * 16 * NI;  // bytes per ring slot
@@ -904,7 +922,7 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
   const uint32_t gub = (uint32_t)a.gu_bytes;
   const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gate + (size_t)e * a.gu_bytes, gub);
   const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.up + (size_t)e * a.gu_bytes, gub);
-  const uint32_t roff = ((uint32_t)min(rt, n_rt - 1) * nsb + sb0) * DS4_UNIT_BYTES;
+  const uint32_t roff = ((uint32_t)min(rt, n_rt - 1) * nsb + sb0) * Unit<B>::BYTES;
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
   // chunk u = 64*q + lane of a slot: token u / XCH, chunk c = u % XCH
   uint32_t src[NI], inc[NI];
@@ -930,7 +948,7 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
   char *ring = ring_lds + wave * (PD * SLOT);  // this wave's PD slots
 
   struct Stage {
-    UnitRegs wg, wu;
+    UnitRegs<B> wg, wu;
   };
   Stage st[PD];
   f4 yg = (f4){0.f, 0.f, 0.f, 0.f}, yu = yg;
@@ -940,12 +958,12 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
 #pragma unroll
     for (int q = 0; q < NI; ++q)
       buf_load_lds16(ws, ring + slot * SLOT + 64 * 16 * q, in ? src[q] + inc[q] * (uint32_t)i : DS4_OOB);
-    const uint32_t wo = in ? roff + (uint32_t)i * DS4_UNIT_BYTES : DS4_OOB;
-    sg.wg = load_unit_buf(gr, wo, lane);
-    sg.wu = load_unit_buf(ur, wo, lane);
+    const uint32_t wo = in ? roff + (uint32_t)i * Unit<B>::BYTES : DS4_OOB;
+    sg.wg = load_unit_buf<B>(gr, wo, lane);
+    sg.wu = load_unit_buf<B>(ur, wo, lane);
   };
   auto compute = [&](const Stage &sg, int slot) {
-    wait_vm<(PD - 1) * (NI + 6)>();  // this step's loads (LDS and registers) have landed
+    wait_vm<(PD - 1) * (NI + 2 * Unit<B>::LOADS)>();  // this step's loads (LDS and registers) have landed
     const char *base = ring + slot * SLOT + brow;
     h8 b[9];
 #pragma unroll
@@ -956,8 +974,8 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
     const UnitDecoded du = decode_unit(sg.wu, g);
     f4 ag = (f4){0.f, 0.f, 0.f, 0.f}, au = ag;
 #define DEC_STEP(S)                                  \
-  ag = mfma16(step_frag<S>(sg.wg, dg), b[S], ag);    \
-  au = mfma16(step_frag<S>(sg.wu, du), b[S], au);
+  ag = mfma16(step_frag<S, B>(sg.wg, dg), b[S], ag);    \
+  au = mfma16(step_frag<S, B>(sg.wu, du), b[S], au);
     DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
 #undef DEC_STEP
     const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
@@ -1015,7 +1033,7 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
 }
 
 // down fused with the combine (I a multiple of 256), activations through LDS
-template <int PD, int NT>
+template <int PD, int NT, int B>
 __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
   constexpr int NI = SlotLoads<NT>::NI;
   constexpr int SLOT = 64 * 16 * NI;
@@ -1061,7 +1079,7 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
   char *ring = ring_lds + wave * (PD * SLOT);  // this wave's PD slots
 
   struct Stage {
-    UnitRegs wd;
+    UnitRegs<B> wd;
     float wt;
   };
   Stage st[PD];
@@ -1082,7 +1100,7 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
       buf_load_lds16(ws, ring + slot * SLOT + 64 * 16 * q, off);
     }
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.down + (size_t)e * a.d_bytes, (uint32_t)a.d_bytes);
-    sg.wd = load_unit_buf(wr, in ? ((uint32_t)rt * nsb + lsb) * DS4_UNIT_BYTES : DS4_OOB, lane);
+    sg.wd = load_unit_buf<B>(wr, in ? ((uint32_t)rt * nsb + lsb) * Unit<B>::BYTES : DS4_OOB, lane);
     sg.wt = a.dtiles[tile].w[r16];  // 0 for tokens that did not choose the expert
     if (++lsb == nsb) {
       lsb = 0;
@@ -1090,7 +1108,7 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
     }
   };
   auto compute = [&](const Stage &sg, int slot) {
-    wait_vm<(PD - 1) * (NI + 4)>();  // this step's loads (LDS and registers) have landed
+    wait_vm<(PD - 1) * (NI + Unit<B>::LOADS + 1)>();  // this step's loads (LDS and registers) have landed
     const char *base = ring + slot * SLOT + brow;
     h8 b[9];
 #pragma unroll
@@ -1099,7 +1117,7 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
     b[8] = *reinterpret_cast<const h8 *>(base + 16 * (32 + 2 * (g >> 1) + (g & 1)));
     const UnitDecoded dd = decode_unit(sg.wd, g);
     f4 ac = (f4){0.f, 0.f, 0.f, 0.f};
-#define DEC_STEP(S) ac = mfma16(step_frag<S>(sg.wd, dd), b[S], ac);
+#define DEC_STEP(S) ac = mfma16(step_frag<S, B>(sg.wd, dd), b[S], ac);
     DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
 #undef DEC_STEP
     const f4 mm = mfma16(dd.mfrag, b[8], (f4){0.f, 0.f, 0.f, 0.f});
@@ -1422,34 +1440,39 @@ static bool act_window(const void *rows, const void *s_hi, const void *s_lo, int
   return true;
 }
 
-hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
-  if (max_tiles <= 0) return hipSuccess;
+template <int B>
+static hipError_t gateup_b(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (a.tile_n > 64) {
     GemmAct xa;
     if (a.tile_n > 16 * PT_NTM || !act_window(a.x16, a.xs_hi, a.xs_lo, a.T, a.H, xa)) return hipErrorInvalidValue;
     const int nrb = (a.I + 16 * PT_NW - 1) / (16 * PT_NW);
-    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1, false>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW), 0,
-               s, a, xa, nrb);
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1, false, B>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW),
+               0, s, a, xa, nrb);
     return hipGetLastError();
   }
   constexpr int R = GEMM_R_GU, NW = GEMM_NW_GU;
   const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.I + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
-  DS4_LAUNCH(tm, (k_moe_gemm<2, R, NW, false>), grid, dim3(64 * NW), 0, s, a, nrb);
+  DS4_LAUNCH(tm, (k_moe_gemm<2, R, NW, false, B>), grid, dim3(64 * NW), 0, s, a, nrb);
   return hipGetLastError();
 }
 
-hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
+hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
+  return a.bits == 4 ? gateup_b<4>(a, max_tiles, s, tm) : gateup_b<2>(a, max_tiles, s, tm);
+}
+
+template <int B>
+static hipError_t down_b(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (a.tile_n > 64) {
     GemmAct xa;
     if (a.tile_n > 16 * PT_NTM || a.I != a.Ipad ||
         !act_window(a.h, a.hs_hi, a.hs_lo, (int64_t)a.T * a.k, a.Ipad, xa))
       return hipErrorInvalidValue;
     const int nrb = (a.H + 32 * PT_NW - 1) / (32 * PT_NW);
-    DS4_LAUNCH(tm, (k_moe_gemm_wide<1, 2, true>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW), 0, s,
-               a, xa, nrb);
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<1, 2, true, B>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW),
+               0, s, a, xa, nrb);
     return hipGetLastError();
   }
   constexpr int R = GEMM_R_DN, NW = GEMM_NW_DN;
@@ -1457,55 +1480,71 @@ hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Ti
   const int nrb = (a.H + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
   if (a.I == a.Ipad)
-    DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, false>), grid, dim3(64 * NW), 0, s, a, nrb);
+    DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, false, B>), grid, dim3(64 * NW), 0, s, a, nrb);
   else
-    DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, true>), grid, dim3(64 * NW), 0, s, a, nrb);
+    DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, true, B>), grid, dim3(64 * NW), 0, s, a, nrb);
   return hipGetLastError();
 }
 
+hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
+  if (max_tiles <= 0) return hipSuccess;
+  return a.bits == 4 ? down_b<4>(a, max_tiles, s, tm) : down_b<2>(a, max_tiles, s, tm);
+}
+
 // Small batches (T <= 16).
-template <int NT>
+template <int NT, int B>
 static void gateup_dec_lds(const GemmArgs &a, int n_rt, const DecRoute *rr, dim3 grid, hipStream_t s,
                            const Timing *tm) {
   if (rr)
-    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, true>), grid, dim3(256), 0, s, a, n_rt, *rr);
+    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, true, B>), grid, dim3(256), 0, s, a, n_rt, *rr);
   else
-    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, false>), grid, dim3(256), 0, s, a, n_rt, DecRoute{});
+    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, false, B>), grid, dim3(256), 0, s, a, n_rt, DecRoute{});
+}
+
+template <int B>
+static hipError_t gateup_dec_b(const GemmArgs &a, int max_tiles, const DecRoute *rr, hipStream_t s,
+                               const Timing *tm) {
+  const int n_rt = a.I >> 4;
+  const int nrb = (n_rt + 1) >> 1;
+  const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
+  switch (a.T) {
+    case 1: gateup_dec_lds<1, B>(a, n_rt, rr, grid, s, tm); break;
+    case 2: gateup_dec_lds<2, B>(a, n_rt, rr, grid, s, tm); break;
+    case 3: gateup_dec_lds<3, B>(a, n_rt, rr, grid, s, tm); break;
+    case 4: gateup_dec_lds<4, B>(a, n_rt, rr, grid, s, tm); break;
+    default: DS4_LAUNCH(tm, (k_gateup_dec<GU_DEC_PD, B>), grid, dim3(256), 0, s, a, n_rt);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, const DecRoute *rr, hipStream_t s,
                              const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
   if (rr && (a.T > 4 || rr->E > 256 || rr->k > 16)) return hipErrorInvalidValue;
-  const int n_rt = a.I >> 4;
-  const int nrb = (n_rt + 1) >> 1;
-  const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
-  switch (a.T) {
-    case 1: gateup_dec_lds<1>(a, n_rt, rr, grid, s, tm); break;
-    case 2: gateup_dec_lds<2>(a, n_rt, rr, grid, s, tm); break;
-    case 3: gateup_dec_lds<3>(a, n_rt, rr, grid, s, tm); break;
-    case 4: gateup_dec_lds<4>(a, n_rt, rr, grid, s, tm); break;
-    default: DS4_LAUNCH(tm, (k_gateup_dec<GU_DEC_PD>), grid, dim3(256), 0, s, a, n_rt);
-  }
-  return hipGetLastError();
+  return a.bits == 4 ? gateup_dec_b<4>(a, max_tiles, rr, s, tm) : gateup_dec_b<2>(a, max_tiles, rr, s, tm);
 }
 
-hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm) {
+template <int B>
+static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Timing *tm) {
   const dim3 grid((unsigned)(a.H >> 4));
   if (a.I == a.Ipad && a.T <= 4) {
     switch (a.T) {
-      case 1: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 1>), grid, dim3(512), 0, s, a); break;
-      case 2: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 2>), grid, dim3(512), 0, s, a); break;
-      case 3: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 3>), grid, dim3(512), 0, s, a); break;
-      default: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 4>), grid, dim3(512), 0, s, a);
+      case 1: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 1, B>), grid, dim3(512), 0, s, a); break;
+      case 2: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 2, B>), grid, dim3(512), 0, s, a); break;
+      case 3: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 3, B>), grid, dim3(512), 0, s, a); break;
+      default: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 4, B>), grid, dim3(512), 0, s, a);
     }
     return hipGetLastError();
   }
   if (a.I == a.Ipad)
-    DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, false>), dim3((unsigned)(a.H >> 4)), dim3(512), 0, s, a);
+    DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, false, B>), grid, dim3(512), 0, s, a);
   else
-    DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, true>), dim3((unsigned)(a.H >> 4)), dim3(512), 0, s, a);
+    DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, true, B>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm) {
+  return a.bits == 4 ? down_combine_dec_b<4>(a, s, tm) : down_combine_dec_b<2>(a, s, tm);
 }
 
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,

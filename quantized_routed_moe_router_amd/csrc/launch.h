@@ -63,6 +63,7 @@ struct GemmArgs {
   // routed experts
   const uint8_t *gate, *up, *down;   // packed, E matrices each
   size_t gu_bytes, d_bytes;          // bytes per expert matrix
+  int bits;                          // code width of the packed units: 2 or 4
   const TileT *tiles;
   const int32_t *ntiles;
   const int32_t *perm;
@@ -82,9 +83,9 @@ struct GemmArgs {
   float *y;                          // [T,H]
 };
 
-hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols,
+hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, int bits,
                        hipStream_t s);
-hipError_t launch_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols,
+hipError_t launch_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, int bits,
                           hipStream_t s);
 
 hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool w_bf16, const float *bias,

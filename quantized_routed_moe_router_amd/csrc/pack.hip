@@ -1,50 +1,78 @@
-// Repacking canonical 2-bit super-blocks into the HBM unit layout, and the
-// reference dequantization of that layout (for bit-exact checks).
+// Repacking canonical 2- or 4-bit super-blocks into the HBM unit layout, and
+// the reference dequantization of that layout (for bit-exact checks).
 //
 // Canonical block (the 2-bit K-quant super-block of the ds4 README "Models"
 // section): 84 bytes per 256 consecutive weights of the row-major flattened
 // matrix: scales[16] @0 (low nibble scale, high nibble min), qs[64] @16
-// (weight i at byte i/4, bits 2*(i%4)), d @80, dmin @82 (binary16).
+// (weight i at byte i/4, bits 2*(i%4)), d @80, dmin @82 (binary16).  The
+// 4-bit block is the same with 4-bit codes: qs[128] @16 (weight i at byte i/2,
+// bits 4*(i%2)), d @144, dmin @146 (148 bytes).
 #include "common.h"
 #include "launch.h"
 
 namespace ds4 {
 
-// One workgroup of 64 threads builds one 1344-byte unit (16 rows x 256 cols).
+// code of weight w (0..255) of a canonical block with B-bit codes
+template <int B>
+__device__ __forceinline__ uint32_t canon_code(const uint8_t *blk, int w) {
+  constexpr int PER = 8 / B;
+  return (blk[16 + w / PER] >> (B * (w % PER))) & ((1u << B) - 1u);
+}
+
+// Position of code i (0..15) of a sub-block inside its lane's code dwords:
+// B = 2: one dword per sub-block, element i at bits 4*(i%8) + 2*(i/8), so a
+// byte converted as two fp4 values yields two codes of one MFMA step.
+// B = 4: two dwords per sub-block (elements 0-7, then 8-15); element e of a
+// dword sits in nibble 2e (e < 4) or 2(e-4)+1 (e >= 4), so the low nibbles
+// of its bytes hold elements 0-3 and the high nibbles 4-7 in order.
+template <int B>
+__device__ __forceinline__ int code_shift(int i) {
+  if (B == 2) return 4 * (i & 7) + 2 * (i >> 3);
+  const int e = i & 7;
+  return 4 * (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+}
+
+// One workgroup of 64 threads builds one unit (16 rows x 256 cols).
+template <int B>
 __global__ __launch_bounds__(64) void k_pack(uint8_t *__restrict__ dst, const uint8_t *__restrict__ src,
                                              int64_t rows, int64_t cols, int nchunks) {
+  constexpr int CB = canon_block_bytes<B>();
   const int64_t unit = blockIdx.x;            // (mat, row_tile, chunk), chunk fastest
   const int64_t n_rt = rows / 16;
   const int chunk = (int)(unit % nchunks);
   const int64_t rt = (unit / nchunks) % n_rt;
   const int64_t mat = unit / nchunks / n_rt;
-  const uint8_t *m = src + mat * (rows * cols / 256) * 84;
-  uint8_t *u = dst + unit * DS4_UNIT_BYTES;
+  const uint8_t *m = src + mat * (rows * cols / 256) * CB;
+  uint8_t *u = dst + unit * Unit<B>::BYTES;
   const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
   const int64_t row = rt * 16 + r;
   const int64_t kbase = (int64_t)chunk * 256;
 
-  // codes: dword q of lane (r,g) = sub-block 4q+g of row r
-  uint32_t raw[4];
+  // codes: lane (r,g) holds sub-blocks g, 4+g, 8+g, 12+g of row r; dword
+  // (B/2)*q + h holds elements 8h.. of sub-block 4q+g (h = 0 only for B = 2);
+  // dword d of the lane sits in code plane d/4, at 1024*(d/4) + 16*lane + 4*(d%4)
+  constexpr int ND = 2 * B;  // dwords per lane
+  uint32_t raw[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) raw[d] = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    uint32_t v = 0;
     const int j = 4 * q + g;
     for (int i = 0; i < 16; ++i) {
       const int64_t k = kbase + 16 * j + i;
       uint32_t code = 0;
       if (k < cols) {
         const int64_t f = row * cols + k;
-        const uint8_t *blk = m + (f >> 8) * 84;
-        const int w = (int)(f & 255);
-        code = (blk[16 + (w >> 2)] >> (2 * (w & 3))) & 3u;
+        code = canon_code<B>(m + (f >> 8) * CB, (int)(f & 255));
       }
-      v |= code << (4 * (i & 7) + 2 * (i >> 3));
+      const int d = B == 2 ? q : 2 * q + (i >> 3);
+      raw[d] |= code << code_shift<B>(i);
     }
-    raw[q] = v;
   }
-  *reinterpret_cast<u4 *>(u + 16 * lane) = (u4){raw[0], raw[1], raw[2], raw[3]};
+#pragma unroll
+  for (int d = 0; d < ND; d += 4)
+    *reinterpret_cast<u4 *>(u + 256 * d + 16 * lane) = (u4){raw[d], raw[d + 1], raw[d + 2], raw[d + 3]};
 
   if (lane < 16) {
     // scale / min nibbles of row `lane`
@@ -56,7 +84,7 @@ __global__ __launch_bounds__(64) void k_pack(uint8_t *__restrict__ dst, const ui
       mn[j] = 0;
       if (k < cols) {
         const int64_t f = rw * cols + k;
-        const uint8_t b = m[(f >> 8) * 84 + ((f & 255) >> 4)];
+        const uint8_t b = m[(f >> 8) * CB + ((f & 255) >> 4)];
         sc[j] = b & 15u;
         mn[j] = b >> 4;
       }
@@ -76,17 +104,18 @@ __global__ __launch_bounds__(64) void k_pack(uint8_t *__restrict__ dst, const ui
       w2 |= (mn[b] | (mn[4 + b] << 4)) << (8 * b);
       w3 |= (mn[8 + b] | (mn[12 + b] << 4)) << (8 * b);
     }
-    *reinterpret_cast<u4 *>(u + DS4_SCALE_OFF + 16 * lane) = (u4){w0, w1, w2, w3};
+    *reinterpret_cast<u4 *>(u + Unit<B>::SCALE_OFF + 16 * lane) = (u4){w0, w1, w2, w3};
     // d and dmin of the block holding this row's chunk
     const int64_t f = rw * cols + kbase;
-    const uint8_t *blk = m + (f >> 8) * 84;
-    const uint32_t d = (uint32_t)blk[80] | ((uint32_t)blk[81] << 8);
-    const uint32_t dm = (uint32_t)blk[82] | ((uint32_t)blk[83] << 8);
-    *reinterpret_cast<uint32_t *>(u + DS4_DD_OFF + 4 * lane) = d | (dm << 16);
+    const uint8_t *blk = m + (f >> 8) * CB;
+    const uint32_t d = (uint32_t)blk[CB - 4] | ((uint32_t)blk[CB - 3] << 8);
+    const uint32_t dm = (uint32_t)blk[CB - 2] | ((uint32_t)blk[CB - 1] << 8);
+    *reinterpret_cast<uint32_t *>(u + Unit<B>::DD_OFF + 4 * lane) = d | (dm << 16);
   }
 }
 
 // One thread per output weight.
+template <int B>
 __global__ __launch_bounds__(256) void k_dequant(float *__restrict__ dst, const uint8_t *__restrict__ src,
                                                  int64_t rows, int64_t cols, int nchunks, int64_t total) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -100,40 +129,49 @@ __global__ __launch_bounds__(256) void k_dequant(float *__restrict__ dst, const 
   const int kk = (int)(k & 255);
   const int j = kk >> 4, i = kk & 15;
   const int g = j & 3, q = j >> 2;
-  const uint8_t *u = src + ((mat * (rows / 16) + rt) * nchunks + chunk) * DS4_UNIT_BYTES;
-  const uint32_t raw = *reinterpret_cast<const uint32_t *>(u + 16 * (16 * g + r) + 4 * q);
-  const uint32_t code = (raw >> (4 * (i & 7) + 2 * (i >> 3))) & 3u;
-  const uint16_t schw = *reinterpret_cast<const uint16_t *>(u + DS4_SCALE_OFF + 16 * r + 2 * g);
+  const uint8_t *u = src + ((mat * (rows / 16) + rt) * nchunks + chunk) * Unit<B>::BYTES;
+  const int dw = B == 2 ? q : 2 * q + (i >> 3);
+  const uint32_t raw = *reinterpret_cast<const uint32_t *>(u + 1024 * (dw >> 2) + 16 * (16 * g + r) + 4 * (dw & 3));
+  const uint32_t code = (raw >> code_shift<B>(i)) & ((1u << B) - 1u);
+  const uint16_t schw = *reinterpret_cast<const uint16_t *>(u + Unit<B>::SCALE_OFF + 16 * r + 2 * g);
   const uint32_t sc = (schw >> (8 * (q & 1) + 4 * (q >> 1))) & 15u;
   const int jj = j & 7;
-  const uint8_t mb = u[DS4_SCALE_OFF + 16 * r + 8 + 4 * (j >> 3) + (jj & 3)];
+  const uint8_t mb = u[Unit<B>::SCALE_OFF + 16 * r + 8 + 4 * (j >> 3) + (jj & 3)];
   const uint32_t mn = (mb >> (4 * (jj >> 2))) & 15u;
-  const uint32_t dd = *reinterpret_cast<const uint32_t *>(u + DS4_DD_OFF + 4 * r);
+  const uint32_t dd = *reinterpret_cast<const uint32_t *>(u + Unit<B>::DD_OFF + 4 * r);
   const float d = half_bits_to_float((uint16_t)(dd & 0xFFFF));
   const float dmin = half_bits_to_float((uint16_t)(dd >> 16));
-  // each product is exact in fp32 (<= 17 significant bits): one rounding
+  // each product is exact in fp32 (<= 19 significant bits): one rounding
   const float a = (d * (float)sc) * (float)code;
   const float b = dmin * (float)mn;
   dst[idx] = a - b;
 }
 
-hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols,
+hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, int bits,
                        hipStream_t s) {
   const int nchunks = (int)((cols + 255) / 256);
   const int64_t units = n_mats * (rows / 16) * nchunks;
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)units), dim3(64), 0, s, (uint8_t *)dst, (const uint8_t *)canonical,
-                     rows, cols, nchunks);
+  if (bits == 4)
+    hipLaunchKernelGGL(k_pack<4>, dim3((unsigned)units), dim3(64), 0, s, (uint8_t *)dst,
+                       (const uint8_t *)canonical, rows, cols, nchunks);
+  else
+    hipLaunchKernelGGL(k_pack<2>, dim3((unsigned)units), dim3(64), 0, s, (uint8_t *)dst,
+                       (const uint8_t *)canonical, rows, cols, nchunks);
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols,
+hipError_t launch_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, int bits,
                           hipStream_t s) {
   const int nchunks = (int)((cols + 255) / 256);
   const int64_t total = n_mats * rows * cols;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, dst,
-                     (const uint8_t *)packed, rows, cols, nchunks, total);
+  if (bits == 4)
+    hipLaunchKernelGGL(k_dequant<4>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, dst,
+                       (const uint8_t *)packed, rows, cols, nchunks, total);
+  else
+    hipLaunchKernelGGL(k_dequant<2>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, dst,
+                       (const uint8_t *)packed, rows, cols, nchunks, total);
   return hipGetLastError();
 }
 

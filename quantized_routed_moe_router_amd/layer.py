@@ -20,13 +20,14 @@ def _as_bf16(bits: np.ndarray, device) -> torch.Tensor:
 
 
 class DeviceLayer:
-    def __init__(self, H, I, E, k, Is=0, x_dtype=B.DS4MOE_BF16, router_dtype=B.DS4MOE_BF16, device="cuda:0"):
-        self.H, self.I, self.E, self.k, self.Is = H, I, E, k, Is
+    def __init__(self, H, I, E, k, Is=0, x_dtype=B.DS4MOE_BF16, router_dtype=B.DS4MOE_BF16, device="cuda:0",
+                 bits=2):
+        self.H, self.I, self.E, self.k, self.Is, self.bits = H, I, E, k, Is, bits
         self.device = torch.device(device)
-        self.dims = B.make_dims(H, I, E, k, Is, x_dtype, router_dtype)
+        self.dims = B.make_dims(H, I, E, k, Is, x_dtype, router_dtype, bits)
         self.x_dtype, self.router_dtype = x_dtype, router_dtype
-        self.gu_bytes = B.ds4moe_packed_bytes(I, H)
-        self.d_bytes = B.ds4moe_packed_bytes(H, I)
+        self.gu_bytes = B.ds4moe_packed_bytes_bits(I, H, bits)
+        self.d_bytes = B.ds4moe_packed_bytes_bits(H, I, bits)
         self._ws = None
         self.router_w = self.router_bias = None
         self.gate = self.up = self.down = None
@@ -37,8 +38,9 @@ class DeviceLayer:
         """Upload E canonical-block matrices and repack them on the GPU."""
         n = canonical.shape[0]
         src = _dev(canonical.reshape(n, -1), self.device)
-        dst = torch.empty(n * B.ds4moe_packed_bytes(rows, cols), dtype=torch.uint8, device=self.device)
-        B.ds4moe_pack_q2k(dst, src, n, rows, cols, stream)
+        dst = torch.empty(n * B.ds4moe_packed_bytes_bits(rows, cols, self.bits), dtype=torch.uint8,
+                          device=self.device)
+        B.ds4moe_pack(dst, src, n, rows, cols, self.bits, stream)
         torch.cuda.current_stream(self.device).synchronize()
         del src
         return dst
@@ -111,7 +113,7 @@ def from_layer_inputs(L, device="cuda:0", experts: bool = True) -> DeviceLayer:
     wl = L.wl
     xd = B.DS4MOE_F32 if wl.x_dtype == "f32" else B.DS4MOE_BF16
     rd = B.DS4MOE_F32 if wl.router_dtype == "f32" else B.DS4MOE_BF16
-    dl = DeviceLayer(wl.H, wl.I, wl.E, wl.k, wl.Is, xd, rd, device)
+    dl = DeviceLayer(wl.H, wl.I, wl.E, wl.k, wl.Is, xd, rd, device, bits=getattr(wl, "bits", 2))
     dl.set_router(L.router_w, L.router_bias)
     if experts:
         dl.set_experts(L.gate, L.up, L.down)

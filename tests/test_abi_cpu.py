@@ -51,10 +51,22 @@ def test_packed_bytes():
     assert q.ds4moe_packed_bytes(16, 8) == 0
 
 
+def test_packed_bytes_bits():
+    # 4-bit codes: 148 bytes per 256 weights, 2368 per 16 x 256 unit
+    assert q.ds4moe_packed_bytes_bits(2048, 4096, 4) == 2048 * 4096 // 256 * 148 == 4849664
+    assert q.ds4moe_packed_bytes_bits(256, 128, 4) == 16 * 2368
+    assert q.ds4moe_packed_bytes_bits(2048, 4096, 2) == q.ds4moe_packed_bytes(2048, 4096)
+    for bits in (0, 1, 3, 8, -2):
+        assert q.ds4moe_packed_bytes_bits(16, 256, bits) == 0
+    assert q.ds4moe_packed_bytes_bits(15, 256, 4) == 0
+    assert q.ds4moe_packed_bytes_bits(16, 384, 4) == 0
+    assert q.ds4moe_packed_bytes_bits((1 << 31) + 16, 256, 4) == 0
+
+
 def dims(**kw):
-    d = dict(H=4096, I=2048, E=256, k=8, Is=0, x_dtype=B.DS4MOE_BF16, router_dtype=B.DS4MOE_BF16)
+    d = dict(H=4096, I=2048, E=256, k=8, Is=0, x_dtype=B.DS4MOE_BF16, router_dtype=B.DS4MOE_BF16, bits=2)
     d.update(kw)
-    return B.make_dims(d["H"], d["I"], d["E"], d["k"], d["Is"], d["x_dtype"], d["router_dtype"])
+    return B.make_dims(d["H"], d["I"], d["E"], d["k"], d["Is"], d["x_dtype"], d["router_dtype"], d["bits"])
 
 
 def test_workspace_bytes():
@@ -75,6 +87,7 @@ def test_workspace_bytes():
     (dict(I=384), B.DS4MOE_ERR_SHAPE), (dict(k=0), B.DS4MOE_ERR_SHAPE), (dict(k=17, E=32), B.DS4MOE_ERR_SHAPE),
     (dict(E=4, k=8), B.DS4MOE_ERR_SHAPE), (dict(E=300), B.DS4MOE_ERR_SHAPE), (dict(Is=100), B.DS4MOE_ERR_SHAPE),
     (dict(x_dtype=5), B.DS4MOE_ERR_DTYPE), (dict(router_dtype=-1), B.DS4MOE_ERR_DTYPE),
+    (dict(bits=0), B.DS4MOE_ERR_SHAPE), (dict(bits=3), B.DS4MOE_ERR_SHAPE), (dict(bits=8), B.DS4MOE_ERR_SHAPE),
 ])
 def test_bad_dims_rejected(bad, status):
     w = B.make_weights(16, 16, 16, 16)
@@ -146,3 +159,15 @@ def test_pack_dequant_argument_errors():
     assert L.ds4moe_dequant_q2k(v(16), None, 1, 16, 256, None) == B.DS4MOE_ERR_NULL
     assert L.ds4moe_dequant_q2k(v(16), v(8), 1, 16, 256, None) == B.DS4MOE_ERR_ALIGN
     assert L.ds4moe_dequant_q2k(v(16), v(16), 1, 16, 100, None) == B.DS4MOE_ERR_SHAPE
+    for bits in (2, 4):
+        assert L.ds4moe_pack(v(16), v(16), 1, 15, 256, bits, None) == B.DS4MOE_ERR_SHAPE
+        assert L.ds4moe_pack(None, v(16), 1, 16, 256, bits, None) == B.DS4MOE_ERR_NULL
+        assert L.ds4moe_pack(v(8), v(16), 1, 16, 256, bits, None) == B.DS4MOE_ERR_ALIGN
+        assert L.ds4moe_pack(v(16), v(16), 0, 16, 256, bits, None) == B.DS4MOE_OK
+        assert L.ds4moe_dequant(v(16), None, 1, 16, 256, bits, None) == B.DS4MOE_ERR_NULL
+        assert L.ds4moe_dequant(v(16), v(8), 1, 16, 256, bits, None) == B.DS4MOE_ERR_ALIGN
+        # more than 2^39 weights in one call: beyond the launch grids
+        assert L.ds4moe_pack(v(16), v(16), 1 << 20, 4096, 4096, bits, None) == B.DS4MOE_ERR_SHAPE
+        assert L.ds4moe_dequant(v(16), v(16), 1 << 20, 4096, 4096, bits, None) == B.DS4MOE_ERR_SHAPE
+    assert L.ds4moe_pack(v(16), v(16), 1, 16, 256, 3, None) == B.DS4MOE_ERR_SHAPE
+    assert L.ds4moe_dequant(v(16), v(16), 1, 16, 256, 1, None) == B.DS4MOE_ERR_SHAPE
