@@ -2,14 +2,16 @@
 """MoE-layer throughput on one MI355X: tokens/s per layer plus the roofline
 fraction of the dominant kernel, with the CPU oracle timed beside it.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode1|decode16|prefill|skewed|tiny|all]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode1|decode16|prefill|skewed|decode1_q4|prefill_q4|tiny|all]
 
 A step is one whole layer call (router -> top-k -> permute -> gate/up+SwiGLU ->
 down -> combine [+ shared expert]) on one batch of synthetic tokens whose
 inputs are already resident in HBM.  Decode workloads rotate over several
 copies of the layer's packed experts and over fresh token batches so the
-2.1 GB of expert weights stream from HBM rather than from the 256 MB
-Infinity Cache.  Prints one JSON line per workload (default: decode1).
+2.1 GB of expert weights (3.7 GB with 4-bit codes: the *_q4 workloads) stream
+from HBM rather than from the 256 MB Infinity Cache.  Prints one JSON line
+per workload (default: decode1).
 """
 from __future__ import annotations
 
@@ -32,6 +34,8 @@ DEFAULTS = {  # workload: (steps, warmup, layer copies, token batches)
     "decode16": (1000, 100, 4, 64),
     "prefill": (50, 5, 1, 4),
     "skewed": (20, 3, 1, 2),
+    "decode1_q4": (2000, 200, 4, 64),
+    "prefill_q4": (50, 5, 1, 4),
 }
 
 
@@ -304,7 +308,8 @@ def run_workload(name: str, args) -> dict:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": name, "T": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
-                   "shared_inter": wl.Is, "layer_copies": n_layers, "token_batches": n_batches,
+                   "shared_inter": wl.Is, "expert_bits": wl.bits, "layer_copies": n_layers,
+                   "token_batches": n_batches,
                    "seed": args.seed, "distinct_experts_mean": float(np.mean(distinct))},
         "roofline": roof,
         "layer_roofline": layer,

@@ -155,6 +155,33 @@ __device__ __forceinline__ void gemm_load_a(UnitRegs<B> (&u)[R][NM], const GemmC
       u[r][m] = load_unit<B>(c.W[m] + (size_t)rts[r] * c.rt_stride + (size_t)sb * Unit<B>::BYTES, lane);
 }
 
+// The same loads in two parts: PART 0 the code planes but the last, PART 1
+// the last plane (4-bit units: issued once the current super-block's first
+// plane is dead, so that the two super-blocks' units need few registers at
+// once).  The scales and d/dmin go with PART 1 when NM == 1 (down: two row
+// tiles, the larger register set), else with PART 0.
+template <int PART, int NM, int R, int B>
+__device__ __forceinline__ void gemm_load_a_part(UnitRegs<B> (&u)[R][NM], const GemmCtx<NM> &c, const int (&rts)[R],
+                                                 int sb, int lane) {
+  constexpr int LAST = B / 2 - 1;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint8_t *unit = c.W[m] + (size_t)rts[r] * c.rt_stride + (size_t)sb * Unit<B>::BYTES;
+      if (PART == 0) {
+#pragma unroll
+        for (int p = 0; p < LAST; ++p) u[r][m].code[p] = *reinterpret_cast<const u4 *>(unit + 1024 * p + 16 * lane);
+      } else {
+        u[r][m].code[LAST] = *reinterpret_cast<const u4 *>(unit + 1024 * LAST + 16 * lane);
+      }
+      if (PART == (NM == 1 ? 1 : 0)) {
+        u[r][m].scale = *reinterpret_cast<const u4 *>(unit + Unit<B>::SCALE_OFF + 16 * (lane & 15));
+        u[r][m].dd = *reinterpret_cast<const u4 *>(unit + Unit<B>::DD_OFF + 16 * (lane >> 4));
+      }
+    }
+}
+
 // Activation staging: thread -> 16-byte chunk column sc = tid % 32 of token
 // rows tid/32 + SROWS*i (SROWS = threads/32), so 32 consecutive lanes move one
 // row's 512 bytes (contiguous in memory and conflict-free in LDS); sums:
@@ -414,9 +441,13 @@ __device__ __forceinline__ int step_chunk(int g) {
   return 2 * (4 * (S >> 1) + g) + (S & 1);
 }
 
+// 4-bit units: between steps 3 and 4, when the first code plane of `u` is
+// dead, the rest of the next super-block's units (sb_next, if >= 0) is
+// loaded into `nxt`
 template <int NM, int R, int NTV, int B>
 __device__ __forceinline__ void pt_compute_sb(const UnitRegs<B> (&u)[R][NM], const char *slot, f4 (&y)[NM][R][NTV],
-                                              int r16, int g) {
+                                              int r16, int g, UnitRegs<B> (&nxt)[R][NM], const GemmCtx<NM> &c,
+                                              const int (&rts)[R], int sb_next, int lane) {
   UnitDecoded dc[R][NM];
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -443,7 +474,13 @@ __device__ __forceinline__ void pt_compute_sb(const UnitRegs<B> (&u)[R][NM], con
       }                                                                                       \
     }                                                                                         \
   }
-  PT_STEP(0) PT_STEP(1) PT_STEP(2) PT_STEP(3) PT_STEP(4) PT_STEP(5) PT_STEP(6) PT_STEP(7)
+  PT_STEP(0) PT_STEP(1) PT_STEP(2) PT_STEP(3)
+  if constexpr (B == 4) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (sb_next >= 0) gemm_load_a_part<1, NM, R, B>(nxt, c, rts, sb_next, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  PT_STEP(4) PT_STEP(5) PT_STEP(6) PT_STEP(7)
 #undef PT_STEP
   h8 bm[NTV];
 #pragma unroll
@@ -539,20 +576,22 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
     __syncthreads();
     if (sb + 1 < nsb) {
       issue(1, sb + 1);
-      gemm_load_a<NM, R, B>(ub, c, rts, sb + 1, lane);
+      if constexpr (B == 4) gemm_load_a_part<0, NM, R, B>(ub, c, rts, sb + 1, lane);
+      else gemm_load_a<NM, R, B>(ub, c, rts, sb + 1, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
-    pt_compute_sb<NM, R, NTV, B>(ua, ring, y, r16, g);
+    pt_compute_sb<NM, R, NTV, B>(ua, ring, y, r16, g, ub, c, rts, sb + 1 < nsb ? sb + 1 : -1, lane);
     if (sb + 1 >= nsb) break;
     // odd super-block: slot 1, weights in ub
     wait_vm<0>();
     __syncthreads();
     if (sb + 2 < nsb) {
       issue(0, sb + 2);
-      gemm_load_a<NM, R, B>(ua, c, rts, sb + 2, lane);
+      if constexpr (B == 4) gemm_load_a_part<0, NM, R, B>(ua, c, rts, sb + 2, lane);
+      else gemm_load_a<NM, R, B>(ua, c, rts, sb + 2, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
-    pt_compute_sb<NM, R, NTV, B>(ub, ring + PT_SLOT_BYTES, y, r16, g);
+    pt_compute_sb<NM, R, NTV, B>(ub, ring + PT_SLOT_BYTES, y, r16, g, ua, c, rts, sb + 2 < nsb ? sb + 2 : -1, lane);
   }
 
   if (rt0 >= n_rt) return;
