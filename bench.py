@@ -3,7 +3,7 @@
 fraction of the dominant kernel, with the CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload decode1|decode16|prefill|skewed|decode1_q4|prefill_q4|tiny|all]
+                    [--workload decode1|decode16|prefill|skewed|decode1_q4|prefill_q4|decode1_cached|tiny|all]
 
 A step is one whole layer call (router -> top-k -> permute -> gate/up+SwiGLU ->
 down -> combine [+ shared expert]) on one batch of synthetic tokens whose
@@ -25,6 +25,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+PCIE_PEAK_GBS = 64.0           # host link, PCIe 5.0 x16, one direction, GB/s
 GRAPH_STEPS = 64               # at most this many layer calls per captured graph
 MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
@@ -36,7 +37,9 @@ DEFAULTS = {  # workload: (steps, warmup, layer copies, token batches)
     "skewed": (20, 3, 1, 2),
     "decode1_q4": (2000, 200, 4, 64),
     "prefill_q4": (50, 5, 1, 4),
+    "decode1_cached": (1000, 300, 1, 1024),
 }
+CACHE_SLOTS = {"decode1_cached": 204}   # 80 % of the 256 experts (the pages' automatic cache budget)
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -161,13 +164,19 @@ def run_workload(name: str, args) -> dict:
     steps = args.steps if args.steps is not None else steps
     warmup = args.warmup if args.warmup is not None else warmup
     n_layers = args.layers if args.layers is not None else n_layers
-    wl = synth.WORKLOADS[name]
+    cached = name in CACHE_SLOTS
+    wname = name[: -len("_cached")] if cached else name
+    wl = synth.WORKLOADS[wname]
     dev = torch.device("cuda:0")
 
     t0 = time.perf_counter()
-    base = synth.make_layer("prefill" if wl.layer_id == 1 else name, seed=args.seed)
-    L = synth.derive(base, name) if wl.layer_id == 1 else base
+    base = synth.make_layer("prefill" if wl.layer_id == 1 else wname, seed=args.seed)
+    L = synth.derive(base, wname) if wl.layer_id == 1 else base
     dl = q.from_layer_inputs(L, dev)
+    if cached:  # experts in pinned host memory, a slot cache in HBM (which also defeats the MALL)
+        n_layers = 1
+        S = CACHE_SLOTS[name]
+        cache = q.ExpertCache(dl, S)
     layers = [dl.weights()]
     copies = []
     for i in range(1, n_layers):  # same bytes at other HBM addresses
@@ -179,7 +188,18 @@ def run_workload(name: str, args) -> dict:
     mode = q.MODE_DECODE if T <= 16 else q.MODE_PREFILL
     y = torch.empty(T, wl.H, dtype=torch.float32, device=dev)
     ws = dl.workspace(T, mode)
-    fwd = q.ds4moe_forward_decode if mode == q.MODE_DECODE else q.ds4moe_forward_prefill
+    fwd0 = q.ds4moe_forward_decode if mode == q.MODE_DECODE else q.ds4moe_forward_prefill
+    if cached:
+        cw = cache.weights()
+
+        def fwd(dims, w, x, T_, y_, r_, ws_, n_, st_, events=None):
+            B.ds4moe_forward_decode_cached(dims, cw, S, cache.buf, cache.nbytes, x, T_, y_, r_, ws_, n_, events, st_)
+    else:
+        def fwd(dims, w, x, T_, y_, r_, ws_, n_, st_, events=None):
+            if events is None:
+                fwd0(dims, w, x, T_, y_, r_, ws_, n_, st_)
+            else:
+                B.ds4moe_forward_timed(mode, dims, w, x, T_, y_, r_, ws_, n_, events, st_)
     stream = torch.cuda.current_stream(dev)
     setup_s = time.perf_counter() - t0
 
@@ -192,10 +212,7 @@ def run_workload(name: str, args) -> dict:
     def step(i, events=None):
         w = layers[i % n_layers]
         x = xs[i % n_batches]
-        if events is None:
-            fwd(dl.dims, w, x, T, y, None, ws, ws.numel(), stream)
-        else:
-            B.ds4moe_forward_timed(mode, dl.dims, w, x, T, y, None, ws, ws.numel(), events, stream)
+        fwd(dl.dims, w, x, T, y, None, ws, ws.numel(), stream, events)
 
     steps_eager = steps
     for i in range(warmup):
@@ -211,7 +228,10 @@ def run_workload(name: str, args) -> dict:
     # same rotation over layer copies and token batches), replayed; the library
     # enqueues kernels only, so a capture holds the whole layer.
     # (exactly `steps` calls: the graph length is the largest divisor of steps <= GRAPH_STEPS)
-    glen = 0 if args.no_graph else max(d for d in range(1, min(GRAPH_STEPS, steps) + 1) if steps % d == 0)
+    # Through the expert cache the timed loop stays eager: a replayed graph would
+    # repeat its token batches, whose experts the cache then already holds.
+    glen = 0 if (args.no_graph or cached) else max(d for d in range(1, min(GRAPH_STEPS, steps) + 1)
+                                                   if steps % d == 0)
     if glen:
         reps = steps // glen
         graph = torch.cuda.CUDAGraph()
@@ -256,6 +276,16 @@ def run_workload(name: str, args) -> dict:
     else:
         elapsed = elapsed_eager
         pct = None
+        if cached:  # spread over the eager steps (an extra pass, an event between steps)
+            marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            marks[0].record()
+            for i in range(steps):
+                step(i)
+                marks[i + 1].record()
+            torch.cuda.synchronize()
+            st_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+            pct = {f"p{q}": round(float(np.percentile(st_ms, q)), 5) for q in (10, 50, 90)}
+            pct["over"] = f"{steps} eager steps"
 
     # second pass with per-kernel events stamped by each kernel's own dispatch
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * B.N_TIMED_KERNELS)] for _ in range(steps_eager)]
@@ -263,11 +293,13 @@ def run_workload(name: str, args) -> dict:
         for e in row:
             e.record(stream)
     torch.cuda.synchronize()
+    stats0 = cache.stats() if cached else None
     t2 = time.perf_counter()
     for i in range(steps_eager):
         step(i, ev[i])
     torch.cuda.synchronize()
     elapsed_ev = time.perf_counter() - t2
+    stats1 = cache.stats() if cached else None
     stage_ms = {s: 0.0 for s in B.KERNEL_SLOTS}
     per_step_gateup = []
     for i in range(steps_eager):
@@ -281,7 +313,22 @@ def run_workload(name: str, args) -> dict:
     H, I, E, k = wl.H, wl.I, wl.E, wl.k
     gu_bytes = dl.gu_bytes
     rk = roofline_kernel(mode == q.MODE_DECODE, T)
-    if mode == q.MODE_DECODE:
+    cache_info = None
+    if cached:
+        # the fill kernel is bound by the host link: expert bytes copied per launch / its duration
+        misses = stats1[2] - stats0[2]
+        hits = stats1[1] - stats0[1]
+        fill_bytes = misses * (2 * gu_bytes + dl.d_bytes)
+        fill_s = stage_ms["cache_fill"] * steps_eager * 1e-3
+        achieved = fill_bytes / fill_s / 1e9
+        roof = {"bound": "pcie", "achieved": round(achieved, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PCIE_PEAK_GBS, 4), "traffic": None, "kernel": "k_cache_fill",
+                "algorithmic_bytes_per_launch": fill_bytes / steps_eager}
+        cache_info = {"slots": S, "experts": E, "hit_rate": round(hits / max(1, hits + misses), 4),
+                      "misses_per_step": round(misses / steps_eager, 3),
+                      "host_bytes": E * (2 * gu_bytes + dl.d_bytes)}
+        layer = None
+    elif mode == q.MODE_DECODE:
         # gate + up packed bytes of the experts each step touches
         gu_total = sum(2 * gu_bytes * distinct[i % n_batches] for i in range(steps_eager))
         achieved = gu_total / (sum(per_step_gateup) * 1e-3) / 1e9
@@ -308,6 +355,7 @@ def run_workload(name: str, args) -> dict:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": name, "T": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
+                   **({"expert_cache": cache_info} if cache_info else {}),
                    "shared_inter": wl.Is, "expert_bits": wl.bits, "layer_copies": n_layers,
                    "token_batches": n_batches,
                    "seed": args.seed, "distinct_experts_mean": float(np.mean(distinct))},
@@ -324,6 +372,8 @@ def run_workload(name: str, args) -> dict:
         out["roofline"]["library_fp16_gemm_reference"] = library_gemm_reference()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    if cached:
+        del cache, cw
     del copies, xs, dl
     torch.cuda.empty_cache()
     return out

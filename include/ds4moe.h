@@ -53,7 +53,8 @@ typedef enum {
   DS4MOE_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
   DS4MOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
   DS4MOE_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
-  DS4MOE_ERR_HIP = 7          /* a HIP launch or runtime call failed */
+  DS4MOE_ERR_HIP = 7,         /* a HIP launch or runtime call failed */
+  DS4MOE_ERR_HOSTMEM = 8      /* host expert weights are not pinned (device-visible) host memory */
 } ds4moe_status;
 
 typedef enum { DS4MOE_F32 = 0, DS4MOE_BF16 = 1 } ds4moe_dtype;
@@ -211,7 +212,7 @@ int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, con
                            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Kernel slots timed by ds4moe_forward_timed. */
-#define DS4MOE_N_TIMED_KERNELS 8
+#define DS4MOE_N_TIMED_KERNELS 10
 
 /* For measurement: the same work as ds4moe_forward_decode (mode
  * DS4MOE_MODE_DECODE) or ds4moe_forward_prefill (DS4MOE_MODE_PREFILL); each
@@ -221,12 +222,61 @@ int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, con
  * created by the caller; pair i = (events[2i], events[2i+1]) times slot i:
  * 0 router logits, 1 top-k (decode: top-k + permutation), 2 permutation
  * (prefill), 3 gate/up + SwiGLU, 4 down, 5 shared gate/up, 6 shared down,
- * 7 combine.  A slot with no kernel in the call gets both events recorded
- * back to back.  Any other mode returns DS4MOE_ERR_SHAPE; a NULL array or
+ * 7 combine, 8 expert-cache plan, 9 expert-cache fill (the last two only in
+ * ds4moe_forward_decode_cached).  A slot with no kernel in the call gets both
+ * events recorded back to back.  Any other mode returns DS4MOE_ERR_SHAPE; a NULL array or
  * event DS4MOE_ERR_NULL. */
 int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
                          float *y, ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *const *events,
                          void *stream);
+
+/* ROUTED-EXPERT CACHE (small batches).  The experts' packed matrices stay in
+ * pinned host memory; a cache buffer in device memory holds n_slots expert
+ * slots (gate, up and down of one expert each).  A call routes the batch,
+ * gives every expert it uses a slot (a slot already holding the expert, else
+ * the least recently used slot, ties to the lower slot index, never one the
+ * batch uses), copies the missing experts from host memory into their slots
+ * (the GPU reads the host memory directly), and runs the expert kernels on
+ * the slots.  The outputs are bitwise those of ds4moe_forward_decode on the
+ * same experts resident in device memory.  This is the bounded routed-expert
+ * cache with loads on a miss of the pages' SSD streaming mode ("antirez-ds4"
+ * insight page, SSD streaming section; DwarfStar architecture article,
+ * "Memory trade-off: resident vs SSD streaming" section), with host memory
+ * as the backing store; the pages fix no eviction policy.
+ *
+ * Bytes of the cache buffer for n_slots slots (1 <= n_slots <= E); 0 for
+ * invalid dims or n_slots.  The pages size the cache as a byte budget or a
+ * slot count; the automatic budget is 80 % of the working set without the
+ * non-routed weights. */
+size_t ds4moe_cache_bytes(const ds4moe_dims *dims, int32_t n_slots);
+
+/* Empty every slot and zero the counters (one kernel on `stream`, no memset,
+ * so it may be captured in a graph).  `cache` is a device buffer of at least
+ * ds4moe_cache_bytes(dims, n_slots) bytes, 256-byte aligned, owned by the
+ * caller.  Every later call on this buffer must pass the same dims and
+ * n_slots.  Errors: DS4MOE_ERR_NULL, _ALIGN, _SHAPE (n_slots), _WORKSPACE
+ * (cache_bytes too small). */
+int ds4moe_cache_reset(const ds4moe_dims *dims, int32_t n_slots, void *cache, size_t cache_bytes, void *stream);
+
+/* ds4moe_forward_decode (1 <= T <= 16) with the routed experts in host
+ * memory: w->gate, w->up, w->down are HOST pointers into pinned memory
+ * (hipHostMalloc, or a pinned torch tensor), in the same layout as the
+ * device weights of ds4moe_forward_decode; router and shared-expert weights
+ * are device pointers as there.  n_slots >= min(E, T*k) (every expert of the
+ * batch holds a slot during the call).  events: NULL, or
+ * 2*DS4MOE_N_TIMED_KERNELS events as for ds4moe_forward_timed.  Calls on one
+ * cache buffer must not overlap (they update its state).  Errors: those of
+ * ds4moe_forward_decode and ds4moe_cache_reset, and DS4MOE_ERR_HOSTMEM when
+ * an expert pointer is not pinned host memory. */
+int ds4moe_forward_decode_cached(const ds4moe_dims *dims, const ds4moe_weights *w, int32_t n_slots, void *cache,
+                                 size_t cache_bytes, const void *x, int32_t T, float *y, ds4moe_routing *route_out,
+                                 void *ws, size_t ws_bytes, void *const *events, void *stream);
+
+/* Enqueue a copy of the cache's counters since its reset to host memory
+ * out[3] = {calls, hits, misses} (hits and misses count experts of calls);
+ * read them after `stream` has synchronised. */
+int ds4moe_cache_stats(const ds4moe_dims *dims, int32_t n_slots, const void *cache, size_t cache_bytes,
+                       uint64_t *out, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ds4moe_status_str(int status);

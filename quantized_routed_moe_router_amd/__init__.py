@@ -11,11 +11,11 @@ from .binding import (DS4MOE_BF16, DS4MOE_F32, MODE_DECODE, MODE_PREFILL, MODE_R
                       ds4moe_forward_timed, ds4moe_pack, ds4moe_pack_q2k, ds4moe_packed_bytes,
                       ds4moe_packed_bytes_bits, ds4moe_route, ds4moe_workspace_bytes, make_dims, make_routing,
                       make_weights)
-from .layer import DeviceLayer, from_layer_inputs
+from .layer import DeviceLayer, ExpertCache, from_layer_inputs
 
 binding.lib()  # load now: a missing build is an error, never a silent fallback
 
-__all__ = ["binding", "DeviceLayer", "from_layer_inputs", "Ds4MoeError", "ds4moe_dequant", "ds4moe_dequant_q2k",
+__all__ = ["binding", "DeviceLayer", "ExpertCache", "from_layer_inputs", "Ds4MoeError", "ds4moe_dequant", "ds4moe_dequant_q2k",
            "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_forward_timed", "ds4moe_pack", "ds4moe_pack_q2k",
            "ds4moe_packed_bytes", "ds4moe_packed_bytes_bits",
            "ds4moe_route", "ds4moe_workspace_bytes", "make_dims", "make_routing", "make_weights",

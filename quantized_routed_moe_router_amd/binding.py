@@ -23,6 +23,7 @@ DS4MOE_ERR_ALIGN = 4
 DS4MOE_ERR_WORKSPACE = 5
 DS4MOE_ERR_UNSUPPORTED = 6
 DS4MOE_ERR_HIP = 7
+DS4MOE_ERR_HOSTMEM = 8
 DS4MOE_F32 = 0
 DS4MOE_BF16 = 1
 MODE_ROUTE, MODE_DECODE, MODE_PREFILL = 0, 1, 2
@@ -30,9 +31,11 @@ MODE_ROUTE, MODE_DECODE, MODE_PREFILL = 0, 1, 2
 EXPORTED = ("ds4moe_packed_bytes", "ds4moe_packed_bytes_bits", "ds4moe_pack_q2k", "ds4moe_pack",
             "ds4moe_dequant_q2k", "ds4moe_dequant", "ds4moe_workspace_bytes",
             "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_status_str",
-            "ds4moe_version", "ds4moe_forward_timed")
-N_TIMED_KERNELS = 8
-KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine")
+            "ds4moe_version", "ds4moe_forward_timed", "ds4moe_cache_bytes", "ds4moe_cache_reset",
+            "ds4moe_forward_decode_cached", "ds4moe_cache_stats")
+N_TIMED_KERNELS = 10
+KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine",
+                "cache_plan", "cache_fill")
 
 
 class Dims(ctypes.Structure):
@@ -81,10 +84,17 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_forward_decode.argtypes = [P, P, P, I32, P, P, P, ctypes.c_size_t, P]
         L.ds4moe_forward_prefill.argtypes = [P, P, P, I32, P, P, P, ctypes.c_size_t, P]
         L.ds4moe_forward_timed.argtypes = [I32, P, P, P, I32, P, P, P, ctypes.c_size_t, P, P]
+        L.ds4moe_cache_bytes.argtypes = [P, I32]
+        L.ds4moe_cache_bytes.restype = ctypes.c_size_t
+        L.ds4moe_cache_reset.argtypes = [P, I32, P, ctypes.c_size_t, P]
+        L.ds4moe_forward_decode_cached.argtypes = [P, P, I32, P, ctypes.c_size_t, P, I32, P, P, P, ctypes.c_size_t,
+                                                   P, P]
+        L.ds4moe_cache_stats.argtypes = [P, I32, P, ctypes.c_size_t, P, P]
         L.ds4moe_status_str.argtypes = [ctypes.c_int]
         L.ds4moe_status_str.restype = ctypes.c_char_p
         L.ds4moe_version.restype = ctypes.c_int
         for fn in ("ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_pack", "ds4moe_dequant", "ds4moe_route",
+                   "ds4moe_cache_reset", "ds4moe_forward_decode_cached", "ds4moe_cache_stats",
                    "ds4moe_forward_decode",
                    "ds4moe_forward_prefill", "ds4moe_forward_timed"):
             getattr(L, fn).restype = ctypes.c_int
@@ -183,9 +193,42 @@ def ds4moe_forward_timed(mode: int, dims: Dims, weights: Weights, x, T: int, y, 
                          ws_bytes: int, events, stream=None) -> None:
     """events: 2*N_TIMED_KERNELS torch.cuda.Event objects (already created) or raw
     hipEvent_t ints; pair i times kernel slot KERNEL_SLOTS[i]."""
-    raw = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events]
-    assert len(raw) == 2 * N_TIMED_KERNELS
-    arr = (ctypes.c_void_p * (2 * N_TIMED_KERNELS))(*raw)
+    arr = _events(events)
     r = ctypes.byref(routing) if routing is not None else None
     _check(lib().ds4moe_forward_timed(mode, ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(y), r,
                                       _ptr(ws), ws_bytes, arr, _stream(stream)), "forward_timed")
+
+
+def _events(events):
+    if events is None:
+        return None
+    raw = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events]
+    assert len(raw) == 2 * N_TIMED_KERNELS
+    return (ctypes.c_void_p * (2 * N_TIMED_KERNELS))(*raw)
+
+
+def ds4moe_cache_bytes(dims: Dims, n_slots: int) -> int:
+    return int(lib().ds4moe_cache_bytes(ctypes.byref(dims), n_slots))
+
+
+def ds4moe_cache_reset(dims: Dims, n_slots: int, cache, cache_bytes: int, stream=None) -> None:
+    _check(lib().ds4moe_cache_reset(ctypes.byref(dims), n_slots, _ptr(cache), cache_bytes, _stream(stream)),
+           "cache_reset")
+
+
+def ds4moe_forward_decode_cached(dims: Dims, weights: Weights, n_slots: int, cache, cache_bytes: int, x, T: int, y,
+                                 routing: Routing | None, ws, ws_bytes: int, events=None, stream=None) -> None:
+    """weights.gate/up/down: pinned host memory; events: None or 2*N_TIMED_KERNELS events."""
+    r = ctypes.byref(routing) if routing is not None else None
+    _check(lib().ds4moe_forward_decode_cached(ctypes.byref(dims), ctypes.byref(weights), n_slots, _ptr(cache),
+                                              cache_bytes, _ptr(x), T, _ptr(y), r, _ptr(ws), ws_bytes,
+                                              _events(events), _stream(stream)), "forward_decode_cached")
+
+
+def ds4moe_cache_stats(dims: Dims, n_slots: int, cache, cache_bytes: int, stream=None) -> tuple:
+    """(calls, hits, misses) since the cache's reset; synchronises the stream."""
+    out = (ctypes.c_uint64 * 3)()
+    st = _stream(stream)
+    _check(lib().ds4moe_cache_stats(ctypes.byref(dims), n_slots, _ptr(cache), cache_bytes, out, st), "cache_stats")
+    torch.cuda.synchronize()
+    return int(out[0]), int(out[1]), int(out[2])

@@ -113,6 +113,58 @@ T *at(void *ws, size_t off) {
   return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
 }
 
+// Routed-expert cache buffer: header, slot tables, fill list, then S slots
+// of gate, up and down matrices.
+struct CacheLayout {
+  size_t hdr, slot_expert, expert_slot, stamp, fill_e, fill_s, gate, up, down, total;
+  size_t gu_bytes, d_bytes;
+};
+
+CacheLayout make_cache_layout(const ds4moe_dims &d, int S) {
+  CacheLayout C{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  C.gu_bytes = ds4moe_packed_bytes_bits(d.inter, d.hidden, d.expert_bits);
+  C.d_bytes = ds4moe_packed_bytes_bits(d.hidden, d.inter, d.expert_bits);
+  C.hdr = take(sizeof(CacheHdr));
+  C.slot_expert = take(4 * (size_t)S);
+  C.expert_slot = take(4 * (size_t)d.n_experts);
+  C.stamp = take(4 * (size_t)S);
+  C.fill_e = take(4 * (size_t)S);
+  C.fill_s = take(4 * (size_t)S);
+  C.gate = take(C.gu_bytes * (size_t)S);
+  C.up = take(C.gu_bytes * (size_t)S);
+  C.down = take(C.d_bytes * (size_t)S);
+  C.total = off;
+  return C;
+}
+
+CacheState cache_state(void *cache, const CacheLayout &C) {
+  CacheState c;
+  c.hdr = at<CacheHdr>(cache, C.hdr);
+  c.slot_expert = at<int32_t>(cache, C.slot_expert);
+  c.expert_slot = at<int32_t>(cache, C.expert_slot);
+  c.stamp = at<uint32_t>(cache, C.stamp);
+  c.fill_e = at<int32_t>(cache, C.fill_e);
+  c.fill_s = at<int32_t>(cache, C.fill_s);
+  c.gate = at<uint8_t>(cache, C.gate);
+  c.up = at<uint8_t>(cache, C.up);
+  c.down = at<uint8_t>(cache, C.down);
+  return c;
+}
+
+// a call through the cache: its state and the device-visible addresses of
+// the host-resident experts
+struct CacheCall {
+  CacheState st;
+  int S;
+  const void *hg, *hu, *hd;
+};
+
 int validate_weights(const ds4moe_dims &d, const ds4moe_weights *w, bool experts) {
   if (!w) return DS4MOE_ERR_NULL;
   if (!w->router_w) return DS4MOE_ERR_NULL;
@@ -181,11 +233,15 @@ Ptrs routing_ptrs(void *ws, const Layout &L, const ds4moe_routing *r) {
 }
 
 // kernel slots of ds4moe_forward_timed
-enum { SL_ROUTER = 0, SL_ROUTE, SL_PERMUTE, SL_GATEUP, SL_DOWN, SL_SHGATEUP, SL_SHDOWN, SL_COMBINE, SL_N };
+enum {
+  SL_ROUTER = 0, SL_ROUTE, SL_PERMUTE, SL_GATEUP, SL_DOWN, SL_SHGATEUP, SL_SHDOWN, SL_COMBINE, SL_CPLAN, SL_CFILL,
+  SL_N
+};
+static_assert(SL_N == DS4MOE_N_TIMED_KERNELS, "timed kernel slots");
 
 int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
             ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream, int mode,
-            const Timing *tms = nullptr) {
+            const Timing *tms = nullptr, const CacheCall *cc = nullptr) {
   Layout L;
   int st = check_call(dims, w, x, T, y, true, route_out, ws, ws_bytes, mode, &L);
   if (st || T == 0) return st;
@@ -213,8 +269,9 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   DecTile *dtiles = nullptr;
   if (dec) dtiles = at<DecTile>(ws, L.tiles);
   int32_t *ntiles = at<int32_t>(ws, L.ntiles);
-  // decode with T <= 4: the gate/up kernel routes the batch itself
-  const bool fused_route = dec && L.sliced && T <= 4;
+  // decode with T <= 4: the gate/up kernel routes the batch itself (not
+  // through the cache, whose plan sits between routing and gate/up)
+  const bool fused_route = dec && L.sliced && T <= 4 && !cc;
   DecRoute rr{at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, d.n_experts, d.top_k, ro,
               dtiles, ntiles};
   if (L.sliced) {
@@ -236,6 +293,14 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.down = (const uint8_t *)w->down;
   ga.gu_bytes = ds4moe_packed_bytes_bits(d.inter, d.hidden, d.expert_bits);
   ga.d_bytes = ds4moe_packed_bytes_bits(d.hidden, d.inter, d.expert_bits);
+  if (cc) {  // experts through the cache: tiles name slots, the kernels read the slot arrays
+    TRY(launch_cache_plan(cc->st, dtiles, ntiles, cc->S, d.n_experts, s, tm(SL_CPLAN)));
+    TRY(launch_cache_fill(cc->st, cc->hg, cc->hu, cc->hd, ga.gu_bytes, ga.d_bytes,
+                          L.max_tiles < cc->S ? L.max_tiles : cc->S, s, tm(SL_CFILL)));
+    ga.gate = cc->st.gate;
+    ga.up = cc->st.up;
+    ga.down = cc->st.down;
+  }
   ga.bits = d.expert_bits;
   ga.tiles = ro.tiles;
   ga.ntiles = ntiles;
@@ -320,6 +385,7 @@ const char *ds4moe_status_str(int status) {
     case DS4MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case DS4MOE_ERR_UNSUPPORTED: return "unsupported request";
     case DS4MOE_ERR_HIP: return "HIP launch or runtime error";
+    case DS4MOE_ERR_HOSTMEM: return "expert weights are not in pinned host memory";
     default: return "unknown status";
   }
 }
@@ -405,6 +471,87 @@ int ds4moe_forward_decode(const ds4moe_dims *dims, const ds4moe_weights *w, cons
 int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
                            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream) {
   return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, DS4MOE_MODE_PREFILL);
+}
+
+size_t ds4moe_cache_bytes(const ds4moe_dims *dims, int32_t n_slots) {
+  if (validate_dims(dims) != DS4MOE_OK) return 0;
+  if (n_slots < 1 || n_slots > dims->n_experts) return 0;
+  return make_cache_layout(*dims, n_slots).total;
+}
+
+namespace {
+int check_cache(const ds4moe_dims *dims, int32_t n_slots, const void *cache, size_t cache_bytes, CacheLayout *C) {
+  int st = validate_dims(dims);
+  if (st) return st;
+  if (n_slots < 1 || n_slots > dims->n_experts) return DS4MOE_ERR_SHAPE;
+  if (!cache) return DS4MOE_ERR_NULL;
+  if (!aligned(cache, 256)) return DS4MOE_ERR_ALIGN;
+  *C = make_cache_layout(*dims, n_slots);
+  if (cache_bytes < C->total) return DS4MOE_ERR_WORKSPACE;
+  return DS4MOE_OK;
+}
+
+// device-visible address of pinned host memory (nullptr for anything else:
+// device memory, pageable host memory)
+const void *host_device_ptr(const void *h) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, h) != hipSuccess || a.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();  // clear the error the query left
+    return nullptr;
+  }
+  void *d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void *>(h), 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return d;
+}
+}  // namespace
+
+int ds4moe_cache_reset(const ds4moe_dims *dims, int32_t n_slots, void *cache, size_t cache_bytes, void *stream) {
+  CacheLayout C;
+  const int st = check_cache(dims, n_slots, cache, cache_bytes, &C);
+  if (st) return st;
+  return hip_status(launch_cache_reset(cache_state(cache, C), n_slots, dims->n_experts, (hipStream_t)stream));
+}
+
+int ds4moe_forward_decode_cached(const ds4moe_dims *dims, const ds4moe_weights *w, int32_t n_slots, void *cache,
+                                 size_t cache_bytes, const void *x, int32_t T, float *y, ds4moe_routing *route_out,
+                                 void *ws, size_t ws_bytes, void *const *events, void *stream) {
+  CacheLayout C;
+  int st = check_cache(dims, n_slots, cache, cache_bytes, &C);
+  if (st) return st;
+  if (T < 1 || T > 16) return DS4MOE_ERR_SHAPE;
+  const int64_t used = (int64_t)T * dims->top_k < dims->n_experts ? (int64_t)T * dims->top_k : dims->n_experts;
+  if (n_slots < used) return DS4MOE_ERR_SHAPE;  // every expert of the batch needs a slot at once
+  st = validate_weights(*dims, w, true);
+  if (st) return st;
+  Layout L;
+  st = check_call(dims, w, x, T, y, true, route_out, ws, ws_bytes, DS4MOE_MODE_DECODE, &L);
+  if (st) return st;
+  Timing tms[SL_N];
+  if (events) {
+    for (int i = 0; i < SL_N; ++i) {
+      if (!events[2 * i] || !events[2 * i + 1]) return DS4MOE_ERR_NULL;
+      tms[i].start = (hipEvent_t)events[2 * i];
+      tms[i].stop = (hipEvent_t)events[2 * i + 1];
+    }
+  }
+  CacheCall cc{cache_state(cache, C), n_slots, host_device_ptr(w->gate), host_device_ptr(w->up),
+               host_device_ptr(w->down)};
+  if (!cc.hg || !cc.hu || !cc.hd) return DS4MOE_ERR_HOSTMEM;
+  return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, DS4MOE_MODE_DECODE, events ? tms : nullptr,
+                 &cc);
+}
+
+int ds4moe_cache_stats(const ds4moe_dims *dims, int32_t n_slots, const void *cache, size_t cache_bytes,
+                       uint64_t *out, void *stream) {
+  CacheLayout C;
+  const int st = check_cache(dims, n_slots, cache, cache_bytes, &C);
+  if (st) return st;
+  if (!out) return DS4MOE_ERR_NULL;
+  const CacheHdr *h = reinterpret_cast<const CacheHdr *>(reinterpret_cast<const char *>(cache) + C.hdr);
+  return hip_status(hipMemcpyAsync(out, &h->calls, 3 * sizeof(uint64_t), hipMemcpyDeviceToHost, (hipStream_t)stream));
 }
 
 int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,

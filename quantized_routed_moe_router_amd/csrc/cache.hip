@@ -1,0 +1,169 @@
+// Routed-expert cache for small batches: every expert's packed matrices live
+// in pinned host memory and a bounded set of S expert slots lives in device
+// memory.  A call routes the batch, plans the slots of the experts it uses
+// (least recently used slot on a miss), copies the missing experts from host
+// memory into their slots, and runs the unchanged expert kernels on the slot
+// arrays: the same bytes, so the same results as with resident experts.
+//
+// This is the bounded routed-expert cache with loads on a miss of the SSD
+// streaming mode ("antirez-ds4" insight page, SSD streaming section; the
+// DwarfStar architecture article, "Memory trade-off: resident vs SSD
+// streaming" section), with host memory in the role of the disk and HBM in
+// the role of RAM.  The pages fix no eviction policy; least recently used,
+// ties to the lower slot, is the one taken here.
+#include "common.h"
+#include "launch.h"
+
+namespace ds4 {
+
+// Slots start empty (expert -1, stamp 0), counters at zero.
+__global__ __launch_bounds__(256) void k_cache_reset(CacheState c, int S, int E) {
+  if (threadIdx.x < sizeof(CacheHdr) / 4) reinterpret_cast<uint32_t *>(c.hdr)[threadIdx.x] = 0u;
+  for (int s = threadIdx.x; s < S; s += 256) {
+    c.slot_expert[s] = -1;
+    c.stamp[s] = 0u;
+  }
+  for (int e = threadIdx.x; e < E; e += 256) c.expert_slot[e] = -1;
+}
+
+// One workgroup.  Input: the batch's DecTile list (one tile per used expert,
+// ascending expert).  Hits take the current step as their stamp first, so no
+// expert of the batch is evicted; then each miss, in tile order, takes the
+// slot with the oldest stamp (ties: the lower slot), evicting its expert.
+// Output: the fill list (expert, slot) of the misses, counters, and every
+// tile's expert field replaced by its slot.
+__global__ __launch_bounds__(256) void k_cache_plan(CacheState c, DecTile *__restrict__ dt,
+                                                    const int32_t *__restrict__ ntile, int S, int E) {
+  __shared__ uint32_t st[256];
+  __shared__ int32_t se[256], es[256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = *ntile;
+  const uint32_t step = c.hdr->step + 1u;
+  for (int s = tid; s < 256; s += 256) {
+    st[s] = s < S ? c.stamp[s] : 0u;
+    se[s] = s < S ? c.slot_expert[s] : -1;
+  }
+  for (int e = tid; e < 256; e += 256) es[e] = e < E ? c.expert_slot[e] : -1;
+  __syncthreads();
+  if (tid < n) {  // distinct experts per tile: no two threads stamp one slot
+    const int s = es[dt[tid].e];
+    if (s >= 0) st[s] = step;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int nf = 0;
+    for (int i = 0; i < n; ++i) {
+      const int e = dt[i].e;  // uniform
+      if (es[e] >= 0) continue;
+      // victim: smallest (stamp, slot) among slots not used by this batch
+      uint64_t key = ~0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = lane + 64 * j;
+        if (s < S && st[s] != step) {
+          const uint64_t k = ((uint64_t)st[s] << 32) | (uint32_t)s;
+          key = k < key ? k : key;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint64_t k = __shfl_xor(key, o);
+        key = k < key ? k : key;
+      }
+      // a victim exists (S >= distinct experts of the batch, checked on the host)
+      if (key == ~0ull) break;
+      const int v = (int)(uint32_t)key;
+      if (lane == 0) {
+        const int old = se[v];
+        if (old >= 0) es[old] = -1;
+        se[v] = e;
+        es[e] = v;
+        st[v] = step;
+        c.fill_e[nf] = e;
+        c.fill_s[nf] = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      ++nf;
+    }
+    if (lane == 0) {
+      CacheHdr *h = c.hdr;
+      h->step = step;
+      h->fill_n = (uint32_t)nf;
+      h->calls += 1ull;
+      h->hits += (unsigned long long)(n - nf);
+      h->misses += (unsigned long long)nf;
+    }
+  }
+  __syncthreads();
+  if (tid < n) dt[tid].e = es[dt[tid].e];
+  for (int s = tid; s < S; s += 256) {
+    c.stamp[s] = st[s];
+    c.slot_expert[s] = se[s];
+  }
+  for (int e = tid; e < E; e += 256) c.expert_slot[e] = es[e];
+}
+
+// Copy the fill list's experts from host memory into their slots: workgroup
+// (item, chunk) moves CACHE_CHUNK bytes of the item's gate | up | down bytes
+// (16-byte words; every matrix is a multiple of 16 bytes).  Workgroups past
+// the list's length return at once.
+constexpr int CACHE_CHUNK = 65536;
+
+__global__ __launch_bounds__(256) void k_cache_fill(CacheState c, const uint8_t *__restrict__ hg,
+                                                    const uint8_t *__restrict__ hu, const uint8_t *__restrict__ hd,
+                                                    uint64_t gu_bytes, uint64_t d_bytes, int chunks) {
+  const int item = blockIdx.x / chunks;
+  const int chunk = blockIdx.x - item * chunks;
+  if (item >= (int)c.hdr->fill_n) return;  // uniform
+  const int e = c.fill_e[item], s = c.fill_s[item];
+  const uint64_t total = 2 * gu_bytes + d_bytes;
+  const uint64_t b0 = (uint64_t)chunk * CACHE_CHUNK;
+  constexpr int PER = CACHE_CHUNK / (256 * 16);  // 16-byte words per thread
+  u4 v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {  // all loads first: host reads have long latency
+    const uint64_t b = b0 + 16ull * (threadIdx.x + 256 * i);
+    if (b < total) {
+      const uint8_t *src = b < gu_bytes ? hg + (uint64_t)e * gu_bytes + b
+                           : b < 2 * gu_bytes ? hu + (uint64_t)e * gu_bytes + (b - gu_bytes)
+                                              : hd + (uint64_t)e * d_bytes + (b - 2 * gu_bytes);
+      v[i] = *reinterpret_cast<const u4 *>(src);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint64_t b = b0 + 16ull * (threadIdx.x + 256 * i);
+    if (b < total) {
+      uint8_t *dst = b < gu_bytes ? c.gate + (uint64_t)s * gu_bytes + b
+                     : b < 2 * gu_bytes ? c.up + (uint64_t)s * gu_bytes + (b - gu_bytes)
+                                        : c.down + (uint64_t)s * d_bytes + (b - 2 * gu_bytes);
+      *reinterpret_cast<u4 *>(dst) = v[i];
+    }
+  }
+}
+
+hipError_t launch_cache_reset(const CacheState &c, int S, int E, hipStream_t s) {
+  hipLaunchKernelGGL(k_cache_reset, dim3(1), dim3(256), 0, s, c, S, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_plan(const CacheState &c, DecTile *dt, const int32_t *ntile, int S, int E, hipStream_t s,
+                             const Timing *tm) {
+  DS4_LAUNCH(tm, k_cache_plan, dim3(1), dim3(256), 0, s, c, dt, ntile, S, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_fill(const CacheState &c, const void *hg, const void *hu, const void *hd, size_t gu_bytes,
+                             size_t d_bytes, int max_items, hipStream_t s, const Timing *tm) {
+  if (max_items <= 0) return hipSuccess;
+  const uint64_t total = 2 * (uint64_t)gu_bytes + d_bytes;
+  const int chunks = (int)((total + CACHE_CHUNK - 1) / CACHE_CHUNK);
+  DS4_LAUNCH(tm, k_cache_fill, dim3((unsigned)((int64_t)max_items * chunks)), dim3(256), 0, s, c,
+             (const uint8_t *)hg, (const uint8_t *)hu, (const uint8_t *)hd, (uint64_t)gu_bytes, (uint64_t)d_bytes,
+             chunks);
+  return hipGetLastError();
+}
+
+}  // namespace ds4

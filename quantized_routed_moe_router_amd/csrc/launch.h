@@ -83,6 +83,29 @@ struct GemmArgs {
   float *y;                          // [T,H]
 };
 
+// Routed-expert cache state (device memory, inside the caller's cache buffer).
+struct CacheHdr {
+  uint32_t step;                    // calls since the reset (the stamp of the current call)
+  uint32_t fill_n;                  // misses of the last call = length of the fill list
+  unsigned long long calls, hits, misses;
+};
+struct CacheState {
+  CacheHdr *hdr;
+  int32_t *slot_expert;             // [S] expert held by each slot, -1 = empty
+  int32_t *expert_slot;             // [E] slot of each expert, -1 = not cached
+  uint32_t *stamp;                  // [S] step of the slot's last use (0 = never)
+  int32_t *fill_e, *fill_s;         // [S] the last call's misses: expert, slot
+  uint8_t *gate, *up, *down;        // S slots of packed matrices each
+};
+
+hipError_t launch_cache_reset(const CacheState &c, int S, int E, hipStream_t s);
+// after the small-batch routing: plan slots, rewrite each DecTile's expert as its slot
+hipError_t launch_cache_plan(const CacheState &c, DecTile *dt, const int32_t *ntile, int S, int E, hipStream_t s,
+                             const Timing *tm = nullptr);
+// copy the planned misses from host memory (device-visible pointers) into their slots
+hipError_t launch_cache_fill(const CacheState &c, const void *hg, const void *hu, const void *hd, size_t gu_bytes,
+                             size_t d_bytes, int max_items, hipStream_t s, const Timing *tm = nullptr);
+
 hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, int bits,
                        hipStream_t s);
 hipError_t launch_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, int bits,

@@ -100,6 +100,15 @@ class DeviceLayer:
         fn(self.dims, w, x, T, y, r, ws, ws.numel(), stream)
         return y
 
+    def host_experts(self) -> tuple:
+        """Pinned host copies of the packed gate, up and down matrices."""
+        out = []
+        for t in (self.gate, self.up, self.down):
+            h = torch.empty(t.numel(), dtype=torch.uint8, pin_memory=True)
+            h.copy_(t)
+            out.append(h)
+        return tuple(out)
+
     def route(self, x: torch.Tensor, stream=None) -> dict:
         T = x.shape[0]
         bufs = self.routing_buffers(T)
@@ -120,3 +129,40 @@ def from_layer_inputs(L, device="cuda:0", experts: bool = True) -> DeviceLayer:
     if wl.Is:
         dl.set_shared(L.sh_gate, L.sh_up, L.sh_down)
     return dl
+
+
+class ExpertCache:
+    """A bounded routed-expert cache in device memory over experts kept in
+    pinned host memory (small batches).  `host`: (gate, up, down) pinned
+    uint8 tensors in the packed layout, by default copies of `dl`'s."""
+
+    def __init__(self, dl: DeviceLayer, n_slots: int, host: tuple | None = None, stream=None):
+        self.dl, self.n_slots = dl, n_slots
+        self.host = host if host is not None else dl.host_experts()
+        self.nbytes = B.ds4moe_cache_bytes(dl.dims, n_slots)
+        if self.nbytes == 0:
+            raise ValueError(f"invalid cache size: {n_slots} slots")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=dl.device)
+        self.reset(stream)
+
+    def reset(self, stream=None):
+        B.ds4moe_cache_reset(self.dl.dims, self.n_slots, self.buf, self.nbytes, stream)
+
+    def weights(self) -> B.Weights:
+        return self.dl.weights(*self.host)
+
+    def forward(self, x: torch.Tensor, y=None, routing: dict | None = None, stream=None, events=None,
+                weights: B.Weights | None = None) -> torch.Tensor:
+        dl = self.dl
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty(T, dl.H, dtype=torch.float32, device=dl.device)
+        ws = dl.workspace(T, B.MODE_DECODE)
+        r = B.make_routing(**routing) if routing is not None else None
+        w = weights if weights is not None else self.weights()
+        B.ds4moe_forward_decode_cached(dl.dims, w, self.n_slots, self.buf, self.nbytes, x, T, y, r, ws, ws.numel(),
+                                       events, stream)
+        return y
+
+    def stats(self, stream=None) -> tuple:
+        return B.ds4moe_cache_stats(self.dl.dims, self.n_slots, self.buf, self.nbytes, stream)

@@ -37,7 +37,7 @@ def test_single_hip_runtime_loaded():
 
 def test_version_and_status_strings():
     assert B.lib().ds4moe_version() >= 100
-    for s in range(8):
+    for s in range(9):
         assert B.status_str(s)
     assert B.status_str(99) == "unknown status"
 
@@ -171,3 +171,45 @@ def test_pack_dequant_argument_errors():
         assert L.ds4moe_dequant(v(16), v(16), 1 << 20, 4096, 4096, bits, None) == B.DS4MOE_ERR_SHAPE
     assert L.ds4moe_pack(v(16), v(16), 1, 16, 256, 3, None) == B.DS4MOE_ERR_SHAPE
     assert L.ds4moe_dequant(v(16), v(16), 1, 16, 256, 1, None) == B.DS4MOE_ERR_SHAPE
+
+
+def test_cache_bytes():
+    d = dims()
+    per_slot = 3 * q.ds4moe_packed_bytes(2048, 4096)
+    b = B.ds4moe_cache_bytes(d, 204)
+    assert 204 * per_slot < b < 204 * per_slot + 64 * 1024
+    for bad in (0, -1, 257):
+        assert B.ds4moe_cache_bytes(d, bad) == 0
+    assert B.ds4moe_cache_bytes(dims(E=64), 65) == 0
+    assert B.ds4moe_cache_bytes(dims(H=100), 8) == 0
+    b4 = B.ds4moe_cache_bytes(dims(bits=4), 8)
+    assert b4 > 8 * 3 * q.ds4moe_packed_bytes_bits(2048, 4096, 4)
+
+
+def test_cache_argument_errors():
+    L = B.lib()
+    v = ctypes.c_void_p
+    d = dims()
+    nb = B.ds4moe_cache_bytes(d, 16)
+    assert L.ds4moe_cache_reset(ctypes.byref(d), 16, None, nb, None) == B.DS4MOE_ERR_NULL
+    assert L.ds4moe_cache_reset(ctypes.byref(d), 16, v(128), nb, None) == B.DS4MOE_ERR_ALIGN
+    assert L.ds4moe_cache_reset(ctypes.byref(d), 16, v(256), nb - 1, None) == B.DS4MOE_ERR_WORKSPACE
+    assert L.ds4moe_cache_reset(ctypes.byref(d), 0, v(256), nb, None) == B.DS4MOE_ERR_SHAPE
+    assert L.ds4moe_cache_reset(ctypes.byref(d), 300, v(256), 1 << 40, None) == B.DS4MOE_ERR_SHAPE
+    assert L.ds4moe_cache_reset(ctypes.byref(dims(bits=3)), 16, v(256), nb, None) == B.DS4MOE_ERR_SHAPE
+    w = B.make_weights(16, 16, 16, 16)
+
+    def fwd(S=16, T=1, cache=256, cb=1 << 40, wt=w):
+        return L.ds4moe_forward_decode_cached(ctypes.byref(d), ctypes.byref(wt), S, v(cache), cb, v(16), T, v(16),
+                                              None, v(256), 1 << 40, None, None)
+    assert fwd(T=0) == B.DS4MOE_ERR_SHAPE
+    assert fwd(T=17) == B.DS4MOE_ERR_SHAPE
+    assert fwd(S=7, T=1) == B.DS4MOE_ERR_SHAPE           # fewer slots than the batch's k = 8 experts
+    assert fwd(S=16, T=3) == B.DS4MOE_ERR_SHAPE          # 24 experts may be used at once
+    assert fwd(cache=0) == B.DS4MOE_ERR_NULL
+    assert fwd(cb=100) == B.DS4MOE_ERR_WORKSPACE
+    assert fwd(wt=B.make_weights(16, None, 16, 16)) == B.DS4MOE_ERR_NULL
+    assert fwd(wt=B.make_weights(16, 24, 16, 16)) == B.DS4MOE_ERR_ALIGN
+    out = (ctypes.c_uint64 * 3)()
+    assert L.ds4moe_cache_stats(ctypes.byref(d), 16, v(256), nb, None, None) == B.DS4MOE_ERR_NULL
+    assert L.ds4moe_cache_stats(ctypes.byref(d), 16, None, nb, out, None) == B.DS4MOE_ERR_NULL
