@@ -246,8 +246,9 @@ int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_wei
  *
  * Bytes of the cache buffer for n_slots slots (1 <= n_slots <= E); 0 for
  * invalid dims or n_slots.  The pages size the cache as a byte budget or a
- * slot count; the automatic budget is 80 % of the working set without the
- * non-routed weights. */
+ * slot count, the automatic budget being 80 % of the working set without the
+ * non-routed weights (aitrends.kr "antirez/ds4" trending page, SSD-streaming
+ * bullet). */
 size_t ds4moe_cache_bytes(const ds4moe_dims *dims, int32_t n_slots);
 
 /* Empty every slot and zero the counters (one kernel on `stream`, no memset,
