@@ -50,6 +50,7 @@ namespace ds4 {
 #define DN_LDS_PD 4
 #endif
 
+
 // One lane's share of a packed unit.  Code plane p (1024 bytes at 1024*p)
 // holds dwords 4p..4p+3 of every lane, 16 bytes per lane, so each plane is one
 // fully coalesced load; dword S of a lane feeds MFMA step S with 4-bit codes,
@@ -461,6 +462,42 @@ __device__ __forceinline__ void pt_compute_sb(const UnitRegs<B> (&u)[R][NM], con
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt) acc[m][r][nt] = (f4){0.f, 0.f, 0.f, 0.f};
   const char *rowb = slot + r16 * (PT_CH * 16);
+  // mid(): 4-bit units, between steps 3 and 4 (see gemm_load_a_part)
+  auto mid = [&]() {
+    if constexpr (B == 4) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (sb_next >= 0) gemm_load_a_part<1, NM, R, B>(nxt, c, rts, sb_next, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if constexpr (NM == 2 && B == 2) {
+    // gate/up, 2-bit: the A fragments of step S+1 are dequantized before the
+    // MFMAs of step S (8 more registers; the other forms would spill)
+    h8 A[2][R][NM];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) A[0][r][m] = step_frag<0, B>(u[r][m], dc[r][m]);
+#define PT_STEP(S)                                                                            \
+  {                                                                                           \
+    h8 b[NTV];                                                                                \
+    _Pragma("unroll") for (int nt = 0; nt < NTV; ++nt) b[nt] =                                \
+        *reinterpret_cast<const h8 *>(rowb + (16 * nt * PT_CH + step_chunk<S>(g)) * 16);       \
+    if constexpr (S < 7) {                                                                    \
+      _Pragma("unroll") for (int r = 0; r < R; ++r)                                           \
+        _Pragma("unroll") for (int m = 0; m < NM; ++m)                                        \
+          A[(S + 1) & 1][r][m] = step_frag<(S < 7 ? S + 1 : 7), B>(u[r][m], dc[r][m]);         \
+    }                                                                                         \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) {                                           \
+      _Pragma("unroll") for (int m = 0; m < NM; ++m) {                                        \
+        _Pragma("unroll") for (int nt = 0; nt < NTV; ++nt) acc[m][r][nt] =                    \
+            mfma16(A[S & 1][r][m], b[nt], acc[m][r][nt]);                                     \
+      }                                                                                       \
+    }                                                                                         \
+  }
+    PT_STEP(0) PT_STEP(1) PT_STEP(2) PT_STEP(3) PT_STEP(4) PT_STEP(5) PT_STEP(6) PT_STEP(7)
+#undef PT_STEP
+  } else {
 #define PT_STEP(S)                                                                            \
   {                                                                                           \
     h8 b[NTV];                                                                                \
@@ -474,14 +511,11 @@ __device__ __forceinline__ void pt_compute_sb(const UnitRegs<B> (&u)[R][NM], con
       }                                                                                       \
     }                                                                                         \
   }
-  PT_STEP(0) PT_STEP(1) PT_STEP(2) PT_STEP(3)
-  if constexpr (B == 4) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (sb_next >= 0) gemm_load_a_part<1, NM, R, B>(nxt, c, rts, sb_next, lane);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  PT_STEP(4) PT_STEP(5) PT_STEP(6) PT_STEP(7)
+    PT_STEP(0) PT_STEP(1) PT_STEP(2) PT_STEP(3)
+    mid();
+    PT_STEP(4) PT_STEP(5) PT_STEP(6) PT_STEP(7)
 #undef PT_STEP
+  }
   h8 bm[NTV];
 #pragma unroll
   for (int nt = 0; nt < NTV; ++nt) bm[nt] = *reinterpret_cast<const h8 *>(rowb + (16 * nt * PT_CH + 32 + g) * 16);
@@ -498,6 +532,8 @@ __device__ __forceinline__ void pt_compute_sb(const UnitRegs<B> (&u)[R][NM], con
           y[m][r][nt][q] = fmaf(-dd_dmin(dc[r][m].dd[q]), mm[q], y[m][r][nt][q]);
         }
       }
+  // let the scheduler interleave the LDS fragment reads with the MFMAs
+  if constexpr (NM == 2 && B == 2) __builtin_amdgcn_iglp_opt(0);
 }
 
 template <int NM, int R, int NTV, int B>
