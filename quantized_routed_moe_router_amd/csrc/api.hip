@@ -35,7 +35,7 @@ int validate_dims(const ds4moe_dims *d) {
 }
 
 struct Layout {
-  size_t logits, part, idx, w, counts, offsets, perm, pos, tiles, ntiles, ccnt, cbase, lrank;
+  size_t logits, part, idx, w, counts, offsets, perm, pos, tiles, ntiles, ccnt, cbase, lrank, dpart;
   size_t x16, xs_hi, xs_lo, h, hs_hi, hs_lo, yp, hsh, ysh, zeros;
   int nzeros;
   size_t total;
@@ -92,6 +92,7 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
     L.hs_lo = take(2 * hrows * (L.Ipad / 16));
     if (mode == DS4MOE_MODE_DECODE) {
       L.tiles = take(sizeof(DecTile) * (size_t)L.max_tiles);
+      if (T > 4) L.dpart = take(sizeof(float) * 2 * T * H);
     } else {
       L.tiles = take(sizeof(TileT) * (size_t)L.max_tiles);
       L.pos = take(sizeof(int32_t) * A);
@@ -328,6 +329,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.o_hs_lo = (uint32_t)L.hs_lo;
   ga.T = T;
   ga.tile_n = L.tile_n;
+  ga.dpart = (dec && T > 4) ? at<float>(ws, L.dpart) : nullptr;
   ga.y = y;
 
   float *ysh = nullptr;
@@ -346,7 +348,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     st = shared();
     if (st) return st;
     ga.ysh = ysh;
-    TRY(launch_down_combine_dec(ga, s, tm(SL_DOWN)));
+    TRY(launch_down_combine_dec(ga, s, tm(SL_DOWN), T > 4 ? tm(SL_COMBINE) : nullptr));
   } else {
     TRY(launch_gateup(ga, L.max_tiles, s, tm(SL_GATEUP)));
     TRY(launch_down(ga, L.max_tiles, s, tm(SL_DOWN)));

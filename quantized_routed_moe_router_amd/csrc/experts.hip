@@ -37,9 +37,6 @@ namespace ds4 {
 #ifndef GEMM_NW_DN
 #define GEMM_NW_DN 4
 #endif
-#ifndef GU_DEC_PD
-#define GU_DEC_PD 2
-#endif
 #ifndef DN_DEC_PD
 #define DN_DEC_PD 3
 #endif
@@ -48,6 +45,12 @@ namespace ds4 {
 #endif
 #ifndef DN_LDS_PD
 #define DN_LDS_PD 4
+#endif
+#ifndef GU_SH_PD
+#define GU_SH_PD 4
+#endif
+#ifndef DN2_PD
+#define DN2_PD 2
 #endif
 
 
@@ -710,120 +713,9 @@ __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAc
 // expert through a PD-deep register pipeline: the loads of reduction step
 // i+PD are in flight while step i is dequantized and multiplied.
 
-// gate/up + SwiGLU.  Workgroup = one tile x two 16-row tiles; wave = (row
-// tile, half of the reduction); the halves meet in LDS (lower half first).
-template <int PD, int B>
-__global__ __launch_bounds__(256) void k_gateup_dec(GemmArgs a, int n_rt) {
-  const int nrb = (n_rt + 1) >> 1;
-  const int tile_id = blockIdx.x / nrb;
-  const int rb = blockIdx.x - tile_id * nrb;
-  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r16 = lane & 15, g = lane >> 4;
-  const int rt = 2 * rb + (wave >> 1), kh = wave & 1;
-  const int e = a.dtiles[tile_id].e;
-  const uint32_t tmask = a.dtiles[tile_id].tmask;
-  const bool valid = (tmask >> r16) & 1u;  // implies r16 < T
-  const int nsb = a.H >> 8;
-  const int half = (nsb + 1) >> 1;
-  const int sb0 = kh * half;
-  const int nit = max(0, min(nsb, sb0 + half) - sb0);
-  const uint32_t gub = (uint32_t)a.gu_bytes;
-  const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gate + (size_t)e * a.gu_bytes, gub);
-  const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.up + (size_t)e * a.gu_bytes, gub);
-  const uint32_t roff = ((uint32_t)min(rt, n_rt - 1) * nsb + sb0) * Unit<B>::BYTES;
-  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
-  // byte offsets of this lane's activations (out of range: zeros)
-  const uint32_t xoff =
-      valid ? a.o_x16 + 2u * ((uint32_t)r16 * a.H + (uint32_t)sb0 * 256 + 16 * g) : DS4_OOB;
-  const uint32_t xsoff =
-      valid ? ((g >> 1) ? a.o_xs_lo : a.o_xs_hi) + 2u * ((uint32_t)r16 * (a.H >> 4) + 8 * (g & 1) + sb0 * 16)
-            : DS4_OOB;
-
-  struct Stage {
-    UnitRegs<B> wg, wu;
-    h8 b[9];
-  };
-  Stage st[PD];
-  f4 yg = (f4){0.f, 0.f, 0.f, 0.f}, yu = yg;
-  // every step issues the same loads (steps past the end read zeros), so the
-  // load counter waits are static and the pipeline never drains
-  auto load = [&](Stage &sg, int i) {
-    const bool in = i < nit;
-    const uint32_t wo = in ? roff + (uint32_t)i * Unit<B>::BYTES : DS4_OOB;
-    sg.wg = load_unit_buf<B>(gr, wo, lane);
-    sg.wu = load_unit_buf<B>(ur, wo, lane);
-    const uint32_t xo = in ? xoff + 512u * i : DS4_OOB;
-    const uint32_t so = in ? xsoff + 32u * i : DS4_OOB;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) sg.b[q] = buf_load_h8(ws, xo + 2u * (64 * (q >> 1) + 8 * (q & 1)));
-    sg.b[8] = buf_load_h8(ws, so);
-  };
-  auto compute = [&](const Stage &sg) {
-    const UnitDecoded dg = decode_unit(sg.wg, g);
-    const UnitDecoded du = decode_unit(sg.wu, g);
-    f4 ag = (f4){0.f, 0.f, 0.f, 0.f}, au = ag;
-#define DEC_STEP(S)                                    \
-  ag = mfma16(step_frag<S, B>(sg.wg, dg), sg.b[S], ag);   \
-  au = mfma16(step_frag<S, B>(sg.wu, du), sg.b[S], au);
-    DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
-#undef DEC_STEP
-    const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
-    const f4 mg = mfma16(dg.mfrag, sg.b[8], z);
-    const f4 mu = mfma16(du.mfrag, sg.b[8], z);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      yg[q] = fmaf(dd_d(dg.dd[q]), ag[q], yg[q]);
-      yg[q] = fmaf(-dd_dmin(dg.dd[q]), mg[q], yg[q]);
-      yu[q] = fmaf(dd_d(du.dd[q]), au[q], yu[q]);
-      yu[q] = fmaf(-dd_dmin(du.dd[q]), mu[q], yu[q]);
-    }
-  };
-#pragma unroll
-  for (int sgi = 0; sgi < PD; ++sgi) load(st[sgi], sgi);
-  for (int i0 = 0; i0 < nit; i0 += PD) {
-#pragma unroll
-    for (int sgi = 0; sgi < PD; ++sgi) {
-      compute(st[sgi]);
-      load(st[sgi], i0 + sgi + PD);
-    }
-  }
-
-  __shared__ f4 red[2][2][64];  // [row tile of the workgroup][gate, up]
-  const int rl = wave >> 1;
-  if (kh == 1) {
-    red[rl][0][lane] = yg;
-    red[rl][1][lane] = yu;
-  }
-  __syncthreads();
-  if (kh == 1 || rt >= n_rt) return;  // uniform per wave
-  const f4 pg = red[rl][0][lane], pu = red[rl][1][lane];
-  half_t hv[4];
-  float ssum = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float gv = yg[q] + pg[q], uv = yu[q] + pu[q];
-    hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
-    ssum += (float)hv[q];
-  }
-  ssum += __shfl_xor(ssum, 16);
-  ssum += __shfl_xor(ssum, 32);
-  if (r16 < a.T) {  // tokens that did not choose the expert get exact zeros
-    const size_t p = (size_t)tile_id * a.T + r16;
-    uint2 pk;
-    __builtin_memcpy(&pk, hv, 8);
-    *reinterpret_cast<uint2 *>(a.h + p * a.Ipad + rt * 16 + 4 * g) = pk;
-    if (g == 0) {
-      const int nj = a.Ipad >> 4;
-      const half_t hi = (half_t)ssum;
-      a.hs_hi[p * nj + rt] = hi;
-      a.hs_lo[p * nj + rt] = (half_t)(ssum - (float)hi);
-    }
-  }
-}
-
-// down fused with the combine.  Workgroup = one 16-row tile of y, 8 waves;
-// wave w takes tiles w, w+8, ... (experts ascending), scales each tile's
+// down fused with the combine, for an intermediate size below 256 (columns
+// past I read as zeros).  Workgroup = one 16-row tile of y, 8 waves; wave w
+// takes tiles w, w+8, ... (experts ascending), scales each tile's
 // contribution to token t by the token's routing weight, and the eight
 // partial sums are added in wave order, then the shared-expert output.
 template <int PD, bool PADDED, int B>
@@ -1232,6 +1124,268 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ small batches, 5 <= T <= 16
+// The activations of one reduction step (x or h of the 16 token slots, 37
+// chunks of 16 bytes each: 592 chunks) are shared by the waves of a
+// workgroup: they come in once per workgroup by direct-to-LDS buffer loads
+// split across the waves into a PD-slot ring, with one barrier per step.
+// After that barrier every wave's loads of the step have landed (each wave
+// waits for its own first) and every wave has finished reading the slot the
+// step's prefetch then refills.  A wave issues 2-3 activation loads per step
+// instead of 9, which is what bounds these kernels at T = 16.
+constexpr int SH_NT = 16;            // token slots
+constexpr int SH_CH = SH_NT * XCH;   // chunks per step
+
+template <int NW>
+struct ShRing {
+  static constexpr int NI = (SH_CH + 64 * NW - 1) / (64 * NW);  // load instructions per wave per step
+  static constexpr int SLOT = NI * NW * 1024;                   // bytes per slot
+};
+
+// gate/up + SwiGLU: workgroup = one tile x four 16-row tiles, the whole
+// reduction per wave.
+template <int PD, int B>
+__global__ __launch_bounds__(256) void k_gateup_dec_sh(GemmArgs a, int n_rt) {
+  constexpr int NW = 4, NI = ShRing<NW>::NI, SLOT = ShRing<NW>::SLOT;
+  static_assert(PD >= 2, "ring depth");
+  __shared__ __attribute__((aligned(16))) char ring[PD * SLOT];
+  const int nrb = (n_rt + NW - 1) / NW;
+  const int tile_id = blockIdx.x / nrb;
+  const int rb = blockIdx.x - tile_id * nrb;
+  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int e = a.dtiles[tile_id].e;
+  const uint32_t tmask = a.dtiles[tile_id].tmask;
+  const int rt = NW * rb + wave;
+  const int nsb = a.H >> 8;
+  const uint32_t gub = (uint32_t)a.gu_bytes;
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gate + (size_t)e * a.gu_bytes, gub);
+  const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.up + (size_t)e * a.gu_bytes, gub);
+  const uint32_t roff = (uint32_t)min(rt, n_rt - 1) * nsb * Unit<B>::BYTES;
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
+  // chunk u = 64*(NW*q + wave) + lane of a slot: token u / XCH, chunk u % XCH
+  uint32_t src[NI], inc[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int u = 64 * (NW * q + wave) + lane;
+    const int t = u / XCH, c = u - t * XCH;
+    src[q] = DS4_OOB;
+    inc[q] = 0;
+    if (t < SH_NT && c < 36 && ((tmask >> t) & 1u)) {  // tmask bits only below T
+      if (c < 32) {
+        src[q] = a.o_x16 + 2u * ((uint32_t)t * a.H + 8 * c);
+        inc[q] = 512;
+      } else {
+        const int cc = c - 32;
+        src[q] = ((cc >> 1) ? a.o_xs_lo : a.o_xs_hi) + 2u * ((uint32_t)t * (a.H >> 4) + 8 * (cc & 1));
+        inc[q] = 32;
+      }
+    }
+  }
+  const uint32_t brow = (uint32_t)r16 * (XCH * 16);  // B fragment of lane (r16, g): token slot r16
+
+  struct Stage {
+    UnitRegs<B> wg, wu;
+  };
+  Stage st[PD];
+  f4 yg = (f4){0.f, 0.f, 0.f, 0.f}, yu = yg;
+  auto load = [&](Stage &sg, int slot, int i) {
+    const bool in = i < nsb;
+#pragma unroll
+    for (int q = 0; q < NI; ++q)
+      buf_load_lds16(ws, ring + slot * SLOT + 1024 * (NW * q + wave), in ? src[q] + inc[q] * (uint32_t)i : DS4_OOB);
+    const uint32_t wo = in ? roff + (uint32_t)i * Unit<B>::BYTES : DS4_OOB;
+    sg.wg = load_unit_buf<B>(gr, wo, lane);
+    sg.wu = load_unit_buf<B>(ur, wo, lane);
+  };
+  auto compute = [&](const Stage &sg, int slot) {
+    const char *base = ring + slot * SLOT + brow;
+    h8 b[9];
+#pragma unroll
+    for (int S = 0; S < 8; ++S)
+      b[S] = *reinterpret_cast<const h8 *>(base + 16 * (2 * (4 * (S >> 1) + g) + (S & 1)));
+    b[8] = *reinterpret_cast<const h8 *>(base + 16 * (32 + 2 * (g >> 1) + (g & 1)));
+    const UnitDecoded dg = decode_unit(sg.wg, g);
+    const UnitDecoded du = decode_unit(sg.wu, g);
+    f4 ag = (f4){0.f, 0.f, 0.f, 0.f}, au = ag;
+#define DEC_STEP(S)                                  \
+  ag = mfma16(step_frag<S, B>(sg.wg, dg), b[S], ag); \
+  au = mfma16(step_frag<S, B>(sg.wu, du), b[S], au);
+    DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
+#undef DEC_STEP
+    const f4 z = (f4){0.f, 0.f, 0.f, 0.f};
+    const f4 mg = mfma16(dg.mfrag, b[8], z);
+    const f4 mu = mfma16(du.mfrag, b[8], z);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      yg[q] = fmaf(dd_d(dg.dd[q]), ag[q], yg[q]);
+      yg[q] = fmaf(-dd_dmin(dg.dd[q]), mg[q], yg[q]);
+      yu[q] = fmaf(dd_d(du.dd[q]), au[q], yu[q]);
+      yu[q] = fmaf(-dd_dmin(du.dd[q]), mu[q], yu[q]);
+    }
+  };
+  // steps past the end load out of range (zeros): every step issues the same
+  // loads, so the waits are static
+#pragma unroll
+  for (int sgi = 0; sgi < PD - 1; ++sgi) load(st[sgi], sgi, sgi);
+  for (int i0 = 0; i0 < nsb; i0 += PD) {
+#pragma unroll
+    for (int sgi = 0; sgi < PD; ++sgi) {
+      wait_vm<(PD - 2) * (NI + 2 * Unit<B>::LOADS)>();  // this wave's loads of step i0+sgi have landed
+      __syncthreads();                                  // ... and every wave's; slot sgi-1 is free
+      load(st[(sgi + PD - 1) % PD], (sgi + PD - 1) % PD, i0 + sgi + PD - 1);
+      compute(st[sgi], sgi);
+    }
+  }
+  wait_vm<0>();  // the trailing out-of-range loads, before the workgroup's LDS is released
+  if (rt >= n_rt) return;
+  half_t hv[4];
+  float ssum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float gv = yg[q], uv = yu[q];
+    hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+    ssum += (float)hv[q];
+  }
+  ssum += __shfl_xor(ssum, 16);
+  ssum += __shfl_xor(ssum, 32);
+  if (r16 < a.T) {  // tokens that did not choose the expert get exact zeros
+    const size_t p = (size_t)tile_id * a.T + r16;
+    uint2 pk;
+    __builtin_memcpy(&pk, hv, 8);
+    *reinterpret_cast<uint2 *>(a.h + p * a.Ipad + rt * 16 + 4 * g) = pk;
+    if (g == 0) {
+      const int nj = a.Ipad >> 4;
+      const half_t hi = (half_t)ssum;
+      a.hs_hi[p * nj + rt] = hi;
+      a.hs_lo[p * nj + rt] = (half_t)(ssum - (float)hi);
+    }
+  }
+}
+
+// down for 5 <= T <= 16 (I a multiple of 256): workgroup = two 16-row tiles
+// of y, both taken by every wave, so that one set of activation loads feeds
+// two units; 8 waves, and the tile list split over two workgroups
+// (blockIdx.y): tile j goes to half j % 2 and wave (j / 2) % 8, experts
+// ascending within a wave.  Each workgroup adds its waves' partial sums in
+// wave order and writes its half's partial; k_down_reduce adds the two halves
+// in order, then the shared-expert output.
+template <int PD, int B>
+__global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
+  const int rt0 = 2 * blockIdx.x, half = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int ntl = *a.ntiles;
+  const int nsb = a.Ipad >> 8;
+  const int nj = a.Ipad >> 4;
+  const int j0 = half + 2 * wave;                          // this wave's first tile
+  const int mt = j0 < ntl ? (ntl - j0 + 15) >> 4 : 0;      // its tiles j0, j0 + 16, ... (<= 16)
+  const int nit = mt * nsb;
+  int e_l = 0;        // lane L: expert of this wave's L-th tile
+  uint32_t m_l = 0u;  // ... and its token mask
+  if (lane < mt) {
+    e_l = a.dtiles[j0 + 16 * lane].e;
+    m_l = a.dtiles[j0 + 16 * lane].tmask;
+  }
+  // wait for them here, before any weight load is in flight, so that the
+  // pipelined loop below never has to drain the load counter for them
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
+  const uint32_t hs_base = ((g >> 1) ? a.o_hs_lo : a.o_hs_hi) + 2u * (8 * (g & 1));
+  const uint32_t ustride = (uint32_t)nsb * Unit<B>::BYTES;  // bytes per row tile
+
+  struct Stage {
+    UnitRegs<B> wd[2];
+    h8 b[9];
+    float wt;
+  };
+  Stage st[PD];
+  f4 y[2] = {(f4){0.f, 0.f, 0.f, 0.f}, (f4){0.f, 0.f, 0.f, 0.f}};
+  int lt = 0, lsb = 0;  // tile and super-block of the next load
+  auto load = [&](Stage &sg) {
+    const bool in = lt < mt;
+    const int tile = min(j0 + 16 * lt, ntl - 1);
+    const int e = __builtin_amdgcn_readlane(e_l, lt & 63);
+    const uint32_t tmask = in ? (uint32_t)__builtin_amdgcn_readlane((int)m_l, lt & 63) : 0u;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.down + (size_t)e * a.d_bytes, (uint32_t)a.d_bytes);
+    const uint32_t wo = in ? (uint32_t)rt0 * ustride + (uint32_t)lsb * Unit<B>::BYTES : DS4_OOB;
+    sg.wd[0] = load_unit_buf<B>(wr, wo, lane);
+    sg.wd[1] = load_unit_buf<B>(wr, in ? wo + ustride : DS4_OOB, lane);
+    // h of token r16 if it chose the expert (zeros otherwise, weight 0)
+    const bool routed = (tmask >> r16) & 1u;  // implies r16 < T
+    const uint32_t p = (uint32_t)tile * a.T + r16;
+    const uint32_t hoff = routed ? a.o_h + 2u * (p * a.Ipad + lsb * 256 + 16 * g) : DS4_OOB;
+    const uint32_t soff = routed ? hs_base + 2u * (p * nj + lsb * 16) : DS4_OOB;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sg.b[q] = buf_load_h8(ws, hoff + 2u * (64 * (q >> 1) + 8 * (q & 1)));
+    sg.b[8] = buf_load_h8(ws, soff);
+    sg.wt = a.dtiles[tile].w[r16];  // 0 for tokens that did not choose the expert
+    if (++lsb == nsb) {
+      lsb = 0;
+      ++lt;
+    }
+  };
+  auto compute = [&](const Stage &sg) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const UnitDecoded dd = decode_unit(sg.wd[r], g);
+      f4 ac = (f4){0.f, 0.f, 0.f, 0.f};
+#define DEC_STEP(S) ac = mfma16(step_frag<S, B>(sg.wd[r], dd), sg.b[S], ac);
+      DEC_STEP(0) DEC_STEP(1) DEC_STEP(2) DEC_STEP(3) DEC_STEP(4) DEC_STEP(5) DEC_STEP(6) DEC_STEP(7)
+#undef DEC_STEP
+      const f4 mm = mfma16(dd.mfrag, sg.b[8], (f4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v = fmaf(dd_d(dd.dd[q]), ac[q], -dd_dmin(dd.dd[q]) * mm[q]);
+        y[r][q] = fmaf(sg.wt, v, y[r][q]);
+      }
+    }
+  };
+#pragma unroll
+  for (int sgi = 0; sgi < PD; ++sgi) load(st[sgi]);
+  for (int i0 = 0; i0 < nit; i0 += PD) {
+#pragma unroll
+    for (int sgi = 0; sgi < PD; ++sgi) {
+      compute(st[sgi]);
+      load(st[sgi]);
+    }
+  }
+  __shared__ f4 red[8][2][64];
+  red[wave][0][lane] = y[0];
+  red[wave][1][lane] = y[1];
+  __syncthreads();
+  if (wave >= 2) return;
+  // wave r adds the 8 waves' sums of row tile rt0 + r in wave order
+  f4 acc = red[0][wave][lane];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) {
+    const f4 v = red[w][wave][lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] += v[q];
+  }
+  if (r16 < a.T)
+    *reinterpret_cast<f4 *>(a.dpart + ((size_t)half * a.T + r16) * a.H + (rt0 + wave) * 16 + 4 * g) = acc;
+}
+
+// y = partial of half 0 + partial of half 1 (+ shared-expert output)
+__global__ __launch_bounds__(256) void k_down_reduce(const float *__restrict__ part, const float *__restrict__ ysh,
+                                                     float *__restrict__ y, int T, int H) {
+  const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (i >= T * H) return;
+  const f4 p0 = *reinterpret_cast<const f4 *>(part + i);
+  const f4 p1 = *reinterpret_cast<const f4 *>(part + (size_t)T * H + i);
+  f4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = p0[q] + p1[q];
+  if (ysh) {
+    const f4 sv = *reinterpret_cast<const f4 *>(ysh + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += sv[q];
+  }
+  *reinterpret_cast<f4 *>(y + i) = v;
+}
+
 // ------------------------------------------------------------------ combine
 // y[t] = sum_j w[t,j] * Yp[pos(t,j)] in rank order, then + shared output.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ yp, const int32_t *__restrict__ pos,
@@ -1580,14 +1734,18 @@ template <int B>
 static hipError_t gateup_dec_b(const GemmArgs &a, int max_tiles, const DecRoute *rr, hipStream_t s,
                                const Timing *tm) {
   const int n_rt = a.I >> 4;
+  if (a.T > 4) {  // activations shared by the workgroup's four row tiles
+    const dim3 grid((unsigned)((int64_t)((n_rt + 3) >> 2) * max_tiles));
+    DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, B>), grid, dim3(256), 0, s, a, n_rt);
+    return hipGetLastError();
+  }
   const int nrb = (n_rt + 1) >> 1;
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
   switch (a.T) {
     case 1: gateup_dec_lds<1, B>(a, n_rt, rr, grid, s, tm); break;
     case 2: gateup_dec_lds<2, B>(a, n_rt, rr, grid, s, tm); break;
     case 3: gateup_dec_lds<3, B>(a, n_rt, rr, grid, s, tm); break;
-    case 4: gateup_dec_lds<4, B>(a, n_rt, rr, grid, s, tm); break;
-    default: DS4_LAUNCH(tm, (k_gateup_dec<GU_DEC_PD, B>), grid, dim3(256), 0, s, a, n_rt);
+    default: gateup_dec_lds<4, B>(a, n_rt, rr, grid, s, tm); break;
   }
   return hipGetLastError();
 }
@@ -1600,7 +1758,7 @@ hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, const DecRoute *r
 }
 
 template <int B>
-static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Timing *tm) {
+static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Timing *tm, const Timing *tm_combine) {
   const dim3 grid((unsigned)(a.H >> 4));
   if (a.I == a.Ipad && a.T <= 4) {
     switch (a.T) {
@@ -1611,15 +1769,21 @@ static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Tim
     }
     return hipGetLastError();
   }
-  if (a.I == a.Ipad)
-    DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, false, B>), grid, dim3(512), 0, s, a);
-  else
-    DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, true, B>), grid, dim3(512), 0, s, a);
+  if (a.I == a.Ipad && a.dpart) {  // two row tiles per wave, the tiles in two halves
+    DS4_LAUNCH(tm, (k_down_dec2<DN2_PD, B>), dim3((unsigned)(a.H >> 5), 2), dim3(512), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    DS4_LAUNCH(tm_combine, k_down_reduce, dim3((unsigned)((a.T * a.H / 4 + 255) / 256)), dim3(256), 0, s, a.dpart,
+               a.ysh, a.y, a.T, a.H);
+    return hipGetLastError();
+  }
+  // I below 256 (padded reduction)
+  DS4_LAUNCH(tm, (k_down_dec<DN_DEC_PD, true, B>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm) {
-  return a.bits == 4 ? down_combine_dec_b<4>(a, s, tm) : down_combine_dec_b<2>(a, s, tm);
+hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm, const Timing *tm_combine) {
+  return a.bits == 4 ? down_combine_dec_b<4>(a, s, tm, tm_combine) : down_combine_dec_b<2>(a, s, tm, tm_combine);
 }
 
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,

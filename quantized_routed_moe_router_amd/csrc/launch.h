@@ -79,6 +79,9 @@ struct GemmArgs {
   const DecTile *dtiles;
   int T;
   int tile_n;                        // tokens per prefill tile (> 64: wide-tile GEMMs)
+  // small batches of 5..16 tokens: the down projection's partial outputs
+  // of the two halves of the tile list [2][T][H]
+  float *dpart;
   const float *ysh;                  // [T,H] shared-expert output or nullptr
   float *y;                          // [T,H]
 };
@@ -152,7 +155,8 @@ struct DecRoute {
 // (writes y)
 hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, const DecRoute *rr, hipStream_t s,
                              const Timing *tm = nullptr);
-hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm = nullptr,
+                                   const Timing *tm_combine = nullptr);
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,
                           int k, int H, hipStream_t s, const Timing *tm = nullptr);
 // dense shared expert, bf16 weights
