@@ -61,7 +61,7 @@ def source_hash() -> str:
 def roofline_kernel(mode_decode: bool, T: int) -> str:
     if not mode_decode:
         return "k_moe_gemm_wide"
-    return "k_gateup_dec_lds" if T <= 4 else "k_gateup_dec"
+    return "k_gateup_dec_lds" if T <= 4 else "k_gateup_dec_sh"
 
 
 def measured_traffic(kernel: str, workload: str):

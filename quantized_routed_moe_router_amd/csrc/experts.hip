@@ -49,6 +49,9 @@ namespace ds4 {
 #ifndef GU_SH_PD
 #define GU_SH_PD 4
 #endif
+#ifndef GU_SH_NW
+#define GU_SH_NW 4
+#endif
 #ifndef DN2_PD
 #define DN2_PD 2
 #endif
@@ -1142,11 +1145,11 @@ struct ShRing {
   static constexpr int SLOT = NI * NW * 1024;                   // bytes per slot
 };
 
-// gate/up + SwiGLU: workgroup = one tile x four 16-row tiles, the whole
+// gate/up + SwiGLU: workgroup = one tile x NW 16-row tiles, the whole
 // reduction per wave.
-template <int PD, int B>
-__global__ __launch_bounds__(256) void k_gateup_dec_sh(GemmArgs a, int n_rt) {
-  constexpr int NW = 4, NI = ShRing<NW>::NI, SLOT = ShRing<NW>::SLOT;
+template <int PD, int NW, int B>
+__global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt) {
+  constexpr int NI = ShRing<NW>::NI, SLOT = ShRing<NW>::SLOT;
   static_assert(PD >= 2, "ring depth");
   __shared__ __attribute__((aligned(16))) char ring[PD * SLOT];
   const int nrb = (n_rt + NW - 1) / NW;
@@ -1734,9 +1737,10 @@ template <int B>
 static hipError_t gateup_dec_b(const GemmArgs &a, int max_tiles, const DecRoute *rr, hipStream_t s,
                                const Timing *tm) {
   const int n_rt = a.I >> 4;
-  if (a.T > 4) {  // activations shared by the workgroup's four row tiles
-    const dim3 grid((unsigned)((int64_t)((n_rt + 3) >> 2) * max_tiles));
-    DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, B>), grid, dim3(256), 0, s, a, n_rt);
+  if (a.T > 4) {  // activations shared by the workgroup's row tiles
+    constexpr int NW = GU_SH_NW;
+    const dim3 grid((unsigned)((int64_t)((n_rt + NW - 1) / NW) * max_tiles));
+    DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, NW, B>), grid, dim3(64 * NW), 0, s, a, n_rt);
     return hipGetLastError();
   }
   const int nrb = (n_rt + 1) >> 1;
