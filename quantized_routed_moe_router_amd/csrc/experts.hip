@@ -863,6 +863,13 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
   if constexpr (ROUTE) {
     static_assert(sizeof(RouteLds<4>) <= sizeof(ring_lds), "routing LDS must fit in the ring");
     RouteLds<4> &L = *reinterpret_cast<RouteLds<4> *>(ring_lds);
+    if (NT == 1) {
+      if (tile_id >= rr.k) return;  // uniform over the workgroup
+      e = route_one_token<256>(L, rr.part, rr.nslice, rr.bias, rr.logits, rr.E, rr.k, rr.ro, rr.dt, rr.ntile,
+                               blockIdx.x == 0, tile_id);
+      tmask = 1u;
+      __syncthreads();  // every wave has read the routing before the ring is filled
+    } else {
     route_small_block<256, 4>(L, rr.part, rr.nslice, rr.bias, rr.logits, a.T, rr.E, rr.k, rr.ro, rr.dt, rr.ntile,
                               blockIdx.x == 0);
     if (tile_id >= L.ntile) return;  // uniform over the workgroup
@@ -878,6 +885,7 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
     e = sel;
     tmask = L.tm[e];
     __syncthreads();  // every wave has read the routing before the ring is filled
+    }
   } else {
     if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
     e = a.dtiles[tile_id].e;

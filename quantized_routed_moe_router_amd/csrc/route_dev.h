@@ -273,4 +273,75 @@ __device__ __forceinline__ void route_small_block(RouteLds<MAXT> &L, const doubl
   }
 }
 
+// The same for one token (T = 1), with less machinery: every selected expert
+// takes one assignment, so the k selected experts, ascending, are the tiles,
+// each expert's count is 0 or 1 and its offset is the number of selected
+// experts below it.  Returns the expert of tile `tile` (< k) to every thread.
+template <int NTH>
+__device__ __forceinline__ int route_one_token(RouteLds<4> &L, const double *__restrict__ part, int nslice,
+                                               const float *__restrict__ bias, float *__restrict__ logits, int E,
+                                               int k, const RouteOut &ro, DecTile *__restrict__ dt,
+                                               int32_t *__restrict__ ntile, bool out, int tile) {
+  static_assert(NTH >= 256 && NTH % 64 == 0, "one thread per expert");
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < E) {
+    double v = 0.0;
+    for (int s0 = 0; s0 < nslice; s0 += 4) {  // the slices in order, four loads in flight
+      double pv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pv[u] = s0 + u < nslice ? part[(int64_t)(s0 + u) * E + tid] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (s0 + u < nslice) v += pv[u];
+    }
+    if (bias) v += (double)bias[tid];
+    const float l = (float)v;
+    L.lg[tid] = l;
+    if (out) logits[tid] = l;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int my_e;
+    float my_w;
+    topk_wave(L.lg, E, k, my_e, my_w, L.sel[0]);
+    int asc = 0;  // selected experts below this lane's (distinct experts)
+    for (int j = 0; j < k; ++j) asc += __builtin_amdgcn_readlane(my_e, j) < my_e ? 1 : 0;
+    if (lane < k) {
+      L.tb[asc] = my_e;  // tile asc -> expert
+      if (out) {
+        ro.idx[lane] = my_e;
+        ro.w[lane] = my_w;
+        ro.perm[asc] = lane;
+        if (ro.pos) ro.pos[lane] = asc;
+        if (dt) {
+          DecTile *d = dt + asc;
+          d->e = my_e;
+          d->tmask = 1u;
+          d->pad0 = 0;
+          d->pad1 = 0;
+          d->w[0] = my_w;
+#pragma unroll
+          for (int t = 1; t < 16; ++t) d->w[t] = 0.0f;
+        }
+      }
+    }
+    if (out && lane == 0) {
+      ro.offsets[E] = k;
+      if (ntile) *ntile = k;
+    }
+  }
+  __syncthreads();
+  if (out && tid < E) {
+    int below = 0, sel = 0;
+    for (int j = 0; j < k; ++j) {
+      const int ej = L.tb[j];
+      below += ej < tid ? 1 : 0;
+      sel += ej == tid ? 1 : 0;
+    }
+    ro.counts[tid] = sel;
+    ro.offsets[tid] = below;
+  }
+  return L.tb[tile];
+}
+
 }  // namespace ds4

@@ -308,7 +308,7 @@ def test_mid_wide_tiles_one_expert():
     assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
 
 
-@pytest.mark.parametrize("T,mode", [(5, "decode"), (16, "decode"), (40, "prefill")])
+@pytest.mark.parametrize("T,mode", [(1, "decode"), (5, "decode"), (16, "decode"), (40, "prefill")])
 def test_k16_e256_limits(T, mode):
     """The largest top-k (16) over the largest expert count (256)."""
     q = _q()
@@ -352,6 +352,29 @@ def test_nan_token_keeps_others(T, mode):
     ref_lg = oracle.logits(L.x[good].astype(np.float32), L.router_w, L.router_bias)
     assert np.array_equal(lg[good].view(np.uint32), ref_lg.view(np.uint32))
     assert per_token_err(y.cpu().numpy()[good], ref) <= TOL_Y
+
+
+def test_nan_single_token_decode():
+    """T = 1 (the one-token routing inside the gate/up kernel) with a NaN in
+    the activations: logits NaN, experts 0..k-1 in rank order, and counts,
+    offsets, permutation and tiles still consistent."""
+    q = _q()
+    wl = synth.Workload("lim1", 0, T=1, H=256, E=256, I=128, k=16, x_dtype="f32", router_dtype="f32",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    L.x = L.x.copy()
+    L.x[0, 7] = np.nan
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(1)
+    dl.forward(dl.x_tensor(L.x), q.MODE_DECODE, routing=bufs)
+    torch.cuda.synchronize()
+    idx = bufs["topk_idx"].cpu().numpy()
+    assert np.array_equal(idx[0], np.arange(16))
+    assert np.all(np.isnan(bufs["logits"].cpu().numpy()))
+    counts, offsets, perm = oracle.permute(idx, 256)
+    assert np.array_equal(bufs["counts"].cpu().numpy(), counts)
+    assert np.array_equal(bufs["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(bufs["perm"].cpu().numpy(), perm)
 
 
 def test_prefill_zero_tokens_is_noop(tiny):
