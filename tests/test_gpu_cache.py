@@ -124,6 +124,19 @@ def test_cache_all_slots_hit():
     assert hits == sum(len(u) for u in used) - misses
 
 
+@pytest.mark.parametrize("T", [2, 12])
+def test_cache_with_shared_expert(T):
+    """Routed experts through the cache beside a resident bf16 shared expert."""
+    q = _q()
+    wl = synth.Workload("cache_sh", 0, T=T, H=512, E=64, I=256, k=4, Is=96, x_dtype="bf16", router_dtype="bf16",
+                        router_sigma=0.05, layer_id=0)
+    L0 = synth.make_layer(wl)
+    dl = q.from_layer_inputs(L0)
+    cache = q.ExpertCache(dl, 48)
+    used = _run_sequence(L0, dl, cache, [T] * 5)
+    assert cache.stats() == (5, *lru_counts(48, used))
+
+
 def test_cache_rejects_device_pointers():
     """Expert pointers that are not pinned host memory are refused before
     anything is launched."""

@@ -288,6 +288,26 @@ def test_mid_shared_expert_prefill(T, Is):
     assert err <= TOL_Y
 
 
+@pytest.mark.parametrize("T,I", [(1, 256), (3, 256), (8, 256), (16, 256), (5, 128)])
+def test_mid_shared_expert_decode(T, I):
+    """Decode with a bf16 shared expert: its output is added by the T <= 4
+    down kernel, by the reduce kernel of the two-half down path (5..16
+    tokens) and by the padded down kernel (I below 256)."""
+    q = _q()
+    wl = synth.Workload("mid_sh_dec", 0, T=T, H=512, E=16, I=I, k=4, Is=96, x_dtype="bf16", router_dtype="bf16",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"shared decode T={T}")
+    ref, _, _ = oracle.layer_inputs(L)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"shared decode T={T} I={I}: per-token rel err {err:.3e}")
+    assert err <= TOL_Y
+
+
 def test_mid_wide_tiles_one_expert():
     """Every token's first choice is expert 5: 300 tokens in tiles of 96, 96,
     96 and 12 for that expert, the other experts share the second choices."""
