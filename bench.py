@@ -293,22 +293,30 @@ def run_workload(name: str, args) -> dict:
         for e in row:
             e.record(stream)
     torch.cuda.synchronize()
+    # a marker before each step: a slot whose start event precedes it was not
+    # launched in that step (its events keep the stamps of the pass above)
+    pre = [torch.cuda.Event(enable_timing=True) for _ in range(steps_eager)]
     stats0 = cache.stats() if cached else None
     t2 = time.perf_counter()
     for i in range(steps_eager):
+        pre[i].record(stream)
         step(i, ev[i])
     torch.cuda.synchronize()
     elapsed_ev = time.perf_counter() - t2
     stats1 = cache.stats() if cached else None
     stage_ms = {s: 0.0 for s in B.KERNEL_SLOTS}
+    stage_n = {s: 0 for s in B.KERNEL_SLOTS}
     per_step_gateup = []
     for i in range(steps_eager):
         for j, s in enumerate(B.KERNEL_SLOTS):
+            if pre[i].elapsed_time(ev[i][2 * j]) < 0.0:
+                continue
             dt = ev[i][2 * j].elapsed_time(ev[i][2 * j + 1])
             stage_ms[s] += dt
+            stage_n[s] += 1
             if s == "gateup":
                 per_step_gateup.append(dt)
-    stage_ms = {s: v / steps_eager for s, v in stage_ms.items()}
+    stage_ms = {s: (v / stage_n[s] if stage_n[s] else None) for s, v in stage_ms.items()}
 
     H, I, E, k = wl.H, wl.I, wl.E, wl.k
     gu_bytes = dl.gu_bytes
@@ -361,7 +369,7 @@ def run_workload(name: str, args) -> dict:
                    "seed": args.seed, "distinct_experts_mean": float(np.mean(distinct))},
         "roofline": roof,
         "layer_roofline": layer,
-        "kernel_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "kernel_ms": {s: round(v, 5) for s, v in stage_ms.items() if v is not None},
         "launch": f"hip graph of {glen} layer calls, replayed" if glen else "eager launches",
         "ms_per_step_percentiles": pct,
         "ms_per_step_eager": round(elapsed_eager / steps_eager * 1e3, 5),

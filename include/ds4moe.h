@@ -223,9 +223,11 @@ int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, con
  * 0 router logits, 1 top-k (decode: top-k + permutation), 2 permutation
  * (prefill), 3 gate/up + SwiGLU, 4 down, 5 shared gate/up, 6 shared down,
  * 7 combine, 8 expert-cache plan, 9 expert-cache fill (the last two only in
- * ds4moe_forward_decode_cached).  A slot with no kernel in the call gets both
- * events recorded back to back.  Any other mode returns DS4MOE_ERR_SHAPE; a NULL array or
- * event DS4MOE_ERR_NULL. */
+ * ds4moe_forward_decode_cached).  The events of a slot with no kernel in the
+ * call are not recorded (they keep their last stamps), so a caller that
+ * records its own event on the stream before the call tells those slots
+ * apart: their start precedes it.  Any other mode returns DS4MOE_ERR_SHAPE; a
+ * NULL array or event DS4MOE_ERR_NULL. */
 int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
                          float *y, ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *const *events,
                          void *stream);

@@ -248,12 +248,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   if (st || T == 0) return st;
   const ds4moe_dims &d = *dims;
   hipStream_t s = (hipStream_t)stream;
-  bool used[SL_N] = {};
-  auto tm = [&](int slot) -> const Timing * {
-    if (!tms) return nullptr;
-    used[slot] = true;
-    return tms + slot;
-  };
+  auto tm = [&](int slot) -> const Timing * { return tms ? tms + slot : nullptr; };
   const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
   const Ptrs p = routing_ptrs(ws, L, route_out);
 
@@ -355,13 +350,6 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     st = shared();
     if (st) return st;
     TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s, tm(SL_COMBINE)));
-  }
-  if (tms) {  // slots without a kernel in this call: empty intervals
-    for (int i = 0; i < SL_N; ++i) {
-      if (used[i]) continue;
-      TRY(hipEventRecord(tms[i].start, s));
-      TRY(hipEventRecord(tms[i].stop, s));
-    }
   }
   return DS4MOE_OK;
 }

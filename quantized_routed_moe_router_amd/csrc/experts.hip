@@ -43,6 +43,10 @@ namespace ds4 {
 #ifndef GU_LDS_PD
 #define GU_LDS_PD 3
 #endif
+// waves sharing one row tile's reduction in the T <= 4 gate/up kernel
+#ifndef GU_LDS_KS
+#define GU_LDS_KS 2
+#endif
 #ifndef DN_LDS_PD
 #define DN_LDS_PD 4
 #endif
@@ -849,12 +853,14 @@ struct SlotLoads {
 // the router's partial sums, one wave per token; the LDS of that step is the
 // ring's, before the ring is used) and takes the tile_id-th used expert;
 // workgroup 0 writes the routing outputs and the tiles for the down kernel.
-template <int PD, int NT, bool ROUTE, int B>
+template <int PD, int NT, bool ROUTE, int B, int KS>
 __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, DecRoute rr) {
   constexpr int NI = SlotLoads<NT>::NI;
   constexpr int SLOT = 64 * 16 * NI;  // bytes per ring slot
+  constexpr int RPW = 4 / KS;         // row tiles per workgroup; KS waves split each one's reduction
+  static_assert(KS == 1 || KS == 2 || KS == 4, "reduction splits");
   __shared__ __attribute__((aligned(16))) char ring_lds[4 * PD * SLOT];
-  const int nrb = (n_rt + 1) >> 1;
+  const int nrb = (n_rt + RPW - 1) / RPW;
   const int tile_id = blockIdx.x / nrb;
   const int rb = blockIdx.x - tile_id * nrb;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -892,11 +898,11 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
     tmask = a.dtiles[tile_id].tmask;
   }
   const int r16 = lane & 15, g = lane >> 4;
-  const int rt = 2 * rb + (wave >> 1), kh = wave & 1;
+  const int rt = RPW * rb + wave / KS, kh = wave % KS;
   const int nsb = a.H >> 8;
-  const int half = (nsb + 1) >> 1;
-  const int sb0 = kh * half;
-  const int nit = max(0, min(nsb, sb0 + half) - sb0);
+  const int part = (nsb + KS - 1) / KS;
+  const int sb0 = kh * part;
+  const int nit = max(0, min(nsb, sb0 + part) - sb0);
   const uint32_t gub = (uint32_t)a.gu_bytes;
   const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gate + (size_t)e * a.gu_bytes, gub);
   const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.up + (size_t)e * a.gu_bytes, gub);
@@ -977,20 +983,26 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
     }
   }
 
-  __shared__ f4 red[2][2][64];  // [row tile of the workgroup][gate, up]
-  const int rl = wave >> 1;
-  if (kh == 1) {
-    red[rl][0][lane] = yg;
-    red[rl][1][lane] = yu;
+  // [row tile of the workgroup][reduction part 1..KS-1][gate, up]
+  __shared__ f4 red[RPW][KS > 1 ? KS - 1 : 1][2][64];
+  const int rl = wave / KS;
+  if (kh > 0) {
+    red[rl][kh - 1][0][lane] = yg;
+    red[rl][kh - 1][1][lane] = yu;
   }
-  __syncthreads();
-  if (kh == 1 || rt >= n_rt) return;  // uniform per wave
-  const f4 pg = red[rl][0][lane], pu = red[rl][1][lane];
+  if constexpr (KS > 1) __syncthreads();
+  if (kh > 0 || rt >= n_rt) return;  // uniform per wave
+#pragma unroll
+  for (int j = 0; j < KS - 1; ++j) {
+    const f4 pg = red[rl][j][0][lane], pu = red[rl][j][1][lane];
+    yg += pg;
+    yu += pu;
+  }
   half_t hv[4];
   float ssum = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float gv = yg[q] + pg[q], uv = yu[q] + pu[q];
+    const float gv = yg[q], uv = yu[q];
     hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
     ssum += (float)hv[q];
   }
@@ -1736,9 +1748,10 @@ template <int NT, int B>
 static void gateup_dec_lds(const GemmArgs &a, int n_rt, const DecRoute *rr, dim3 grid, hipStream_t s,
                            const Timing *tm) {
   if (rr)
-    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, true, B>), grid, dim3(256), 0, s, a, n_rt, *rr);
+    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, true, B, GU_LDS_KS>), grid, dim3(256), 0, s, a, n_rt, *rr);
   else
-    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, false, B>), grid, dim3(256), 0, s, a, n_rt, DecRoute{});
+    DS4_LAUNCH(tm, (k_gateup_dec_lds<GU_LDS_PD, NT, false, B, GU_LDS_KS>), grid, dim3(256), 0, s, a, n_rt,
+               DecRoute{});
 }
 
 template <int B>
@@ -1751,7 +1764,7 @@ static hipError_t gateup_dec_b(const GemmArgs &a, int max_tiles, const DecRoute 
     DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, NW, B>), grid, dim3(64 * NW), 0, s, a, n_rt);
     return hipGetLastError();
   }
-  const int nrb = (n_rt + 1) >> 1;
+  const int nrb = (n_rt + 4 / GU_LDS_KS - 1) / (4 / GU_LDS_KS);
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
   switch (a.T) {
     case 1: gateup_dec_lds<1, B>(a, n_rt, rr, grid, s, tm); break;

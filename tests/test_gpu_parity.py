@@ -397,6 +397,44 @@ def test_nan_single_token_decode():
     assert np.array_equal(bufs["perm"].cpu().numpy(), perm)
 
 
+@pytest.mark.parametrize("mode,T,Is", [("decode", 1, 0), ("decode", 8, 96), ("prefill", 100, 96), ("prefill", 40, 0)])
+def test_forward_timed_same_result_and_slots(mode, T, Is):
+    """The timed entry point computes bitwise what the plain one does; the
+    slots of kernels it launched are stamped after a marker recorded before
+    the call, the others (the cache slots, the shared expert without one)
+    keep their earlier stamps."""
+    q = _q()
+    B = q.binding
+    wl = synth.Workload("timed", 0, T=T, H=512, E=16, I=256, k=4, Is=Is, x_dtype="bf16", router_dtype="bf16",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    dl = q.from_layer_inputs(L)
+    m = q.MODE_DECODE if mode == "decode" else q.MODE_PREFILL
+    x = dl.x_tensor(L.x)
+    y0 = dl.forward(x, m)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * B.N_TIMED_KERNELS)]
+    for e in ev:
+        e.record(stream)
+    marker = torch.cuda.Event(enable_timing=True)
+    marker.record(stream)
+    y = torch.empty(T, wl.H, dtype=torch.float32, device=dl.device)
+    ws = dl.workspace(T, m)
+    B.ds4moe_forward_timed(m, dl.dims, dl.weights(), x, T, y, None, ws, ws.numel(), ev, stream)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y0.view(torch.int32))
+    launched = {s for j, s in enumerate(B.KERNEL_SLOTS) if marker.elapsed_time(ev[2 * j]) >= 0.0}
+    assert {"router", "gateup", "down"} <= launched
+    assert not {"cache_plan", "cache_fill"} & launched
+    assert ({"shared_gateup", "shared_down"} <= launched) == bool(Is)
+    assert not ({"shared_gateup", "shared_down"} & launched) or Is
+    if mode == "prefill":
+        assert {"route", "permute", "combine"} <= launched
+    for j, s in enumerate(B.KERNEL_SLOTS):
+        if s in launched:
+            assert ev[2 * j].elapsed_time(ev[2 * j + 1]) > 0.0, s
+
+
 def test_prefill_zero_tokens_is_noop(tiny):
     q = _q()
     L, dl = tiny
