@@ -56,6 +56,9 @@ namespace ds4 {
 #ifndef GU_SH_NW
 #define GU_SH_NW 4
 #endif
+// smallest batch that takes the shared-activation gate/up kernel (one token
+// takes the per-wave kernel)
+#define GU_SH_MIN_T 2
 #ifndef DN2_PD
 #define DN2_PD 2
 #endif
@@ -833,7 +836,8 @@ __global__ __launch_bounds__(512) void k_down_dec(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------ small batches, T <= 4
-// Variants of the two kernels above for batches of at most four tokens: the
+// Variants of the two kernels above for batches of at most four tokens (the
+// gate/up one is used for a single token, the down one up to four): the
 // activations of each reduction step (x or h of the T tokens: 256 values and
 // the 16-column sums, 36 chunks of 16 bytes per token, padded to 37) come in
 // through one to three direct-to-LDS buffer loads per step instead of nine
@@ -849,10 +853,44 @@ struct SlotLoads {
 };
 
 
-// ROUTE: the workgroup first routes the batch itself (route_small_block on
-// the router's partial sums, one wave per token; the LDS of that step is the
-// ring's, before the ring is used) and takes the tile_id-th used expert;
-// workgroup 0 writes the routing outputs and the tiles for the down kernel.
+// Routing folded into a small-batch gate/up workgroup of 256 threads: the
+// workgroup routes the batch itself from the router's partial sums (one
+// token: route_one_token; 2-4 tokens: route_small_block, one wave per token)
+// in `lds` (the kernel's ring, before the ring is used) and takes the
+// tile_id-th used expert; workgroup 0 writes the routing outputs and the
+// tiles for the down kernel.  Returns false (uniformly) when the batch uses
+// fewer than tile_id + 1 experts.
+template <int NT>
+__device__ __forceinline__ bool route_take_tile(char *lds, const DecRoute &rr, int T, int tile_id, int &e,
+                                                uint32_t &tmask) {
+  RouteLds<4> &L = *reinterpret_cast<RouteLds<4> *>(lds);
+  const int lane = threadIdx.x & 63;
+  if (NT == 1) {
+    if (tile_id >= rr.k) return false;
+    e = route_one_token<256>(L, rr.part, rr.nslice, rr.bias, rr.logits, rr.E, rr.k, rr.ro, rr.dt, rr.ntile,
+                             blockIdx.x == 0, tile_id);
+    tmask = 1u;
+  } else {
+    route_small_block<256, 4>(L, rr.part, rr.nslice, rr.bias, rr.logits, T, rr.E, rr.k, rr.ro, rr.dt, rr.ntile,
+                              blockIdx.x == 0);
+    if (tile_id >= L.ntile) return false;
+    // the used expert whose tile index is tile_id (lowest e among equal tb: the used one)
+    int sel = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = lane + 64 * i;
+      const bool hit = ee < rr.E && L.tm[ee] != 0u && L.tb[ee] == tile_id;
+      const uint64_t b = __ballot(hit);
+      if (sel < 0 && b) sel = 64 * i + __ffsll((unsigned long long)b) - 1;
+    }
+    e = sel;
+    tmask = L.tm[e];
+  }
+  __syncthreads();  // every wave has read the routing before the ring is filled
+  return true;
+}
+
+// ROUTE: the workgroup routes the batch itself (route_take_tile).
 template <int PD, int NT, bool ROUTE, int B, int KS>
 __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, DecRoute rr) {
   constexpr int NI = SlotLoads<NT>::NI;
@@ -868,30 +906,7 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
   uint32_t tmask;
   if constexpr (ROUTE) {
     static_assert(sizeof(RouteLds<4>) <= sizeof(ring_lds), "routing LDS must fit in the ring");
-    RouteLds<4> &L = *reinterpret_cast<RouteLds<4> *>(ring_lds);
-    if (NT == 1) {
-      if (tile_id >= rr.k) return;  // uniform over the workgroup
-      e = route_one_token<256>(L, rr.part, rr.nslice, rr.bias, rr.logits, rr.E, rr.k, rr.ro, rr.dt, rr.ntile,
-                               blockIdx.x == 0, tile_id);
-      tmask = 1u;
-      __syncthreads();  // every wave has read the routing before the ring is filled
-    } else {
-    route_small_block<256, 4>(L, rr.part, rr.nslice, rr.bias, rr.logits, a.T, rr.E, rr.k, rr.ro, rr.dt, rr.ntile,
-                              blockIdx.x == 0);
-    if (tile_id >= L.ntile) return;  // uniform over the workgroup
-    // the used expert whose tile index is tile_id (lowest e among equal tb: the used one)
-    int sel = -1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ee = lane + 64 * i;
-      const bool hit = ee < rr.E && L.tm[ee] != 0u && L.tb[ee] == tile_id;
-      const uint64_t b = __ballot(hit);
-      if (sel < 0 && b) sel = 64 * i + __ffsll((unsigned long long)b) - 1;
-    }
-    e = sel;
-    tmask = L.tm[e];
-    __syncthreads();  // every wave has read the routing before the ring is filled
-    }
+    if (!route_take_tile<NT>(ring_lds, rr, a.T, tile_id, e, tmask)) return;  // uniform over the workgroup
   } else {
     if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
     e = a.dtiles[tile_id].e;
@@ -1147,39 +1162,47 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ small batches, 5 <= T <= 16
-// The activations of one reduction step (x or h of the 16 token slots, 37
-// chunks of 16 bytes each: 592 chunks) are shared by the waves of a
-// workgroup: they come in once per workgroup by direct-to-LDS buffer loads
-// split across the waves into a PD-slot ring, with one barrier per step.
-// After that barrier every wave's loads of the step have landed (each wave
-// waits for its own first) and every wave has finished reading the slot the
-// step's prefetch then refills.  A wave issues 2-3 activation loads per step
-// instead of 9, which is what bounds these kernels at T = 16.
-constexpr int SH_NT = 16;            // token slots
-constexpr int SH_CH = SH_NT * XCH;   // chunks per step
-
-template <int NW>
+// ------------------------------------------------------------------ small batches, 2 <= T <= 16
+// The activations of one reduction step (x or h of NT token slots, 37 chunks
+// of 16 bytes each: 592 chunks for 16 slots, 148 for 4) are shared by the
+// waves of a workgroup: they come in once per workgroup by direct-to-LDS
+// buffer loads split across the waves into a PD-slot ring, with one barrier
+// per step.  After that barrier every wave's loads of the step have landed
+// (each wave waits for its own first) and every wave has finished reading the
+// slot the step's prefetch then refills.  At T = 16 a wave issues 2-3
+// activation loads per step instead of 9, which is what bounds these kernels
+// there; at 2-4 tokens (four slots) one, and the per-wave ring kernel above
+// is then 1.3-1.4x slower.  With 2-4 tokens the gate/up workgroup also
+// routes the batch itself.
+template <int NW, int NT>
 struct ShRing {
-  static constexpr int NI = (SH_CH + 64 * NW - 1) / (64 * NW);  // load instructions per wave per step
-  static constexpr int SLOT = NI * NW * 1024;                   // bytes per slot
+  static constexpr int NI = (NT * XCH + 64 * NW - 1) / (64 * NW);  // load instructions per wave per step
+  static constexpr int SLOT = NI * NW * 1024;                      // bytes per slot
 };
 
 // gate/up + SwiGLU: workgroup = one tile x NW 16-row tiles, the whole
 // reduction per wave.
-template <int PD, int NW, int B>
-__global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt) {
-  constexpr int NI = ShRing<NW>::NI, SLOT = ShRing<NW>::SLOT;
+template <int PD, int NW, int B, int NT, bool ROUTE>
+__global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt, DecRoute rr) {
+  constexpr int NI = ShRing<NW, NT>::NI, SLOT = ShRing<NW, NT>::SLOT;
   static_assert(PD >= 2, "ring depth");
+  static_assert(!ROUTE || (NW == 4 && NT <= 4), "routing: 256 threads, at most 4 tokens");
   __shared__ __attribute__((aligned(16))) char ring[PD * SLOT];
   const int nrb = (n_rt + NW - 1) / NW;
   const int tile_id = blockIdx.x / nrb;
   const int rb = blockIdx.x - tile_id * nrb;
-  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int e = a.dtiles[tile_id].e;
-  const uint32_t tmask = a.dtiles[tile_id].tmask;
+  int e;
+  uint32_t tmask;
+  if constexpr (ROUTE) {
+    static_assert(sizeof(RouteLds<4>) <= sizeof(ring), "routing LDS must fit in the ring");
+    if (!route_take_tile<NT>(ring, rr, a.T, tile_id, e, tmask)) return;  // uniform over the workgroup
+  } else {
+    if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
+    e = a.dtiles[tile_id].e;
+    tmask = a.dtiles[tile_id].tmask;
+  }
   const int rt = NW * rb + wave;
   const int nsb = a.H >> 8;
   const uint32_t gub = (uint32_t)a.gu_bytes;
@@ -1195,7 +1218,7 @@ __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt)
     const int t = u / XCH, c = u - t * XCH;
     src[q] = DS4_OOB;
     inc[q] = 0;
-    if (t < SH_NT && c < 36 && ((tmask >> t) & 1u)) {  // tmask bits only below T
+    if (t < NT && c < 36 && ((tmask >> t) & 1u)) {  // tmask bits only below T
       if (c < 32) {
         src[q] = a.o_x16 + 2u * ((uint32_t)t * a.H + 8 * c);
         inc[q] = 512;
@@ -1206,7 +1229,8 @@ __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt)
       }
     }
   }
-  const uint32_t brow = (uint32_t)r16 * (XCH * 16);  // B fragment of lane (r16, g): token slot r16
+  // B fragment of lane (r16, g): token slot r16 (columns r16 >= NT read slot 0 and are discarded)
+  const uint32_t brow = (uint32_t)(r16 < NT ? r16 : 0) * (XCH * 16);
 
   struct Stage {
     UnitRegs<B> wg, wu;
@@ -1758,20 +1782,25 @@ template <int B>
 static hipError_t gateup_dec_b(const GemmArgs &a, int max_tiles, const DecRoute *rr, hipStream_t s,
                                const Timing *tm) {
   const int n_rt = a.I >> 4;
-  if (a.T > 4) {  // activations shared by the workgroup's row tiles
-    constexpr int NW = GU_SH_NW;
-    const dim3 grid((unsigned)((int64_t)((n_rt + NW - 1) / NW) * max_tiles));
-    DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, NW, B>), grid, dim3(64 * NW), 0, s, a, n_rt);
+  if (a.T >= GU_SH_MIN_T) {  // activations shared by the workgroup's row tiles
+    if (a.T > 4) {
+      constexpr int NW = GU_SH_NW;
+      const dim3 grid((unsigned)((int64_t)((n_rt + NW - 1) / NW) * max_tiles));
+      DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, NW, B, 16, false>), grid, dim3(64 * NW), 0, s, a, n_rt, DecRoute{});
+    } else {  // four token slots, four waves (the routing takes 256 threads)
+      const dim3 grid((unsigned)((int64_t)((n_rt + 3) / 4) * max_tiles));
+      if (rr)
+        DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, 4, B, 4, true>), grid, dim3(256), 0, s, a, n_rt, *rr);
+      else
+        DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, 4, B, 4, false>), grid, dim3(256), 0, s, a, n_rt, DecRoute{});
+    }
     return hipGetLastError();
   }
+  // one token: row tiles split over two waves each, activations per wave
+  static_assert(GU_SH_MIN_T == 2, "the per-wave kernel is instantiated for one token");
   const int nrb = (n_rt + 4 / GU_LDS_KS - 1) / (4 / GU_LDS_KS);
   const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
-  switch (a.T) {
-    case 1: gateup_dec_lds<1, B>(a, n_rt, rr, grid, s, tm); break;
-    case 2: gateup_dec_lds<2, B>(a, n_rt, rr, grid, s, tm); break;
-    case 3: gateup_dec_lds<3, B>(a, n_rt, rr, grid, s, tm); break;
-    default: gateup_dec_lds<4, B>(a, n_rt, rr, grid, s, tm); break;
-  }
+  gateup_dec_lds<1, B>(a, n_rt, rr, grid, s, tm);
   return hipGetLastError();
 }
 

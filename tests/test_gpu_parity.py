@@ -472,7 +472,7 @@ def test_full_decode1(full):
     _full_case(full, "decode1", "decode")
 
 
-@pytest.mark.parametrize("T", [2, 4, 7])
+@pytest.mark.parametrize("T", [2, 3, 4, 7])
 def test_full_decode_small_batches(full, T):
     """Full-size decode at batch sizes between the two decode workloads."""
     q = _q()
