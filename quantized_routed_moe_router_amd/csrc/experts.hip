@@ -51,7 +51,7 @@ namespace ds4 {
 #define DN_LDS_PD 4
 #endif
 #ifndef GU_SH_PD
-#define GU_SH_PD 4
+#define GU_SH_PD 2
 #endif
 #ifndef GU_SH_NW
 #define GU_SH_NW 4
@@ -1182,9 +1182,14 @@ struct ShRing {
 
 // gate/up + SwiGLU: workgroup = one tile x NW 16-row tiles, the whole
 // reduction per wave.
-template <int PD, int NW, int B, int NT, bool ROUTE>
+template <int PD, int NW, int B, int NT, bool ROUTE, bool SDL = false>
 __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt, DecRoute rr) {
-  constexpr int NI = ShRing<NW, NT>::NI, SLOT = ShRing<NW, NT>::SLOT;
+  constexpr int NI = ShRing<NW, NT>::NI;
+  // SDL: each wave's gate and up scales + d|dmin (320 bytes per unit) land in
+  // the slot after the activations by one 20-lane direct load per unit
+  constexpr int SDW = SDL ? 640 : 0;
+  constexpr int SLOT = ShRing<NW, NT>::SLOT + NW * SDW;
+  constexpr int LPS = NI + (SDL ? B + 2 : 2 * Unit<B>::LOADS);  // vector memory instructions per step
   static_assert(PD >= 2, "ring depth");
   static_assert(!ROUTE || (NW == 4 && NT <= 4), "routing: 256 threads, at most 4 tokens");
   __shared__ __attribute__((aligned(16))) char ring[PD * SLOT];
@@ -1243,10 +1248,34 @@ __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt,
     for (int q = 0; q < NI; ++q)
       buf_load_lds16(ws, ring + slot * SLOT + 1024 * (NW * q + wave), in ? src[q] + inc[q] * (uint32_t)i : DS4_OOB);
     const uint32_t wo = in ? roff + (uint32_t)i * Unit<B>::BYTES : DS4_OOB;
-    sg.wg = load_unit_buf<B>(gr, wo, lane);
-    sg.wu = load_unit_buf<B>(ur, wo, lane);
+    if constexpr (SDL) {
+      char *sd = ring + slot * SLOT + ShRing<NW, NT>::SLOT + wave * SDW;
+      if (lane < 20) {  // 320 bytes: lane l's 16 land at sd + 16*l
+        const uint32_t so = in ? wo + Unit<B>::SCALE_OFF + 16u * lane : DS4_OOB;
+        buf_load_lds16(gr, sd, so);
+        buf_load_lds16(ur, sd + 320, so);
+      }
+#pragma unroll
+      for (int p = 0; p < B / 2; ++p) {
+        sg.wg.code[p] =
+            __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(gr, wo + 1024 * p + 16 * lane, 0, 0));
+        sg.wu.code[p] =
+            __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(ur, wo + 1024 * p + 16 * lane, 0, 0));
+      }
+    } else {
+      sg.wg = load_unit_buf<B>(gr, wo, lane);
+      sg.wu = load_unit_buf<B>(ur, wo, lane);
+    }
   };
-  auto compute = [&](const Stage &sg, int slot) {
+  auto compute = [&](const Stage &sg0, int slot) {
+    Stage sg = sg0;
+    if constexpr (SDL) {  // scales of row r16, d|dmin of rows 4g..4g+3 (the unit's byte layout)
+      const char *sd = ring + slot * SLOT + ShRing<NW, NT>::SLOT + wave * SDW;
+      sg.wg.scale = *reinterpret_cast<const u4 *>(sd + 16 * r16);
+      sg.wg.dd = *reinterpret_cast<const u4 *>(sd + 256 + 16 * g);
+      sg.wu.scale = *reinterpret_cast<const u4 *>(sd + 320 + 16 * r16);
+      sg.wu.dd = *reinterpret_cast<const u4 *>(sd + 576 + 16 * g);
+    }
     const char *base = ring + slot * SLOT + brow;
     h8 b[9];
 #pragma unroll
@@ -1279,7 +1308,7 @@ __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt,
   for (int i0 = 0; i0 < nsb; i0 += PD) {
 #pragma unroll
     for (int sgi = 0; sgi < PD; ++sgi) {
-      wait_vm<(PD - 2) * (NI + 2 * Unit<B>::LOADS)>();  // this wave's loads of step i0+sgi have landed
+      wait_vm<(PD - 2) * LPS>();  // this wave's loads of step i0+sgi have landed
       __syncthreads();                                  // ... and every wave's; slot sgi-1 is free
       load(st[(sgi + PD - 1) % PD], (sgi + PD - 1) % PD, i0 + sgi + PD - 1);
       compute(st[sgi], sgi);
@@ -1786,13 +1815,20 @@ static hipError_t gateup_dec_b(const GemmArgs &a, int max_tiles, const DecRoute 
     if (a.T > 4) {
       constexpr int NW = GU_SH_NW;
       const dim3 grid((unsigned)((int64_t)((n_rt + NW - 1) / NW) * max_tiles));
-      DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, NW, B, 16, false>), grid, dim3(64 * NW), 0, s, a, n_rt, DecRoute{});
+      DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, NW, B, 16, false, true>), grid, dim3(64 * NW), 0, s, a, n_rt,
+                 DecRoute{});
     } else {  // four token slots, four waves (the routing takes 256 threads)
       const dim3 grid((unsigned)((int64_t)((n_rt + 3) / 4) * max_tiles));
-      if (rr)
-        DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, 4, B, 4, true>), grid, dim3(256), 0, s, a, n_rt, *rr);
-      else
-        DS4_LAUNCH(tm, (k_gateup_dec_sh<GU_SH_PD, 4, B, 4, false>), grid, dim3(256), 0, s, a, n_rt, DecRoute{});
+      // two tokens: scales through registers and a 4-slot ring; three or four:
+      // scales through LDS and a 2-slot ring (fewer registers, more workgroups)
+      const DecRoute r = rr ? *rr : DecRoute{};
+      if (a.T == 2) {
+        if (rr) DS4_LAUNCH(tm, (k_gateup_dec_sh<4, 4, B, 4, true, false>), grid, dim3(256), 0, s, a, n_rt, r);
+        else DS4_LAUNCH(tm, (k_gateup_dec_sh<4, 4, B, 4, false, false>), grid, dim3(256), 0, s, a, n_rt, r);
+      } else {
+        if (rr) DS4_LAUNCH(tm, (k_gateup_dec_sh<2, 4, B, 4, true, true>), grid, dim3(256), 0, s, a, n_rt, r);
+        else DS4_LAUNCH(tm, (k_gateup_dec_sh<2, 4, B, 4, false, true>), grid, dim3(256), 0, s, a, n_rt, r);
+      }
     }
     return hipGetLastError();
   }
