@@ -62,6 +62,9 @@ namespace ds4 {
 #ifndef DN2_PD
 #define DN2_PD 2
 #endif
+#ifndef DN2_SDL
+#define DN2_SDL true
+#endif
 
 
 // One lane's share of a packed unit.  Code plane p (1024 bytes at 1024*p)
@@ -1347,8 +1350,12 @@ __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt,
 // ascending within a wave.  Each workgroup adds its waves' partial sums in
 // wave order and writes its half's partial; k_down_reduce adds the two halves
 // in order, then the shared-expert output.
-template <int PD, int B>
+template <int PD, int B, bool SDL>
 __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
+  // SDL: the two units' scales and d|dmin (320 bytes each) land in a
+  // per-wave LDS slot by one 20-lane direct load per unit
+  constexpr int LPS = 9 + (SDL ? 2 * (B / 2) + 2 : 2 * Unit<B>::LOADS);  // vector memory instructions per step
+  __shared__ __attribute__((aligned(16))) char sdl[SDL ? 8 * PD * 640 : 16];
   const int rt0 = 2 * blockIdx.x, half = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -1379,15 +1386,31 @@ __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
   Stage st[PD];
   f4 y[2] = {(f4){0.f, 0.f, 0.f, 0.f}, (f4){0.f, 0.f, 0.f, 0.f}};
   int lt = 0, lsb = 0;  // tile and super-block of the next load
-  auto load = [&](Stage &sg) {
+  auto load = [&](Stage &sg, int slot) {
     const bool in = lt < mt;
     const int tile = min(j0 + 16 * lt, ntl - 1);
     const int e = __builtin_amdgcn_readlane(e_l, lt & 63);
     const uint32_t tmask = in ? (uint32_t)__builtin_amdgcn_readlane((int)m_l, lt & 63) : 0u;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.down + (size_t)e * a.d_bytes, (uint32_t)a.d_bytes);
     const uint32_t wo = in ? (uint32_t)rt0 * ustride + (uint32_t)lsb * Unit<B>::BYTES : DS4_OOB;
-    sg.wd[0] = load_unit_buf<B>(wr, wo, lane);
-    sg.wd[1] = load_unit_buf<B>(wr, in ? wo + ustride : DS4_OOB, lane);
+    if constexpr (SDL) {
+      char *sd = sdl + (wave * PD + slot) * 640;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier reads of this slot are done
+      if (lane < 20) {  // 320 bytes per unit: lane l's 16 land at sd + 16*l
+        buf_load_lds16(wr, sd, in ? wo + Unit<B>::SCALE_OFF + 16u * lane : DS4_OOB);
+        buf_load_lds16(wr, sd + 320, in ? wo + ustride + Unit<B>::SCALE_OFF + 16u * lane : DS4_OOB);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int p = 0; p < B / 2; ++p)
+          sg.wd[r].code[p] = __builtin_bit_cast(
+              u4, __builtin_amdgcn_raw_buffer_load_b128(wr, (in ? wo + r * ustride : DS4_OOB) + 1024 * p + 16 * lane,
+                                                        0, 0));
+    } else {
+      sg.wd[0] = load_unit_buf<B>(wr, wo, lane);
+      sg.wd[1] = load_unit_buf<B>(wr, in ? wo + ustride : DS4_OOB, lane);
+    }
     // h of token r16 if it chose the expert (zeros otherwise, weight 0)
     const bool routed = (tmask >> r16) & 1u;  // implies r16 < T
     const uint32_t p = (uint32_t)tile * a.T + r16;
@@ -1402,7 +1425,17 @@ __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
       ++lt;
     }
   };
-  auto compute = [&](const Stage &sg) {
+  auto compute = [&](const Stage &sg0, int slot) {
+    Stage sg = sg0;
+    if constexpr (SDL) {  // scales of row r16, d|dmin of rows 4g..4g+3 (the unit's byte layout)
+      wait_vm<(PD - 1) * LPS>();  // this step's loads (LDS and registers) have landed
+      const char *sd = sdl + (wave * PD + slot) * 640;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        sg.wd[r].scale = *reinterpret_cast<const u4 *>(sd + 320 * r + 16 * r16);
+        sg.wd[r].dd = *reinterpret_cast<const u4 *>(sd + 320 * r + 256 + 16 * g);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const UnitDecoded dd = decode_unit(sg.wd[r], g);
@@ -1419,14 +1452,15 @@ __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
     }
   };
 #pragma unroll
-  for (int sgi = 0; sgi < PD; ++sgi) load(st[sgi]);
+  for (int sgi = 0; sgi < PD; ++sgi) load(st[sgi], sgi);
   for (int i0 = 0; i0 < nit; i0 += PD) {
 #pragma unroll
     for (int sgi = 0; sgi < PD; ++sgi) {
-      compute(st[sgi]);
-      load(st[sgi]);
+      compute(st[sgi], sgi);
+      load(st[sgi], sgi);
     }
   }
+  if constexpr (SDL) wait_vm<0>();  // the trailing loads into LDS, before the workgroup's LDS is released
   __shared__ f4 red[8][2][64];
   red[wave][0][lane] = y[0];
   red[wave][1][lane] = y[1];
@@ -1860,7 +1894,7 @@ static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Tim
     return hipGetLastError();
   }
   if (a.I == a.Ipad && a.dpart) {  // two row tiles per wave, the tiles in two halves
-    DS4_LAUNCH(tm, (k_down_dec2<DN2_PD, B>), dim3((unsigned)(a.H >> 5), 2), dim3(512), 0, s, a);
+    DS4_LAUNCH(tm, (k_down_dec2<DN2_PD, B, DN2_SDL>), dim3((unsigned)(a.H >> 5), 2), dim3(512), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     DS4_LAUNCH(tm_combine, k_down_reduce, dim3((unsigned)((a.T * a.H / 4 + 255) / 256)), dim3(256), 0, s, a.dpart,
