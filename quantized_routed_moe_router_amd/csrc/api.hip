@@ -92,7 +92,7 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
     L.hs_lo = take(2 * hrows * (L.Ipad / 16));
     if (mode == DS4MOE_MODE_DECODE) {
       L.tiles = take(sizeof(DecTile) * (size_t)L.max_tiles);
-      if (T > 4) L.dpart = take(sizeof(float) * 2 * T * H);
+      if (T > 4) L.dpart = take(sizeof(float) * DEC_DOWN_SPLITS * T * H);
     } else {
       L.tiles = take(sizeof(TileT) * (size_t)L.max_tiles);
       L.pos = take(sizeof(int32_t) * A);

@@ -62,6 +62,13 @@ namespace ds4 {
 #ifndef DN2_PD
 #define DN2_PD 2
 #endif
+// T = 5..16 down: row tiles per wave, and the ways the tile list is split
+#ifndef DN2_R
+#define DN2_R 4
+#endif
+#ifndef DN2_NH
+#define DN2_NH 4
+#endif
 #ifndef DN2_SDL
 #define DN2_SDL true
 #endif
@@ -1343,33 +1350,34 @@ __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt,
   }
 }
 
-// down for 5 <= T <= 16 (I a multiple of 256): workgroup = two 16-row tiles
-// of y, both taken by every wave, so that one set of activation loads feeds
-// two units; 8 waves, and the tile list split over two workgroups
-// (blockIdx.y): tile j goes to half j % 2 and wave (j / 2) % 8, experts
-// ascending within a wave.  Each workgroup adds its waves' partial sums in
-// wave order and writes its half's partial; k_down_reduce adds the two halves
-// in order, then the shared-expert output.
-template <int PD, int B, bool SDL>
+// down for 5 <= T <= 16 (I a multiple of 256): workgroup = R 16-row tiles
+// of y, all taken by every wave, so that one set of activation loads feeds R
+// units; 8 waves, and the tile list split over NH workgroups (blockIdx.y):
+// tile j goes to part j % NH and wave (j / NH) % 8, experts ascending within
+// a wave.  Each workgroup adds its waves' partial sums in wave order and
+// writes its part's partial; k_down_reduce adds the NH parts in order, then
+// the shared-expert output.
+template <int PD, int B, bool SDL, int R, int NH>
 __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
-  // SDL: the two units' scales and d|dmin (320 bytes each) land in a
+  // SDL: the R units' scales and d|dmin (320 bytes each) land in a
   // per-wave LDS slot by one 20-lane direct load per unit
-  constexpr int LPS = 9 + (SDL ? 2 * (B / 2) + 2 : 2 * Unit<B>::LOADS);  // vector memory instructions per step
-  __shared__ __attribute__((aligned(16))) char sdl[SDL ? 8 * PD * 640 : 16];
-  const int rt0 = 2 * blockIdx.x, half = blockIdx.y;
+  constexpr int LPS = 9 + (SDL ? R * (B / 2) + R : R * Unit<B>::LOADS);  // vector memory instructions per step
+  constexpr int TS = 8 * NH;                                             // tile stride of a wave
+  __shared__ __attribute__((aligned(16))) char sdl[SDL ? 8 * PD * R * 320 : 16];
+  const int rt0 = R * blockIdx.x, half = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int ntl = *a.ntiles;
   const int nsb = a.Ipad >> 8;
   const int nj = a.Ipad >> 4;
-  const int j0 = half + 2 * wave;                          // this wave's first tile
-  const int mt = j0 < ntl ? (ntl - j0 + 15) >> 4 : 0;      // its tiles j0, j0 + 16, ... (<= 16)
+  const int j0 = half + NH * wave;                         // this wave's first tile
+  const int mt = j0 < ntl ? (ntl - j0 + TS - 1) / TS : 0;  // its tiles j0, j0 + TS, ... (<= 16)
   const int nit = mt * nsb;
   int e_l = 0;        // lane L: expert of this wave's L-th tile
   uint32_t m_l = 0u;  // ... and its token mask
   if (lane < mt) {
-    e_l = a.dtiles[j0 + 16 * lane].e;
-    m_l = a.dtiles[j0 + 16 * lane].tmask;
+    e_l = a.dtiles[j0 + TS * lane].e;
+    m_l = a.dtiles[j0 + TS * lane].tmask;
   }
   // wait for them here, before any weight load is in flight, so that the
   // pipelined loop below never has to drain the load counter for them
@@ -1379,37 +1387,40 @@ __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
   const uint32_t ustride = (uint32_t)nsb * Unit<B>::BYTES;  // bytes per row tile
 
   struct Stage {
-    UnitRegs<B> wd[2];
+    UnitRegs<B> wd[R];
     h8 b[9];
     float wt;
   };
   Stage st[PD];
-  f4 y[2] = {(f4){0.f, 0.f, 0.f, 0.f}, (f4){0.f, 0.f, 0.f, 0.f}};
+  f4 y[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) y[r] = (f4){0.f, 0.f, 0.f, 0.f};
   int lt = 0, lsb = 0;  // tile and super-block of the next load
   auto load = [&](Stage &sg, int slot) {
     const bool in = lt < mt;
-    const int tile = min(j0 + 16 * lt, ntl - 1);
+    const int tile = min(j0 + TS * lt, ntl - 1);
     const int e = __builtin_amdgcn_readlane(e_l, lt & 63);
     const uint32_t tmask = in ? (uint32_t)__builtin_amdgcn_readlane((int)m_l, lt & 63) : 0u;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.down + (size_t)e * a.d_bytes, (uint32_t)a.d_bytes);
     const uint32_t wo = in ? (uint32_t)rt0 * ustride + (uint32_t)lsb * Unit<B>::BYTES : DS4_OOB;
     if constexpr (SDL) {
-      char *sd = sdl + (wave * PD + slot) * 640;
+      char *sd = sdl + (wave * PD + slot) * (R * 320);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier reads of this slot are done
       if (lane < 20) {  // 320 bytes per unit: lane l's 16 land at sd + 16*l
-        buf_load_lds16(wr, sd, in ? wo + Unit<B>::SCALE_OFF + 16u * lane : DS4_OOB);
-        buf_load_lds16(wr, sd + 320, in ? wo + ustride + Unit<B>::SCALE_OFF + 16u * lane : DS4_OOB);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          buf_load_lds16(wr, sd + 320 * r, in ? wo + r * ustride + Unit<B>::SCALE_OFF + 16u * lane : DS4_OOB);
       }
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int p = 0; p < B / 2; ++p)
           sg.wd[r].code[p] = __builtin_bit_cast(
               u4, __builtin_amdgcn_raw_buffer_load_b128(wr, (in ? wo + r * ustride : DS4_OOB) + 1024 * p + 16 * lane,
                                                         0, 0));
     } else {
-      sg.wd[0] = load_unit_buf<B>(wr, wo, lane);
-      sg.wd[1] = load_unit_buf<B>(wr, in ? wo + ustride : DS4_OOB, lane);
+#pragma unroll
+      for (int r = 0; r < R; ++r) sg.wd[r] = load_unit_buf<B>(wr, in ? wo + r * ustride : DS4_OOB, lane);
     }
     // h of token r16 if it chose the expert (zeros otherwise, weight 0)
     const bool routed = (tmask >> r16) & 1u;  // implies r16 < T
@@ -1429,15 +1440,15 @@ __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
     Stage sg = sg0;
     if constexpr (SDL) {  // scales of row r16, d|dmin of rows 4g..4g+3 (the unit's byte layout)
       wait_vm<(PD - 1) * LPS>();  // this step's loads (LDS and registers) have landed
-      const char *sd = sdl + (wave * PD + slot) * 640;
+      const char *sd = sdl + (wave * PD + slot) * (R * 320);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < R; ++r) {
         sg.wd[r].scale = *reinterpret_cast<const u4 *>(sd + 320 * r + 16 * r16);
         sg.wd[r].dd = *reinterpret_cast<const u4 *>(sd + 320 * r + 256 + 16 * g);
       }
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < R; ++r) {
       const UnitDecoded dd = decode_unit(sg.wd[r], g);
       f4 ac = (f4){0.f, 0.f, 0.f, 0.f};
 #define DEC_STEP(S) ac = mfma16(step_frag<S, B>(sg.wd[r], dd), sg.b[S], ac);
@@ -1461,11 +1472,11 @@ __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
     }
   }
   if constexpr (SDL) wait_vm<0>();  // the trailing loads into LDS, before the workgroup's LDS is released
-  __shared__ f4 red[8][2][64];
-  red[wave][0][lane] = y[0];
-  red[wave][1][lane] = y[1];
+  __shared__ f4 red[8][R][64];
+#pragma unroll
+  for (int r = 0; r < R; ++r) red[wave][r][lane] = y[r];
   __syncthreads();
-  if (wave >= 2) return;
+  if (wave >= R) return;
   // wave r adds the 8 waves' sums of row tile rt0 + r in wave order
   f4 acc = red[0][wave][lane];
 #pragma unroll
@@ -1478,16 +1489,19 @@ __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
     *reinterpret_cast<f4 *>(a.dpart + ((size_t)half * a.T + r16) * a.H + (rt0 + wave) * 16 + 4 * g) = acc;
 }
 
-// y = partial of half 0 + partial of half 1 (+ shared-expert output)
+// y = the NH partials added in order (+ shared-expert output)
+template <int NH>
 __global__ __launch_bounds__(256) void k_down_reduce(const float *__restrict__ part, const float *__restrict__ ysh,
                                                      float *__restrict__ y, int T, int H) {
   const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (i >= T * H) return;
-  const f4 p0 = *reinterpret_cast<const f4 *>(part + i);
-  const f4 p1 = *reinterpret_cast<const f4 *>(part + (size_t)T * H + i);
-  f4 v;
+  f4 v = *reinterpret_cast<const f4 *>(part + i);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = p0[q] + p1[q];
+  for (int h = 1; h < NH; ++h) {
+    const f4 p = *reinterpret_cast<const f4 *>(part + (size_t)h * T * H + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += p[q];
+  }
   if (ysh) {
     const f4 sv = *reinterpret_cast<const f4 *>(ysh + i);
 #pragma unroll
@@ -1894,11 +1908,13 @@ static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Tim
     return hipGetLastError();
   }
   if (a.I == a.Ipad && a.dpart) {  // two row tiles per wave, the tiles in two halves
-    DS4_LAUNCH(tm, (k_down_dec2<DN2_PD, B, DN2_SDL>), dim3((unsigned)(a.H >> 5), 2), dim3(512), 0, s, a);
+    static_assert(DN2_NH <= DEC_DOWN_SPLITS, "workspace partials");
+    DS4_LAUNCH(tm, (k_down_dec2<DN2_PD, B, DN2_SDL, DN2_R, DN2_NH>), dim3((unsigned)(a.H / (16 * DN2_R)), DN2_NH),
+               dim3(512), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    DS4_LAUNCH(tm_combine, k_down_reduce, dim3((unsigned)((a.T * a.H / 4 + 255) / 256)), dim3(256), 0, s, a.dpart,
-               a.ysh, a.y, a.T, a.H);
+    DS4_LAUNCH(tm_combine, k_down_reduce<DN2_NH>, dim3((unsigned)((a.T * a.H / 4 + 255) / 256)), dim3(256), 0, s,
+               a.dpart, a.ysh, a.y, a.T, a.H);
     return hipGetLastError();
   }
   // I below 256 (padded reduction)

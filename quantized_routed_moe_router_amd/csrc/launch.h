@@ -59,6 +59,10 @@ struct GemmAct {
   uint32_t row_bytes, srow_bytes;
 };
 
+// ways the 5..16-token down projection may split its tile list (workspace
+// partials of T x H floats each)
+constexpr int DEC_DOWN_SPLITS = 4;
+
 struct GemmArgs {
   // routed experts
   const uint8_t *gate, *up, *down;   // packed, E matrices each
@@ -80,7 +84,7 @@ struct GemmArgs {
   int T;
   int tile_n;                        // tokens per prefill tile (> 64: wide-tile GEMMs)
   // small batches of 5..16 tokens: the down projection's partial outputs
-  // of the two halves of the tile list [2][T][H]
+  // of the parts of the tile list [DEC_DOWN_SPLITS][T][H]
   float *dpart;
   const float *ysh;                  // [T,H] shared-expert output or nullptr
   float *y;                          // [T,H]
