@@ -1047,25 +1047,31 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
   }
 }
 
-// down fused with the combine (I a multiple of 256), activations through LDS
-template <int PD, int NT, int B>
-__global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
+// down fused with the combine (I a multiple of 256), activations through LDS.
+// Workgroup = one 16-row tile of y, 8 * KSP waves: wave w takes tiles w % 8,
+// w % 8 + 8, ... (experts ascending) over super-blocks part w / 8 of KSP;
+// the partial sums are added in wave order, then the shared output.
+template <int PD, int NT, int B, int KSP>
+__global__ __launch_bounds__(512 * KSP) void k_down_dec_lds(GemmArgs a) {
   constexpr int NI = SlotLoads<NT>::NI;
   constexpr int SLOT = 64 * 16 * NI;
-  __shared__ __attribute__((aligned(16))) char ring_lds[8 * PD * SLOT];
+  constexpr int NWV = 8 * KSP;  // KSP waves split each tile's reduction
+  __shared__ __attribute__((aligned(16))) char ring_lds[NWV * PD * SLOT];
   const int rt = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = wave & 7, kh = wave >> 3;
   const int r16 = lane & 15, g = lane >> 4;
   const int ntl = *a.ntiles;
   const int nsb = a.Ipad >> 8;
   const int nj = a.Ipad >> 4;
-  const int mt = wave < ntl ? (ntl - wave + 7) >> 3 : 0;  // tiles of this wave (<= 32)
-  const int nit = mt * nsb;
+  const int mt = wv < ntl ? (ntl - wv + 7) >> 3 : 0;  // tiles of this wave (<= 32)
+  const int nsw = nsb / KSP, sbb = kh * nsw;            // its super-blocks sbb .. sbb + nsw - 1 of each
+  const int nit = mt * nsw;
   int e_l = 0;        // lane L: expert of this wave's L-th tile
   uint32_t m_l = 0u;  // ... and its token mask
   if (lane < mt) {
-    e_l = a.dtiles[wave + 8 * lane].e;
-    m_l = a.dtiles[wave + 8 * lane].tmask;
+    e_l = a.dtiles[wv + 8 * lane].e;
+    m_l = a.dtiles[wv + 8 * lane].tmask;
   }
   // wait for them here, before any weight load is in flight, so that the
   // pipelined loop below never has to drain the load counter for them
@@ -1099,10 +1105,10 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
   };
   Stage st[PD];
   f4 y = (f4){0.f, 0.f, 0.f, 0.f};
-  int lt = 0, lsb = 0;  // tile and super-block of the next load
+  int lt = 0, lsb = sbb;  // tile and super-block of the next load
   auto load = [&](Stage &sg, int slot) {
     const bool in = lt < mt;
-    const int tile = min(wave + 8 * lt, ntl - 1);
+    const int tile = min(wv + 8 * lt, ntl - 1);
     const int e = __builtin_amdgcn_readlane(e_l, lt & 63);
     const uint32_t tmask = in ? (uint32_t)__builtin_amdgcn_readlane((int)m_l, lt & 63) : 0u;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): earlier reads of this slot are done
@@ -1117,8 +1123,8 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.down + (size_t)e * a.d_bytes, (uint32_t)a.d_bytes);
     sg.wd = load_unit_buf<B>(wr, in ? ((uint32_t)rt * nsb + lsb) * Unit<B>::BYTES : DS4_OOB, lane);
     sg.wt = a.dtiles[tile].w[r16];  // 0 for tokens that did not choose the expert
-    if (++lsb == nsb) {
-      lsb = 0;
+    if (++lsb == sbb + nsw) {
+      lsb = sbb;
       ++lt;
     }
   };
@@ -1151,12 +1157,12 @@ __global__ __launch_bounds__(512) void k_down_dec_lds(GemmArgs a) {
       load(st[sgi], sgi);
     }
   }
-  __shared__ f4 red[8][64];
+  __shared__ f4 red[NWV][64];
   red[wave][lane] = y;
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 1; w < 8; ++w) {
+  for (int w = 1; w < NWV; ++w) {
     const f4 p = red[w][lane];
 #pragma unroll
     for (int q = 0; q < 4; ++q) y[q] += p[q];
@@ -1900,10 +1906,16 @@ static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Tim
   const dim3 grid((unsigned)(a.H >> 4));
   if (a.I == a.Ipad && a.T <= 4) {
     switch (a.T) {
-      case 1: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 1, B>), grid, dim3(512), 0, s, a); break;
-      case 2: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 2, B>), grid, dim3(512), 0, s, a); break;
-      case 3: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 3, B>), grid, dim3(512), 0, s, a); break;
-      default: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 4, B>), grid, dim3(512), 0, s, a);
+      case 1:  // one token: 16 waves, each tile's reduction split over two (a shorter chain per wave)
+        if (a.Ipad % 512 == 0) {
+          DS4_LAUNCH(tm, (k_down_dec_lds<2, 1, B, 2>), grid, dim3(1024), 0, s, a);
+        } else {
+          DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 1, B, 1>), grid, dim3(512), 0, s, a);
+        }
+        break;
+      case 2: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 2, B, 1>), grid, dim3(512), 0, s, a); break;
+      case 3: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 3, B, 1>), grid, dim3(512), 0, s, a); break;
+      default: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 4, B, 1>), grid, dim3(512), 0, s, a);
     }
     return hipGetLastError();
   }
