@@ -169,32 +169,39 @@ __global__ __launch_bounds__(256) void k_router_sliced(const void *__restrict__ 
 }
 
 // ---------------------------------------------------------------- logits, MFMA fp64
-// 64 tokens x 64 experts per workgroup; wave w owns tokens 16w..16w+15 and
-// all 64 experts (four 16x16 fp64 accumulators).  Operands are staged in LDS
-// as fp32 (bf16 and fp32 inputs are exact there) and widened to fp64;
+// 32 tokens x EW experts per workgroup (see the kernel).  Operands are
+// staged in LDS as fp32 (bf16 and fp32 inputs are exact there) and widened to
+// fp64;
 // v_mfma_f64_16x16x4_f64 accumulates in fp64, where every product of two
 // fp32 numbers is exact.
 typedef double d4 __attribute__((ext_vector_type(4)));
+// experts per tile: 32 gives T = 2048 twice the workgroups of 64 (one wave per
+// SIMD left the fp64 MFMA latency exposed there) and leaves T = 8192 as it was
+constexpr int ROUTER_EW = 32;
 
-template <bool XB, bool WB>
+template <bool XB, bool WB, int EW>
 __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x, const void *__restrict__ wr,
                                                      const float *__restrict__ bias, float *__restrict__ logits,
                                                      int T, int E, int H) {
-  // tile: 32 tokens x 64 experts; wave (tw, ew) = 16 tokens x 32 experts.
-  // K-chunks of 32, staged in LDS as fp32 ([k][token], [k][expert]) from raw
-  // registers loaded one chunk ahead; double-buffered, one barrier per chunk.
+  // tile: 32 tokens x EW experts (64 or 32); wave (tw, ew) = 16 tokens x EW/2
+  // experts.  K-chunks of 32, staged in LDS as fp32 ([k][token], [k][expert])
+  // from raw registers loaded one chunk ahead; double-buffered, one barrier
+  // per chunk.
+  static_assert(EW == 64 || EW == 32, "expert tile");
+  constexpr int NA = EW / 32;  // 16x16 accumulators per wave
+  constexpr int WPT = EW / 8;  // weights staged per thread and chunk
   __shared__ float xs[2][32][36];
-  __shared__ float ws[2][32][68];
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
+  __shared__ float ws[2][32][EW + 4];
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * EW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int tw = wave & 1, ew = wave >> 1;
-  d4 acc[2];
+  d4 acc[NA];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) acc[n] = (d4){0.0, 0.0, 0.0, 0.0};
-  // staging: x token tid/8, k (tid%8)*4 (4 values); w expert tid/4, k (tid%4)*8 (8 values)
+  for (int n = 0; n < NA; ++n) acc[n] = (d4){0.0, 0.0, 0.0, 0.0};
+  // staging: x token tid/8, k (tid%8)*4 (4 values); w expert tid/(32/WPT), k (tid%(32/WPT))*WPT
   const int xt = tid >> 3, xk = (tid & 7) * 4;
-  const int we = tid >> 2, wk = (tid & 3) * 8;
+  const int we = tid / (32 / WPT), wk = (tid % (32 / WPT)) * WPT;
   const bool xv = t0 + xt < T, wv = e0 + we < E;
   const int64_t xoff = (int64_t)(xv ? t0 + xt : 0) * H + xk;
   const int64_t woff = (int64_t)(wv ? e0 + we : 0) * H + wk;
@@ -206,12 +213,15 @@ __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x,
     } else {
       rx = xv ? *reinterpret_cast<const u4 *>(reinterpret_cast<const float *>(x) + xoff + k0) : (u4){0u, 0u, 0u, 0u};
     }
-    if (WB) {
+    if (WB && WPT == 8) {
       rw0 = wv ? *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(wr) + woff + k0) : (u4){0u, 0u, 0u, 0u};
+    } else if (WB) {
+      const u2 v = wv ? *reinterpret_cast<const u2 *>(reinterpret_cast<const uint16_t *>(wr) + woff + k0) : (u2){0u, 0u};
+      rw0 = (u4){v.x, v.y, 0u, 0u};
     } else {
       const float *p = reinterpret_cast<const float *>(wr) + woff + k0;
       rw0 = wv ? *reinterpret_cast<const u4 *>(p) : (u4){0u, 0u, 0u, 0u};
-      rw1 = wv ? *reinterpret_cast<const u4 *>(p + 4) : (u4){0u, 0u, 0u, 0u};
+      if (WPT == 8) rw1 = wv ? *reinterpret_cast<const u4 *>(p + 4) : (u4){0u, 0u, 0u, 0u};
     }
   };
   auto store = [&](int b) {
@@ -227,21 +237,22 @@ __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x,
     }
     if (WB) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < WPT / 2; ++i) {
         wf[2 * i] = bf16_bits_to_float((uint16_t)(rw0[i] & 0xFFFFu));
         wf[2 * i + 1] = bf16_bits_to_float((uint16_t)(rw0[i] >> 16));
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wf[i] = __uint_as_float(rw0[i]);
-        wf[4 + i] = __uint_as_float(rw1[i]);
+      for (int i = 0; i < 4; ++i) wf[i] = __uint_as_float(rw0[i]);
+      if (WPT == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wf[4 + i] = __uint_as_float(rw1[i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) xs[b][xk + i][xt] = xf[i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ws[b][wk + i][we] = wf[i];
+    for (int i = 0; i < WPT; ++i) ws[b][wk + i][we] = wf[i];
   };
   const int nk = H / 32;
   load(0);
@@ -254,8 +265,8 @@ __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x,
     for (int kk = 0; kk < 32; kk += 4) {
       const double av = (double)xs[b][kk + g][16 * tw + r16];
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const double bv = (double)ws[b][kk + g][32 * ew + 16 * n + r16];
+      for (int n = 0; n < NA; ++n) {
+        const double bv = (double)ws[b][kk + g][(EW / 2) * ew + 16 * n + r16];
         acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[n], 0, 0, 0);
       }
     }
@@ -265,8 +276,8 @@ __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x,
   // D (fp64 16x16x4): lane holds rows (tokens) g, g+4, g+8, g+12 of the wave's 16,
   // column (expert) r16
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int e = e0 + 32 * ew + 16 * n + r16;
+  for (int n = 0; n < NA; ++n) {
+    const int e = e0 + (EW / 2) * ew + 16 * n + r16;
     if (e >= E) continue;
     const double bb = bias ? (double)bias[e] : 0.0;
 #pragma unroll
@@ -502,7 +513,7 @@ __global__ __launch_bounds__(1024) void k_route_dec(const double *__restrict__ p
 template <bool XB, bool WB>
 static hipError_t router_tiled_t(const void *x, const void *wr, const float *bias, float *logits, int T, int E,
                                  int H, hipStream_t s, const Timing *tm) {
-  DS4_LAUNCH(tm, (k_router_mfma<XB, WB>), dim3((T + 31) / 32, (E + 63) / 64), dim3(256), 0, s, x, wr, bias,
+  DS4_LAUNCH(tm, (k_router_mfma<XB, WB, ROUTER_EW>), dim3((T + 31) / 32, (E + ROUTER_EW - 1) / ROUTER_EW), dim3(256), 0, s, x, wr, bias,
              logits, T, E, H);
   return hipGetLastError();
 }
