@@ -338,15 +338,21 @@ __device__ void xprep_token(int t, int H, const void *xptr, bool x_bf16, _Float1
 // Besides top-k and the activation preparation it records, for the stable
 // permutation, the chunk's count per expert and each assignment's rank among
 // the chunk's assignments to the same expert (earlier tokens first).
-constexpr int CHUNK = 64;
+// Tokens per chunk: 32 up to 4096 tokens (twice the workgroups of 64, so
+// T = 2048 routes in 18 rather than 33 us), 64 above (the scan over chunks
+// then grows faster than the top-k shrinks).
+static int chunk_size(int T) { return T <= 4096 ? 32 : 64; }
 
-// One workgroup of 16 waves per chunk of 64 tokens; wave w takes tokens
-// 4w..4w+3 of the chunk: their logits are loaded together, staged in the
+// One workgroup of 16 waves per chunk of CHUNK tokens; wave w takes tokens
+// TPW*w .. TPW*w+TPW-1 of the chunk: their logits are loaded together, staged in the
 // wave's LDS row and ranked by topk_wave; then the per-expert token masks of
 // the chunk give its counts and each assignment's rank inside the chunk.
+template <int CHUNK>
 __global__ __launch_bounds__(1024) void k_topk_chunk(const float *__restrict__ logits, int T, int E, int k, int H,
                                                      XPrep xp, bool do_x, RouteOut ro, int32_t *__restrict__ ccnt,
                                                      int32_t *__restrict__ lrank) {
+  constexpr int TPW = CHUNK / 16;  // tokens per wave
+  static_assert(CHUNK % 16 == 0 && CHUNK <= 64, "chunk: 16 waves, token masks of two words");
   __shared__ int32_t s_idx[CHUNK * 16];
   __shared__ uint32_t s_mask[256 * 2];
   __shared__ float s_lg[16][256];
@@ -354,10 +360,10 @@ __global__ __launch_bounds__(1024) void k_topk_chunk(const float *__restrict__ l
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = blockIdx.x * CHUNK;
   for (int i = tid; i < E * 2; i += 1024) s_mask[i] = 0u;
-  float lv[4][4];
+  float lv[TPW][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int t = c0 + 4 * wave + q;
+  for (int q = 0; q < TPW; ++q) {
+    const int t = c0 + TPW * wave + q;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
@@ -365,8 +371,8 @@ __global__ __launch_bounds__(1024) void k_topk_chunk(const float *__restrict__ l
     }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int tl = 4 * wave + q;
+  for (int q = 0; q < TPW; ++q) {
+    const int tl = TPW * wave + q;
     const int t = c0 + tl;
     if (t >= T) break;  // uniform per wave
 #pragma unroll
@@ -383,8 +389,8 @@ __global__ __launch_bounds__(1024) void k_topk_chunk(const float *__restrict__ l
     wave_lds_order();
   }
   if (do_x)
-    for (int q = 0; q < 4; ++q) {
-      const int t = c0 + 4 * wave + q;
+    for (int q = 0; q < TPW; ++q) {
+      const int t = c0 + TPW * wave + q;
       if (t >= T) break;
       xprep_token(t, H, xp.x, xp.x_bf16, xp.x16, xp.xs_hi, xp.xs_lo);
     }
@@ -485,10 +491,10 @@ __global__ __launch_bounds__(1024) void k_scan_chunks(int T, int E, int k, int n
 }
 
 // One workgroup per chunk: perm[offsets[e] + base[chunk][e] + rank] = a.
-__global__ __launch_bounds__(256) void k_place_chunks(int T, int E, int k, const int32_t *__restrict__ base,
+__global__ __launch_bounds__(256) void k_place_chunks(int T, int E, int k, int chunk, const int32_t *__restrict__ base,
                                                       const int32_t *__restrict__ lrank, RouteOut ro) {
-  const int c0 = blockIdx.x * CHUNK;
-  const int nt = min(CHUNK, T - c0);
+  const int c0 = blockIdx.x * chunk;
+  const int nt = min(chunk, T - c0);
   for (int i = threadIdx.x; i < nt * k; i += 256) {
     const int64_t a = (int64_t)c0 * k + i;
     const int e = ro.idx[a];
@@ -526,24 +532,28 @@ hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool 
   return router_tiled_t<false, false>(x, wr, bias, logits, T, E, H, s, tm);
 }
 
-int chunk_count(int T) { return (T + CHUNK - 1) / CHUNK; }
+int chunk_count(int T) { return (T + chunk_size(T) - 1) / chunk_size(T); }
 
 int router_slices(int H) { return (H + RSLICE - 1) / RSLICE; }
 
 hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
                                 int32_t *ccnt, int32_t *base, int32_t *lrank, hipStream_t s, const Timing *tm_topk,
                                 const Timing *tm_perm) {
-  const int nchunk = chunk_count(T);
+  const int chunk = chunk_size(T), nchunk = chunk_count(T);
   XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
-  DS4_LAUNCH(tm_topk, k_topk_chunk, dim3(nchunk), dim3(1024), 0, s, logits, T, E, k, H, x, xp != nullptr, ro, ccnt,
-             lrank);
+  if (chunk == 32)
+    DS4_LAUNCH(tm_topk, k_topk_chunk<32>, dim3(nchunk), dim3(1024), 0, s, logits, T, E, k, H, x, xp != nullptr, ro,
+               ccnt, lrank);
+  else
+    DS4_LAUNCH(tm_topk, k_topk_chunk<64>, dim3(nchunk), dim3(1024), 0, s, logits, T, E, k, H, x, xp != nullptr, ro,
+               ccnt, lrank);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the permutation slot times the scan; the placement follows it directly
   DS4_LAUNCH(tm_perm, k_scan_chunks, dim3(1), dim3(1024), 0, s, T, E, k, nchunk, ccnt, base, ro);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_place_chunks, dim3(nchunk), dim3(256), 0, s, T, E, k, base, lrank, ro);
+  hipLaunchKernelGGL(k_place_chunks, dim3(nchunk), dim3(256), 0, s, T, E, k, chunk, base, lrank, ro);
   return hipGetLastError();
 }
 
