@@ -347,7 +347,8 @@ def test_mid_wide_tiles_one_expert():
     assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
 
 
-@pytest.mark.parametrize("T,mode", [(1, "decode"), (5, "decode"), (16, "decode"), (40, "prefill")])
+@pytest.mark.parametrize("T,mode", [(1, "decode"), (2, "decode"), (4, "decode"), (5, "decode"), (16, "decode"),
+                                    (40, "prefill")])
 def test_k16_e256_limits(T, mode):
     """The largest top-k (16) over the largest expert count (256)."""
     q = _q()
@@ -361,6 +362,27 @@ def test_k16_e256_limits(T, mode):
     check_routing(bufs, L, label=f"k16 {mode} T={T}")
     ref, _, _ = oracle.layer_inputs(L)
     assert per_token_err(y.cpu().numpy(), ref) <= TOL_Y
+
+
+@pytest.mark.parametrize("T", [4096, 4100])
+def test_prefill_routing_chunk_sizes(T):
+    """Prefill routes in 32-token chunks up to 4096 tokens and 64-token chunks
+    above: both sides of the switch, the second with a ragged last chunk."""
+    q = _q()
+    wl = synth.Workload("chunks", 0, T=T, H=256, E=64, I=128, k=4, x_dtype="f32", router_dtype="f32",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    idx = check_routing(bufs, L, label=f"chunks T={T}")
+    toks = _sample_tokens(idx)
+    ref, ridx, _ = oracle.layer_inputs(L, tokens=toks)
+    assert np.array_equal(ridx, idx[toks])
+    err = per_token_err(y.cpu().numpy()[toks], ref)
+    print(f"chunks T={T}: {len(toks)} tokens checked, per-token rel err {err:.3e}")
+    assert err <= TOL_Y
 
 
 @pytest.mark.parametrize("T,mode", [(3, "decode"), (12, "decode"), (70, "prefill")])
