@@ -308,22 +308,22 @@ def test_mid_shared_expert_decode(T, I):
     assert err <= TOL_Y
 
 
-@pytest.mark.parametrize("I", [512, 1024])
-def test_mid_decode_one_token_split_down(I):
+@pytest.mark.parametrize("I,bits", [(512, 2), (1024, 2), (512, 4)])
+def test_mid_decode_one_token_split_down(I, bits):
     """One token with I a multiple of 512: the down kernel splits each tile's
     reduction over two waves (one and two super-blocks per wave)."""
     q = _q()
     wl = synth.Workload("mid_split", 0, T=1, H=512, E=16, I=I, k=4, x_dtype="f32", router_dtype="f32",
-                        router_sigma=0.05, layer_id=0)
+                        router_sigma=0.05, layer_id=0, bits=bits)
     L = synth.make_layer(wl)
     dl = q.from_layer_inputs(L)
     bufs = dl.routing_buffers(1)
     y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE, routing=bufs)
     torch.cuda.synchronize()
-    check_routing(bufs, L, label=f"split down I={I}")
+    check_routing(bufs, L, label=f"split down I={I} bits={bits}")
     ref, _, _ = oracle.layer_inputs(L)
     err = per_token_err(y.cpu().numpy(), ref)
-    print(f"split down I={I}: per-token rel err {err:.3e}")
+    print(f"split down I={I} bits={bits}: per-token rel err {err:.3e}")
     assert err <= TOL_Y
 
 
