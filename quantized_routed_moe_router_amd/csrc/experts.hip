@@ -1906,16 +1906,24 @@ static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Tim
   const dim3 grid((unsigned)(a.H >> 4));
   if (a.I == a.Ipad && a.T <= 4) {
     switch (a.T) {
-      case 1:  // one token: 16 waves, each tile's reduction split over two (a shorter chain per wave)
+      case 1:  // 16 waves, each tile's reduction split over two (a shorter chain per wave)
         if (a.Ipad % 512 == 0) {
           DS4_LAUNCH(tm, (k_down_dec_lds<2, 1, B, 2>), grid, dim3(1024), 0, s, a);
         } else {
           DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 1, B, 1>), grid, dim3(512), 0, s, a);
         }
         break;
-      case 2: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 2, B, 1>), grid, dim3(512), 0, s, a); break;
-      case 3: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 3, B, 1>), grid, dim3(512), 0, s, a); break;
-      default: DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 4, B, 1>), grid, dim3(512), 0, s, a);
+      case 2:
+        if (a.Ipad % 512 == 0) DS4_LAUNCH(tm, (k_down_dec_lds<2, 2, B, 2>), grid, dim3(1024), 0, s, a);
+        else DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 2, B, 1>), grid, dim3(512), 0, s, a);
+        break;
+      case 3:
+        if (a.Ipad % 512 == 0) DS4_LAUNCH(tm, (k_down_dec_lds<2, 3, B, 2>), grid, dim3(1024), 0, s, a);
+        else DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 3, B, 1>), grid, dim3(512), 0, s, a);
+        break;
+      default:
+        if (a.Ipad % 512 == 0) DS4_LAUNCH(tm, (k_down_dec_lds<2, 4, B, 2>), grid, dim3(1024), 0, s, a);
+        else DS4_LAUNCH(tm, (k_down_dec_lds<DN_LDS_PD, 4, B, 1>), grid, dim3(512), 0, s, a);
     }
     return hipGetLastError();
   }

@@ -308,22 +308,23 @@ def test_mid_shared_expert_decode(T, I):
     assert err <= TOL_Y
 
 
-@pytest.mark.parametrize("I,bits", [(512, 2), (1024, 2), (512, 4)])
-def test_mid_decode_one_token_split_down(I, bits):
-    """One token with I a multiple of 512: the down kernel splits each tile's
-    reduction over two waves (one and two super-blocks per wave)."""
+@pytest.mark.parametrize("T,I,bits", [(1, 512, 2), (1, 1024, 2), (1, 512, 4), (3, 512, 2), (4, 1024, 4)])
+def test_mid_decode_split_down(T, I, bits):
+    """Batches of up to four tokens with I a multiple of 512: the down kernel
+    splits each tile's reduction over two waves (one and two super-blocks per
+    wave)."""
     q = _q()
-    wl = synth.Workload("mid_split", 0, T=1, H=512, E=16, I=I, k=4, x_dtype="f32", router_dtype="f32",
+    wl = synth.Workload("mid_split", 0, T=T, H=512, E=16, I=I, k=4, x_dtype="f32", router_dtype="f32",
                         router_sigma=0.05, layer_id=0, bits=bits)
     L = synth.make_layer(wl)
     dl = q.from_layer_inputs(L)
-    bufs = dl.routing_buffers(1)
+    bufs = dl.routing_buffers(T)
     y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE, routing=bufs)
     torch.cuda.synchronize()
-    check_routing(bufs, L, label=f"split down I={I} bits={bits}")
+    check_routing(bufs, L, label=f"split down T={T} I={I} bits={bits}")
     ref, _, _ = oracle.layer_inputs(L)
     err = per_token_err(y.cpu().numpy(), ref)
-    print(f"split down I={I} bits={bits}: per-token rel err {err:.3e}")
+    print(f"split down T={T} I={I} bits={bits}: per-token rel err {err:.3e}")
     assert err <= TOL_Y
 
 
