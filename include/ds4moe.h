@@ -190,7 +190,9 @@ int ds4moe_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows,
                    void *stream);
 
 /* Workspace bytes needed by a call with `T` tokens in `mode`
- * (ds4moe_mode).  Returns 0 if dims is NULL or invalid. */
+ * (ds4moe_mode).  Never decreases with T within a mode, so a workspace sized
+ * for the largest batch serves every smaller one.  Returns 0 if dims is NULL
+ * or invalid. */
 size_t ds4moe_workspace_bytes(const ds4moe_dims *dims, int32_t T, int32_t mode);
 
 /* Router only: logits, scores, top-k, weights, per-expert histogram, scan and

@@ -68,14 +68,16 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
   }
   L.max_tiles = mode == DS4MOE_MODE_DECODE ? (int)(A < E ? A : E) : (int)(A / L.tile_n + (A < E ? A : E));
   L.logits = take(sizeof(float) * T * E);
-  L.part = L.sliced ? take(sizeof(double) * router_slices((int)H) * T * E) : 0;
+  // the sliced router's partial sums; reserved at T > 16 too, so that the
+  // workspace never shrinks as T grows
+  L.part = take(sizeof(double) * router_slices((int)H) * (T < 16 ? T : 16) * E);
   L.idx = take(sizeof(int32_t) * A);
   L.w = take(sizeof(float) * A);
   L.counts = take(sizeof(int32_t) * E);
   L.offsets = take(sizeof(int32_t) * (E + 1));
   L.perm = take(sizeof(int32_t) * A);
   if (!L.sliced) {
-    const int64_t nch = chunk_count((int)T);
+    const int64_t nch = chunk_count_max((int)T);  // the smallest chunk: sizes grow with T
     L.ccnt = take(sizeof(int32_t) * nch * E);
     L.cbase = take(sizeof(int32_t) * nch * E);
     L.lrank = take(sizeof(int32_t) * A);

@@ -122,6 +122,8 @@ hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool 
                                float *logits, int T, int E, int H, hipStream_t s, const Timing *tm = nullptr);
 // large T: top-k + activation prep + per-chunk counts/ranks, scan, placement
 int chunk_count(int T);
+// an upper bound of chunk_count that never decreases with T (workspace sizing)
+int chunk_count_max(int T);
 hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,
                                 int32_t *ccnt, int32_t *base, int32_t *lrank, hipStream_t s,
                                 const Timing *tm_topk = nullptr, const Timing *tm_perm = nullptr);

@@ -534,6 +534,8 @@ hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool 
 
 int chunk_count(int T) { return (T + chunk_size(T) - 1) / chunk_size(T); }
 
+int chunk_count_max(int T) { return (T + 31) / 32; }
+
 int router_slices(int H) { return (H + RSLICE - 1) / RSLICE; }
 
 hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H, const XPrep *xp, RouteOut ro,

@@ -82,6 +82,22 @@ def test_workspace_bytes():
     assert B.lib().ds4moe_workspace_bytes(None, 16, 1) == 0
 
 
+def test_workspace_bytes_grow_with_T():
+    """A workspace sized for the largest batch serves every smaller one, in
+    every mode, across the decode kernel classes and the prefill routing's
+    chunk-size switch; decode T >= 5 holds the down projection's partials."""
+    for d in (dims(), dims(Is=2048), dims(H=256, I=128, E=8, k=2, x_dtype=B.DS4MOE_F32, router_dtype=B.DS4MOE_F32)):
+        for mode, Ts in ((B.MODE_DECODE, range(1, 17)),
+                         (B.MODE_PREFILL, [0, 1, 16, 17, 64, 65, 2048, 4095, 4096, 4097, 4160, 8192]),
+                         (B.MODE_ROUTE, [1, 16, 17, 4096, 4097, 8192])):
+            sizes = [B.ds4moe_workspace_bytes(d, T, mode) for T in Ts]
+            assert all(x > 0 for x in sizes), (mode, sizes)
+            assert sizes == sorted(sizes), (mode, list(zip(Ts, sizes)))
+    d = dims()
+    for T in (5, 16):
+        assert B.ds4moe_workspace_bytes(d, T, B.MODE_DECODE) >= 4 * T * 4096 * 4
+
+
 @pytest.mark.parametrize("bad,status", [
     (dict(H=100), B.DS4MOE_ERR_SHAPE), (dict(H=0), B.DS4MOE_ERR_SHAPE), (dict(I=8), B.DS4MOE_ERR_SHAPE),
     (dict(I=384), B.DS4MOE_ERR_SHAPE), (dict(k=0), B.DS4MOE_ERR_SHAPE), (dict(k=17, E=32), B.DS4MOE_ERR_SHAPE),
