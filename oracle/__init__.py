@@ -32,7 +32,7 @@ _lib = None
 
 def build_lib(force: bool = False) -> str:
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", _SRC,
+        cmd = ["gcc", "-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", _SRC,
                "-o", _LIB_PATH + ".tmp", "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(_LIB_PATH + ".tmp", _LIB_PATH)

@@ -62,32 +62,44 @@ static double half_to_double(uint16_t h) {
 static int64_t block_bytes(int bits) { return 16 + 32 * bits + 4; }
 
 /* Value of weight i (0..255) of one canonical block with `bits`-bit codes,
- * exact in double: every product has at most 19 significant bits and the
- * difference of two such numbers of the binary16 range fits in 53 bits.
- * [workload] */
-static double block_weight(const uint8_t *blk, int i, int bits) {
-  const int per_byte = 8 / bits, nb = (int)block_bytes(bits);
+ * given the block's d and dmin; exact in double: every product has at most
+ * 19 significant bits and the difference of two such numbers of the binary16
+ * range fits in 53 bits.  [workload] */
+static double block_weight_dm(const uint8_t *blk, int i, int bits, double d, double dmin) {
+  const int per_byte = 8 / bits;
   int j = i / 16;                                  /* sub-block */
   int sc = blk[j] & 0x0F;                          /* low nibble: scale */
   int mn = blk[j] >> 4;                            /* high nibble: min  */
   int q = (blk[16 + i / per_byte] >> (bits * (i % per_byte))) & ((1 << bits) - 1);
-  double d = half_to_double((uint16_t)(blk[nb - 4] | (blk[nb - 3] << 8)));
-  double dmin = half_to_double((uint16_t)(blk[nb - 2] | (blk[nb - 1] << 8)));
   return d * sc * q - dmin * mn;
+}
+
+/* d (bytes nb-4, nb-3) and dmin (bytes nb-2, nb-1) of one block. */
+static void block_d_dmin(const uint8_t *blk, int bits, double *d, double *dmin) {
+  const int nb = (int)block_bytes(bits);
+  *d = half_to_double((uint16_t)(blk[nb - 4] | (blk[nb - 3] << 8)));
+  *dmin = half_to_double((uint16_t)(blk[nb - 2] | (blk[nb - 1] << 8)));
 }
 
 /* Dequantize n blocks (256 weights each) to doubles. */
 void oracle_dequant_f64_bits(const uint8_t *blocks, int64_t nblocks, int bits, double *out) {
   const int64_t nb = block_bytes(bits);
-  for (int64_t b = 0; b < nblocks; ++b)
-    for (int i = 0; i < 256; ++i) out[b * 256 + i] = block_weight(blocks + nb * b, i, bits);
+#pragma omp parallel for schedule(static) if (nblocks >= 4096)
+  for (int64_t b = 0; b < nblocks; ++b) {
+    double d, dmin;
+    block_d_dmin(blocks + nb * b, bits, &d, &dmin);
+    for (int i = 0; i < 256; ++i) out[b * 256 + i] = block_weight_dm(blocks + nb * b, i, bits, d, dmin);
+  }
 }
 
 /* Dequantize n blocks to fp32: the exact value rounded once to nearest. */
 void oracle_dequant_f32_bits(const uint8_t *blocks, int64_t nblocks, int bits, float *out) {
   const int64_t nb = block_bytes(bits);
-  for (int64_t b = 0; b < nblocks; ++b)
-    for (int i = 0; i < 256; ++i) out[b * 256 + i] = (float)block_weight(blocks + nb * b, i, bits);
+  for (int64_t b = 0; b < nblocks; ++b) {
+    double d, dmin;
+    block_d_dmin(blocks + nb * b, bits, &d, &dmin);
+    for (int i = 0; i < 256; ++i) out[b * 256 + i] = (float)block_weight_dm(blocks + nb * b, i, bits, d, dmin);
+  }
 }
 
 void oracle_dequant_f64(const uint8_t *blocks, int64_t nblocks, double *out) {
@@ -184,23 +196,74 @@ void oracle_permute(const int32_t *idx, int64_t T, int64_t k, int64_t E, int32_t
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* Dense SwiGLU FFN on one token: y = Wd * (silu(Wg x) * (Wu x)).
- * Wg, Wu [I,H], Wd [H,I] row-major doubles; every dot product sequential. */
-static void swiglu_ffn(const double *Wg, const double *Wu, const double *Wd, const double *x, int64_t H,
-                       int64_t I, double *hbuf, double *y) {
-  for (int64_t i = 0; i < I; ++i) {
-    double g = 0.0, u = 0.0;
-    for (int64_t c = 0; c < H; ++c) {
-      g += Wg[i * H + c] * x[c];
-      u += Wu[i * H + c] * x[c];
+/* Outputs computed side by side: 4 rows of W by 8 tokens.  Lane j of a
+ * 4-wide vector below belongs to one token, so every output keeps its own
+ * accumulator and its arithmetic is that of a lone dot product. */
+#define TB 8
+#define RB 4
+typedef double dvec4 __attribute__((vector_size(32)));
+
+/* out[t][r] = sum_{c=0}^{K-1} W[r][c] * v[t][c] for the n rows v[t] of
+ * vT, stored transposed in blocks of TB tokens: vT[blk][c][j] is
+ * v[TB*blk + j][c] (rows beyond n are zero and their outputs are dropped).
+ * W [R,K] row-major; out [n,R].  Every sum is taken in order c = 0, 1, ...,
+ * product first, then the addition, both rounded in double. */
+static void rows_times_tokens(const double *W, int64_t R, int64_t K, const double *vT, int64_t n, double *out) {
+  const int64_t nblk = (n + TB - 1) / TB;
+  for (int64_t b0 = 0; b0 < nblk; b0 += 16)      /* 128 tokens at a time, so that they stay in cache */
+#pragma omp parallel for schedule(static)
+  for (int64_t r0 = 0; r0 < R; r0 += RB)
+    for (int64_t b = b0; b < nblk && b < b0 + 16; ++b) {
+      const double *w[RB];
+      for (int i = 0; i < RB; ++i) w[i] = W + (r0 + i < R ? r0 + i : R - 1) * K;   /* rows past R: dropped */
+      dvec4 lo[RB] = {{0}}, hi[RB] = {{0}};          /* tokens 0-3 and 4-7 of the block */
+      const double *v = vT + b * K * TB;
+      for (int64_t c = 0; c < K; ++c) {
+        dvec4 v_lo, v_hi;
+        memcpy(&v_lo, v + c * TB, sizeof v_lo);
+        memcpy(&v_hi, v + c * TB + 4, sizeof v_hi);
+        for (int i = 0; i < RB; ++i) {
+          lo[i] += w[i][c] * v_lo;
+          hi[i] += w[i][c] * v_hi;
+        }
+      }
+      for (int i = 0; i < RB && r0 + i < R; ++i)
+        for (int j = 0; j < TB && TB * b + j < n; ++j)
+          out[(TB * b + j) * R + r0 + i] = j < 4 ? lo[i][j] : hi[i][j - 4];
     }
-    hbuf[i] = silu(g) * u;
-  }
-  for (int64_t r = 0; r < H; ++r) {
-    double acc = 0.0;
-    for (int64_t i = 0; i < I; ++i) acc += Wd[r * I + i] * hbuf[i];
-    y[r] = acc;
-  }
+}
+
+/* v [n,K] row-major -> the transposed token blocks read by rows_times_tokens. */
+static double *token_blocks(const double *v, int64_t n, int64_t K) {
+  const int64_t nblk = (n + TB - 1) / TB;
+  double *vT = (double *)calloc((size_t)(nblk * K * TB), sizeof(double));
+  if (!vT) return NULL;
+  for (int64_t t = 0; t < n; ++t)
+    for (int64_t c = 0; c < K; ++c) vT[(t / TB) * K * TB + c * TB + t % TB] = v[t * K + c];
+  return vT;
+}
+
+/* Dense SwiGLU FFN on n tokens: y_t = Wd * (silu(Wg x_t) * (Wu x_t)).
+ * Wg, Wu [I,H], Wd [H,I] row-major doubles; xs [n,H]; y [n,H].  Each token's
+ * FFN is computed on its own (rows_times_tokens).  Returns 0, or 1 when out
+ * of memory. */
+static int swiglu_ffn(const double *Wg, const double *Wu, const double *Wd, const double *xs, int64_t n, int64_t H,
+                      int64_t I, double *y) {
+  double *xT = token_blocks(xs, n, H);
+  double *g = (double *)malloc(sizeof(double) * (size_t)(n * I));
+  double *u = (double *)malloc(sizeof(double) * (size_t)(n * I));
+  if (!xT || !g || !u) { free(xT); free(g); free(u); return 1; }
+  rows_times_tokens(Wg, I, H, xT, n, g);
+  rows_times_tokens(Wu, I, H, xT, n, u);
+  free(xT);
+  for (int64_t i = 0; i < n * I; ++i) g[i] = silu(g[i]) * u[i];   /* h */
+  free(u);
+  double *hT = token_blocks(g, n, I);
+  free(g);
+  if (!hT) return 1;
+  rows_times_tokens(Wd, H, I, hT, n, y);
+  free(hT);
+  return 0;
 }
 
 /*
@@ -210,76 +273,69 @@ static void swiglu_ffn(const double *Wg, const double *Wu, const double *Wd, con
  *   gate, up: E canonical-block matrices W[I,H]; down: E matrices W[H,I];
  *   sh_gate, sh_up [Is,H], sh_down [H,Is] fp32 values or NULL (Is = 0);
  * Outputs: y [T,H] fp32; idx/w [T,k] (nullable).
- * Each routed expert is dequantized once and applied to each of its tokens
- * separately; every token's FFN is computed densely and independently.
+ * Each routed expert is dequantized once and applied to each of its tokens;
+ * every token's FFN is computed densely and independently.
  */
 int oracle_layer_bits(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,
                       const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down, int bits,
                       int64_t Is, const float *sh_gate, const float *sh_up, const float *sh_down, float *y,
                       int32_t *idx_out, float *w_out) {
   if (T <= 0) return 0;
+  int rc = 0;
   float *logits = (float *)malloc(sizeof(float) * (size_t)(T * E));
   int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * k));
   float *w = (float *)malloc(sizeof(float) * (size_t)(T * k));
   double *wd = (double *)malloc(sizeof(double) * (size_t)(T * k));
-  double *Y = (double *)calloc((size_t)(T * k * H), sizeof(double));
-  if (!logits || !idx || !w || !wd || !Y) return 1;
+  double *Y = (double *)calloc((size_t)(T * k * H), sizeof(double));   /* per assignment a = t*k + j */
+  double *xd = (double *)malloc(sizeof(double) * (size_t)(T * H));
+  int64_t *as = (int64_t *)malloc(sizeof(int64_t) * (size_t)(T * k));
+  double *Wg = (double *)malloc(sizeof(double) * (size_t)(I * H));
+  double *Wu = (double *)malloc(sizeof(double) * (size_t)(I * H));
+  double *Wd = (double *)malloc(sizeof(double) * (size_t)(H * I));
+  double *xs = (double *)malloc(sizeof(double) * (size_t)(T * H));
+  double *ys = (double *)malloc(sizeof(double) * (size_t)(T * H));
+  if (!logits || !idx || !w || !wd || !Y || !xd || !as || !Wg || !Wu || !Wd || !xs || !ys) { rc = 1; goto done; }
   oracle_logits(x, wr, bias, T, E, H, logits);
   oracle_topk(logits, T, E, k, idx, w, wd);
-  int64_t mat_blocks = I * H / 256;
+  for (int64_t i = 0; i < T * H; ++i) xd[i] = (double)x[i];
 
-#pragma omp parallel for schedule(dynamic, 1)
+  const int64_t mat_blocks = I * H / 256, mat_bytes = mat_blocks * block_bytes(bits);
   for (int64_t e = 0; e < E; ++e) {
-    int64_t n = 0;
-    for (int64_t a = 0; a < T * k; ++a) n += idx[a] == e;
+    int64_t n = 0;                                   /* the expert's assignments, a ascending */
+    for (int64_t a = 0; a < T * k; ++a)
+      if (idx[a] == e) as[n++] = a;
     if (!n) continue;
-    double *Wg = (double *)malloc(sizeof(double) * (size_t)(I * H));
-    double *Wu = (double *)malloc(sizeof(double) * (size_t)(I * H));
-    double *Wd = (double *)malloc(sizeof(double) * (size_t)(H * I));
-    double *xt = (double *)malloc(sizeof(double) * (size_t)H);
-    double *hb = (double *)malloc(sizeof(double) * (size_t)I);
-    const int64_t mat_bytes = mat_blocks * block_bytes(bits);
     oracle_dequant_f64_bits(gate + e * mat_bytes, mat_blocks, bits, Wg);
     oracle_dequant_f64_bits(up + e * mat_bytes, mat_blocks, bits, Wu);
     oracle_dequant_f64_bits(down + e * mat_bytes, mat_blocks, bits, Wd);
-    for (int64_t a = 0; a < T * k; ++a) {
-      if (idx[a] != e) continue;
-      int64_t t = a / k;
-      for (int64_t c = 0; c < H; ++c) xt[c] = (double)x[t * H + c];
-      swiglu_ffn(Wg, Wu, Wd, xt, H, I, hb, Y + a * H);
-    }
-    free(Wg); free(Wu); free(Wd); free(xt); free(hb);
+    for (int64_t j = 0; j < n; ++j) memcpy(xs + j * H, xd + (as[j] / k) * H, sizeof(double) * (size_t)H);
+    if (swiglu_ffn(Wg, Wu, Wd, xs, n, H, I, ys)) { rc = 1; goto done; }
+    for (int64_t j = 0; j < n; ++j) memcpy(Y + as[j] * H, ys + j * H, sizeof(double) * (size_t)H);
   }
 
-  double *Sg = NULL, *Su = NULL, *Sd = NULL;
-  if (Is > 0) {
-    Sg = (double *)malloc(sizeof(double) * (size_t)(Is * H));
-    Su = (double *)malloc(sizeof(double) * (size_t)(Is * H));
-    Sd = (double *)malloc(sizeof(double) * (size_t)(H * Is));
-    for (int64_t i = 0; i < Is * H; ++i) { Sg[i] = sh_gate[i]; Su[i] = sh_up[i]; Sd[i] = sh_down[i]; }
+  if (Is > 0) {                                      /* the shared expert on every token */
+    free(Wg); free(Wu); free(Wd);
+    Wg = (double *)malloc(sizeof(double) * (size_t)(Is * H));
+    Wu = (double *)malloc(sizeof(double) * (size_t)(Is * H));
+    Wd = (double *)malloc(sizeof(double) * (size_t)(H * Is));
+    if (!Wg || !Wu || !Wd) { rc = 1; goto done; }
+    for (int64_t i = 0; i < Is * H; ++i) { Wg[i] = sh_gate[i]; Wu[i] = sh_up[i]; Wd[i] = sh_down[i]; }
+    if (swiglu_ffn(Wg, Wu, Wd, xd, T, H, Is, ys)) { rc = 1; goto done; }
   }
 #pragma omp parallel for schedule(static)
-  for (int64_t t = 0; t < T; ++t) {
-    double *acc = (double *)calloc((size_t)H, sizeof(double));
-    for (int64_t j = 0; j < k; ++j)              /* rank order */
-      for (int64_t c = 0; c < H; ++c) acc[c] += wd[t * k + j] * Y[(t * k + j) * H + c];
-    if (Is > 0) {
-      double *xt = (double *)malloc(sizeof(double) * (size_t)H);
-      double *hb = (double *)malloc(sizeof(double) * (size_t)Is);
-      double *ys = (double *)malloc(sizeof(double) * (size_t)H);
-      for (int64_t c = 0; c < H; ++c) xt[c] = (double)x[t * H + c];
-      swiglu_ffn(Sg, Su, Sd, xt, H, Is, hb, ys);
-      for (int64_t c = 0; c < H; ++c) acc[c] += ys[c];
-      free(xt); free(hb); free(ys);
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < k; ++j) acc += wd[t * k + j] * Y[(t * k + j) * H + c];   /* rank order */
+      if (Is > 0) acc += ys[t * H + c];
+      y[t * H + c] = (float)acc;
     }
-    for (int64_t c = 0; c < H; ++c) y[t * H + c] = (float)acc[c];
-    free(acc);
-  }
   if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * (size_t)(T * k));
   if (w_out) memcpy(w_out, w, sizeof(float) * (size_t)(T * k));
-  free(Sg); free(Su); free(Sd);
-  free(logits); free(idx); free(w); free(wd); free(Y);
-  return 0;
+done:
+  free(logits); free(idx); free(w); free(wd); free(Y); free(xd); free(as);
+  free(Wg); free(Wu); free(Wd); free(xs); free(ys);
+  return rc;
 }
 
 int oracle_layer(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,

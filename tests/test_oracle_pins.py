@@ -242,6 +242,30 @@ def test_topk_ties_and_uniform():
     assert idx.tolist() == [[1, 2, 4, 3, 7]]
 
 
+def test_topk_nan_and_inf_ordering_bruteforce():
+    """NaN logits (out of contract) rank below every number, -inf included,
+    and among themselves by expert index; +inf ranks first.  Checked against
+    a plain Python sort on the key (is NaN, -logit, expert) over random rows
+    mixing NaN, +-inf, exact ties and ordinary values, k from 1 to E."""
+    rng = np.random.default_rng(23)
+    for trial in range(300):
+        E = int(rng.integers(2, 20))
+        k = int(rng.integers(1, E + 1))
+        lg = rng.standard_normal((1, E)).astype(np.float32)
+        r = rng.random(E)
+        lg[0, r < 0.25] = np.nan
+        lg[0, (r >= 0.25) & (r < 0.32)] = -np.inf
+        lg[0, (r >= 0.32) & (r < 0.36)] = np.inf
+        lg[0, (r >= 0.36) & (r < 0.46)] = 0.5          # exact ties
+        idx, _, _ = oracle.topk(lg, k)
+        row = [float(v) for v in lg[0]]
+        order = sorted(range(E), key=lambda e: (math.isnan(row[e]), 0.0 if math.isnan(row[e]) else -row[e], e))
+        assert list(idx[0]) == order[:k], (row, k)
+    lg = np.full((1, 6), np.nan, np.float32)
+    idx, _, _ = oracle.topk(lg, 4)
+    assert idx.tolist() == [[0, 1, 2, 3]]                     # all NaN: experts in index order
+
+
 def test_topk_weights_invariants():
     rng = np.random.default_rng(22)
     lg = (3 * rng.standard_normal((200, 256))).astype(np.float32)
