@@ -378,11 +378,10 @@ def test_prefill_routing_chunk_sizes(T):
     y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
     torch.cuda.synchronize()
     idx = check_routing(bufs, L, label=f"chunks T={T}")
-    toks = _sample_tokens(idx)
-    ref, ridx, _ = oracle.layer_inputs(L, tokens=toks)
-    assert np.array_equal(ridx, idx[toks])
-    err = per_token_err(y.cpu().numpy()[toks], ref)
-    print(f"chunks T={T}: {len(toks)} tokens checked, per-token rel err {err:.3e}")
+    ref, ridx, _ = oracle.layer_inputs(L)
+    assert np.array_equal(ridx, idx)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"chunks T={T}: all tokens checked, per-token rel err {err:.3e}")
     assert err <= TOL_Y
 
 
@@ -537,29 +536,19 @@ def test_full_decode16(full):
     assert 40 <= d <= 128
 
 
-def _sample_tokens(idx, n=12):
-    """First, last, and tokens routed to the most and least loaded experts."""
-    T = idx.shape[0]
-    counts = np.bincount(idx.reshape(-1), minlength=256)
-    hot = int(np.argmax(counts))
-    cold = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
-    toks = {0, T - 1, T // 2}
-    toks |= set(np.where((idx == hot).any(axis=1))[0][:4].tolist())
-    toks |= set(np.where((idx == cold).any(axis=1))[0][:4].tolist())
-    rng = np.random.default_rng(T)
-    toks |= set(rng.integers(0, T, size=n).tolist())
-    return sorted(toks)
+def test_full_prefill_all_tokens(full):
+    """The 2048-token prefill chunk, every token against the oracle."""
+    _full_case(full, "prefill", "prefill")
 
 
-def test_full_prefill_sampled(full):
-    _full_case(full, "prefill", "prefill", sample=_sample_tokens)
-
-
-def test_full_skewed_sampled(full, full_shared):
-    y, idx = _full_case(full, "skewed", "prefill", sample=_sample_tokens, shared=full_shared)
+def test_full_skewed_all_tokens(full, full_shared):
+    """The 8192-token Zipf-skewed prefill with the shared expert, every token
+    against the oracle: the hottest expert's ~6000 tokens run through
+    dozens of full tiles, the coldest expert's few through one partial tile."""
+    y, idx = _full_case(full, "skewed", "prefill", shared=full_shared)
     counts = np.bincount(idx.reshape(-1), minlength=256)
     print(f"skewed loads: min {counts.min()} median {int(np.median(counts))} max {counts.max()}")
-    assert counts.max() > 1000
+    assert counts.max() > 1000 and counts.min() < 64
 
 
 def test_full_deterministic(full):
