@@ -23,7 +23,8 @@
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns
  *     every buffer; the library never allocates, frees or keeps a pointer
  *     after a call returns.  Scratch memory comes from the caller's workspace,
- *     sized by ds4moe_workspace_bytes().
+ *     sized by ds4moe_workspace_bytes() (one exception:
+ *     ds4moe_forward_decode_noalloc, whose scratch is a fixed array per GPU).
  *   - Calls only enqueue work on `stream` (a hipStream_t passed as void*,
  *     NULL = the null stream) and return; there is no host synchronisation.
  *   - The small descriptor structs are HOST memory, read during the call only.
@@ -282,6 +283,28 @@ int ds4moe_forward_decode_cached(const ds4moe_dims *dims, const ds4moe_weights *
  * read them after `stream` has synchronised. */
 int ds4moe_cache_stats(const ds4moe_dims *dims, int32_t n_slots, const void *cache, size_t cache_bytes,
                        uint64_t *out, void *stream);
+
+/* NO-ALLOCATION DECODE, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  ds4moe_forward_decode without a workspace argument: the
+ * scratch memory is a fixed array of DS4MOE_NOALLOC_SCRATCH_BYTES in each
+ * GPU's memory, held by the library from the first call on that GPU until
+ * the process ends.  The call allocates nothing (no hipMalloc, no hipFree,
+ * no allocating library routine); on a GPU's first call it looks up the
+ * array's device address, with that GPU current on the calling thread.
+ * Inputs, outputs and results are those of ds4moe_forward_decode (the same
+ * kernels).  Shapes whose decode workspace (ds4moe_workspace_bytes(dims, T,
+ * DS4MOE_MODE_DECODE)) exceeds the array return DS4MOE_ERR_WORKSPACE before
+ * anything is launched; every other argument is checked as there, also
+ * before any HIP call.  All calls on one GPU share its array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  No state carries over from one call to the
+ * next (the decode kernels read no scratch they did not write in the same
+ * call), so nothing has to be cleared between calls. */
+#define DS4MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int ds4moe_forward_decode_noalloc(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
+                                  float *y, ds4moe_routing *route_out, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ds4moe_status_str(int status);

@@ -24,6 +24,7 @@ DS4MOE_ERR_WORKSPACE = 5
 DS4MOE_ERR_UNSUPPORTED = 6
 DS4MOE_ERR_HIP = 7
 DS4MOE_ERR_HOSTMEM = 8
+DS4MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 DS4MOE_F32 = 0
 DS4MOE_BF16 = 1
 MODE_ROUTE, MODE_DECODE, MODE_PREFILL = 0, 1, 2
@@ -32,7 +33,7 @@ EXPORTED = ("ds4moe_packed_bytes", "ds4moe_packed_bytes_bits", "ds4moe_pack_q2k"
             "ds4moe_dequant_q2k", "ds4moe_dequant", "ds4moe_workspace_bytes",
             "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_status_str",
             "ds4moe_version", "ds4moe_forward_timed", "ds4moe_cache_bytes", "ds4moe_cache_reset",
-            "ds4moe_forward_decode_cached", "ds4moe_cache_stats")
+            "ds4moe_forward_decode_cached", "ds4moe_cache_stats", "ds4moe_forward_decode_noalloc")
 N_TIMED_KERNELS = 10
 KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine",
                 "cache_plan", "cache_fill")
@@ -90,12 +91,13 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_forward_decode_cached.argtypes = [P, P, I32, P, ctypes.c_size_t, P, I32, P, P, P, ctypes.c_size_t,
                                                    P, P]
         L.ds4moe_cache_stats.argtypes = [P, I32, P, ctypes.c_size_t, P, P]
+        L.ds4moe_forward_decode_noalloc.argtypes = [P, P, P, I32, P, P, P]
         L.ds4moe_status_str.argtypes = [ctypes.c_int]
         L.ds4moe_status_str.restype = ctypes.c_char_p
         L.ds4moe_version.restype = ctypes.c_int
         for fn in ("ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_pack", "ds4moe_dequant", "ds4moe_route",
                    "ds4moe_cache_reset", "ds4moe_forward_decode_cached", "ds4moe_cache_stats",
-                   "ds4moe_forward_decode",
+                   "ds4moe_forward_decode", "ds4moe_forward_decode_noalloc",
                    "ds4moe_forward_prefill", "ds4moe_forward_timed"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -180,6 +182,14 @@ def ds4moe_forward_decode(dims: Dims, weights: Weights, x, T: int, y, routing: R
     r = ctypes.byref(routing) if routing is not None else None
     _check(lib().ds4moe_forward_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(y), r,
                                        _ptr(ws), ws_bytes, _stream(stream)), "forward_decode")
+
+
+def ds4moe_forward_decode_noalloc(dims: Dims, weights: Weights, x, T: int, y, routing: Routing | None,
+                                  stream=None) -> None:
+    """ds4moe_forward_decode on the library's fixed per-GPU scratch array (no workspace)."""
+    r = ctypes.byref(routing) if routing is not None else None
+    _check(lib().ds4moe_forward_decode_noalloc(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), T, _ptr(y), r,
+                                               _stream(stream)), "forward_decode_noalloc")
 
 
 def ds4moe_forward_prefill(dims: Dims, weights: Weights, x, T: int, y, routing: Routing | None, ws, ws_bytes: int,

@@ -2,6 +2,8 @@
 // launch), workspace layout, and the launch sequences of the three calls.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/ds4moe.h"
 #include "launch.h"
 
@@ -534,6 +536,50 @@ int ds4moe_forward_decode_cached(const ds4moe_dims *dims, const ds4moe_weights *
   if (!cc.hg || !cc.hu || !cc.hd) return DS4MOE_ERR_HOSTMEM;
   return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, DS4MOE_MODE_DECODE, events ? tms : nullptr,
                  &cc);
+}
+
+// Scratch memory of ds4moe_forward_decode_noalloc: a fixed array in every
+// GPU's memory, in place of the caller's workspace.  In host code `scratch`
+// names a host-side stand-in, never the device array: its device address is
+// looked up once per device and only that address is handed to the kernels.
+constexpr size_t kNoAllocScratchBytes = DS4MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// device address of `scratch` on the current device (looked up on the
+// device's first call, with that device current)
+int scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DS4MOE_ERR_HIP;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return DS4MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DS4MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DS4MOE_OK;
+}
+}  // namespace
+
+int ds4moe_forward_decode_noalloc(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
+                                  float *y, ds4moe_routing *route_out, void *stream) {
+  // every argument is checked before any HIP call: a stand-in workspace
+  // address (aligned, never dereferenced) of the scratch size makes check_call
+  // report a call whose workspace would not fit as DS4MOE_ERR_WORKSPACE
+  Layout L;
+  int st = check_call(dims, w, x, T, y, true, route_out, reinterpret_cast<void *>((uintptr_t)256),
+                      kNoAllocScratchBytes, DS4MOE_MODE_DECODE, &L);
+  if (st) return st;
+  void *ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st) return st;
+  return forward(dims, w, x, T, y, route_out, ws, kNoAllocScratchBytes, stream, DS4MOE_MODE_DECODE);
 }
 
 int ds4moe_cache_stats(const ds4moe_dims *dims, int32_t n_slots, const void *cache, size_t cache_bytes,

@@ -229,3 +229,26 @@ def test_cache_argument_errors():
     out = (ctypes.c_uint64 * 3)()
     assert L.ds4moe_cache_stats(ctypes.byref(d), 16, v(256), nb, None, None) == B.DS4MOE_ERR_NULL
     assert L.ds4moe_cache_stats(ctypes.byref(d), 16, None, nb, out, None) == B.DS4MOE_ERR_NULL
+
+
+def test_decode_noalloc_rejects_on_host():
+    """The no-allocation decode checks every argument, and that the call's
+    workspace fits the fixed scratch array, before any HIP call."""
+    L = B.lib()
+    d = dims()
+    w = B.make_weights(256, 256, 256, 256)
+    f = L.ds4moe_forward_decode_noalloc
+    assert f(None, ctypes.byref(w), ctypes.c_void_p(256), 1, ctypes.c_void_p(256), None, None) == B.DS4MOE_ERR_NULL
+    for T in (0, 17, -1):
+        assert f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(256), T, ctypes.c_void_p(256), None,
+                 None) == B.DS4MOE_ERR_SHAPE
+    assert f(ctypes.byref(d), ctypes.byref(w), None, 1, ctypes.c_void_p(256), None, None) == B.DS4MOE_ERR_NULL
+    assert f(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(258), 1, ctypes.c_void_p(256), None,
+             None) == B.DS4MOE_ERR_ALIGN
+    big = dims(H=65536, I=32768, k=16, bits=4)       # decode workspace far above the scratch array
+    assert B.ds4moe_workspace_bytes(big, 16, B.MODE_DECODE) > B.DS4MOE_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), ctypes.byref(w), ctypes.c_void_p(256), 16, ctypes.c_void_p(256), None,
+             None) == B.DS4MOE_ERR_WORKSPACE
+    # the full-size decode shapes fit: T = 16 with k = 16 and 4-bit experts
+    full = dims(k=16, Is=2048, bits=4)
+    assert B.ds4moe_workspace_bytes(full, 16, B.MODE_DECODE) <= B.DS4MOE_NOALLOC_SCRATCH_BYTES
