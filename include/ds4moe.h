@@ -235,6 +235,18 @@ int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_wei
                          float *y, ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *const *events,
                          void *stream);
 
+/* MEASUREMENT: a plain streaming read, the ceiling the HBM-bound expert
+ * kernels are compared against on the same GPU.  Reads `bytes` (a multiple
+ * of 16) from the device buffer `buf` (16-byte aligned) with n_workgroups
+ * (1..2^20) workgroups of 256 threads, each thread keeping 8 16-byte loads
+ * in flight over a grid-stride loop, and writes one checksum word per
+ * workgroup to sink[n_workgroups] (device, uint32).  start_event and
+ * stop_event: both NULL, or two hipEvent_t created by the caller that the
+ * kernel's own dispatch stamps (their elapsed time is the kernel duration).
+ * Errors: DS4MOE_ERR_NULL, _SHAPE, _ALIGN before any launch; _HIP. */
+int ds4moe_read_probe(const void *buf, size_t bytes, int32_t n_workgroups, uint32_t *sink, void *start_event,
+                      void *stop_event, void *stream);
+
 /* ROUTED-EXPERT CACHE (small batches).  The experts' packed matrices stay in
  * pinned host memory; a cache buffer in device memory holds n_slots expert
  * slots (gate, up and down of one expert each).  A call routes the batch,

@@ -33,7 +33,8 @@ EXPORTED = ("ds4moe_packed_bytes", "ds4moe_packed_bytes_bits", "ds4moe_pack_q2k"
             "ds4moe_dequant_q2k", "ds4moe_dequant", "ds4moe_workspace_bytes",
             "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_status_str",
             "ds4moe_version", "ds4moe_forward_timed", "ds4moe_cache_bytes", "ds4moe_cache_reset",
-            "ds4moe_forward_decode_cached", "ds4moe_cache_stats", "ds4moe_forward_decode_noalloc")
+            "ds4moe_forward_decode_cached", "ds4moe_cache_stats", "ds4moe_forward_decode_noalloc",
+            "ds4moe_read_probe")
 N_TIMED_KERNELS = 10
 KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine",
                 "cache_plan", "cache_fill")
@@ -92,12 +93,13 @@ def lib() -> ctypes.CDLL:
                                                    P, P]
         L.ds4moe_cache_stats.argtypes = [P, I32, P, ctypes.c_size_t, P, P]
         L.ds4moe_forward_decode_noalloc.argtypes = [P, P, P, I32, P, P, P]
+        L.ds4moe_read_probe.argtypes = [P, ctypes.c_size_t, I32, P, P, P, P]
         L.ds4moe_status_str.argtypes = [ctypes.c_int]
         L.ds4moe_status_str.restype = ctypes.c_char_p
         L.ds4moe_version.restype = ctypes.c_int
         for fn in ("ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_pack", "ds4moe_dequant", "ds4moe_route",
                    "ds4moe_cache_reset", "ds4moe_forward_decode_cached", "ds4moe_cache_stats",
-                   "ds4moe_forward_decode", "ds4moe_forward_decode_noalloc",
+                   "ds4moe_forward_decode", "ds4moe_forward_decode_noalloc", "ds4moe_read_probe",
                    "ds4moe_forward_prefill", "ds4moe_forward_timed"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -242,3 +244,11 @@ def ds4moe_cache_stats(dims: Dims, n_slots: int, cache, cache_bytes: int, stream
     _check(lib().ds4moe_cache_stats(ctypes.byref(dims), n_slots, _ptr(cache), cache_bytes, out, st), "cache_stats")
     torch.cuda.synchronize()
     return int(out[0]), int(out[1]), int(out[2])
+
+
+def ds4moe_read_probe(buf, nbytes: int, n_workgroups: int, sink, events=None, stream=None) -> None:
+    """A plain streaming read of nbytes of `buf` (measurement); events: None or a
+    (start, stop) pair of torch.cuda.Event stamped by the kernel's dispatch."""
+    ev = (None, None) if events is None else tuple(ctypes.c_void_p(e.cuda_event) for e in events)
+    _check(lib().ds4moe_read_probe(_ptr(buf), nbytes, n_workgroups, _ptr(sink), ev[0], ev[1], _stream(stream)),
+           "read_probe")
