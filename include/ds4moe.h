@@ -197,19 +197,32 @@ int ds4moe_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows,
 size_t ds4moe_workspace_bytes(const ds4moe_dims *dims, int32_t T, int32_t mode);
 
 /* Router only: logits, scores, top-k, weights, per-expert histogram, scan and
- * stable permutation.  x [T,H] in dims->x_dtype; T >= 0 (0 = no-op).
+ * stable permutation.  The router stays at high precision, as the routed
+ * experts alone are quantized (molayo1419.me "antirez-ds4" insight, "Models"
+ * section); the score is sqrt(softplus) in the stable form of the router
+ * numeric test (opensource-hub.com "antirez/ds4" page, FAQ #1), where fp32
+ * log(1 + exp(x)) loses its digits near logit -12.  x [T,H] in dims->x_dtype; T >= 0 (0 = no-op).
  * Needs router_w (and router_bias if any) in `w`; `out` (host struct) must
  * not be NULL but any field may be.  ws: ds4moe_workspace_bytes(dims, T, 0). */
 int ds4moe_route(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T,
                  ds4moe_routing *out, void *ws, size_t ws_bytes, void *stream);
 
-/* Whole layer for a small batch, 1 <= T <= 16 (decode).  y [T,H] fp32 is
+/* Whole layer for a small batch, 1 <= T <= 16 (decode): every new token is
+ * routed through the experts again, so decode streams the chosen experts'
+ * 2-bit weights once per call (molayo1419.me "antirez-ds4" insight, SSD
+ * streaming section: generation is the phase that re-reads routed experts;
+ * the 16-token batch stands for the server's micro-batched sessions,
+ * blog.123qwe.co.kr DwarfStar article, baseline table).  y [T,H] fp32 is
  * overwritten.  route_out (host struct, nullable) receives the routing.
  * ws: ds4moe_workspace_bytes(dims, T, DS4MOE_MODE_DECODE). */
 int ds4moe_forward_decode(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
                           ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream);
 
-/* Whole layer for any T >= 0 (prefill; T = 0 is a no-op).  Same arguments as
+/* Whole layer for any T >= 0 (prefill; T = 0 is a no-op): the tokens are
+ * grouped by expert so that each expert's 2-bit weights are read once per
+ * chunk and multiplied against all of its tokens (the 2048-token chunk of the
+ * pages' prefill benchmark, blog.123qwe.co.kr DwarfStar article, "Repository
+ * layout and evaluation" section).  Same arguments as
  * ds4moe_forward_decode; ws: ds4moe_workspace_bytes(dims, T, DS4MOE_MODE_PREFILL). */
 int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int32_t T, float *y,
                            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream);

@@ -25,53 +25,25 @@
 namespace ds4 {
 
 #define WAVES 4
-#ifndef GEMM_R_GU
-#define GEMM_R_GU 1
-#endif
-#ifndef GEMM_R_DN
-#define GEMM_R_DN 2
-#endif
-#ifndef GEMM_NW_GU
-#define GEMM_NW_GU 4
-#endif
-#ifndef GEMM_NW_DN
-#define GEMM_NW_DN 4
-#endif
-#ifndef DN_DEC_PD
-#define DN_DEC_PD 3
-#endif
-#ifndef GU_LDS_PD
-#define GU_LDS_PD 3
-#endif
-// waves sharing one row tile's reduction in the T <= 4 gate/up kernel
-#ifndef GU_LDS_KS
-#define GU_LDS_KS 2
-#endif
-#ifndef DN_LDS_PD
-#define DN_LDS_PD 4
-#endif
-#ifndef GU_SH_PD
-#define GU_SH_PD 2
-#endif
-#ifndef GU_SH_NW
-#define GU_SH_NW 4
-#endif
+// Launch shapes and pipeline depths (each fixed by measurement on MI355X; the
+// parity tests cover exactly these instantiations).
+constexpr int GEMM_R_GU = 1;   // 64-token GEMMs: row tiles per wave, gate/up
+constexpr int GEMM_R_DN = 2;   // ... down
+constexpr int GEMM_NW_GU = 4;  // ... waves per workgroup, gate/up
+constexpr int GEMM_NW_DN = 4;  // ... down
+constexpr int DN_DEC_PD = 3;   // decode down with I below 256: pipeline depth
+constexpr int GU_LDS_PD = 3;   // one-token gate/up: pipeline depth
+constexpr int GU_LDS_KS = 2;   // ... waves sharing one row tile's reduction
+constexpr int DN_LDS_PD = 4;   // decode down, T <= 4, I not a multiple of 512: pipeline depth
+constexpr int GU_SH_PD = 2;    // gate/up of 5..16 tokens: pipeline depth
+constexpr int GU_SH_NW = 4;    // ... waves (row tiles) per workgroup
 // smallest batch that takes the shared-activation gate/up kernel (one token
 // takes the per-wave kernel)
-#define GU_SH_MIN_T 2
-#ifndef DN2_PD
-#define DN2_PD 2
-#endif
-// T = 5..16 down: row tiles per wave, and the ways the tile list is split
-#ifndef DN2_R
-#define DN2_R 4
-#endif
-#ifndef DN2_NH
-#define DN2_NH 4
-#endif
-#ifndef DN2_SDL
-#define DN2_SDL true
-#endif
+constexpr int GU_SH_MIN_T = 2;
+constexpr int DN2_PD = 2;         // down of 5..16 tokens: pipeline depth
+constexpr int DN2_R = 4;          // ... row tiles per wave
+constexpr int DN2_NH = 4;         // ... ways the tile list is split
+constexpr bool DN2_SDL = true;    // ... unit scales and d|dmin through LDS
 
 
 // One lane's share of a packed unit.  Code plane p (1024 bytes at 1024*p)

@@ -616,3 +616,28 @@ def test_graph_replay_matches_eager(full, name, T):
         torch.cuda.synchronize()
         assert torch.equal(y2.view(torch.int32), ref2.view(torch.int32)), f"eager after replay {rep}"
     del g
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_prefill_past_the_wide_tile_window(bits):
+    """T * k * I large enough (60000 * 16 * 1024) that the down projection's
+    activations no longer fit the 2 GiB window of the wide-tile kernels:
+    both projections fall back to the 64-token GEMMs with I a multiple of
+    256 (the unpadded down instance).  Every token against the oracle."""
+    q = _q()
+    T = 60000
+    wl = synth.Workload("window", 0, T=T, H=256, E=16, I=1024, k=16, x_dtype="f32", router_dtype="f32",
+                        router_sigma=0.05, layer_id=0, bits=bits)
+    L = synth.make_layer(wl)
+    dl = q.from_layer_inputs(L)
+    A = T * wl.k
+    assert 2 * A * wl.I + 4 * A * (wl.I // 16) > (1 << 31)     # past the window
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    idx = check_routing(bufs, L, label=f"window bits={bits}")
+    ref, ridx, _ = oracle.layer_inputs(L)
+    assert np.array_equal(ridx, idx)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"window bits={bits}: all {T} tokens, per-token rel err {err:.3e}")
+    assert err <= TOL_Y
