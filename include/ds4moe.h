@@ -69,7 +69,14 @@ typedef enum { DS4MOE_MODE_ROUTE = 0, DS4MOE_MODE_DECODE = 1, DS4MOE_MODE_PREFIL
  *   n_experts     E: top_k <= E <= 256
  *   top_k         k: 1..16
  *   shared_inter  Is: 0 (no shared expert) or a multiple of 32
- *   x_dtype       dtype of x: DS4MOE_F32 or DS4MOE_BF16
+ *   x_dtype       dtype of x: DS4MOE_F32 or DS4MOE_BF16.  The expert
+ *                 products take fp16 operands: each token enters them as
+ *                 x * 2^-e with max |x| in [2^e, 2^(e+1)), and its SwiGLU
+ *                 intermediate as h * 2^-2e, so activations of any finite
+ *                 magnitude (the whole bf16 / fp32 range) are represented
+ *                 to fp16 precision relative to the token's largest element
+ *                 and the result carries 2^2e back exactly (results are
+ *                 finite while y itself fits fp32)
  *   router_dtype  dtype of Wr: DS4MOE_F32 or DS4MOE_BF16
  *   expert_bits   code width of the packed routed experts: 2 or 4 */
 typedef struct {

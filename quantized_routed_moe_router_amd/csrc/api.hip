@@ -37,8 +37,8 @@ int validate_dims(const ds4moe_dims *d) {
 }
 
 struct Layout {
-  size_t logits, part, idx, w, counts, offsets, perm, pos, tiles, ntiles, ccnt, cbase, lrank, dpart;
-  size_t x16, xs_hi, xs_lo, h, hs_hi, hs_lo, yp, hsh, ysh, zeros;
+  size_t logits, part, idx, w, counts, offsets, perm, pos, pexp, tiles, ntiles, ccnt, cbase, lrank, dpart;
+  size_t x16, xs_hi, xs_lo, xexp, xe16, h, hs_hi, hs_lo, yp, hsh, ysh, zeros;
   int nzeros;
   size_t total;
   int tile_n, max_tiles, Ipad;
@@ -61,9 +61,11 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
   L.Ipad = d.inter % 256 ? 256 : d.inter;
   L.tile_n = mode == DS4MOE_MODE_PREFILL ? kTilePrefill : kTileDecode;
   if (mode == DS4MOE_MODE_PREFILL && d.inter % 256 == 0) {
-    // wide tiles when the activation windows (x16 or h and their hi/lo sums,
-    // contiguous below) fit 2 GiB
-    const int64_t xw = (int64_t)align256(2 * T * H) + (int64_t)align256(2 * T * (H / 16)) + 2 * T * (H / 16);
+    // wide tiles when the activation windows (x16, its hi/lo sums, the token
+    // exponents and their 16-byte rows, or h and its hi/lo sums, contiguous
+    // below) fit 2 GiB
+    const int64_t xw = (int64_t)align256(2 * T * H) + 2 * (int64_t)align256(2 * T * (H / 16)) +
+                       (int64_t)align256(4 * T) + 16 * T;
     const int64_t hw = (int64_t)align256(2 * A * L.Ipad) + (int64_t)align256(2 * A * (L.Ipad / 16)) +
                        2 * A * (L.Ipad / 16);
     if (xw <= ((int64_t)1 << 31) && hw <= ((int64_t)1 << 31)) L.tile_n = kTilePrefillWide;
@@ -89,6 +91,8 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
     L.x16 = take(2 * T * H);
     L.xs_hi = take(2 * T * (H / 16));
     L.xs_lo = take(2 * T * (H / 16));
+    L.xexp = take(sizeof(int32_t) * T);
+    if (mode == DS4MOE_MODE_PREFILL) L.xe16 = take(16 * T);
     // rows of h: assignments (prefill) or (tile, token) pairs (decode)
     const int64_t hrows = mode == DS4MOE_MODE_DECODE ? (int64_t)L.max_tiles * T : A;
     L.h = take(2 * hrows * L.Ipad);
@@ -100,6 +104,7 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
     } else {
       L.tiles = take(sizeof(TileT) * (size_t)L.max_tiles);
       L.pos = take(sizeof(int32_t) * A);
+      L.pexp = take(sizeof(int32_t) * A);
       L.yp = take(sizeof(float) * A * H);
       L.nzeros = (int)(H > L.Ipad ? H : L.Ipad);
       L.zeros = take(2 * (size_t)L.nzeros);
@@ -256,11 +261,13 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   const bool xb = d.x_dtype == DS4MOE_BF16, wb = d.router_dtype == DS4MOE_BF16;
   const Ptrs p = routing_ptrs(ws, L, route_out);
 
-  XPrep xp{x, xb, at<_Float16>(ws, L.x16), at<_Float16>(ws, L.xs_hi), at<_Float16>(ws, L.xs_lo)};
+  XPrep xp{x, xb, at<_Float16>(ws, L.x16), at<_Float16>(ws, L.xs_hi), at<_Float16>(ws, L.xs_lo),
+           at<int32_t>(ws, L.xexp), mode == DS4MOE_MODE_PREFILL ? at<int32_t>(ws, L.xe16) : nullptr};
   const bool dec = mode == DS4MOE_MODE_DECODE;
-  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, L.tile_n, nullptr, 0};
+  RouteOut ro{p.idx, p.w, p.counts, p.offsets, p.perm, nullptr, nullptr, nullptr, L.tile_n, nullptr, 0, xp.xexp};
   if (!dec) {
     ro.pos = at<int32_t>(ws, L.pos);
+    ro.pexp = at<int32_t>(ws, L.pexp);
     ro.tiles = at<TileT>(ws, L.tiles);
     ro.ntiles = at<int32_t>(ws, L.ntiles);
     ro.zeros = at<_Float16>(ws, L.zeros);
@@ -312,6 +319,9 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.x16 = xp.x16;
   ga.xs_hi = xp.xs_hi;
   ga.xs_lo = xp.xs_lo;
+  ga.xexp = xp.xexp;
+  ga.pexp = dec ? nullptr : ro.pexp;
+  ga.xe16 = xp.xe16;
   ga.h = at<_Float16>(ws, L.h);
   ga.hs_hi = at<_Float16>(ws, L.hs_hi);
   ga.hs_lo = at<_Float16>(ws, L.hs_lo);
@@ -336,9 +346,9 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     if (d.shared_inter <= 0) return DS4MOE_OK;
     _Float16 *hsh = at<_Float16>(ws, L.hsh);
     ysh = at<float>(ws, L.ysh);
-    TRY(launch_shared_gateup((const uint16_t *)w->sh_gate, (const uint16_t *)w->sh_up, xp.x16, hsh, T, d.hidden,
-                             d.shared_inter, s, tm(SL_SHGATEUP)));
-    TRY(launch_shared_down((const uint16_t *)w->sh_down, hsh, ysh, T, d.hidden, d.shared_inter, s,
+    TRY(launch_shared_gateup((const uint16_t *)w->sh_gate, (const uint16_t *)w->sh_up, xp.x16, xp.xexp, hsh, T,
+                             d.hidden, d.shared_inter, s, tm(SL_SHGATEUP)));
+    TRY(launch_shared_down((const uint16_t *)w->sh_down, hsh, xp.xexp, ysh, T, d.hidden, d.shared_inter, s,
                            tm(SL_SHDOWN)));
     return DS4MOE_OK;
   };
@@ -353,7 +363,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     TRY(launch_down(ga, L.max_tiles, s, tm(SL_DOWN)));
     st = shared();
     if (st) return st;
-    TRY(launch_combine(ga.yp, ro.pos, p.w, ysh, y, T, d.top_k, d.hidden, s, tm(SL_COMBINE)));
+    TRY(launch_combine(ga.yp, ro.pos, p.w, xp.xexp, ysh, y, T, d.top_k, d.hidden, s, tm(SL_COMBINE)));
   }
   return DS4MOE_OK;
 }

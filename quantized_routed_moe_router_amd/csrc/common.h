@@ -129,3 +129,29 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ h8 buf_load_h8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+
+// ---------------------------------------------------------------- token pre-scale
+// Each token's activations enter the fp16 operands as x' = x * 2^-e with
+// max |x| in [2^e, 2^(e+1)), so max |x'| lies in [1, 2) whatever the range of
+// x (bf16 covers far more than fp16).  Gate and up are linear in x, so the
+// MFMA sums are g' = g 2^-e and u' = u 2^-e, exactly; the intermediate is
+// stored as h' = h 2^-2e = g' u' sigmoid(g' 2^e) and the token's expert
+// outputs carry the factor 2^2e back.  Every scaling is by a power of two,
+// hence exact while no value leaves the fp32 range.
+//
+// e for a token whose largest magnitude is `amax` (0 for an all-zero,
+// infinite or NaN row, which is then converted unscaled).
+__device__ __forceinline__ int token_exp(float amax) {
+  return (amax > 0.0f && amax <= 3.40282347e38f) ? ilogbf(amax) : 0;
+}
+
+// SwiGLU of a pre-scaled token: h' = silu(g) u 2^-2e from g' = g 2^-e and
+// u' = u 2^-e (the same operations as silu(g) * u, each result scaled by a
+// power of two).
+__device__ __forceinline__ float swiglu_scaled(float gs, float us, int e) {
+  const float g = ldexpf(gs, e);
+  return gs / (1.0f + expf(-g)) * us;
+}
+
+// v * 2^(2e) in two exact steps (2^(2e) itself may not be representable).
+__device__ __forceinline__ float scale_2e(float v, int e) { return ldexpf(ldexpf(v, e), e); }

@@ -281,6 +281,11 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   constexpr bool GU = NM == 2;
+  // gate/up epilogue: the pre-scale exponents of the tile's tokens, loaded
+  // first and staged in LDS once the first prefetches are issued (visible
+  // after the first barrier of the loop)
+  __shared__ int32_t s_xe[16 * GEMM_NT];
+  const int32_t xe_ld = (GU && tid < tl.n) ? a.pexp[tl.p0 + tid] : 0;
   const int K = GU ? a.H : a.Ipad;
   const int kreal = GU ? a.H : a.I;
   const int jreal = kreal >> 4;
@@ -340,6 +345,7 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   UnitRegs<B> ua[R][NM], ub[R][NM];
   stage_load<NR, PADDED>(st, rowp, sp, 0, sc, sq, kreal, jreal);
   gemm_load_a<NM, R, B>(ua, c, rts, 0, lane);
+  if (GU && tid < tl.n) s_xe[tid] = xe_ld;
   for (int sb = 0; sb < nsb; sb += 2) {
     // even super-block: weights in ua, prefetch into ub
     __syncthreads();
@@ -373,12 +379,12 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
       for (int nt = 0; nt < GEMM_NT; ++nt) {
         const int col = 16 * nt + r16;
         const bool valid = col < tl.n;
+        const int e = valid ? s_xe[col] : 0;  // the token's pre-scale
         half_t hv[4];
         float ssum = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float gv = y[0][r][nt][q], uv = y[NM - 1][r][nt][q];
-          hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+          hv[q] = (half_t)swiglu_scaled(y[0][r][nt][q], y[NM - 1][r][nt][q], e);
           ssum += (float)hv[q];
         }
         ssum += __shfl_xor(ssum, 16);
@@ -563,14 +569,16 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
     const uint32_t sr = (uint32_t)(GU ? srow[q] / a.k : srow[q]);
     src[q] = DS4_OOB;
     inc[q] = 0;
-    if (row < tl.n && c < 36) {
+    if (row < tl.n) {
       if (c < 32) {
         src[q] = sr * xa.row_bytes + 16u * c;
         inc[q] = 512;
-      } else {
+      } else if (c < 36) {
         const int cc = c - 32;
         src[q] = ((cc >> 1) ? xa.o_slo : xa.o_shi) + sr * xa.srow_bytes + 16u * (cc & 1);
         inc[q] = 32;
+      } else if (GU) {  // chunk 36: the token's pre-scale exponent, the same every super-block
+        src[q] = xa.o_xe + 16u * sr;
       }
     }
   }
@@ -628,6 +636,8 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
   if (rt0 >= n_rt) return;
   if (GU) {
     const int nj = a.Ipad >> 4;
+    // the last super-block's slot holds each token row's exponent in chunk 36
+    const char *last = ring + ((nsb - 1) & 1) * PT_SLOT_BYTES;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const bool rv = rt0 + r < n_rt;
@@ -636,12 +646,12 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
       for (int nt = 0; nt < NTV; ++nt) {
         const int col = 16 * nt + r16;
         const bool valid = col < tl.n;
+        const int e = valid ? *reinterpret_cast<const int32_t *>(last + (col * PT_CH + 36) * 16) : 0;
         half_t hv[4];
         float ssum = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float gv = y[0][r][nt][q], uv = y[NM - 1][r][nt][q];
-          hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+          hv[q] = (half_t)swiglu_scaled(y[0][r][nt][q], y[NM - 1][r][nt][q], e);
           ssum += (float)hv[q];
         }
         ssum += __shfl_xor(ssum, 16);
@@ -995,12 +1005,12 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
     yg += pg;
     yu += pu;
   }
+  const int xe = r16 < a.T ? a.xexp[r16] : 0;  // token r16's pre-scale
   half_t hv[4];
   float ssum = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float gv = yg[q], uv = yu[q];
-    hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+    hv[q] = (half_t)swiglu_scaled(yg[q], yu[q], xe);
     ssum += (float)hv[q];
   }
   ssum += __shfl_xor(ssum, 16);
@@ -1304,12 +1314,12 @@ __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt,
   }
   wait_vm<0>();  // the trailing out-of-range loads, before the workgroup's LDS is released
   if (rt >= n_rt) return;
+  const int xe = r16 < a.T ? a.xexp[r16] : 0;  // token r16's pre-scale
   half_t hv[4];
   float ssum = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float gv = yg[q], uv = yu[q];
-    hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
+    hv[q] = (half_t)swiglu_scaled(yg[q], yu[q], xe);
     ssum += (float)hv[q];
   }
   ssum += __shfl_xor(ssum, 16);
@@ -1489,10 +1499,12 @@ __global__ __launch_bounds__(256) void k_down_reduce(const float *__restrict__ p
 }
 
 // ------------------------------------------------------------------ combine
-// y[t] = sum_j w[t,j] * Yp[pos(t,j)] in rank order, then + shared output.
+// y[t] = 2^2e * sum_j w[t,j] * Yp[pos(t,j)] in rank order (e: the token's
+// pre-scale), then + shared output.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ yp, const int32_t *__restrict__ pos,
-                                                 const float *__restrict__ w, const float *__restrict__ ysh,
-                                                 float *__restrict__ y, int T, int k, int H) {
+                                                 const float *__restrict__ w, const int32_t *__restrict__ xexp,
+                                                 const float *__restrict__ ysh, float *__restrict__ y, int T, int k,
+                                                 int H) {
   const int t = blockIdx.x;
   const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= H) return;
@@ -1503,6 +1515,9 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ yp, c
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
   }
+  const int e = xexp[t];  // Yp carries the token's 2^-2e
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = scale_2e(acc[i], e);
   if (ysh) {
     const f4 v = *reinterpret_cast<const f4 *>(ysh + (size_t)t * H + c);
 #pragma unroll
@@ -1526,7 +1541,8 @@ __device__ __forceinline__ h8 bf16x8_to_h8(u4 v) {
 template <int R, int NT>
 __global__ __launch_bounds__(256) void k_shared_gateup(const uint16_t *__restrict__ wg,
                                                        const uint16_t *__restrict__ wu,
-                                                       const half_t *__restrict__ x16, half_t *__restrict__ hs,
+                                                       const half_t *__restrict__ x16,
+                                                       const int32_t *__restrict__ xexp, half_t *__restrict__ hs,
                                                        int T, int H, int Is) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
@@ -1574,12 +1590,10 @@ __global__ __launch_bounds__(256) void k_shared_gateup(const uint16_t *__restric
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if (!valid[nt]) continue;
+      const int e = xexp[tok[nt]];
       half_t hv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float gv = ag[r][nt][i], uv = au[r][nt][i];
-        hv[i] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
-      }
+      for (int i = 0; i < 4; ++i) hv[i] = (half_t)swiglu_scaled(ag[r][nt][i], au[r][nt][i], e);
       uint2 pk;
       __builtin_memcpy(&pk, hv, 8);
       *reinterpret_cast<uint2 *>(hs + (size_t)tok[nt] * Is + row0) = pk;
@@ -1589,7 +1603,8 @@ __global__ __launch_bounds__(256) void k_shared_gateup(const uint16_t *__restric
 
 template <int R, int NT>
 __global__ __launch_bounds__(256) void k_shared_down(const uint16_t *__restrict__ wd, const half_t *__restrict__ hs,
-                                                     float *__restrict__ ysh, int T, int H, int Is) {
+                                                     const int32_t *__restrict__ xexp, float *__restrict__ ysh, int T,
+                                                     int H, int Is) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int n_rt = H >> 4;
@@ -1627,8 +1642,14 @@ __global__ __launch_bounds__(256) void k_shared_down(const uint16_t *__restrict_
     if (rt0 + r >= n_rt) continue;
     const int row0 = (rt0 + r) * 16 + 4 * g;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      if (valid[nt]) *reinterpret_cast<f4 *>(ysh + (size_t)tok[nt] * H + row0) = ac[r][nt];
+    for (int nt = 0; nt < NT; ++nt) {
+      if (!valid[nt]) continue;
+      const int e = xexp[tok[nt]];  // h carries 2^-2e
+      f4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = scale_2e(ac[r][nt][q], e);
+      *reinterpret_cast<f4 *>(ysh + (size_t)tok[nt] * H + row0) = v;
+    }
   }
 }
 
@@ -1650,8 +1671,8 @@ constexpr int DG_ROWS = 256, DG_TOK = 128;
 
 template <bool GU>
 __global__ __launch_bounds__(256) void k_dense_gemm(const uint16_t *__restrict__ wa, const uint16_t *__restrict__ wb,
-                                                    const half_t *__restrict__ x, void *__restrict__ out, int T,
-                                                    int K, int rows) {
+                                                    const half_t *__restrict__ x, const int32_t *__restrict__ xexp,
+                                                    void *__restrict__ out, int T, int K, int rows) {
   __shared__ __attribute__((aligned(16))) half_t sA[2][DG_ROWS * DG_LD];
   __shared__ __attribute__((aligned(16))) half_t sX[2][DG_TOK * DG_LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1725,6 +1746,7 @@ __global__ __launch_bounds__(256) void k_dense_gemm(const uint16_t *__restrict__
   for (int j = 0; j < 4; ++j) {
     const int t = t0 + 64 * wc + 16 * j + r16;
     if (t >= T) continue;
+    const int e = xexp[t];  // the token's pre-scale
     if (GU) {
       half_t *hs = reinterpret_cast<half_t *>(out);
 #pragma unroll
@@ -1733,10 +1755,7 @@ __global__ __launch_bounds__(256) void k_dense_gemm(const uint16_t *__restrict__
         if (row >= rows) continue;
         half_t hv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float gv = acc[i][j][q], uv = acc[4 + i][j][q];
-          hv[q] = (half_t)(gv / (1.0f + expf(-gv)) * uv);
-        }
+        for (int q = 0; q < 4; ++q) hv[q] = (half_t)swiglu_scaled(acc[i][j][q], acc[4 + i][j][q], e);
         uint2 pk;
         __builtin_memcpy(&pk, hv, 8);
         *reinterpret_cast<uint2 *>(hs + (size_t)t * rows + row) = pk;
@@ -1746,7 +1765,11 @@ __global__ __launch_bounds__(256) void k_dense_gemm(const uint16_t *__restrict__
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = row0 + 128 * wr + 16 * i + 4 * g;
-        if (row < rows) *reinterpret_cast<f4 *>(y + (size_t)t * rows + row) = acc[i][j];
+        if (row >= rows) continue;
+        f4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = scale_2e(acc[i][j][q], e);
+        *reinterpret_cast<f4 *>(y + (size_t)t * rows + row) = v;
       }
     }
   }
@@ -1756,12 +1779,18 @@ __global__ __launch_bounds__(256) void k_dense_gemm(const uint16_t *__restrict__
 // Prefill: four n-tiles (64 tokens) per workgroup.
 // Activations of the wide-tile GEMMs: one buffer window from the activation
 // rows to the end of their hi/lo sums (false if it does not fit 2 GiB).
-static bool act_window(const void *rows, const void *s_hi, const void *s_lo, int64_t nrows, int K, GemmAct &xa) {
+static bool act_window(const void *rows, const void *s_hi, const void *s_lo, const void *xe16, int64_t nrows, int K,
+                       GemmAct &xa) {
   const uint8_t *b = (const uint8_t *)rows;
   const int64_t ohi = (const uint8_t *)s_hi - b, olo = (const uint8_t *)s_lo - b;
   const int64_t sbytes = nrows * (int64_t)(K / 16) * 2;
-  const int64_t end = (ohi > olo ? ohi : olo) + sbytes;
-  if (ohi < nrows * (int64_t)K * 2 || olo < nrows * (int64_t)K * 2 || end > (int64_t)0x80000000LL) return false;
+  int64_t end = (ohi > olo ? ohi : olo) + sbytes;
+  const int64_t oxe = xe16 ? (const uint8_t *)xe16 - b : -1;
+  if (xe16 && oxe + 16 * nrows > end) end = oxe + 16 * nrows;
+  if (ohi < nrows * (int64_t)K * 2 || olo < nrows * (int64_t)K * 2 || (xe16 && oxe < nrows * (int64_t)K * 2) ||
+      end > (int64_t)0x80000000LL)
+    return false;
+  xa.o_xe = xe16 ? (uint32_t)oxe : DS4_OOB;
   xa.base = b;
   xa.len = (uint32_t)end;
   xa.o_shi = (uint32_t)ohi;
@@ -1775,7 +1804,7 @@ template <int B>
 static hipError_t gateup_b(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (a.tile_n > 64) {
     GemmAct xa;
-    if (a.tile_n > 16 * PT_NTM || !act_window(a.x16, a.xs_hi, a.xs_lo, a.T, a.H, xa)) return hipErrorInvalidValue;
+    if (a.tile_n > 16 * PT_NTM || !act_window(a.x16, a.xs_hi, a.xs_lo, a.xe16, a.T, a.H, xa)) return hipErrorInvalidValue;
     const int nrb = (a.I + 16 * PT_NW - 1) / (16 * PT_NW);
     DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1, false, B>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW),
                0, s, a, xa, nrb);
@@ -1799,7 +1828,7 @@ static hipError_t down_b(const GemmArgs &a, int max_tiles, hipStream_t s, const 
   if (a.tile_n > 64) {
     GemmAct xa;
     if (a.tile_n > 16 * PT_NTM || a.I != a.Ipad ||
-        !act_window(a.h, a.hs_hi, a.hs_lo, (int64_t)a.T * a.k, a.Ipad, xa))
+        !act_window(a.h, a.hs_hi, a.hs_lo, nullptr, (int64_t)a.T * a.k, a.Ipad, xa))
       return hipErrorInvalidValue;
     const int nrb = (a.H + 32 * PT_NW - 1) / (32 * PT_NW);
     DS4_LAUNCH(tm, (k_moe_gemm_wide<1, 2, true, B>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW),
@@ -1918,38 +1947,38 @@ hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timin
   return a.bits == 4 ? down_combine_dec_b<4>(a, s, tm, tm_combine) : down_combine_dec_b<2>(a, s, tm, tm_combine);
 }
 
-hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,
-                          int k, int H, hipStream_t s, const Timing *tm) {
+hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const int32_t *xexp, const float *ysh,
+                          float *y, int T, int k, int H, hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
-  DS4_LAUNCH(tm, k_combine, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, yp, pos, w, ysh, y, T, k, H);
+  DS4_LAUNCH(tm, k_combine, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, yp, pos, w, xexp, ysh, y, T, k, H);
   return hipGetLastError();
 }
 
-hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, _Float16 *hs, int T,
-                                int H, int Is, hipStream_t s, const Timing *tm) {
+hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, const int32_t *xexp,
+                                _Float16 *hs, int T, int H, int Is, hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
   if (T > 64) {
     const dim3 grid((Is + DG_ROWS / 2 - 1) / (DG_ROWS / 2), (T + DG_TOK - 1) / DG_TOK);
-    DS4_LAUNCH(tm, (k_dense_gemm<true>), grid, dim3(256), 0, s, wg, wu, x16, hs, T, H, Is);
+    DS4_LAUNCH(tm, (k_dense_gemm<true>), grid, dim3(256), 0, s, wg, wu, x16, xexp, hs, T, H, Is);
     return hipGetLastError();
   }
   constexpr int R = 1, NT = 4;
   const dim3 grid((Is + 16 * R * WAVES - 1) / (16 * R * WAVES), (T + 16 * NT - 1) / (16 * NT));
-  DS4_LAUNCH(tm, (k_shared_gateup<R, NT>), grid, dim3(256), 0, s, wg, wu, x16, hs, T, H, Is);
+  DS4_LAUNCH(tm, (k_shared_gateup<R, NT>), grid, dim3(256), 0, s, wg, wu, x16, xexp, hs, T, H, Is);
   return hipGetLastError();
 }
 
-hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, float *ysh, int T, int H, int Is,
-                              hipStream_t s, const Timing *tm) {
+hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, const int32_t *xexp, float *ysh, int T, int H,
+                              int Is, hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
   if (T > 64) {
     const dim3 grid((H + DG_ROWS - 1) / DG_ROWS, (T + DG_TOK - 1) / DG_TOK);
-    DS4_LAUNCH(tm, (k_dense_gemm<false>), grid, dim3(256), 0, s, wd, nullptr, hs, ysh, T, Is, H);
+    DS4_LAUNCH(tm, (k_dense_gemm<false>), grid, dim3(256), 0, s, wd, nullptr, hs, xexp, ysh, T, Is, H);
     return hipGetLastError();
   }
   constexpr int R = 1, NT = 4;
   const dim3 grid((H + 16 * R * WAVES - 1) / (16 * R * WAVES), (T + 16 * NT - 1) / (16 * NT));
-  DS4_LAUNCH(tm, (k_shared_down<R, NT>), grid, dim3(256), 0, s, wd, hs, ysh, T, H, Is);
+  DS4_LAUNCH(tm, (k_shared_down<R, NT>), grid, dim3(256), 0, s, wd, hs, xexp, ysh, T, H, Is);
   return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@ struct XPrep {
   _Float16 *x16;       // [T,H]
   _Float16 *xs_hi;     // [T,H/16]
   _Float16 *xs_lo;     // [T,H/16]
+  int32_t *xexp;       // [T] e of each token: x16 holds x * 2^-e (see token_exp)
+  int32_t *xe16;       // [T][4] e again, one 16-byte row per token (nullable)
 };
 
 struct RouteOut {
@@ -48,6 +50,9 @@ struct RouteOut {
   int tile_n;          // tokens per tile
   _Float16 *zeros;     // cleared here each call: read by GEMM lanes with no token
   int nzeros;          // halves
+  const int32_t *xexp; // [T] token exponents (x16 = x * 2^-e): the decode tile
+                       // weights carry 2^2e (nullable: no tiles)
+  int32_t *pexp;       // [T*k] the exponent of each permuted position's token (nullable)
 };
 
 // Activations of a wide-tile grouped GEMM through one buffer window: rows of
@@ -57,6 +62,7 @@ struct GemmAct {
   uint32_t len;
   uint32_t o_shi, o_slo;
   uint32_t row_bytes, srow_bytes;
+  uint32_t o_xe;  // gate/up: 16-byte rows whose first word is the token's pre-scale exponent (else DS4_OOB)
 };
 
 // ways the 5..16-token down projection may split its tile list (workspace
@@ -73,6 +79,9 @@ struct GemmArgs {
   const int32_t *perm;
   int k, H, I, Ipad;
   const _Float16 *x16, *xs_hi, *xs_lo;
+  const int32_t *xexp;               // [T] token exponents: x16 = x * 2^-e, h = silu(g) u * 2^-2e
+  const int32_t *pexp;               // [T*k] prefill: exponent of each permuted position's token
+  const int32_t *xe16;               // [T][4] prefill: the token exponents in 16-byte rows
   _Float16 *h, *hs_hi, *hs_lo;       // [T*k, Ipad], [T*k, Ipad/16]
   float *yp;                         // [T*k, H]
   const _Float16 *zeros;             // >= max(H, Ipad) zero halves
@@ -163,13 +172,13 @@ hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, const DecRoute *r
                              const Timing *tm = nullptr);
 hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm = nullptr,
                                    const Timing *tm_combine = nullptr);
-hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const float *ysh, float *y, int T,
-                          int k, int H, hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const int32_t *xexp, const float *ysh,
+                          float *y, int T, int k, int H, hipStream_t s, const Timing *tm = nullptr);
 // dense shared expert, bf16 weights
-hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, _Float16 *hs, int T,
-                                int H, int Is, hipStream_t s, const Timing *tm = nullptr);
-hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, float *ysh, int T, int H, int Is,
-                              hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, const int32_t *xexp,
+                                _Float16 *hs, int T, int H, int Is, hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, const int32_t *xexp, float *ysh, int T, int H,
+                              int Is, hipStream_t s, const Timing *tm = nullptr);
 
 // Launch `kernel` plainly, or with dispatch-stamped timing events.
 #define DS4_LAUNCH(tm, kernel, grid, block, shmem, stream, ...)                                                  \

@@ -23,6 +23,80 @@ __device__ __forceinline__ void load4_as_double(const void *p, int64_t idx, doub
   }
 }
 
+// 16 consecutive elements of x as fp32 (bf16 widening is exact)
+__device__ __forceinline__ void load_x16(const void *xptr, bool x_bf16, int64_t base, float v[16]) {
+  if (x_bf16) {
+    const u4 a = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base);
+    const u4 b = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_float((uint16_t)(a[i] & 0xFFFF));
+      v[2 * i + 1] = bf16_bits_to_float((uint16_t)(a[i] >> 16));
+      v[8 + 2 * i] = bf16_bits_to_float((uint16_t)(b[i] & 0xFFFF));
+      v[8 + 2 * i + 1] = bf16_bits_to_float((uint16_t)(b[i] >> 16));
+    }
+  } else {
+    const float *p = reinterpret_cast<const float *>(xptr) + base;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f4 a = *reinterpret_cast<const f4 *>(p + 4 * q);
+      v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
+    }
+  }
+}
+
+// Token t of x -> x' = x * 2^-e in fp16 (max |x'| in [1, 2), see token_exp),
+// the per-16-element sums of the fp16 values (hi + lo), and e.  NT threads
+// cooperate (one wave, or a whole workgroup of NT threads with `red`: NT/64
+// floats of LDS); tix is the thread's index among them.
+template <int NT>
+__device__ void xprep_token(int t, int H, const XPrep &xp, int tix, float *red) {
+  const int nsub = H >> 4;
+  float amax = 0.0f;
+  for (int j = tix; j < nsub; j += NT) {
+    float v[16];
+    load_x16(xp.x, xp.x_bf16, (int64_t)t * H + 16 * j, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if constexpr (NT > 64) {
+    __syncthreads();  // the previous token's readers of red are done
+    if ((tix & 63) == 0) red[tix >> 6] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
+  }
+  const int e = token_exp(amax);
+  if (tix == 0) {
+    xp.xexp[t] = e;
+    if (xp.xe16) *reinterpret_cast<u4 *>(xp.xe16 + 4 * (int64_t)t) = (u4){(uint32_t)e, 0u, 0u, 0u};
+  }
+  for (int j = tix; j < nsub; j += NT) {
+    const int64_t base = (int64_t)t * H + 16 * j;
+    float v[16];
+    load_x16(xp.x, xp.x_bf16, base, v);
+    h8 o0, o1;
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o0[i] = (half_t)ldexpf(v[i], -e);
+      sum += (float)o0[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o1[i] = (half_t)ldexpf(v[8 + i], -e);
+      sum += (float)o1[i];
+    }
+    *reinterpret_cast<h8 *>(xp.x16 + base) = o0;
+    *reinterpret_cast<h8 *>(xp.x16 + base + 8) = o1;
+    const half_t hi = (half_t)sum;
+    xp.xs_hi[(int64_t)t * nsub + j] = hi;
+    xp.xs_lo[(int64_t)t * nsub + j] = (half_t)(sum - (float)hi);
+  }
+}
+
 // ---------------------------------------------------------------- logits, T <= 16, sliced
 // Grid (E/4 expert groups) x (H/1024 column slices), 256 threads.  The slice
 // of x (T tokens x up to 1024 columns) is staged in LDS as fp32; wave = one
@@ -139,32 +213,11 @@ __global__ __launch_bounds__(256) void k_router_sliced(const void *__restrict__ 
   acc[0] += __shfl_xor(acc[0], 1);
   const int tok = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
   if ((lane & 3) == 0 && tok < T && e < E) part[((int64_t)slice * T + tok) * E + e] = acc[0];
-  if (do_x && blockIdx.x == 0) {
-    // x slice -> fp16 and per-16-column sums of the fp16 values (hi + lo)
-    const int nsub = cw >> 4;
-    for (int q = tid; q < T * nsub; q += 256) {
-      const int t = q / nsub, j = q - t * nsub;
-      const float *src = xs + t * RSLICE + 16 * j;
-      h8 o0, o1;
-      float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o0[i] = (half_t)src[i];
-        sum += (float)o0[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o1[i] = (half_t)src[8 + i];
-        sum += (float)o1[i];
-      }
-      const int64_t base = (int64_t)t * H + c0 + 16 * j;
-      *reinterpret_cast<h8 *>(xp.x16 + base) = o0;
-      *reinterpret_cast<h8 *>(xp.x16 + base + 8) = o1;
-      const int64_t sj = (int64_t)t * (H >> 4) + (c0 >> 4) + j;
-      const half_t hi = (half_t)sum;
-      xp.xs_hi[sj] = hi;
-      xp.xs_lo[sj] = (half_t)(sum - (float)hi);
-    }
+  if (do_x && blockIdx.y == 0) {
+    // whole rows of x -> pre-scaled fp16 and 16-column sums, one token per
+    // workgroup of the first column slice
+    __shared__ float red[4];
+    for (int t = blockIdx.x; t < T; t += gridDim.x) xprep_token<256>(t, H, xp, tid, red);
   }
 }
 
@@ -288,52 +341,6 @@ __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x,
   }
 }
 
-// x[t] -> fp16 and the per-16-element sums of the fp16 values (hi + lo), one wave.
-__device__ void xprep_token(int t, int H, const void *xptr, bool x_bf16, _Float16 *x16, _Float16 *xs_hi,
-                            _Float16 *xs_lo) {
-  const int lane = threadIdx.x & 63;
-  const int nsub = H >> 4;
-  for (int j = lane; j < nsub; j += 64) {
-    const int64_t base = (int64_t)t * H + 16 * j;
-    float v[16];
-    if (x_bf16) {
-      const u4 a = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base);
-      const u4 b = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(xptr) + base + 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_bits_to_float((uint16_t)(a[i] & 0xFFFF));
-        v[2 * i + 1] = bf16_bits_to_float((uint16_t)(a[i] >> 16));
-        v[8 + 2 * i] = bf16_bits_to_float((uint16_t)(b[i] & 0xFFFF));
-        v[8 + 2 * i + 1] = bf16_bits_to_float((uint16_t)(b[i] >> 16));
-      }
-    } else {
-      const float *p = reinterpret_cast<const float *>(xptr) + base;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 a = *reinterpret_cast<const f4 *>(p + 4 * q);
-        v[4 * q] = a[0]; v[4 * q + 1] = a[1]; v[4 * q + 2] = a[2]; v[4 * q + 3] = a[3];
-      }
-    }
-    h8 o0, o1;
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      o0[i] = (half_t)v[i];
-      sum += (float)o0[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      o1[i] = (half_t)v[8 + i];
-      sum += (float)o1[i];
-    }
-    *reinterpret_cast<h8 *>(x16 + base) = o0;
-    *reinterpret_cast<h8 *>(x16 + base + 8) = o1;
-    const half_t hi = (half_t)sum;
-    xs_hi[(int64_t)t * nsub + j] = hi;
-    xs_lo[(int64_t)t * nsub + j] = (half_t)(sum - (float)hi);
-  }
-}
-
 // Large T: one workgroup per chunk of 64 tokens (wave w: tokens 16w..16w+15).
 // Besides top-k and the activation preparation it records, for the stable
 // permutation, the chunk's count per expert and each assignment's rank among
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(1024) void k_topk_chunk(const float *__restrict__ l
     for (int q = 0; q < TPW; ++q) {
       const int t = c0 + TPW * wave + q;
       if (t >= T) break;
-      xprep_token(t, H, xp.x, xp.x_bf16, xp.x16, xp.xs_hi, xp.xs_lo);
+      xprep_token<64>(t, H, xp, lane, nullptr);
     }
   __syncthreads();
   const int nt = min(CHUNK, T - c0);
@@ -501,6 +508,7 @@ __global__ __launch_bounds__(256) void k_place_chunks(int T, int E, int k, int c
     const int p = ro.offsets[e] + base[(int64_t)blockIdx.x * E + e] + lrank[a];
     ro.perm[p] = (int32_t)a;
     if (ro.pos) ro.pos[a] = p;
+    if (ro.pexp) ro.pexp[p] = ro.xexp[a / k];
   }
 }
 

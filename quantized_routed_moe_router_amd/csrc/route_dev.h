@@ -147,7 +147,8 @@ struct RouteLds {
 // token t; then the per-expert token masks, counts and offsets (exclusive
 // scan over experts), the stable permutation (tokens ascending within an
 // expert) and one DecTile per used expert, in ascending expert order, with
-// its token mask and the token's weight for each token that chose it.
+// its token mask and the token's weight for each token that chose it (times
+// 2^2e for a token pre-scaled by 2^-e, see token_exp; topk_w is unscaled).
 // L.tm, L.tb and L.ntile are valid for every thread on return.  Global
 // outputs (logits, ro, dt, ntile) are written only when `out` is set.
 template <int NTH, int MAXT>
@@ -269,7 +270,7 @@ __device__ __forceinline__ void route_small_block(RouteLds<MAXT> &L, const doubl
     const int p = L.off[e] + __popc(L.tm[e] & ((1u << t) - 1u));
     ro.perm[p] = i;
     if (ro.pos) ro.pos[i] = p;
-    if (dt) dt[L.tb[e]].w[t] = L.w[i];
+    if (dt) dt[L.tb[e]].w[t] = ro.xexp ? scale_2e(L.w[i], ro.xexp[t]) : L.w[i];
   }
 }
 
@@ -319,7 +320,7 @@ __device__ __forceinline__ int route_one_token(RouteLds<4> &L, const double *__r
           d->tmask = 1u;
           d->pad0 = 0;
           d->pad1 = 0;
-          d->w[0] = my_w;
+          d->w[0] = ro.xexp ? scale_2e(my_w, ro.xexp[0]) : my_w;
 #pragma unroll
           for (int t = 1; t < 16; ++t) d->w[t] = 0.0f;
         }

@@ -641,3 +641,37 @@ def test_prefill_past_the_wide_tile_window(bits):
     err = per_token_err(y.cpu().numpy(), ref)
     print(f"window bits={bits}: all {T} tokens, per-token rel err {err:.3e}")
     assert err <= TOL_Y
+
+
+# Per-token activation scales far outside the fp16 range (x is bf16 on the
+# boundary, whose range is that of fp32): each token enters the fp16 operands
+# pre-scaled by a power of two, so scales from 1e-15 to 1e12 within one batch
+# meet the same bar as unit-scale tokens (y scales as x^2: up to ~1e24).
+ACT_SCALES = [1e-15, 1e-8, 3e-3, 1.0, 300.0, 6e4, 2e6, 1e12]
+
+
+@pytest.mark.parametrize("mode,T", [("decode", 1), ("decode", 3), ("decode", 8), ("decode", 16), ("prefill", 40),
+                                    ("prefill", 100)])
+def test_activation_range(mode, T):
+    """Decode at every batch class and prefill on both shared-expert kernel
+    forms (T <= 64 per-wave, T > 64 LDS-tiled), tokens cycling through
+    ACT_SCALES (T = 1: the largest)."""
+    q = _q()
+    wl = synth.Workload("range", 0, T=T, H=512, E=16, I=256, k=4, Is=96, x_dtype="bf16", router_dtype="bf16",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    xf = oracle.bf16_to_f32(L.x).astype(np.float64)
+    sc = np.array([ACT_SCALES[(t + (len(ACT_SCALES) - 1 if T == 1 else 0)) % len(ACT_SCALES)] for t in range(T)])
+    L.x = synth.f32_to_bf16_bits((xf * sc[:, None]).astype(np.float32))
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_DECODE if mode == "decode" else q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"range {mode} T={T}")
+    ref, _, _ = oracle.layer_inputs(L)
+    yy = y.cpu().numpy()
+    assert np.all(np.isfinite(yy)) and np.all(np.isfinite(ref))
+    err = per_token_err(yy, ref)
+    print(f"range {mode} T={T}: per-token rel err {err:.3e}, |y| from {np.abs(ref).max(axis=1).min():.2e} "
+          f"to {np.abs(ref).max(axis=1).max():.2e}")
+    assert err <= TOL_Y
