@@ -3,13 +3,15 @@
 fraction of the dominant kernel, with the CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload default|decode1|decode16|prefill|skewed|decode1_q4|prefill_q4|decode1_cached|tiny|all]
+                    [--workload default|decode1|decode16|prefill|skewed|decode1_q4|prefill_q4|decode1_mix|
+                                prefill_mix|decode1_cached|tiny|all]
 
 A step is one whole layer call (router -> top-k -> permute -> gate/up+SwiGLU ->
 down -> combine [+ shared expert]) on one batch of synthetic tokens whose
 inputs are already resident in HBM.  Decode workloads rotate over several
 copies of the layer's packed experts and over fresh token batches so the
-2.1 GB of expert weights (3.7 GB with 4-bit codes: the *_q4 workloads) stream
+2.1 GB of expert weights (3.7 GB with 4-bit codes: the *_q4 workloads; 2.7 GB
+with 2-bit gate/up and 4-bit down: the *_mix workloads) stream
 from HBM rather than from the 256 MB Infinity Cache.
 
 The default prints ONE JSON line: the one-token decode workload as the
@@ -44,6 +46,8 @@ DEFAULTS = {  # workload: (steps, warmup, layer copies, token batches)
     "skewed": (20, 3, 1, 2),
     "decode1_q4": (2000, 200, 4, 64),
     "prefill_q4": (50, 5, 1, 4),
+    "decode1_mix": (2000, 200, 4, 64),
+    "prefill_mix": (50, 5, 1, 4),
     "decode1_cached": (1000, 300, 1, 1024),
 }
 NESTED = ("decode16", "prefill")    # the metric's other two workloads, nested in the default line
@@ -404,7 +408,7 @@ def run_workload(name: str, args) -> dict:
             rc = read_ceiling(int(gu_total / steps_eager))
             roof["read_ceiling"] = rc
             roof["frac_of_read_ceiling"] = round(achieved / rc["GBs"], 4)
-        layer_bytes = np.mean([d * 3 * gu_bytes for d in distinct]) + E * H * 2 + T * H * (2 + 4)
+        layer_bytes = np.mean([d * (2 * gu_bytes + dl.d_bytes) for d in distinct]) + E * H * 2 + T * H * (2 + 4)
         layer = {"bytes_per_step": float(layer_bytes),
                  "achieved_GBs": round(layer_bytes / (elapsed / steps) / 1e9, 1),
                  "frac": round(layer_bytes / (elapsed / steps) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -423,13 +427,15 @@ def run_workload(name: str, args) -> dict:
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(elapsed / steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "operands": {"x": wl.x_dtype, "router": f"{wl.router_dtype} weights, fp64 accumulation",
-                     "routed_experts": f"{wl.bits}-bit codes in 256-weight super-blocks (fp16 d, dmin)",
+                     "routed_experts": f"{wl.bits}-bit gate/up and {wl.down_width}-bit down codes in 256-weight "
+                                       "super-blocks (fp16 d, dmin)",
                      "expert_products": "f16 x f16 -> f32 MFMA (exact code*scale, fp16 activations)",
                      "shared_expert": "bf16 weights as f16 operands" if wl.Is else None, "y": "f32"},
         "data": "synthetic",
         "config": {"workload": name, "T": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
                    **({"expert_cache": cache_info} if cache_info else {}),
-                   "shared_inter": wl.Is, "expert_bits": wl.bits, "layer_copies": n_layers,
+                   "shared_inter": wl.Is, "expert_bits": wl.bits, "down_bits": wl.down_width,
+                   "layer_copies": n_layers,
                    "token_batches": n_batches,
                    "seed": args.seed, "distinct_experts_mean": float(np.mean(distinct))},
         "roofline": roof,

@@ -78,7 +78,14 @@ typedef enum { DS4MOE_MODE_ROUTE = 0, DS4MOE_MODE_DECODE = 1, DS4MOE_MODE_PREFIL
  *                 and the result carries 2^2e back exactly (results are
  *                 finite while y itself fits fp32)
  *   router_dtype  dtype of Wr: DS4MOE_F32 or DS4MOE_BF16
- *   expert_bits   code width of the packed routed experts: 2 or 4 */
+ *   expert_bits   code width of the packed routed experts: 2 or 4 (gate and
+ *                 up, and down unless down_bits says otherwise)
+ *   down_bits     code width of the routed down matrices: 0 (= expert_bits),
+ *                 2 or 4.  The pages' quant mixes give the down projection a
+ *                 format of its own (molayo1419.me "antirez-ds4" insight,
+ *                 "Models" section: ds4's 2-bit model stores routed gate/up
+ *                 and routed down in different block types; the GLM notes
+ *                 pair 2- to 5-bit gate/up with down up to 6 bits) */
 typedef struct {
   int32_t hidden;
   int32_t inter;
@@ -88,6 +95,7 @@ typedef struct {
   int32_t x_dtype;
   int32_t router_dtype;
   int32_t expert_bits;
+  int32_t down_bits;
 } ds4moe_dims;
 
 /* Weights (host struct of device pointers).
@@ -97,8 +105,9 @@ typedef struct {
  *   gate, up   E packed matrices W[I,H] each (ds4moe_pack layout with
  *              dims->expert_bits), expert e at byte offset
  *              e * ds4moe_packed_bytes_bits(I, H, expert_bits)
- *   down       E packed matrices W[H,I], expert e at
- *              e * ds4moe_packed_bytes_bits(H, I, expert_bits)
+ *   down       E packed matrices W[H,I] (width down_bits, or expert_bits
+ *              when down_bits is 0), expert e at
+ *              e * ds4moe_packed_bytes_bits(H, I, that width)
  *   sh_gate, sh_up  [Is,H] bf16 row-major; sh_down [H,Is] bf16; all NULL
  *              when shared_inter == 0.  The shared expert is computed with
  *              fp16 operands: its weights must lie inside the binary16 range. */

@@ -58,6 +58,9 @@ def lib():
         L.oracle_dequant_f32_bits.argtypes = [P, I64, ctypes.c_int, P]
         L.oracle_layer_bits.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, ctypes.c_int, I64, P, P, P, P,
                                         P, P]
+        L.oracle_layer_bits2.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, ctypes.c_int, ctypes.c_int, I64,
+                                         P, P, P, P, P, P]
+        L.oracle_layer_bits2.restype = ctypes.c_int
         L.oracle_layer.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
@@ -138,9 +141,10 @@ def permute(idx: np.ndarray, E: int):
     return counts, offsets, perm
 
 
-def layer(x, wr, bias, gate, up, down, H, I, E, k, sh_gate=None, sh_up=None, sh_down=None, bits=2):
+def layer(x, wr, bias, gate, up, down, H, I, E, k, sh_gate=None, sh_up=None, sh_down=None, bits=2, down_bits=None):
     """Whole layer.  x [T,H] and wr [E,H] as fp32 values; gate/up/down canonical
-    blocks [E, nbytes]; shared weights as fp32 values or None.
+    blocks [E, nbytes] (gate/up with `bits`-bit codes, down with `down_bits`,
+    default the same); shared weights as fp32 values or None.
     Returns (y fp32 [T,H], idx int32 [T,k], w fp32 [T,k])."""
     x = _c(x, np.float32).reshape(-1, H)
     T = x.shape[0]
@@ -155,8 +159,9 @@ def layer(x, wr, bias, gate, up, down, H, I, E, k, sh_gate=None, sh_up=None, sh_
     y = np.empty((T, H), dtype=np.float32)
     idx = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float32)
-    rc = lib().oracle_layer_bits(_p(x), T, H, I, E, k, _p(wr), _p(b), _p(g), _p(u), _p(d), bits, Is,
-                                 _p(sg), _p(su), _p(sd), _p(y), _p(idx), _p(w))
+    rc = lib().oracle_layer_bits2(_p(x), T, H, I, E, k, _p(wr), _p(b), _p(g), _p(u), _p(d), bits,
+                                  bits if down_bits is None else down_bits, Is, _p(sg), _p(su), _p(sd), _p(y),
+                                  _p(idx), _p(w))
     if rc != 0:
         raise MemoryError("oracle_layer failed to allocate")
     return y, idx, w
@@ -177,7 +182,8 @@ def layer_inputs(L, tokens=None):
     sh = (None, None, None)
     if L.sh_gate is not None:
         sh = (bf16_to_f32(L.sh_gate), bf16_to_f32(L.sh_up), bf16_to_f32(L.sh_down))
-    return layer(x, wr, L.router_bias, L.gate, L.up, L.down, wl.H, wl.I, wl.E, wl.k, *sh, bits=wl.bits)
+    return layer(x, wr, L.router_bias, L.gate, L.up, L.down, wl.H, wl.I, wl.E, wl.k, *sh, bits=wl.bits,
+                 down_bits=getattr(wl, "bits_down", 0) or wl.bits)
 
 
 def num_threads() -> int:

@@ -32,6 +32,8 @@
  *     page keeps some layers at 4 bits; no page gives a 4-bit block): the same
  *     block with 4-bit codes, weight i -> byte 16+i/2, bits 4*(i%2), d @144,
  *     dmin @146 (148 bytes), w = d*scale*q - dmin*min with q in 0..15;
+ *   - the down matrices may use a code width of their own (the [models] page
+ *     gives routed gate/up and routed down different block types);
  *   - blocks tile the row-major flattened tensor (a block may span rows);
  *   - router logit = round-to-fp32 of the fp64 sum over h of x*W plus bias;
  *   - selection ranks logits (sqrt(softplus) is strictly increasing), ties
@@ -276,10 +278,10 @@ static int swiglu_ffn(const double *Wg, const double *Wu, const double *Wd, cons
  * Each routed expert is dequantized once and applied to each of its tokens;
  * every token's FFN is computed densely and independently.
  */
-int oracle_layer_bits(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,
-                      const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down, int bits,
-                      int64_t Is, const float *sh_gate, const float *sh_up, const float *sh_down, float *y,
-                      int32_t *idx_out, float *w_out) {
+int oracle_layer_bits2(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,
+                       const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down, int bits,
+                       int bits_down, int64_t Is, const float *sh_gate, const float *sh_up, const float *sh_down,
+                       float *y, int32_t *idx_out, float *w_out) {
   if (T <= 0) return 0;
   int rc = 0;
   float *logits = (float *)malloc(sizeof(float) * (size_t)(T * E));
@@ -300,6 +302,7 @@ int oracle_layer_bits(const float *x, int64_t T, int64_t H, int64_t I, int64_t E
   for (int64_t i = 0; i < T * H; ++i) xd[i] = (double)x[i];
 
   const int64_t mat_blocks = I * H / 256, mat_bytes = mat_blocks * block_bytes(bits);
+  const int64_t down_bytes = mat_blocks * block_bytes(bits_down);   /* down in its own code width */
   for (int64_t e = 0; e < E; ++e) {
     int64_t n = 0;                                   /* the expert's assignments, a ascending */
     for (int64_t a = 0; a < T * k; ++a)
@@ -307,7 +310,7 @@ int oracle_layer_bits(const float *x, int64_t T, int64_t H, int64_t I, int64_t E
     if (!n) continue;
     oracle_dequant_f64_bits(gate + e * mat_bytes, mat_blocks, bits, Wg);
     oracle_dequant_f64_bits(up + e * mat_bytes, mat_blocks, bits, Wu);
-    oracle_dequant_f64_bits(down + e * mat_bytes, mat_blocks, bits, Wd);
+    oracle_dequant_f64_bits(down + e * down_bytes, mat_blocks, bits_down, Wd);
     for (int64_t j = 0; j < n; ++j) memcpy(xs + j * H, xd + (as[j] / k) * H, sizeof(double) * (size_t)H);
     if (swiglu_ffn(Wg, Wu, Wd, xs, n, H, I, ys)) { rc = 1; goto done; }
     for (int64_t j = 0; j < n; ++j) memcpy(Y + as[j] * H, ys + j * H, sizeof(double) * (size_t)H);
@@ -336,6 +339,14 @@ done:
   free(logits); free(idx); free(w); free(wd); free(Y); free(xd); free(as);
   free(Wg); free(Wu); free(Wd); free(xs); free(ys);
   return rc;
+}
+
+int oracle_layer_bits(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,
+                      const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down, int bits,
+                      int64_t Is, const float *sh_gate, const float *sh_up, const float *sh_down, float *y,
+                      int32_t *idx_out, float *w_out) {
+  return oracle_layer_bits2(x, T, H, I, E, k, wr, bias, gate, up, down, bits, bits, Is, sh_gate, sh_up, sh_down, y,
+                            idx_out, w_out);
 }
 
 int oracle_layer(const float *x, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const float *wr,

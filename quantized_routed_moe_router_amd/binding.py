@@ -43,7 +43,7 @@ KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup",
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
-                ("router_dtype", ctypes.c_int32), ("expert_bits", ctypes.c_int32)]
+                ("router_dtype", ctypes.c_int32), ("expert_bits", ctypes.c_int32), ("down_bits", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -131,8 +131,9 @@ def _check(status: int, what: str) -> None:
         raise Ds4MoeError(status, what)
 
 
-def make_dims(H, I, E, k, Is=0, x_dtype=DS4MOE_BF16, router_dtype=DS4MOE_BF16, expert_bits=2) -> Dims:
-    return Dims(H, I, E, k, Is, x_dtype, router_dtype, expert_bits)
+def make_dims(H, I, E, k, Is=0, x_dtype=DS4MOE_BF16, router_dtype=DS4MOE_BF16, expert_bits=2, down_bits=0) -> Dims:
+    """down_bits = 0: the down matrices use expert_bits too."""
+    return Dims(H, I, E, k, Is, x_dtype, router_dtype, expert_bits, down_bits)
 
 
 def make_weights(router_w, gate, up, down, router_bias=None, sh_gate=None, sh_up=None, sh_down=None) -> Weights:

@@ -11,7 +11,7 @@ using namespace ds4;
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: ds4moe_dims.down_bits
 constexpr int kTileDecode = 16;
 constexpr int kTilePrefill = 64;      // tokens per prefill tile (64-token GEMM kernels)
 constexpr int kTilePrefillWide = 96;  // with the wide-tile GEMM kernels
@@ -33,8 +33,12 @@ int validate_dims(const ds4moe_dims *d) {
   if (d->n_experts < d->top_k || d->n_experts > 256) return DS4MOE_ERR_SHAPE;
   if (d->shared_inter < 0 || d->shared_inter > 65536 || d->shared_inter % 32) return DS4MOE_ERR_SHAPE;
   if (d->expert_bits != 2 && d->expert_bits != 4) return DS4MOE_ERR_SHAPE;
+  if (d->down_bits != 0 && d->down_bits != 2 && d->down_bits != 4) return DS4MOE_ERR_SHAPE;
   return DS4MOE_OK;
 }
+
+// code width of the routed down matrices
+inline int down_bits(const ds4moe_dims &d) { return d.down_bits ? d.down_bits : d.expert_bits; }
 
 struct Layout {
   size_t logits, part, idx, w, counts, offsets, perm, pos, pexp, tiles, ntiles, ccnt, cbase, lrank, dpart;
@@ -139,7 +143,7 @@ CacheLayout make_cache_layout(const ds4moe_dims &d, int S) {
     return o;
   };
   C.gu_bytes = ds4moe_packed_bytes_bits(d.inter, d.hidden, d.expert_bits);
-  C.d_bytes = ds4moe_packed_bytes_bits(d.hidden, d.inter, d.expert_bits);
+  C.d_bytes = ds4moe_packed_bytes_bits(d.hidden, d.inter, down_bits(d));
   C.hdr = take(sizeof(CacheHdr));
   C.slot_expert = take(4 * (size_t)S);
   C.expert_slot = take(4 * (size_t)d.n_experts);
@@ -299,7 +303,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.up = (const uint8_t *)w->up;
   ga.down = (const uint8_t *)w->down;
   ga.gu_bytes = ds4moe_packed_bytes_bits(d.inter, d.hidden, d.expert_bits);
-  ga.d_bytes = ds4moe_packed_bytes_bits(d.hidden, d.inter, d.expert_bits);
+  ga.d_bytes = ds4moe_packed_bytes_bits(d.hidden, d.inter, down_bits(d));
   if (cc) {  // experts through the cache: tiles name slots, the kernels read the slot arrays
     TRY(launch_cache_plan(cc->st, dtiles, ntiles, cc->S, d.n_experts, s, tm(SL_CPLAN)));
     TRY(launch_cache_fill(cc->st, cc->hg, cc->hu, cc->hd, ga.gu_bytes, ga.d_bytes,
@@ -309,6 +313,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     ga.down = cc->st.down;
   }
   ga.bits = d.expert_bits;
+  ga.bits_dn = down_bits(d);
   ga.tiles = ro.tiles;
   ga.ntiles = ntiles;
   ga.perm = p.perm;

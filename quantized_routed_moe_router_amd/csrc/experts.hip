@@ -1848,7 +1848,7 @@ static hipError_t down_b(const GemmArgs &a, int max_tiles, hipStream_t s, const 
 
 hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
-  return a.bits == 4 ? down_b<4>(a, max_tiles, s, tm) : down_b<2>(a, max_tiles, s, tm);
+  return a.bits_dn == 4 ? down_b<4>(a, max_tiles, s, tm) : down_b<2>(a, max_tiles, s, tm);
 }
 
 // Small batches (T <= 16).
@@ -1944,7 +1944,7 @@ static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Tim
 }
 
 hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm, const Timing *tm_combine) {
-  return a.bits == 4 ? down_combine_dec_b<4>(a, s, tm, tm_combine) : down_combine_dec_b<2>(a, s, tm, tm_combine);
+  return a.bits_dn == 4 ? down_combine_dec_b<4>(a, s, tm, tm_combine) : down_combine_dec_b<2>(a, s, tm, tm_combine);
 }
 
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const int32_t *xexp, const float *ysh,

@@ -21,26 +21,28 @@ def _as_bf16(bits: np.ndarray, device) -> torch.Tensor:
 
 class DeviceLayer:
     def __init__(self, H, I, E, k, Is=0, x_dtype=B.DS4MOE_BF16, router_dtype=B.DS4MOE_BF16, device="cuda:0",
-                 bits=2):
+                 bits=2, down_bits=0):
         self.H, self.I, self.E, self.k, self.Is, self.bits = H, I, E, k, Is, bits
+        self.down_bits = down_bits or bits
         self.device = torch.device(device)
-        self.dims = B.make_dims(H, I, E, k, Is, x_dtype, router_dtype, bits)
+        self.dims = B.make_dims(H, I, E, k, Is, x_dtype, router_dtype, bits, down_bits)
         self.x_dtype, self.router_dtype = x_dtype, router_dtype
         self.gu_bytes = B.ds4moe_packed_bytes_bits(I, H, bits)
-        self.d_bytes = B.ds4moe_packed_bytes_bits(H, I, bits)
+        self.d_bytes = B.ds4moe_packed_bytes_bits(H, I, self.down_bits)
         self._ws = None
         self.router_w = self.router_bias = None
         self.gate = self.up = self.down = None
         self.sh_gate = self.sh_up = self.sh_down = None
 
     # ------------------------------------------------------------ weights
-    def pack(self, canonical: np.ndarray, rows: int, cols: int, stream=None) -> torch.Tensor:
+    def pack(self, canonical: np.ndarray, rows: int, cols: int, stream=None, bits=None) -> torch.Tensor:
         """Upload E canonical-block matrices and repack them on the GPU."""
+        bits = self.bits if bits is None else bits
         n = canonical.shape[0]
         src = _dev(canonical.reshape(n, -1), self.device)
-        dst = torch.empty(n * B.ds4moe_packed_bytes_bits(rows, cols, self.bits), dtype=torch.uint8,
+        dst = torch.empty(n * B.ds4moe_packed_bytes_bits(rows, cols, bits), dtype=torch.uint8,
                           device=self.device)
-        B.ds4moe_pack(dst, src, n, rows, cols, self.bits, stream)
+        B.ds4moe_pack(dst, src, n, rows, cols, bits, stream)
         torch.cuda.current_stream(self.device).synchronize()
         del src
         return dst
@@ -55,7 +57,7 @@ class DeviceLayer:
     def set_experts(self, gate: np.ndarray, up: np.ndarray, down: np.ndarray):
         self.gate = self.pack(gate, self.I, self.H)
         self.up = self.pack(up, self.I, self.H)
-        self.down = self.pack(down, self.H, self.I)
+        self.down = self.pack(down, self.H, self.I, bits=self.down_bits)
 
     def set_shared(self, sh_gate, sh_up, sh_down):
         self.sh_gate = _as_bf16(sh_gate, self.device)
@@ -122,7 +124,8 @@ def from_layer_inputs(L, device="cuda:0", experts: bool = True) -> DeviceLayer:
     wl = L.wl
     xd = B.DS4MOE_F32 if wl.x_dtype == "f32" else B.DS4MOE_BF16
     rd = B.DS4MOE_F32 if wl.router_dtype == "f32" else B.DS4MOE_BF16
-    dl = DeviceLayer(wl.H, wl.I, wl.E, wl.k, wl.Is, xd, rd, device, bits=getattr(wl, "bits", 2))
+    dl = DeviceLayer(wl.H, wl.I, wl.E, wl.k, wl.Is, xd, rd, device, bits=getattr(wl, "bits", 2),
+                     down_bits=getattr(wl, "bits_down", 0))
     dl.set_router(L.router_w, L.router_bias)
     if experts:
         dl.set_experts(L.gate, L.up, L.down)

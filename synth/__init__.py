@@ -174,6 +174,11 @@ class Workload:
     layer_id: int = 1              # weight streams: workloads of one shape share a layer
     description: str = ""
     bits: int = 2                  # routed-expert code width: 2 (84-byte blocks) or 4 (148-byte blocks)
+    bits_down: int = 0             # code width of the down matrices (0: the same as `bits`)
+
+    @property
+    def down_width(self) -> int:
+        return self.bits_down or self.bits
 
 
 WORKLOADS = {
@@ -192,6 +197,11 @@ WORKLOADS = {
                            description="decode, one token, 4-bit routed experts"),
     "prefill_q4": Workload("prefill_q4", 6, T=2048, H=4096, E=256, I=2048, k=8, layer_id=2, bits=4,
                            description="prefill chunk of 2048 tokens, 4-bit routed experts"),
+    # gate/up with 2-bit codes, down with 4-bit codes (own layer)
+    "decode1_mix": Workload("decode1_mix", 7, T=1, H=4096, E=256, I=2048, k=8, layer_id=3, bits=2, bits_down=4,
+                            description="decode, one token, 2-bit gate/up and 4-bit down"),
+    "prefill_mix": Workload("prefill_mix", 8, T=2048, H=4096, E=256, I=2048, k=8, layer_id=3, bits=2, bits_down=4,
+                            description="prefill chunk of 2048 tokens, 2-bit gate/up and 4-bit down"),
 }
 
 
@@ -257,7 +267,7 @@ def make_layer(wl: Workload | str, seed: int = DEFAULT_SEED, T: int | None = Non
     if experts:
         gate = qk_matrices(seed, stream_id(lid, K_GATE), E, I, H, wl.w_sigma, wl.bits)
         up = qk_matrices(seed, stream_id(lid, K_UP), E, I, H, wl.w_sigma, wl.bits)
-        down = qk_matrices(seed, stream_id(lid, K_DOWN), E, H, I, wl.w_sigma, wl.bits)
+        down = qk_matrices(seed, stream_id(lid, K_DOWN), E, H, I, wl.w_sigma, wl.down_width)
     else:
         gate = up = down = None
     shg = shu = shd = None
@@ -275,7 +285,8 @@ def derive(base: LayerInputs, wl: Workload | str, T: int | None = None, batch: i
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
     b = base.wl
-    assert (wl.H, wl.E, wl.I, wl.layer_id, wl.bits) == (b.H, b.E, b.I, b.layer_id, b.bits)
+    assert (wl.H, wl.E, wl.I, wl.layer_id, wl.bits, wl.down_width) == (b.H, b.E, b.I, b.layer_id, b.bits,
+                                                                       b.down_width)
     T = wl.T if T is None else T
     shared = make_layer(wl, base.seed, T=1, experts=False) if (wl.Is or wl.zipf_s) else None
     return LayerInputs(wl, base.seed, T, make_x(wl, base.seed, T, batch), base.router_w,

@@ -252,3 +252,20 @@ def test_decode_noalloc_rejects_on_host():
     # the full-size decode shapes fit: T = 16 with k = 16 and 4-bit experts
     full = dims(k=16, Is=2048, bits=4)
     assert B.ds4moe_workspace_bytes(full, 16, B.MODE_DECODE) <= B.DS4MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_down_bits_validation():
+    assert B.ds4moe_workspace_bytes(dims(), 16, B.MODE_DECODE) > 0
+    d = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 2, 4)
+    assert B.ds4moe_workspace_bytes(d, 16, B.MODE_DECODE) > 0
+    for bad in (1, 3, 8, -2):
+        d = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 2, bad)
+        assert B.ds4moe_workspace_bytes(d, 16, B.MODE_DECODE) == 0
+        w = B.make_weights(256, 256, 256, 256)
+        assert B.lib().ds4moe_forward_decode(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(256), 1,
+                                             ctypes.c_void_p(256), None, ctypes.c_void_p(256), 1 << 30,
+                                             None) == B.DS4MOE_ERR_SHAPE
+    # a cache slot holds gate and up at expert_bits and down at down_bits
+    d2 = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 2, 0)
+    d4 = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 2, 4)
+    assert B.ds4moe_cache_bytes(d4, 10) - B.ds4moe_cache_bytes(d2, 10) == 10 * (4849664 - 2752512)

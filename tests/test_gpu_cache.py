@@ -67,16 +67,17 @@ def _run_sequence(L0, dl, cache, Ts, seed_batch0=1):
     return used
 
 
-def _mid(E=64, k=4, bits=2):
+def _mid(E=64, k=4, bits=2, bits_down=0):
     return synth.Workload("mid_cache", 0, T=1, H=512, E=E, I=256, k=k, x_dtype="f32", router_dtype="f32",
-                          router_sigma=0.05, layer_id=0, bits=bits)
+                          router_sigma=0.05, layer_id=0, bits=bits, bits_down=bits_down)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
-def test_cache_matches_resident_with_evictions(bits):
-    """E = 64, k = 4, 16 slots: batches of 1-4 tokens evict all the time."""
+@pytest.mark.parametrize("bits,bits_down", [(2, 0), (4, 0), (2, 4), (4, 2)])
+def test_cache_matches_resident_with_evictions(bits, bits_down):
+    """E = 64, k = 4, 16 slots: batches of 1-4 tokens evict all the time
+    (also with the down matrices in the other code width)."""
     q = _q()
-    L0 = synth.make_layer(_mid(bits=bits))
+    L0 = synth.make_layer(_mid(bits=bits, bits_down=bits_down))
     dl = q.from_layer_inputs(L0)
     cache = q.ExpertCache(dl, 16)
     # the first call also against the oracle

@@ -8,6 +8,7 @@ that both formats can hold, and a float64 dense FFN for the one-expert layer.
 from fractions import Fraction
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -150,3 +151,36 @@ def test_q4_generator_blocks_decode_near_draws():
     assert m.shape == (2, 32 * 148)
     w = oracle.dequant_f64(m, bits=4)
     assert np.all(np.isfinite(w)) and 0.01 < w.std() < 0.03
+
+
+@pytest.mark.parametrize("gu_bits,dn_bits", [(2, 4), (4, 2)])
+def test_mixed_widths_two_experts_equal_dense_ffns(gu_bits, dn_bits):
+    """Gate/up in one code width and down in the other: two experts, k = 2,
+    against the float64 library FFN on each expert's dequantized matrices
+    (each width's dequantization is pinned above), combined with the routing
+    weights.  A slip in which matrix takes which width, or in the down
+    matrices' expert stride, fails here."""
+    rng = np.random.default_rng(44 + gu_bits)
+    T, H, I, E = 5, 256, 256, 2
+
+    def qb(rows, cols, bits):
+        return synth.quantize_blocks((0.02 * rng.standard_normal((rows, cols))).astype(np.float32), bits=bits)
+
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (0.05 * rng.standard_normal((E, H))).astype(np.float32)
+    g = np.stack([qb(I, H, gu_bits) for _ in range(E)])
+    u = np.stack([qb(I, H, gu_bits) for _ in range(E)])
+    d = np.stack([qb(H, I, dn_bits) for _ in range(E)])
+    y, idx, w = oracle.layer(x, wr, None, g, u, d, H, I, E, 2, bits=gu_bits, down_bits=dn_bits)
+    _, _, wd = oracle.topk(oracle.logits(x, wr), 2)
+    xt = torch.from_numpy(x).double()
+    ref = torch.zeros(T, H, dtype=torch.float64)
+    for e in range(E):
+        Wg = torch.from_numpy(oracle.dequant_f64(g[e], bits=gu_bits).reshape(I, H))
+        Wu = torch.from_numpy(oracle.dequant_f64(u[e], bits=gu_bits).reshape(I, H))
+        Wd = torch.from_numpy(oracle.dequant_f64(d[e], bits=dn_bits).reshape(H, I))
+        ye = _dense_swiglu_f64(Wg, Wu, Wd, xt)
+        for t in range(T):
+            j = int(np.where(idx[t] == e)[0][0])
+            ref[t] += wd[t, j] * ye[t]
+    np.testing.assert_allclose(y, ref.float().numpy(), rtol=1e-6, atol=1e-7)
