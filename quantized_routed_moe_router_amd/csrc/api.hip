@@ -14,7 +14,7 @@ namespace {
 constexpr int kVersion = 200;  // 0.2.0: ds4moe_dims.down_bits
 constexpr int kTileDecode = 16;
 constexpr int kTilePrefill = 64;      // tokens per prefill tile (64-token GEMM kernels)
-constexpr int kTilePrefillWide = 96;  // with the wide-tile GEMM kernels
+constexpr int kTilePrefillWide = 80;  // with the wide-tile GEMM kernels
 constexpr int64_t kMaxTokens = 1 << 20;
 // decode kernels address their activations as 32-bit byte offsets into the workspace
 constexpr int64_t DS4_WS_WINDOW = (int64_t)1 << 31;

@@ -417,7 +417,7 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
 }
 
 // ------------------------------------------------------------------ prefill grouped GEMM, wide tiles
-// Workgroup = one tile of up to 96 tokens x (8 waves * R * 16) rows of NM
+// Workgroup = one tile of up to 80 tokens x (8 waves * R * 16) rows of NM
 // packed matrices.  Per super-block every token row of the tile (256 fp16
 // activations and the 32 halves of their 16-column sums, hi then lo: 36
 // chunks of 16 bytes, plus one pad chunk so that rows start on different
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
 // multiplied (the packed weights of the next super-block load into the
 // other register set meanwhile).  The multiply is instantiated for the tile's
 // number of live 16-token n-tiles, so partial tiles issue no dead MFMAs.
-constexpr int PT_NTM = 6;                                          // n-tiles per tile (96 tokens)
+constexpr int PT_NTM = 5;                                          // n-tiles per tile (80 tokens)
 constexpr int PT_CH = 37;                                          // chunks per token row
 constexpr int PT_NW = 8;                                           // waves per workgroup
 constexpr int PT_SLOT_CH = ((PT_NTM * 16 * PT_CH + 64 * PT_NW - 1) / (64 * PT_NW)) * (64 * PT_NW);
@@ -703,8 +703,7 @@ __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAc
     case 2: pt_tile<NM, R, 2, B>(a, xa, tl, rb, ring); break;
     case 3: pt_tile<NM, R, 3, B>(a, xa, tl, rb, ring); break;
     case 4: pt_tile<NM, R, 4, B>(a, xa, tl, rb, ring); break;
-    case 5: pt_tile<NM, R, 5, B>(a, xa, tl, rb, ring); break;
-    default: pt_tile<NM, R, 6, B>(a, xa, tl, rb, ring); break;
+    default: pt_tile<NM, R, 5, B>(a, xa, tl, rb, ring); break;
   }
 }
 
