@@ -283,13 +283,13 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   // decode with T <= 4: the gate/up kernel routes the batch itself (not
   // through the cache, whose plan sits between routing and gate/up)
   const bool fused_route = dec && L.sliced && T <= 4 && !cc;
-  DecRoute rr{at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, d.n_experts, d.top_k, ro,
+  DecRoute rr{at<double>(ws, L.part), router_nslice(d.hidden, T), w->router_bias, p.logits, d.n_experts, d.top_k, ro,
               dtiles, ntiles};
   if (L.sliced) {
     TRY(launch_router_sliced(x, xb, w->router_w, wb, at<double>(ws, L.part), T, d.n_experts, d.hidden, &xp, s,
                              tm(SL_ROUTER)));
     if (!fused_route)
-      TRY(launch_route_dec(at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, T,
+      TRY(launch_route_dec(at<double>(ws, L.part), router_nslice(d.hidden, T), w->router_bias, p.logits, T,
                            d.n_experts, d.top_k, ro, dtiles, ntiles, s, tm(SL_ROUTE)));
   } else {
     TRY(launch_router_tiled(x, xb, w->router_w, wb, w->router_bias, p.logits, T, d.n_experts, d.hidden, s,
@@ -462,7 +462,7 @@ int ds4moe_route(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x
   if (L.sliced) {
     TRY(launch_router_sliced(x, xb, w->router_w, wb, at<double>(ws, L.part), T, d.n_experts, d.hidden, nullptr,
                              s));
-    TRY(launch_route_dec(at<double>(ws, L.part), router_slices(d.hidden), w->router_bias, p.logits, T, d.n_experts,
+    TRY(launch_route_dec(at<double>(ws, L.part), router_nslice(d.hidden, T), w->router_bias, p.logits, T, d.n_experts,
                          d.top_k, ro, nullptr, nullptr, s));
     return DS4MOE_OK;
   }

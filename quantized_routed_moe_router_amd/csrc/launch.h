@@ -140,6 +140,11 @@ hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H,
 // T <= 16: logits as fp64 partial sums per column slice [router_slices(H)][T][E],
 // with the activation preparation (if xp != nullptr)
 int router_slices(int H);
+// batches of at most this many tokens: one expert per workgroup and a single
+// slice (the whole row)
+constexpr int ROUTER_ROWS_MAX_T = 4;
+// slices the router of a T-token batch leaves in part[]
+int router_nslice(int H, int T);
 hipError_t launch_router_sliced(const void *x, bool x_bf16, const void *wr, bool w_bf16, double *part, int T,
                                 int E, int H, const XPrep *xp, hipStream_t s, const Timing *tm = nullptr);
 // one workgroup, T <= 16: slice sums + bias -> logits, top-k, counts, offsets,

@@ -48,9 +48,11 @@ __device__ __forceinline__ void load_x16(const void *xptr, bool x_bf16, int64_t 
 // Token t of x -> x' = x * 2^-e in fp16 (max |x'| in [1, 2), see token_exp),
 // the per-16-element sums of the fp16 values (hi + lo), and e.  NT threads
 // cooperate (one wave, or a whole workgroup of NT threads with `red`: NT/64
-// floats of LDS); tix is the thread's index among them.
+// floats of LDS); tix is the thread's index among them.  e comes from the
+// whole row; the conversion covers the 16-element chunks [j0, j1) (callers
+// that split a row write e from the part with j0 = 0).
 template <int NT>
-__device__ void xprep_token(int t, int H, const XPrep &xp, int tix, float *red) {
+__device__ void xprep_token(int t, int H, const XPrep &xp, int tix, float *red, int j0 = 0, int j1 = 1 << 30) {
   const int nsub = H >> 4;
   float amax = 0.0f;
   for (int j = tix; j < nsub; j += NT) {
@@ -69,11 +71,11 @@ __device__ void xprep_token(int t, int H, const XPrep &xp, int tix, float *red) 
     for (int w = 0; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
   }
   const int e = token_exp(amax);
-  if (tix == 0) {
+  if (tix == 0 && j0 == 0) {
     xp.xexp[t] = e;
     if (xp.xe16) *reinterpret_cast<u4 *>(xp.xe16 + 4 * (int64_t)t) = (u4){(uint32_t)e, 0u, 0u, 0u};
   }
-  for (int j = tix; j < nsub; j += NT) {
+  for (int j = j0 + tix; j < min(j1, nsub); j += NT) {
     const int64_t base = (int64_t)t * H + 16 * j;
     float v[16];
     load_x16(xp.x, xp.x_bf16, base, v);
@@ -103,8 +105,9 @@ __device__ void xprep_token(int t, int H, const XPrep &xp, int tix, float *red) 
 // expert, lane = columns 4*lane + 256*i (i < 4).  Products of bf16/fp32
 // inputs are exact in fp64, so the per-token sums over the lanes (a
 // reduce-scatter butterfly) and over the slices (routing kernel, slice order)
-// give the fp64 dot product up to fp64 rounding.  Workgroups of expert group
-// 0 also convert their slice of x to fp16 and form the 16-column sums.
+// give the fp64 dot product up to fp64 rounding.  Workgroups also convert
+// their column slice of x (token t in expert group t) to pre-scaled fp16 and
+// form the 16-column sums.
 constexpr int RSLICE = 1024;
 
 template <bool XB, bool WB>
@@ -213,12 +216,83 @@ __global__ __launch_bounds__(256) void k_router_sliced(const void *__restrict__ 
   acc[0] += __shfl_xor(acc[0], 1);
   const int tok = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
   if ((lane & 3) == 0 && tok < T && e < E) part[((int64_t)slice * T + tok) * E + e] = acc[0];
-  if (do_x && blockIdx.y == 0) {
-    // whole rows of x -> pre-scaled fp16 and 16-column sums, one token per
-    // workgroup of the first column slice
+  if (do_x) {
+    // x -> pre-scaled fp16 and 16-column sums: token t by the workgroups of
+    // expert group t (mod the groups), each converting its own column slice
+    // (the exponent comes from the whole row)
     __shared__ float red[4];
-    for (int t = blockIdx.x; t < T; t += gridDim.x) xprep_token<256>(t, H, xp, tid, red);
+    for (int t = blockIdx.x; t < T; t += gridDim.x)
+      xprep_token<256>(t, H, xp, tid, red, c0 >> 4, (c0 + cw) >> 4);
   }
+}
+
+// ---------------------------------------------------------------- logits, T <= 4, one expert per workgroup
+// Grid E, 256 threads: thread i takes the 8-column chunks i, i+256, ... of
+// expert e's row and of the NT token rows of x (read from memory: they are
+// small and every workgroup reads them), multiplies in fp64 (exact for
+// bf16 / fp32 inputs) and sums its products in order; the 256 sums are added
+// by a wave butterfly and then the four waves in order.  The result is the
+// whole fp64 dot product of each token with the row (one "slice").  The
+// first 4T workgroups also convert a quarter of a token's row of x each
+// (pre-scaled fp16 and 16-column sums; the exponent from the whole row).
+template <bool XB>
+__device__ __forceinline__ void load8_as_double(const void *p, int64_t idx, double out[8]) {
+  if (XB) {
+    const u4 v = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(p) + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = (double)bf16_bits_to_float((uint16_t)(v[i] & 0xFFFF));
+      out[2 * i + 1] = (double)bf16_bits_to_float((uint16_t)(v[i] >> 16));
+    }
+  } else {
+    const f4 a = *reinterpret_cast<const f4 *>(reinterpret_cast<const float *>(p) + idx);
+    const f4 b = *reinterpret_cast<const f4 *>(reinterpret_cast<const float *>(p) + idx + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[i] = a[i];
+      out[4 + i] = b[i];
+    }
+  }
+}
+
+template <bool XB, bool WB, int NT>
+__global__ __launch_bounds__(256) void k_router_rows(const void *__restrict__ x, const void *__restrict__ wr,
+                                                     double *__restrict__ part, int T, int E, int H, XPrep xp,
+                                                     bool do_x) {
+  __shared__ double red[4][NT];
+  __shared__ float xred[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x;
+  const int nch = H >> 3;
+  double acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.0;
+  for (int ch = tid; ch < nch; ch += 256) {
+    double w[8];
+    load8_as_double<WB>(wr, (int64_t)e * H + 8 * ch, w);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < T) {
+        double xv[8];
+        load8_as_double<XB>(x, (int64_t)t * H + 8 * ch, xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[t] = fma(xv[i], w[i], acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc[t] += __shfl_xor(acc[t], o);
+    if (lane == 0) red[wave][t] = acc[t];
+  }
+  __syncthreads();
+  if (tid < T) part[(int64_t)tid * E + e] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  if (do_x)
+    for (int q = blockIdx.x; q < 4 * T; q += gridDim.x) {
+      const int t = q >> 2, j0 = (q & 3) * (H >> 6);
+      xprep_token<256>(t, H, xp, tid, xred, j0, j0 + (H >> 6));
+    }
 }
 
 // ---------------------------------------------------------------- logits, MFMA fp64
@@ -583,8 +657,28 @@ static hipError_t router_sliced_t(const void *x, const void *wr, double *part, i
   return hipGetLastError();
 }
 
+template <bool XB, bool WB>
+static hipError_t router_rows_t(const void *x, const void *wr, double *part, int T, int E, int H, const XPrep *xp,
+                                hipStream_t s, const Timing *tm) {
+  const XPrep xv = xp ? *xp : XPrep{};
+  switch (T) {
+    case 1: DS4_LAUNCH(tm, (k_router_rows<XB, WB, 1>), dim3(E), dim3(256), 0, s, x, wr, part, T, E, H, xv, xp != nullptr); break;
+    case 2: DS4_LAUNCH(tm, (k_router_rows<XB, WB, 2>), dim3(E), dim3(256), 0, s, x, wr, part, T, E, H, xv, xp != nullptr); break;
+    default: DS4_LAUNCH(tm, (k_router_rows<XB, WB, 4>), dim3(E), dim3(256), 0, s, x, wr, part, T, E, H, xv, xp != nullptr);
+  }
+  return hipGetLastError();
+}
+
+int router_nslice(int H, int T) { return T <= ROUTER_ROWS_MAX_T ? 1 : router_slices(H); }
+
 hipError_t launch_router_sliced(const void *x, bool x_bf16, const void *wr, bool w_bf16, double *part, int T,
                                 int E, int H, const XPrep *xp, hipStream_t s, const Timing *tm) {
+  if (T <= ROUTER_ROWS_MAX_T) {  // one expert per workgroup, the whole row
+    if (x_bf16 && w_bf16) return router_rows_t<true, true>(x, wr, part, T, E, H, xp, s, tm);
+    if (x_bf16) return router_rows_t<true, false>(x, wr, part, T, E, H, xp, s, tm);
+    if (w_bf16) return router_rows_t<false, true>(x, wr, part, T, E, H, xp, s, tm);
+    return router_rows_t<false, false>(x, wr, part, T, E, H, xp, s, tm);
+  }
   if (x_bf16 && w_bf16) return router_sliced_t<true, true>(x, wr, part, T, E, H, xp, s, tm);
   if (x_bf16) return router_sliced_t<true, false>(x, wr, part, T, E, H, xp, s, tm);
   if (w_bf16) return router_sliced_t<false, true>(x, wr, part, T, E, H, xp, s, tm);
