@@ -276,7 +276,7 @@ int ds4moe_forward_timed(int32_t mode, const ds4moe_dims *dims, const ds4moe_wei
 int ds4moe_read_probe(const void *buf, size_t bytes, int32_t n_workgroups, uint32_t *sink, void *start_event,
                       void *stop_event, void *stream);
 
-/* ROUTED-EXPERT CACHE (small batches).  The experts' packed matrices stay in
+/* ROUTED-EXPERT CACHE.  The experts' packed matrices stay in
  * pinned host memory; a cache buffer in device memory holds n_slots expert
  * slots (gate, up and down of one expert each).  A call routes the batch,
  * gives every expert it uses a slot (a slot already holding the expert, else
@@ -318,6 +318,30 @@ int ds4moe_cache_reset(const ds4moe_dims *dims, int32_t n_slots, void *cache, si
 int ds4moe_forward_decode_cached(const ds4moe_dims *dims, const ds4moe_weights *w, int32_t n_slots, void *cache,
                                  size_t cache_bytes, const void *x, int32_t T, float *y, ds4moe_routing *route_out,
                                  void *ws, size_t ws_bytes, void *const *events, void *stream);
+
+/* ds4moe_forward_prefill (any T up to 2^20) with the routed experts in host
+ * memory, as for ds4moe_forward_decode_cached (same weights convention, same
+ * cache buffer, any 1 <= n_slots <= E).  A long batch may use more experts
+ * than there are slots, so the used experts go through the slots in batches
+ * of at most n_slots: the first batch holds every expert already cached (the
+ * hits) and then misses in ascending expert order while slots remain, each
+ * later batch the next n_slots misses; inside a batch each miss, in
+ * ascending order, takes the least recently used slot (ties to the lower
+ * slot index) that the batch has not taken, and a batch's misses are copied
+ * in before its experts run.  Every used expert is copied at most once per
+ * call, so a call copies max(0, used - cached) experts when the cache held
+ * min(used, n_slots) of them.  The outputs are bitwise those of
+ * ds4moe_forward_prefill on the same experts resident in device memory.
+ * This is the pages' streaming mode serving long prefills, which it keeps
+ * fast ("antirez-ds4" insight page, SSD streaming section; DwarfStar
+ * architecture article, "Memory trade-off: resident vs SSD streaming"
+ * section), with host memory as the backing store.  ws: ds4moe_workspace_bytes(dims, T,
+ * DS4MOE_MODE_PREFILL).  Calls on one cache buffer must not overlap.
+ * Errors: those of ds4moe_forward_prefill and ds4moe_cache_reset, and
+ * DS4MOE_ERR_HOSTMEM when an expert pointer is not pinned host memory. */
+int ds4moe_forward_prefill_cached(const ds4moe_dims *dims, const ds4moe_weights *w, int32_t n_slots, void *cache,
+                                  size_t cache_bytes, const void *x, int32_t T, float *y, ds4moe_routing *route_out,
+                                  void *ws, size_t ws_bytes, void *stream);
 
 /* Enqueue a copy of the cache's counters since its reset to host memory
  * out[3] = {calls, hits, misses} (hits and misses count experts of calls);

@@ -33,7 +33,8 @@ EXPORTED = ("ds4moe_packed_bytes", "ds4moe_packed_bytes_bits", "ds4moe_pack_q2k"
             "ds4moe_dequant_q2k", "ds4moe_dequant", "ds4moe_workspace_bytes",
             "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_status_str",
             "ds4moe_version", "ds4moe_forward_timed", "ds4moe_cache_bytes", "ds4moe_cache_reset",
-            "ds4moe_forward_decode_cached", "ds4moe_cache_stats", "ds4moe_forward_decode_noalloc",
+            "ds4moe_forward_decode_cached", "ds4moe_forward_prefill_cached", "ds4moe_cache_stats",
+            "ds4moe_forward_decode_noalloc",
             "ds4moe_read_probe")
 N_TIMED_KERNELS = 10
 KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine",
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_cache_reset.argtypes = [P, I32, P, ctypes.c_size_t, P]
         L.ds4moe_forward_decode_cached.argtypes = [P, P, I32, P, ctypes.c_size_t, P, I32, P, P, P, ctypes.c_size_t,
                                                    P, P]
+        L.ds4moe_forward_prefill_cached.argtypes = [P, P, I32, P, ctypes.c_size_t, P, I32, P, P, P, ctypes.c_size_t,
+                                                    P]
         L.ds4moe_cache_stats.argtypes = [P, I32, P, ctypes.c_size_t, P, P]
         L.ds4moe_forward_decode_noalloc.argtypes = [P, P, P, I32, P, P, P]
         L.ds4moe_read_probe.argtypes = [P, ctypes.c_size_t, I32, P, P, P, P]
@@ -98,7 +101,8 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_status_str.restype = ctypes.c_char_p
         L.ds4moe_version.restype = ctypes.c_int
         for fn in ("ds4moe_pack_q2k", "ds4moe_dequant_q2k", "ds4moe_pack", "ds4moe_dequant", "ds4moe_route",
-                   "ds4moe_cache_reset", "ds4moe_forward_decode_cached", "ds4moe_cache_stats",
+                   "ds4moe_cache_reset", "ds4moe_forward_decode_cached", "ds4moe_forward_prefill_cached",
+                   "ds4moe_cache_stats",
                    "ds4moe_forward_decode", "ds4moe_forward_decode_noalloc", "ds4moe_read_probe",
                    "ds4moe_forward_prefill", "ds4moe_forward_timed"):
             getattr(L, fn).restype = ctypes.c_int
@@ -236,6 +240,15 @@ def ds4moe_forward_decode_cached(dims: Dims, weights: Weights, n_slots: int, cac
     _check(lib().ds4moe_forward_decode_cached(ctypes.byref(dims), ctypes.byref(weights), n_slots, _ptr(cache),
                                               cache_bytes, _ptr(x), T, _ptr(y), r, _ptr(ws), ws_bytes,
                                               _events(events), _stream(stream)), "forward_decode_cached")
+
+
+def ds4moe_forward_prefill_cached(dims: Dims, weights: Weights, n_slots: int, cache, cache_bytes: int, x, T: int,
+                                  y, routing: Routing | None, ws, ws_bytes: int, stream=None) -> None:
+    """weights.gate/up/down: pinned host memory; ws: the prefill workspace."""
+    r = ctypes.byref(routing) if routing is not None else None
+    _check(lib().ds4moe_forward_prefill_cached(ctypes.byref(dims), ctypes.byref(weights), n_slots, _ptr(cache),
+                                               cache_bytes, _ptr(x), T, _ptr(y), r, _ptr(ws), ws_bytes,
+                                               _stream(stream)), "forward_prefill_cached")
 
 
 def ds4moe_cache_stats(dims: Dims, n_slots: int, cache, cache_bytes: int, stream=None) -> tuple:

@@ -11,7 +11,7 @@ using namespace ds4;
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: ds4moe_dims.down_bits
+constexpr int kVersion = 300;  // 0.3.0: ds4moe_forward_prefill_cached
 constexpr int kTileDecode = 16;
 constexpr int kTilePrefill = 64;      // tokens per prefill tile (64-token GEMM kernels)
 constexpr int kTilePrefillWide = 80;  // with the wide-tile GEMM kernels
@@ -127,10 +127,10 @@ T *at(void *ws, size_t off) {
   return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
 }
 
-// Routed-expert cache buffer: header, slot tables, fill list, then S slots
-// of gate, up and down matrices.
+// Routed-expert cache buffer: header, slot tables, fill list and the
+// batches' fill and tile ranges, then S slots of gate, up and down matrices.
 struct CacheLayout {
-  size_t hdr, slot_expert, expert_slot, stamp, fill_e, fill_s, gate, up, down, total;
+  size_t hdr, slot_expert, expert_slot, stamp, fill_e, fill_s, frange, brange, gate, up, down, total;
   size_t gu_bytes, d_bytes;
 };
 
@@ -148,8 +148,10 @@ CacheLayout make_cache_layout(const ds4moe_dims &d, int S) {
   C.slot_expert = take(4 * (size_t)S);
   C.expert_slot = take(4 * (size_t)d.n_experts);
   C.stamp = take(4 * (size_t)S);
-  C.fill_e = take(4 * (size_t)S);
-  C.fill_s = take(4 * (size_t)S);
+  C.fill_e = take(4 * (size_t)d.n_experts);
+  C.fill_s = take(4 * (size_t)d.n_experts);
+  C.frange = take(8 * (size_t)d.n_experts);
+  C.brange = take(8 * (size_t)d.n_experts);
   C.gate = take(C.gu_bytes * (size_t)S);
   C.up = take(C.gu_bytes * (size_t)S);
   C.down = take(C.d_bytes * (size_t)S);
@@ -165,6 +167,8 @@ CacheState cache_state(void *cache, const CacheLayout &C) {
   c.stamp = at<uint32_t>(cache, C.stamp);
   c.fill_e = at<int32_t>(cache, C.fill_e);
   c.fill_s = at<int32_t>(cache, C.fill_s);
+  c.frange = at<int32_t>(cache, C.frange);
+  c.brange = at<int32_t>(cache, C.brange);
   c.gate = at<uint8_t>(cache, C.gate);
   c.up = at<uint8_t>(cache, C.up);
   c.down = at<uint8_t>(cache, C.down);
@@ -305,9 +309,13 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.gu_bytes = ds4moe_packed_bytes_bits(d.inter, d.hidden, d.expert_bits);
   ga.d_bytes = ds4moe_packed_bytes_bits(d.hidden, d.inter, down_bits(d));
   if (cc) {  // experts through the cache: tiles name slots, the kernels read the slot arrays
-    TRY(launch_cache_plan(cc->st, dtiles, ntiles, cc->S, d.n_experts, s, tm(SL_CPLAN)));
-    TRY(launch_cache_fill(cc->st, cc->hg, cc->hu, cc->hd, ga.gu_bytes, ga.d_bytes,
-                          L.max_tiles < cc->S ? L.max_tiles : cc->S, s, tm(SL_CFILL)));
+    if (dec) {
+      TRY(launch_cache_plan(cc->st, dtiles, ntiles, cc->S, d.n_experts, s, tm(SL_CPLAN)));
+      TRY(launch_cache_fill(cc->st, cc->st.frange, cc->hg, cc->hu, cc->hd, ga.gu_bytes, ga.d_bytes,
+                            L.max_tiles < cc->S ? L.max_tiles : cc->S, s, tm(SL_CFILL)));
+    } else {
+      TRY(launch_cache_plan_prefill(cc->st, p.counts, p.offsets, ro.tiles, L.tile_n, cc->S, d.n_experts, s));
+    }
     ga.gate = cc->st.gate;
     ga.up = cc->st.up;
     ga.down = cc->st.down;
@@ -363,6 +371,26 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     if (st) return st;
     ga.ysh = ysh;
     TRY(launch_down_combine_dec(ga, s, tm(SL_DOWN), T > 4 ? tm(SL_COMBINE) : nullptr));
+  } else if (cc) {
+    // batch j: load its misses, then its tiles through gate/up and down; the
+    // host launches the most batches the call can need, the plan leaves the
+    // ones past the last empty (no fill items, no tiles)
+    const int64_t A = (int64_t)T * d.top_k;
+    const int used_max = (int)(A < d.n_experts ? A : d.n_experts);
+    const int nb_max = (used_max + cc->S - 1) / cc->S;
+    const int64_t cap64 = A / L.tile_n + (cc->S < used_max ? cc->S : used_max);
+    const int cap = (int)(cap64 < L.max_tiles ? cap64 : L.max_tiles);  // tiles of one batch
+    for (int j = 0; j < nb_max; ++j) {
+      TRY(launch_cache_fill(cc->st, cc->st.frange + 2 * j, cc->hg, cc->hu, cc->hd, ga.gu_bytes, ga.d_bytes,
+                            cc->S < used_max ? cc->S : used_max, s));
+      GemmArgs gb = ga;
+      gb.ntiles = cc->st.brange + 2 * j;
+      TRY(launch_gateup(gb, cap, s));
+      TRY(launch_down(gb, cap, s));
+    }
+    st = shared();
+    if (st) return st;
+    TRY(launch_combine(ga.yp, ro.pos, p.w, xp.xexp, ysh, y, T, d.top_k, d.hidden, s, tm(SL_COMBINE)));
   } else {
     TRY(launch_gateup(ga, L.max_tiles, s, tm(SL_GATEUP)));
     TRY(launch_down(ga, L.max_tiles, s, tm(SL_DOWN)));
@@ -595,6 +623,23 @@ int ds4moe_forward_decode_noalloc(const ds4moe_dims *dims, const ds4moe_weights 
   st = scratch_ptr(&ws);
   if (st) return st;
   return forward(dims, w, x, T, y, route_out, ws, kNoAllocScratchBytes, stream, DS4MOE_MODE_DECODE);
+}
+
+int ds4moe_forward_prefill_cached(const ds4moe_dims *dims, const ds4moe_weights *w, int32_t n_slots, void *cache,
+                                  size_t cache_bytes, const void *x, int32_t T, float *y, ds4moe_routing *route_out,
+                                  void *ws, size_t ws_bytes, void *stream) {
+  CacheLayout C;
+  int st = check_cache(dims, n_slots, cache, cache_bytes, &C);
+  if (st) return st;
+  st = validate_weights(*dims, w, true);
+  if (st) return st;
+  Layout L;
+  st = check_call(dims, w, x, T, y, true, route_out, ws, ws_bytes, DS4MOE_MODE_PREFILL, &L);
+  if (st || T == 0) return st;
+  CacheCall cc{cache_state(cache, C), n_slots, host_device_ptr(w->gate), host_device_ptr(w->up),
+               host_device_ptr(w->down)};
+  if (!cc.hg || !cc.hu || !cc.hd) return DS4MOE_ERR_HOSTMEM;
+  return forward(dims, w, x, T, y, route_out, ws, ws_bytes, stream, DS4MOE_MODE_PREFILL, nullptr, &cc);
 }
 
 int ds4moe_cache_stats(const ds4moe_dims *dims, int32_t n_slots, const void *cache, size_t cache_bytes,

@@ -276,8 +276,8 @@ __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   __shared__ __attribute__((aligned(16))) half_t sS[64 * SS_STRIDE];
   const int tile_id = blockIdx.x / nrb;
   const int rb = blockIdx.x - tile_id * nrb;
-  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
-  const TileT tl = a.tiles[tile_id];
+  if (tile_id >= a.ntiles[0]) return;  // uniform over the workgroup
+  const TileT tl = a.tiles[a.ntiles[1] + tile_id];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   constexpr bool GU = NM == 2;
@@ -692,8 +692,8 @@ __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAc
   __shared__ __attribute__((aligned(16))) char ring[2 * PT_SLOT_BYTES];
   const int tile_id = blockIdx.x / nrb;
   const int rb = blockIdx.x - tile_id * nrb;
-  if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
-  const TileT tl = a.tiles[tile_id];
+  if (tile_id >= a.ntiles[0]) return;  // uniform over the workgroup
+  const TileT tl = a.tiles[a.ntiles[1] + tile_id];
   if (ALL) {
     pt_tile<NM, R, PT_NTM, B>(a, xa, tl, rb, ring);
     return;

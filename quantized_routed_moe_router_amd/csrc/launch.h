@@ -46,7 +46,7 @@ struct RouteOut {
   int32_t *perm;       // [T*k]
   int32_t *pos;        // [T*k] inverse of perm (nullable)
   TileT *tiles;        // [max_tiles] (nullable)
-  int32_t *ntiles;     // [1]       (nullable)
+  int32_t *ntiles;     // [2] tile count, first tile (0) (nullable)
   int tile_n;          // tokens per tile
   _Float16 *zeros;     // cleared here each call: read by GEMM lanes with no token
   int nzeros;          // halves
@@ -76,7 +76,7 @@ struct GemmArgs {
   int bits;                          // code width of the packed gate/up units: 2 or 4
   int bits_dn;                       // code width of the packed down units: 2 or 4
   const TileT *tiles;
-  const int32_t *ntiles;
+  const int32_t *ntiles;             // decode: [1] DecTiles; prefill: [2] tile count, first tile
   const int32_t *perm;
   int k, H, I, Ipad;
   const _Float16 *x16, *xs_hi, *xs_lo;
@@ -103,7 +103,7 @@ struct GemmArgs {
 // Routed-expert cache state (device memory, inside the caller's cache buffer).
 struct CacheHdr {
   uint32_t step;                    // calls since the reset (the stamp of the current call)
-  uint32_t fill_n;                  // misses of the last call = length of the fill list
+  uint32_t fill_n;                  // misses of the last call = length of its fill list
   unsigned long long calls, hits, misses;
 };
 struct CacheState {
@@ -111,7 +111,9 @@ struct CacheState {
   int32_t *slot_expert;             // [S] expert held by each slot, -1 = empty
   int32_t *expert_slot;             // [E] slot of each expert, -1 = not cached
   uint32_t *stamp;                  // [S] step of the slot's last use (0 = never)
-  int32_t *fill_e, *fill_s;         // [S] the last call's misses: expert, slot
+  int32_t *fill_e, *fill_s;         // [E] the last call's misses in batch order: expert, slot
+  int32_t *frange;                  // [E][2] each batch's fill items [begin, end)
+  int32_t *brange;                  // [E][2] each batch's prefill tiles: count, first
   uint8_t *gate, *up, *down;        // S slots of packed matrices each
 };
 
@@ -119,9 +121,15 @@ hipError_t launch_cache_reset(const CacheState &c, int S, int E, hipStream_t s);
 // after the small-batch routing: plan slots, rewrite each DecTile's expert as its slot
 hipError_t launch_cache_plan(const CacheState &c, DecTile *dt, const int32_t *ntile, int S, int E, hipStream_t s,
                              const Timing *tm = nullptr);
-// copy the planned misses from host memory (device-visible pointers) into their slots
-hipError_t launch_cache_fill(const CacheState &c, const void *hg, const void *hu, const void *hd, size_t gu_bytes,
-                             size_t d_bytes, int max_items, hipStream_t s, const Timing *tm = nullptr);
+// prefill: split the used experts into batches that fit the slots, plan each
+// batch's slots and write the tile list in batch order with slots for experts
+hipError_t launch_cache_plan_prefill(const CacheState &c, const int32_t *counts, const int32_t *offsets,
+                                     TileT *tiles, int tile_n, int S, int E, hipStream_t s);
+// copy the fill items [fr[0], fr[1]) from host memory (device-visible
+// pointers) into their slots
+hipError_t launch_cache_fill(const CacheState &c, const int32_t *fr, const void *hg, const void *hu, const void *hd,
+                             size_t gu_bytes, size_t d_bytes, int max_items, hipStream_t s,
+                             const Timing *tm = nullptr);
 
 hipError_t launch_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, int bits,
                        hipStream_t s);

@@ -553,7 +553,10 @@ __global__ __launch_bounds__(1024) void k_scan_chunks(int T, int E, int k, int n
     }
     if (lane == 63) {
       ro.offsets[E] = ic;
-      if (ro.ntiles) *ro.ntiles = it;
+      if (ro.ntiles) {  // the whole list: count, first tile
+        ro.ntiles[0] = it;
+        ro.ntiles[1] = 0;
+      }
     }
   }
   __syncthreads();

@@ -136,8 +136,10 @@ def from_layer_inputs(L, device="cuda:0", experts: bool = True) -> DeviceLayer:
 
 class ExpertCache:
     """A bounded routed-expert cache in device memory over experts kept in
-    pinned host memory (small batches).  `host`: (gate, up, down) pinned
-    uint8 tensors in the packed layout, by default copies of `dl`'s."""
+    pinned host memory.  `host`: (gate, up, down) pinned uint8 tensors in the
+    packed layout, by default copies of `dl`'s.  forward: small batches
+    (decode); forward_prefill: any batch, the used experts streamed through
+    the slots in batches."""
 
     def __init__(self, dl: DeviceLayer, n_slots: int, host: tuple | None = None, stream=None):
         self.dl, self.n_slots = dl, n_slots
@@ -165,6 +167,19 @@ class ExpertCache:
         w = weights if weights is not None else self.weights()
         B.ds4moe_forward_decode_cached(dl.dims, w, self.n_slots, self.buf, self.nbytes, x, T, y, r, ws, ws.numel(),
                                        events, stream)
+        return y
+
+    def forward_prefill(self, x: torch.Tensor, y=None, routing: dict | None = None, stream=None,
+                        weights: B.Weights | None = None) -> torch.Tensor:
+        dl = self.dl
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty(T, dl.H, dtype=torch.float32, device=dl.device)
+        ws = dl.workspace(T, B.MODE_PREFILL)
+        r = B.make_routing(**routing) if routing is not None else None
+        w = weights if weights is not None else self.weights()
+        B.ds4moe_forward_prefill_cached(dl.dims, w, self.n_slots, self.buf, self.nbytes, x, T, y, r, ws, ws.numel(),
+                                        stream)
         return y
 
     def stats(self, stream=None) -> tuple:

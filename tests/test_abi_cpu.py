@@ -226,6 +226,23 @@ def test_cache_argument_errors():
     assert fwd(cb=100) == B.DS4MOE_ERR_WORKSPACE
     assert fwd(wt=B.make_weights(16, None, 16, 16)) == B.DS4MOE_ERR_NULL
     assert fwd(wt=B.make_weights(16, 24, 16, 16)) == B.DS4MOE_ERR_ALIGN
+
+    def pf(S=16, T=1, cache=256, cb=1 << 40, wt=w, ws=256, wsb=1 << 40):
+        return L.ds4moe_forward_prefill_cached(ctypes.byref(d), ctypes.byref(wt), S, v(cache), cb, v(16), T, v(16),
+                                               None, v(ws), wsb, None)
+    # any slot count 1..E and any T up to 2^20: checks end before the pinned-memory query
+    assert pf(T=0, S=1) == B.DS4MOE_OK                   # nothing to do, nothing launched
+    assert pf(T=0, S=0) == B.DS4MOE_ERR_SHAPE
+    assert pf(T=-1) == B.DS4MOE_ERR_SHAPE
+    assert pf(T=(1 << 20) + 1) == B.DS4MOE_ERR_SHAPE
+    assert pf(S=257) == B.DS4MOE_ERR_SHAPE
+    assert pf(cache=0) == B.DS4MOE_ERR_NULL
+    assert pf(cache=128) == B.DS4MOE_ERR_ALIGN
+    assert pf(cb=100) == B.DS4MOE_ERR_WORKSPACE
+    assert pf(ws=0) == B.DS4MOE_ERR_WORKSPACE
+    assert pf(T=2048, wsb=B.ds4moe_workspace_bytes(d, 2048, B.MODE_PREFILL) - 1) == B.DS4MOE_ERR_WORKSPACE
+    assert pf(wt=B.make_weights(16, None, 16, 16)) == B.DS4MOE_ERR_NULL
+    assert pf(wt=B.make_weights(16, 24, 16, 16)) == B.DS4MOE_ERR_ALIGN
     out = (ctypes.c_uint64 * 3)()
     assert L.ds4moe_cache_stats(ctypes.byref(d), 16, v(256), nb, None, None) == B.DS4MOE_ERR_NULL
     assert L.ds4moe_cache_stats(ctypes.byref(d), 16, None, nb, out, None) == B.DS4MOE_ERR_NULL
