@@ -26,221 +26,257 @@ __global__ __launch_bounds__(256) void k_cache_reset(CacheState c, int S, int E)
   for (int e = threadIdx.x; e < E; e += 256) c.expert_slot[e] = -1;
 }
 
-// One workgroup.  Input: the batch's DecTile list (one tile per used expert,
-// ascending expert).  Hits take the current step as their stamp first, so no
-// expert of the batch is evicted; then each miss, in tile order, takes the
-// slot with the oldest stamp (ties: the lower slot), evicting its expert.
-// Output: the fill list (expert, slot) of the misses, counters, and every
-// tile's expert field replaced by its slot.
+// The slot policy.  A call's used experts split into hits (already in a
+// slot) and misses.  The misses, in ascending expert order, go through the
+// slots in batches: batch 0 is the hits and the first S - hits misses, each
+// later batch the next S misses (a small batch is batch 0 alone).  Batch j
+// has stamp step+1+j; its hits take the stamp first, then each miss in
+// order takes the slot with the smallest (stamp, slot) that the batch has
+// not stamped, evicting its expert.  That sequence has a closed form:
+//  * batch 0's misses take the slots that are not hits in (stamp, slot)
+//    order, since every stamp before the call is below the batch's own;
+//  * a later batch exists only when batch 0 filled every slot, and it
+//    starts with every slot on the same stamp (the previous batch's), so its
+//    i-th miss takes slot i.
+// The plan kernels below compute it in parallel: one workgroup of 256
+// threads (S <= E <= 256), thread t standing for slot t and for expert (or
+// tile) t.
+
+// Exclusive prefix sums, in thread order, of NV values per thread at once;
+// tot[i] = the sum over the workgroup.  Ends with a barrier.
+template <int NV>
+__device__ __forceinline__ void block_scan(int (&v)[NV], int (&tot)[NV], int (*lds)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) x[i] = v[i];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int y = __shfl_up(x[i], o);
+      if (lane >= o) x[i] += y;
+    }
+  if (lane == 63)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) lds[i][wave] = x[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int base = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) base += w < wave ? lds[i][w] : 0;
+    tot[i] = lds[i][0] + lds[i][1] + lds[i][2] + lds[i][3];
+    v[i] = base + x[i] - v[i];
+  }
+  __syncthreads();
+}
+
+// Rank of free slot t (stamp below `step`) by (stamp, slot) among the free
+// slots; slots stamped `step` (the hits) sort after every free slot, so
+// counting all slots below it suffices.  Writes q0[rank] = t; returns the
+// rank, or -1 for a hit slot or t >= S.
+__device__ __forceinline__ int rank_free_slot(const uint32_t *st, int S, uint32_t step, int32_t *q0) {
+  const int t = threadIdx.x;
+  if (t >= S || st[t] == step) return -1;
+  const uint32_t k = st[t];
+  int r = 0;
+#pragma unroll 8
+  for (int i = 0; i < S; ++i) {
+    const uint32_t ki = st[i];
+    r += (ki < k || (ki == k && i < t)) ? 1 : 0;
+  }
+  q0[r] = t;
+  return r;
+}
+
+// Small batches.  Input: the batch's DecTile list (one tile per used expert,
+// ascending expert; the host makes S at least its length, so it is batch 0
+// alone).  Output: the fill list (expert, slot) of the misses and its range,
+// counters, and every tile's expert field replaced by its slot.  Global
+// stores come after the last barrier (a barrier would wait for them).
 __global__ __launch_bounds__(256) void k_cache_plan(CacheState c, DecTile *__restrict__ dt,
                                                     const int32_t *__restrict__ ntile, int S, int E) {
   __shared__ uint32_t st[256];
-  __shared__ int32_t se[256], es[256];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int n = *ntile;
+  __shared__ int32_t q0[256], ml[256], es[256];
+  __shared__ int scan_lds[2][4];
+  const int t = threadIdx.x;
+  const int n = *ntile;  // <= E <= 256
   const uint32_t step = c.hdr->step + 1u;
-  for (int s = tid; s < 256; s += 256) {
-    st[s] = s < S ? c.stamp[s] : 0u;
-    se[s] = s < S ? c.slot_expert[s] : -1;
-  }
-  for (int e = tid; e < 256; e += 256) es[e] = e < E ? c.expert_slot[e] : -1;
+  const int e = t < n ? dt[t].e : -1;
+  const int slot0 = e >= 0 ? c.expert_slot[e] : -1;
+  const bool hit = slot0 >= 0, miss = e >= 0 && slot0 < 0;
+  const int se_in = t < S ? c.slot_expert[t] : -1;
+  st[t] = t < S ? c.stamp[t] : 0u;
+  es[t] = -1;
   __syncthreads();
-  if (tid < n) {  // distinct experts per tile: no two threads stamp one slot
-    const int s = es[dt[tid].e];
-    if (s >= 0) st[s] = step;
-  }
+  if (hit) st[slot0] = step;  // distinct experts hold distinct slots
+  int sv[2] = {miss ? 1 : 0, hit ? 1 : 0}, tot[2];
+  block_scan<2>(sv, tot, scan_lds);
+  const int m = sv[0], nm = tot[0], nhit = tot[1];
+  const int room0 = S - nhit;
+  const int r0 = nm > 0 ? rank_free_slot(st, S, step, q0) : -1;
+  if (miss) ml[m] = e;
   __syncthreads();
-  if (tid < 64) {
-    int nf = 0;
-    for (int i = 0; i < n; ++i) {
-      const int e = dt[i].e;  // uniform
-      if (es[e] >= 0) continue;
-      // victim: smallest (stamp, slot) among slots not used by this batch
-      uint64_t key = ~0ull;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = lane + 64 * j;
-        if (s < S && st[s] != step) {
-          const uint64_t k = ((uint64_t)st[s] << 32) | (uint32_t)s;
-          key = k < key ? k : key;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const uint64_t k = __shfl_xor(key, o);
-        key = k < key ? k : key;
-      }
-      // a victim exists (S >= distinct experts of the batch, checked on the host)
-      if (key == ~0ull) break;
-      const int v = (int)(uint32_t)key;
-      if (lane == 0) {
-        const int old = se[v];
-        if (old >= 0) es[old] = -1;
-        se[v] = e;
-        es[e] = v;
-        st[v] = step;
-        c.fill_e[nf] = e;
-        c.fill_s[nf] = v;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      ++nf;
-    }
-    if (lane == 0) {
-      CacheHdr *h = c.hdr;
-      c.frange[0] = 0;
-      c.frange[1] = nf;
-      h->step = step;
-      h->fill_n = (uint32_t)nf;
-      h->calls += 1ull;
-      h->hits += (unsigned long long)(n - nf);
-      h->misses += (unsigned long long)nf;
-    }
+  const int v = miss ? (m < room0 ? q0[m] : 0) : slot0;  // m < room0: S >= n, checked on the host
+  int se_f = se_in;
+  uint32_t st_f = t < S ? st[t] : 0u;
+  if (r0 >= 0 && r0 < nm) {
+    se_f = ml[r0];
+    st_f = step;
   }
+  if (t < S && se_f >= 0) es[se_f] = t;
   __syncthreads();
-  if (tid < n) dt[tid].e = es[dt[tid].e];
-  for (int s = tid; s < S; s += 256) {
-    c.stamp[s] = st[s];
-    c.slot_expert[s] = se[s];
+  if (miss) {
+    c.fill_e[m] = e;
+    c.fill_s[m] = v;
   }
-  for (int e = tid; e < E; e += 256) c.expert_slot[e] = es[e];
-}
-
-// Prefill through the cache.  One workgroup (E <= 256).  The experts the
-// call uses (count > 0) go through the slots in batches of at most S: batch 0
-// holds every hit and then misses in ascending expert order while slots
-// remain, each later batch the next S misses.  Batch j has the stamp
-// step+1+j, and inside it each miss, in ascending order, takes the slot with
-// the oldest stamp (ties: the lower slot) among the slots the batch has not
-// taken: the small-batch plan above, batch after batch.  A victim always
-// exists: a batch holds at most S experts and every older stamp is below its
-// own.  Outputs: the fill list in batch order with each batch's range of it,
-// each batch's tile count and first tile, and the tile list rewritten in
-// batch order (experts ascending inside a batch) with each expert's slot in
-// place of the expert.  A batch's expert may lose its slot to a later batch:
-// the kernels of its batch have run by then (stream order).
-__global__ __launch_bounds__(256) void k_cache_plan_prefill(CacheState c, const int32_t *__restrict__ counts,
-                                                            const int32_t *__restrict__ offsets,
-                                                            TileT *__restrict__ tiles, int tile_n, int S, int E) {
-  __shared__ uint32_t st[256];
-  __shared__ int32_t se[256], es[256], cn[256], off[256], nt[256], eb[256], bs[256], ts[256], ml[256], bcnt[256];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const uint32_t step0 = c.hdr->step + 1u;
-  st[tid] = tid < S ? c.stamp[tid] : 0u;
-  se[tid] = tid < S ? c.slot_expert[tid] : -1;
-  const int cnt = tid < E ? counts[tid] : 0;
-  const int slot0 = tid < E ? c.expert_slot[tid] : -1;
-  const bool hit = cnt > 0 && slot0 >= 0;
-  es[tid] = slot0;
-  cn[tid] = cnt;
-  off[tid] = tid < E ? offsets[tid] : 0;
-  nt[tid] = cnt > 0 ? (cnt + tile_n - 1) / tile_n : 0;
-  eb[tid] = hit ? 0 : -1;
-  bs[tid] = hit ? slot0 : -1;
-  bcnt[tid] = 0;
-  __syncthreads();
-  if (hit) st[slot0] = step0;  // distinct experts hold distinct slots
-  const int nhit = __syncthreads_count(hit);
-  const int nused = __syncthreads_count(cnt > 0);
-  const int nm = nused - nhit;
-  const int room0 = S - nhit;  // misses that fit batch 0
-  const int nb = (nused + S - 1) / S;
-  if (tid < 64) {
-    // the misses in ascending order
-    int base = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = 64 * q + lane;
-      const bool miss = nt[e] > 0 && eb[e] < 0;
-      const uint64_t m = __ballot(miss);
-      if (miss) ml[base + __popcll(m & ((1ull << lane) - 1ull))] = e;
-      base += __popcll(m);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    for (int m = 0; m < nm; ++m) {
-      const int e = ml[m];  // uniform
-      const int j = m < room0 ? 0 : 1 + (m - room0) / S;
-      const uint32_t step = step0 + (uint32_t)j;
-      uint64_t key = ~0ull;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = lane + 64 * i;
-        if (s < S && st[s] != step) {
-          const uint64_t k = ((uint64_t)st[s] << 32) | (uint32_t)s;
-          key = k < key ? k : key;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const uint64_t k = __shfl_xor(key, o);
-        key = k < key ? k : key;
-      }
-      if (key == ~0ull) break;  // not reached (see above); keeps LDS indexes in range
-      const int v = (int)(uint32_t)key;
-      if (lane == 0) {
-        const int old = se[v];
-        if (old >= 0) es[old] = -1;
-        se[v] = e;
-        es[e] = v;
-        st[v] = step;
-        eb[e] = j;
-        bs[e] = v;
-        c.fill_e[m] = e;
-        c.fill_s[m] = v;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
+  if (e >= 0) dt[t].e = v;
+  if (t < S) {
+    c.stamp[t] = st_f;
+    c.slot_expert[t] = se_f;
   }
-  __syncthreads();
-  // first tile of each expert: tiles of the experts before it in (batch, expert) order
-  const int e = tid;
-  if (nt[e] > 0) {
-    const int key = eb[e] * 256 + e;
-    int t0 = 0;
-    for (int i = 0; i < 256; ++i) t0 += (nt[i] > 0 && eb[i] * 256 + i < key) ? nt[i] : 0;
-    ts[e] = t0;
-    if (eb[e] >= 0) atomicAdd(&bcnt[eb[e]], nt[e]);
-  }
-  __syncthreads();
-  if (tid < E) {
-    const int j = tid;
-    int first = 0;
-    for (int i = 0; i < j; ++i) first += bcnt[i];
-    c.brange[2 * j] = bcnt[j];
-    c.brange[2 * j + 1] = first;
-    const int f0 = j == 0 ? 0 : min(nm, room0 + (j - 1) * S), f1 = min(nm, room0 + j * S);
-    c.frange[2 * j] = j < nb ? f0 : nm;
-    c.frange[2 * j + 1] = j < nb ? f1 : nm;
-  }
-  for (int x = 0; x < E; ++x) {  // uniform
-    const int n = nt[x];
-    const int slot = bs[x] >= 0 ? bs[x] : 0;
-    for (int i = tid; i < n; i += 256) {
-      TileT tl;
-      tl.e = slot;
-      tl.p0 = off[x] + i * tile_n;
-      tl.n = min(tile_n, cn[x] - i * tile_n);
-      tl.pad = 0;
-      tiles[ts[x] + i] = tl;
-    }
-  }
-  if (tid < S) {
-    c.stamp[tid] = st[tid];
-    c.slot_expert[tid] = se[tid];
-  }
-  if (tid < E) c.expert_slot[tid] = es[tid];
-  if (tid == 0) {
+  if (t < E) c.expert_slot[t] = es[t];
+  if (t == 0) {
     CacheHdr *h = c.hdr;
-    h->step = step0 + (uint32_t)(nb > 0 ? nb - 1 : 0);
+    c.frange[0] = 0;
+    c.frange[1] = nm;
+    h->step = step;
     h->fill_n = (uint32_t)nm;
     h->calls += 1ull;
     h->hits += (unsigned long long)nhit;
     h->misses += (unsigned long long)nm;
+  }
+}
+
+// Prefill.  Input: the routing's per-expert counts and offsets.  Outputs:
+// the fill list in batch order with each batch's range of it, each batch's
+// tile count and first tile, and the tile list rewritten in batch order
+// (experts ascending inside a batch, the tiles of an expert as the routing
+// cut them) with each expert's slot in place of the expert.  An expert may
+// lose its slot to a later batch of the same call: the kernels of its own
+// batch have run by then (stream order).  Global stores come after the
+// last barrier.
+__global__ __launch_bounds__(256) void k_cache_plan_prefill(CacheState c, const int32_t *__restrict__ counts,
+                                                            const int32_t *__restrict__ offsets,
+                                                            TileT *__restrict__ tiles, int tile_n, int S, int E) {
+  __shared__ uint32_t st[256];
+  __shared__ int32_t q0[256], ml[256], es[256], bpre[257], ord[256], tst[256];
+  __shared__ int32_t x_slot[256], x_off[256], x_cnt[256];  // per expert: slot, first position, count
+  __shared__ int scan_lds[3][4];
+  const int t = threadIdx.x;
+  const uint32_t step0 = c.hdr->step + 1u;
+  const int cnt = t < E ? counts[t] : 0;
+  const int slot0 = t < E ? c.expert_slot[t] : -1;
+  const bool hit = cnt > 0 && slot0 >= 0, miss = cnt > 0 && slot0 < 0;
+  const int ntl = cnt > 0 ? (cnt + tile_n - 1) / tile_n : 0;
+  const int se_in = t < S ? c.slot_expert[t] : -1;
+  st[t] = t < S ? c.stamp[t] : 0u;
+  es[t] = -1;
+  x_off[t] = t < E ? offsets[t] : 0;
+  x_cnt[t] = cnt;
+  __syncthreads();
+  if (hit) st[slot0] = step0;
+  int sv[2] = {miss ? 1 : 0, hit ? 1 : 0}, tot[2];
+  block_scan<2>(sv, tot, scan_lds);
+  const int m = sv[0], nm = tot[0], nhit = tot[1];
+  const int room0 = S - nhit;                  // misses batch 0 takes at most
+  const int nB = nm > room0 ? nm - room0 : 0;  // misses of the later batches
+  const int nb = (nhit + nm + S - 1) / S;      // batches (>= 1: every call uses an expert)
+  const bool inA = hit || (miss && m < room0), inB = miss && m >= room0;
+  const int r0 = nm > 0 ? rank_free_slot(st, S, step0, q0) : -1;
+  if (miss) ml[m] = t;
+  // tile order: batch 0's experts ascending, then the later batches' (their misses ascending)
+  int pv[3] = {inA ? 1 : 0, inA ? ntl : 0, inB ? ntl : 0}, ptot[3];
+  block_scan<3>(pv, ptot, scan_lds);  // its barriers also publish q0 and ml
+  const int nA = ptot[0], tA = ptot[1], tB = ptot[2];
+  const int v = miss ? (m < room0 ? q0[m] : (m - room0) % S) : slot0;
+  x_slot[t] = cnt > 0 ? v : 0;
+  if (cnt > 0) {
+    const int r = inA ? pv[0] : nA + (m - room0);
+    ord[r] = t;
+    tst[r] = inA ? pv[1] : tA + pv[2];
+  }
+  if (inB) bpre[m - room0] = pv[2];
+  if (t == 0) bpre[nB] = tB;
+  // final slot contents: the last miss that took slot t, if any
+  int se_f = se_in;
+  uint32_t st_f = t < S ? st[t] : 0u;
+  if (t < S) {
+    int mf = -1;
+    if (nb == 1) {
+      if (r0 >= 0 && r0 < nm) {
+        mf = r0;
+        st_f = step0;
+      }
+    } else {
+      const int szl = nB - (nb - 2) * S;  // misses of the last batch (1..S)
+      if (t < szl) {
+        mf = room0 + (nb - 2) * S + t;
+        st_f = step0 + (uint32_t)(nb - 1);
+      } else if (nb >= 3) {
+        mf = room0 + (nb - 3) * S + t;
+        st_f = step0 + (uint32_t)(nb - 2);
+      } else {  // batch 0 took every free slot; hit slots keep their expert
+        mf = r0;
+        st_f = step0;
+      }
+    }
+    if (mf >= 0) se_f = ml[mf];
+    if (se_f >= 0) es[se_f] = t;
+  }
+  __syncthreads();
+  if (miss) {
+    c.fill_e[m] = t;
+    c.fill_s[m] = v;
+  }
+  if (t < E) {  // batch t
+    int cj = 0, first = 0, f0 = nm, f1 = nm;
+    if (t == 0) {
+      cj = tA;
+      f0 = 0;
+      f1 = nm < room0 ? nm : room0;
+    } else if (t < nb) {
+      const int b0 = (t - 1) * S, b1 = t * S < nB ? t * S : nB;
+      first = tA + bpre[b0];
+      cj = bpre[b1] - bpre[b0];
+      f0 = room0 + b0;
+      f1 = room0 + b1;
+    }
+    c.brange[2 * t] = cj;
+    c.brange[2 * t + 1] = first;
+    c.frange[2 * t] = f0;
+    c.frange[2 * t + 1] = f1;
+    c.expert_slot[t] = es[t];
+  }
+  if (t < S) {
+    c.stamp[t] = st_f;
+    c.slot_expert[t] = se_f;
+  }
+  if (t == 0) {
+    CacheHdr *h = c.hdr;
+    h->step = step0 + (uint32_t)(nb - 1);
+    h->fill_n = (uint32_t)nm;
+    h->calls += 1ull;
+    h->hits += (unsigned long long)nhit;
+    h->misses += (unsigned long long)nm;
+  }
+  // the tiles: tile i belongs to the last expert (in tile order) starting at or before it
+  const int U = nhit + nm, ntot = tA + tB;
+  for (int i = t; i < ntot; i += 256) {
+    int lo = 0, hi = U - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tst[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int x = ord[lo], li = i - tst[lo];
+    TileT tl;
+    tl.e = x_slot[x];
+    tl.p0 = x_off[x] + li * tile_n;
+    tl.n = min(tile_n, x_cnt[x] - li * tile_n);
+    tl.pad = 0;
+    tiles[i] = tl;
   }
 }
 
