@@ -244,7 +244,7 @@ int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, con
                            ds4moe_routing *route_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Kernel slots timed by ds4moe_forward_timed. */
-#define DS4MOE_N_TIMED_KERNELS 10
+#define DS4MOE_N_TIMED_KERNELS 11
 
 /* For measurement: the same work as ds4moe_forward_decode (mode
  * DS4MOE_MODE_DECODE) or ds4moe_forward_prefill (DS4MOE_MODE_PREFILL); each
@@ -254,8 +254,9 @@ int ds4moe_forward_prefill(const ds4moe_dims *dims, const ds4moe_weights *w, con
  * created by the caller; pair i = (events[2i], events[2i+1]) times slot i:
  * 0 router logits, 1 top-k (decode: top-k + permutation), 2 permutation
  * (prefill), 3 gate/up + SwiGLU, 4 down, 5 shared gate/up, 6 shared down,
- * 7 combine, 8 expert-cache plan, 9 expert-cache fill (the last two only in
- * ds4moe_forward_decode_cached).  The events of a slot with no kernel in the
+ * 7 combine, 8 expert-cache plan, 9 expert-cache fill (those two only in
+ * ds4moe_forward_decode_cached), 10 fp16 copy of the shared expert's bf16
+ * weights (prefill with more than 64 tokens).  The events of a slot with no kernel in the
  * call are not recorded (they keep their last stamps), so a caller that
  * records its own event on the stream before the call tells those slots
  * apart: their start precedes it.  Any other mode returns DS4MOE_ERR_SHAPE; a

@@ -36,9 +36,9 @@ EXPORTED = ("ds4moe_packed_bytes", "ds4moe_packed_bytes_bits", "ds4moe_pack_q2k"
             "ds4moe_forward_decode_cached", "ds4moe_forward_prefill_cached", "ds4moe_cache_stats",
             "ds4moe_forward_decode_noalloc",
             "ds4moe_read_probe")
-N_TIMED_KERNELS = 10
+N_TIMED_KERNELS = 11
 KERNEL_SLOTS = ("router", "route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine",
-                "cache_plan", "cache_fill")
+                "cache_plan", "cache_fill", "shared_convert")
 
 
 class Dims(ctypes.Structure):

@@ -42,7 +42,7 @@ inline int down_bits(const ds4moe_dims &d) { return d.down_bits ? d.down_bits : 
 
 struct Layout {
   size_t logits, part, idx, w, counts, offsets, perm, pos, pexp, tiles, ntiles, ccnt, cbase, lrank, dpart;
-  size_t x16, xs_hi, xs_lo, xexp, xe16, h, hs_hi, hs_lo, yp, hsh, ysh, zeros;
+  size_t x16, xs_hi, xs_lo, xexp, xe16, h, hs_hi, hs_lo, yp, hsh, ysh, shw, zeros;
   int nzeros;
   size_t total;
   int tile_n, max_tiles, Ipad;
@@ -116,6 +116,8 @@ Layout make_layout(const ds4moe_dims &d, int64_t T, int mode) {
     if (Is > 0) {
       L.hsh = take(2 * T * Is);
       L.ysh = take(sizeof(float) * T * H);
+      // fp16 copies of the shared expert's weights for the dense GEMMs
+      if (mode == DS4MOE_MODE_PREFILL && T >= SHARED_DENSE_MIN_T) L.shw = take(2 * 3 * H * Is);
     }
   }
   L.total = off;
@@ -253,7 +255,7 @@ Ptrs routing_ptrs(void *ws, const Layout &L, const ds4moe_routing *r) {
 // kernel slots of ds4moe_forward_timed
 enum {
   SL_ROUTER = 0, SL_ROUTE, SL_PERMUTE, SL_GATEUP, SL_DOWN, SL_SHGATEUP, SL_SHDOWN, SL_COMBINE, SL_CPLAN, SL_CFILL,
-  SL_N
+  SL_SHCONV, SL_N
 };
 static_assert(SL_N == DS4MOE_N_TIMED_KERNELS, "timed kernel slots");
 
@@ -359,10 +361,15 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
     if (d.shared_inter <= 0) return DS4MOE_OK;
     _Float16 *hsh = at<_Float16>(ws, L.hsh);
     ysh = at<float>(ws, L.ysh);
-    TRY(launch_shared_gateup((const uint16_t *)w->sh_gate, (const uint16_t *)w->sh_up, xp.x16, xp.xexp, hsh, T,
-                             d.hidden, d.shared_inter, s, tm(SL_SHGATEUP)));
-    TRY(launch_shared_down((const uint16_t *)w->sh_down, hsh, xp.xexp, ysh, T, d.hidden, d.shared_inter, s,
-                           tm(SL_SHDOWN)));
+    const uint16_t *sg = (const uint16_t *)w->sh_gate, *su = (const uint16_t *)w->sh_up,
+                   *sd = (const uint16_t *)w->sh_down;
+    _Float16 *w16 = nullptr;
+    if (!dec && T >= SHARED_DENSE_MIN_T) {
+      w16 = at<_Float16>(ws, L.shw);
+      TRY(launch_shared_convert(sg, su, sd, w16, d.hidden, d.shared_inter, s, tm(SL_SHCONV)));
+    }
+    TRY(launch_shared_gateup(sg, su, w16, xp.x16, xp.xexp, hsh, T, d.hidden, d.shared_inter, s, tm(SL_SHGATEUP)));
+    TRY(launch_shared_down(sd, w16, hsh, xp.xexp, ysh, T, d.hidden, d.shared_inter, s, tm(SL_SHDOWN)));
     return DS4MOE_OK;
   };
   if (dec) {

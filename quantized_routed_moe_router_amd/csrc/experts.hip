@@ -1653,65 +1653,86 @@ __global__ __launch_bounds__(256) void k_shared_down(const uint16_t *__restrict_
 }
 
 // ------------------------------------------------------------------ shared expert, larger batches
-// Dense C[rows, tokens] = W[rows, K] (bf16) x X[tokens, K]^T (fp16), fp32
-// accumulation.  Workgroup = 4 waves, tile of 256 weight rows x 128 tokens;
-// per K-chunk of 32 the weight rows (converted to fp16 once, while staging)
-// and the token rows go to LDS through registers that are loaded one chunk
-// ahead, double-buffered, one barrier per chunk.  Wave (wr, wc) holds 8
-// row n-tiles x 4 token n-tiles of 16x16 accumulators, so every LDS fragment
-// feeds 4 or 8 MFMAs.  GU: the tile's rows are 128 gate rows and the same
-// 128 up rows, a wave takes 64 of each, and the epilogue writes
-// h = silu(gate)*up (fp16); otherwise the rows are 256 down rows, 128 per
-// wave, and the epilogue writes fp32.  Rows past `rows` and tokens past T
-// are zero-filled and not written.
-constexpr int DG_KC = 32;            // K per chunk
-constexpr int DG_LD = 40;            // halves per LDS row (32 + pad: 5 chunks of 16 bytes)
+// The shared expert's bf16 weights are first copied to fp16 (exact inside the
+// binary16 range, the same conversion as the small-batch kernels), so the
+// GEMM below has two fp16 operands and no conversion in its loop.
+__global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t *__restrict__ wg, const uint16_t *__restrict__ wu,
+                                                     const uint16_t *__restrict__ wd, half_t *__restrict__ dst,
+                                                     uint64_t n8) {  // 16-byte groups per matrix
+  const uint64_t stride = (uint64_t)gridDim.x * 256;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < 3 * n8; i += stride) {
+    const uint16_t *src = i < n8 ? wg + 8 * i : i < 2 * n8 ? wu + 8 * (i - n8) : wd + 8 * (i - 2 * n8);
+    *reinterpret_cast<h8 *>(dst + 8 * i) = bf16x8_to_h8(*reinterpret_cast<const u4 *>(src));
+  }
+}
+
+// Dense C[rows, tokens] = W[rows, K] x X[tokens, K]^T, both fp16, fp32
+// accumulation.  Workgroup = 4 waves, tile of 256 weight rows x 128 tokens.
+// Per K-chunk of 32 both operands go from global memory straight into a
+// 3-stage LDS ring (direct loads, two chunks ahead; no registers held, no
+// stores); a row is 64 bytes and its 16-byte chunk c sits at position
+// c ^ ((r >> 1) & 3), which spreads a fragment read over the banks.  One
+// barrier per chunk.  Wave (wr, wc) holds 8 row n-tiles x 4 token n-tiles of
+// 16x16 accumulators, so every LDS fragment feeds 4 or 8 MFMAs.  GU: the
+// tile's rows are 128 gate rows and the same 128 up rows, a wave takes 64 of
+// each, and the epilogue writes h = silu(gate)*up (fp16); otherwise the rows
+// are 256 down rows, 128 per wave, and the epilogue writes fp32.  Rows past
+// `rows` and tokens past T load as zeros and are not written.
+constexpr int DG_KC = 32;  // K per chunk
 constexpr int DG_ROWS = 256, DG_TOK = 128;
+constexpr int DG_STAGES = 3;
+constexpr int DG_A_BYTES = DG_ROWS * 2 * DG_KC, DG_X_BYTES = DG_TOK * 2 * DG_KC;
+constexpr int DG_STAGE_BYTES = DG_A_BYTES + DG_X_BYTES;
+
+__device__ __forceinline__ int dg_swz(int r) { return (r >> 1) & 3; }
 
 template <bool GU>
-__global__ __launch_bounds__(256) void k_dense_gemm(const uint16_t *__restrict__ wa, const uint16_t *__restrict__ wb,
+__global__ __launch_bounds__(256) void k_dense_gemm(const half_t *__restrict__ wa, const half_t *__restrict__ wb,
                                                     const half_t *__restrict__ x, const int32_t *__restrict__ xexp,
                                                     void *__restrict__ out, int T, int K, int rows) {
-  __shared__ __attribute__((aligned(16))) half_t sA[2][DG_ROWS * DG_LD];
-  __shared__ __attribute__((aligned(16))) half_t sX[2][DG_TOK * DG_LD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) char ring[DG_STAGES * DG_STAGE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int wr = wave >> 1, wc = wave & 1;
   const int row0 = blockIdx.x * (GU ? DG_ROWS / 2 : DG_ROWS);
   const int t0 = blockIdx.y * DG_TOK;
 
-  // staging: thread tid loads 64 bytes (32 k) of LDS row tid of A and 32
-  // bytes of token row tid/2 of X
-  const int arow = tid;
-  const int wrow = GU ? row0 + (arow & 127) : row0 + arow;
-  const bool aval = wrow < rows;
-  const uint16_t *asrc = (GU && arow >= 128 ? wb : wa) + (size_t)(aval ? wrow : 0) * K;
-  const int xt = tid >> 1, xh = tid & 1;
-  const bool xval = t0 + xt < T;
-  const half_t *xsrc = x + (size_t)(xval ? t0 + xt : 0) * K + 16 * xh;
-  u4 ra[4], rx[2];
-  auto load = [&](int k0) {
+  // buffer windows over this tile's weight rows and token rows (loads past them read zeros)
+  const uint32_t kb = 2u * (uint32_t)K;
+  const int na = min(GU ? DG_ROWS / 2 : DG_ROWS, rows - row0);
+  const int nx = min(DG_TOK, T - t0);
+  // the wave's 4 weight loads per chunk (LDS rows 64*wave .. +63): GU waves 0-1 gate, 2-3 up
+  const half_t *wsrc = (GU && wave >= 2) ? wb : wa;
+  const int wrow0 = GU ? 64 * (wave & 1) : 64 * wave;  // first row of the matrix the wave loads
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wsrc + (size_t)row0 * K, (uint32_t)na * kb);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)t0 * K, (uint32_t)max(nx, 0) * kb);
+  uint32_t oa[4], ox[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = aval ? *reinterpret_cast<const u4 *>(asrc + k0 + 8 * i) : (u4){0u, 0u, 0u, 0u};
+  for (int i = 0; i < 4; ++i) {
+    const int lr = 16 * i + (lane >> 2);  // row within the wave's 64
+    oa[i] = (uint32_t)(wrow0 + lr) * kb + 16u * (uint32_t)((lane & 3) ^ dg_swz(lr));
+  }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      rx[i] = xval ? *reinterpret_cast<const u4 *>(xsrc + k0 + 8 * i) : (u4){0u, 0u, 0u, 0u};
-  };
-  auto store = [&](int b) {
-    half_t *da = sA[b] + arow * DG_LD;
+  for (int i = 0; i < 2; ++i) {
+    const int lr = 16 * (2 * wave + i) + (lane >> 2);
+    ox[i] = (uint32_t)lr * kb + 16u * (uint32_t)((lane & 3) ^ dg_swz(lr));
+  }
+  auto issue = [&](int st, int c) {
+    char *sa = ring + st * DG_STAGE_BYTES + wave * 4096;
+    char *sx = ring + st * DG_STAGE_BYTES + DG_A_BYTES + wave * 2048;
+    const uint32_t k0 = (uint32_t)c * 2u * DG_KC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<h8 *>(da + 8 * i) = bf16x8_to_h8(ra[i]);
-    half_t *dx = sX[b] + xt * DG_LD + 16 * xh;
+    for (int i = 0; i < 4; ++i) buf_load_lds16(rw, sa + 1024 * i, oa[i] + k0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u4 *>(dx + 8 * i) = rx[i];
+    for (int i = 0; i < 2; ++i) buf_load_lds16(rx, sx + 1024 * i, ox[i] + k0);
   };
 
-  // this wave's A fragments: LDS rows of row n-tile i
+  // this wave's A fragments: LDS rows of row n-tile i (gate rows 0-127, up rows 128-255)
   int arow_base[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     arow_base[i] = GU ? (i < 4 ? 64 * wr + 16 * i : 128 + 64 * wr + 16 * (i - 4)) : 128 * wr + 16 * i;
+  const int fo = 16 * (g ^ dg_swz(r16));  // the lane's chunk in its fragment row
 
   f4 acc[8][4];
 #pragma unroll
@@ -1720,24 +1741,24 @@ __global__ __launch_bounds__(256) void k_dense_gemm(const uint16_t *__restrict__
     for (int j = 0; j < 4; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / DG_KC;
-  load(0);
-  store(0);
-  __syncthreads();
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
   for (int c = 0; c < nk; ++c) {
-    const int b = c & 1;
-    if (c + 1 < nk) load((c + 1) * DG_KC);
+    if (c + 1 < nk) wait_vm<6>();  // this wave's loads of chunk c have landed
+    else wait_vm<0>();
+    __syncthreads();  // ... every wave's; and every wave is done with chunk c-1's stage
+    if (c + 2 < nk) issue((c + 2) % DG_STAGES, c + 2);
+    const char *sa = ring + (c % DG_STAGES) * DG_STAGE_BYTES;
+    const char *sx = sa + DG_A_BYTES;
     h8 bx[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bx[j] = *reinterpret_cast<const h8 *>(sX[b] + (64 * wc + 16 * j + r16) * DG_LD + 8 * g);
+    for (int j = 0; j < 4; ++j) bx[j] = *reinterpret_cast<const h8 *>(sx + (64 * wc + 16 * j + r16) * 64 + fo);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const h8 av = *reinterpret_cast<const h8 *>(sA[b] + (arow_base[i] + r16) * DG_LD + 8 * g);
+      const h8 av = *reinterpret_cast<const h8 *>(sa + (arow_base[i] + r16) * 64 + fo);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(av, bx[j], acc[i][j]);
     }
-    if (c + 1 < nk) store(b ^ 1);
-    __syncthreads();
   }
 
   // epilogue: accumulator (i, j) lane (r16, g) = row n-tile i rows 4g..4g+3, token 16j + r16
@@ -1953,12 +1974,22 @@ hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, c
   return hipGetLastError();
 }
 
-hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, const int32_t *xexp,
-                                _Float16 *hs, int T, int H, int Is, hipStream_t s, const Timing *tm) {
+hipError_t launch_shared_convert(const uint16_t *wg, const uint16_t *wu, const uint16_t *wd, _Float16 *dst, int H,
+                                 int Is, hipStream_t s, const Timing *tm) {
+  const uint64_t n8 = (uint64_t)H * Is / 8;
+  const uint64_t groups = (3 * n8 + 255) / 256;
+  DS4_LAUNCH(tm, k_bf16_to_f16, dim3((unsigned)(groups < 8192 ? groups : 8192)), dim3(256), 0, s, wg, wu, wd, dst, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *w16, const _Float16 *x16,
+                                const int32_t *xexp, _Float16 *hs, int T, int H, int Is, hipStream_t s,
+                                const Timing *tm) {
   if (T <= 0) return hipSuccess;
-  if (T > 64) {
+  if (T >= SHARED_DENSE_MIN_T) {  // fp16 copies: gate at w16, up after it
+    if (!w16) return hipErrorInvalidValue;
     const dim3 grid((Is + DG_ROWS / 2 - 1) / (DG_ROWS / 2), (T + DG_TOK - 1) / DG_TOK);
-    DS4_LAUNCH(tm, (k_dense_gemm<true>), grid, dim3(256), 0, s, wg, wu, x16, xexp, hs, T, H, Is);
+    DS4_LAUNCH(tm, (k_dense_gemm<true>), grid, dim3(256), 0, s, w16, w16 + (size_t)Is * H, x16, xexp, hs, T, H, Is);
     return hipGetLastError();
   }
   constexpr int R = 1, NT = 4;
@@ -1967,12 +1998,14 @@ hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _F
   return hipGetLastError();
 }
 
-hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, const int32_t *xexp, float *ysh, int T, int H,
-                              int Is, hipStream_t s, const Timing *tm) {
+hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *w16, const _Float16 *hs, const int32_t *xexp,
+                              float *ysh, int T, int H, int Is, hipStream_t s, const Timing *tm) {
   if (T <= 0) return hipSuccess;
-  if (T > 64) {
+  if (T >= SHARED_DENSE_MIN_T) {  // fp16 copies: down after gate and up
+    if (!w16) return hipErrorInvalidValue;
     const dim3 grid((H + DG_ROWS - 1) / DG_ROWS, (T + DG_TOK - 1) / DG_TOK);
-    DS4_LAUNCH(tm, (k_dense_gemm<false>), grid, dim3(256), 0, s, wd, nullptr, hs, xexp, ysh, T, Is, H);
+    DS4_LAUNCH(tm, (k_dense_gemm<false>), grid, dim3(256), 0, s, w16 + 2 * (size_t)Is * H, nullptr, hs, xexp, ysh,
+               T, Is, H);
     return hipGetLastError();
   }
   constexpr int R = 1, NT = 4;

@@ -188,11 +188,17 @@ hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timin
                                    const Timing *tm_combine = nullptr);
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const int32_t *xexp, const float *ysh,
                           float *y, int T, int k, int H, hipStream_t s, const Timing *tm = nullptr);
-// dense shared expert, bf16 weights
-hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *x16, const int32_t *xexp,
-                                _Float16 *hs, int T, int H, int Is, hipStream_t s, const Timing *tm = nullptr);
-hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *hs, const int32_t *xexp, float *ysh, int T, int H,
-                              int Is, hipStream_t s, const Timing *tm = nullptr);
+// dense shared expert, bf16 weights.  From SHARED_DENSE_MIN_T tokens on the
+// GEMMs read fp16 copies of the weights (w16: gate | up | down, 3*H*Is
+// halves, written by launch_shared_convert in the same call)
+constexpr int SHARED_DENSE_MIN_T = 65;
+hipError_t launch_shared_convert(const uint16_t *wg, const uint16_t *wu, const uint16_t *wd, _Float16 *dst, int H,
+                                 int Is, hipStream_t s, const Timing *tm = nullptr);
+hipError_t launch_shared_gateup(const uint16_t *wg, const uint16_t *wu, const _Float16 *w16, const _Float16 *x16,
+                                const int32_t *xexp, _Float16 *hs, int T, int H, int Is, hipStream_t s,
+                                const Timing *tm = nullptr);
+hipError_t launch_shared_down(const uint16_t *wd, const _Float16 *w16, const _Float16 *hs, const int32_t *xexp,
+                              float *ysh, int T, int H, int Is, hipStream_t s, const Timing *tm = nullptr);
 
 // Launch `kernel` plainly, or with dispatch-stamped timing events.
 #define DS4_LAUNCH(tm, kernel, grid, block, shmem, stream, ...)                                                  \

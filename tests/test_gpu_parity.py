@@ -469,6 +469,8 @@ def test_forward_timed_same_result_and_slots(mode, T, Is):
     assert not {"cache_plan", "cache_fill"} & launched
     assert ({"shared_gateup", "shared_down"} <= launched) == bool(Is)
     assert not ({"shared_gateup", "shared_down"} & launched) or Is
+    # the fp16 copy of the shared weights feeds the dense GEMMs (prefill past 64 tokens)
+    assert ("shared_convert" in launched) == (mode == "prefill" and bool(Is) and T > 64)
     if mode == "prefill":
         assert {"route", "permute", "combine"} <= launched
     for j, s in enumerate(B.KERNEL_SLOTS):
