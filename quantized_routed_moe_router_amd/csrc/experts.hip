@@ -270,12 +270,29 @@ __device__ __forceinline__ void gemm_compute_sb(const UnitRegs<B> (&u)[R][NM], c
       }
 }
 
+// XCD-aware order of a grouped GEMM's (tile, row block) workgroups.  The
+// hardware hands workgroups to the chip's 8 XCDs in turn (workgroup b to XCD
+// b % 8), so workgroup b takes tile 8 * (slot / nrb) + b % 8 and row block
+// slot % nrb, slot = b / 8: every row block of a tile runs on one XCD and
+// reads the tile's activations through that XCD's L2 (one HBM read per tile
+// instead of one per XCD).  The grid is a whole number of 8 * nrb workgroups
+// (gemm_grid); tiles past the list exit at once.
+constexpr int N_XCD = 8;
+__device__ __forceinline__ void xcd_tile(int nrb, int &tile, int &rb) {
+  const int b = blockIdx.x, slot = b / N_XCD, grp = slot / nrb;
+  tile = N_XCD * grp + b % N_XCD;
+  rb = slot - grp * nrb;
+}
+static dim3 gemm_grid(int nrb, int max_tiles) {
+  return dim3((unsigned)((int64_t)nrb * ((max_tiles + N_XCD - 1) / N_XCD) * N_XCD));
+}
+
 template <int NM, int R, int NW, bool PADDED, int B>
 __global__ __launch_bounds__(64 * NW) void k_moe_gemm(GemmArgs a, int nrb) {
   __shared__ __attribute__((aligned(16))) half_t sB[64 * SB_STRIDE];
   __shared__ __attribute__((aligned(16))) half_t sS[64 * SS_STRIDE];
-  const int tile_id = blockIdx.x / nrb;
-  const int rb = blockIdx.x - tile_id * nrb;
+  int tile_id, rb;
+  xcd_tile(nrb, tile_id, rb);
   if (tile_id >= a.ntiles[0]) return;  // uniform over the workgroup
   const TileT tl = a.tiles[a.ntiles[1] + tile_id];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -690,8 +707,8 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
 template <int NM, int R, bool ALL, int B>
 __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAct xa, int nrb) {
   __shared__ __attribute__((aligned(16))) char ring[2 * PT_SLOT_BYTES];
-  const int tile_id = blockIdx.x / nrb;
-  const int rb = blockIdx.x - tile_id * nrb;
+  int tile_id, rb;
+  xcd_tile(nrb, tile_id, rb);
   if (tile_id >= a.ntiles[0]) return;  // uniform over the workgroup
   const TileT tl = a.tiles[a.ntiles[1] + tile_id];
   if (ALL) {
@@ -1826,14 +1843,14 @@ static hipError_t gateup_b(const GemmArgs &a, int max_tiles, hipStream_t s, cons
     GemmAct xa;
     if (a.tile_n > 16 * PT_NTM || !act_window(a.x16, a.xs_hi, a.xs_lo, a.xe16, a.T, a.H, xa)) return hipErrorInvalidValue;
     const int nrb = (a.I + 16 * PT_NW - 1) / (16 * PT_NW);
-    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1, false, B>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW),
-               0, s, a, xa, nrb);
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1, false, B>), gemm_grid(nrb, max_tiles), dim3(64 * PT_NW), 0, s, a, xa,
+               nrb);
     return hipGetLastError();
   }
   constexpr int R = GEMM_R_GU, NW = GEMM_NW_GU;
   const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.I + rows_per_wg - 1) / rows_per_wg;
-  const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
+  const dim3 grid = gemm_grid(nrb, max_tiles);
   DS4_LAUNCH(tm, (k_moe_gemm<2, R, NW, false, B>), grid, dim3(64 * NW), 0, s, a, nrb);
   return hipGetLastError();
 }
@@ -1851,14 +1868,14 @@ static hipError_t down_b(const GemmArgs &a, int max_tiles, hipStream_t s, const 
         !act_window(a.h, a.hs_hi, a.hs_lo, nullptr, (int64_t)a.T * a.k, a.Ipad, xa))
       return hipErrorInvalidValue;
     const int nrb = (a.H + 32 * PT_NW - 1) / (32 * PT_NW);
-    DS4_LAUNCH(tm, (k_moe_gemm_wide<1, 2, true, B>), dim3((unsigned)((int64_t)nrb * max_tiles)), dim3(64 * PT_NW),
-               0, s, a, xa, nrb);
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<1, 2, true, B>), gemm_grid(nrb, max_tiles), dim3(64 * PT_NW), 0, s, a, xa,
+               nrb);
     return hipGetLastError();
   }
   constexpr int R = GEMM_R_DN, NW = GEMM_NW_DN;
   const int rows_per_wg = 16 * R * NW;
   const int nrb = (a.H + rows_per_wg - 1) / rows_per_wg;
-  const dim3 grid((unsigned)((int64_t)nrb * max_tiles));
+  const dim3 grid = gemm_grid(nrb, max_tiles);
   if (a.I == a.Ipad)
     DS4_LAUNCH(tm, (k_moe_gemm<1, R, NW, false, B>), grid, dim3(64 * NW), 0, s, a, nrb);
   else
