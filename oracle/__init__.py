@@ -76,8 +76,8 @@ def _p(a):
 
 
 def block_bytes(bits: int = 2) -> int:
-    """Bytes of one block of 256 weights with 2- or 4-bit codes."""
-    assert bits in (2, 4)
+    """Bytes of one block of 256 weights with 2-, 4-, 5- or 6-bit codes."""
+    assert bits in (2, 4, 5, 6)
     return 16 + 32 * bits + 4
 
 

@@ -32,6 +32,11 @@
  *     page keeps some layers at 4 bits; no page gives a 4-bit block): the same
  *     block with 4-bit codes, weight i -> byte 16+i/2, bits 4*(i%2), d @144,
  *     dmin @146 (148 bytes), w = d*scale*q - dmin*min with q in 0..15;
+ *   - 5- and 6-bit variants (the [models] page's GLM notes name 5-bit gate/up
+ *     and down up to 6 bits; no page gives their blocks): the same block with
+ *     5- or 6-bit codes as one bit stream from byte 16, lowest bits first
+ *     (weight i at bits b*i .. b*i+b-1, which is the 2- and 4-bit order
+ *     above), d @16+32b, dmin @18+32b (180 and 212 bytes), q in 0..2^b-1;
  *   - the down matrices may use a code width of their own (the [models] page
  *     gives routed gate/up and routed down different block types);
  *   - blocks tile the row-major flattened tensor (a block may span rows);
@@ -60,19 +65,22 @@ static double half_to_double(uint16_t h) {
   return sign ? -v : v;
 }
 
-/* Bytes of one block of 256 weights with `bits`-bit codes (2 or 4). */
+/* Bytes of one block of 256 weights with `bits`-bit codes (2, 4, 5 or 6). */
 static int64_t block_bytes(int bits) { return 16 + 32 * bits + 4; }
 
 /* Value of weight i (0..255) of one canonical block with `bits`-bit codes,
  * given the block's d and dmin; exact in double: every product has at most
- * 19 significant bits and the difference of two such numbers of the binary16
+ * 21 significant bits and the difference of two such numbers of the binary16
  * range fits in 53 bits.  [workload] */
 static double block_weight_dm(const uint8_t *blk, int i, int bits, double d, double dmin) {
-  const int per_byte = 8 / bits;
   int j = i / 16;                                  /* sub-block */
   int sc = blk[j] & 0x0F;                          /* low nibble: scale */
   int mn = blk[j] >> 4;                            /* high nibble: min  */
-  int q = (blk[16 + i / per_byte] >> (bits * (i % per_byte))) & ((1 << bits) - 1);
+  /* code i: bits bits*i .. bits*i+bits-1 of the stream from byte 16 (the
+   * byte after the last code byte is d's, inside the block) */
+  const int bit = bits * i;
+  const unsigned two = blk[16 + (bit >> 3)] | ((unsigned)blk[16 + (bit >> 3) + 1] << 8);
+  int q = (int)((two >> (bit & 7)) & ((1u << bits) - 1u));
   return d * sc * q - dmin * mn;
 }
 

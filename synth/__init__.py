@@ -111,7 +111,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 def block_bytes(bits: int = 2) -> int:
     """Bytes of one canonical block of 256 weights with 2- or 4-bit codes."""
-    assert bits in (2, 4)
+    assert bits in (2, 4, 5, 6)
     return 16 + 32 * bits + 4
 
 
@@ -173,7 +173,7 @@ class Workload:
     zipf_scale: float = 0.75
     layer_id: int = 1              # weight streams: workloads of one shape share a layer
     description: str = ""
-    bits: int = 2                  # routed-expert code width: 2 (84-byte blocks) or 4 (148-byte blocks)
+    bits: int = 2                  # routed-expert code width: 2, 4, 5 or 6 (84-, 148-, 180-, 212-byte blocks)
     bits_down: int = 0             # code width of the down matrices (0: the same as `bits`)
 
     @property

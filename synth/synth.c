@@ -145,16 +145,17 @@ static float f16_to_f32(uint16_t h) {
 
 static inline int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-/* Bytes of one canonical block of 256 weights with `bits`-bit codes (2 or 4):
- * scales[16], codes (256*bits/8 bytes), d, dmin. */
+/* Bytes of one canonical block of 256 weights with `bits`-bit codes (2, 4, 5
+ * or 6): scales[16], codes (256*bits/8 bytes), d, dmin. */
 static inline int block_bytes(int bits) { return 16 + 32 * bits + 4; }
 
-/* Quantize 256 fp32 weights into one canonical block (RTN), 2- or 4-bit
+/* Quantize 256 fp32 weights into one canonical block (RTN), `bits`-bit
  * codes: per sub-block of 16 the range [min(0, min w), max w] is split into
- * 2^bits - 1 steps of d*sc, the offset is dmin*m; code i sits at byte
- * 16 + i*bits/8, lowest bits first. */
+ * 2^bits - 1 steps of d*sc, the offset is dmin*m; the codes form one bit
+ * stream from byte 16, lowest bits first (code i at bits bits*i ..
+ * bits*i + bits - 1; for 2 and 4 bits: byte 16 + i*bits/8). */
 void synth_quantize_block_bits(const float *w, uint8_t *blk, int bits) {
-  const int levels = (1 << bits) - 1, per_byte = 8 / bits, nb = block_bytes(bits);
+  const int levels = (1 << bits) - 1, nb = block_bytes(bits);
   float scf[16], mnv[16];
   float max_scf = 0.f, max_mn = 0.f;
   for (int j = 0; j < 16; ++j) {
@@ -180,8 +181,10 @@ void synth_quantize_block_bits(const float *w, uint8_t *blk, int bits) {
     float step = d * (float)sc, off = dmin * (float)m;
     for (int i = 0; i < 16; ++i) {
       int q = step > 0.f ? clampi((int)lrintf((w[16 * j + i] + off) / step), 0, levels) : 0;
-      int idx = 16 * j + i;
-      blk[16 + idx / per_byte] |= (uint8_t)(q << (bits * (idx % per_byte)));
+      const int bit = bits * (16 * j + i);
+      const unsigned v = (unsigned)q << (bit & 7);
+      blk[16 + (bit >> 3)] |= (uint8_t)(v & 0xFFu);
+      if ((bit & 7) + bits > 8) blk[16 + (bit >> 3) + 1] |= (uint8_t)(v >> 8);
     }
   }
   blk[nb - 4] = (uint8_t)(d_bits & 0xFF);
