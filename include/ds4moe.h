@@ -141,11 +141,14 @@ typedef struct {
 } ds4moe_routing;
 
 /* Bytes of one packed matrix of `rows` x `cols` weights (cols = reduction
- * length) with `bits`-bit codes (2 or 4).  Same byte count as the canonical
- * blocks (84 bytes per 256 weights, 2.625 bits per weight, with 2-bit codes;
- * 148 bytes, 4.625 bits per weight, with 4-bit codes) when cols is a multiple
- * of 256; a divisor of 256 is padded to 256.  Returns 0 for an unsupported
- * shape or width (rows, cols above 2^31 included). */
+ * length) with `bits`-bit codes (2, 4, 5 or 6).  Same byte count as the
+ * canonical blocks (84 bytes per 256 weights, 2.625 bits per weight, with
+ * 2-bit codes; 148 bytes, 4.625 bits per weight, with 4-bit codes; 212
+ * bytes, 6.625 bits per weight, with 6-bit codes) when cols is a multiple of
+ * 256; 5-bit codes are packed into the 6-bit unit (212 bytes per 256
+ * weights, against 180 canonical).  A divisor of 256 is padded to 256.
+ * Returns 0 for an unsupported shape or width (rows, cols above 2^31
+ * included). */
 size_t ds4moe_packed_bytes_bits(int64_t rows, int64_t cols, int32_t bits);
 
 /* ds4moe_packed_bytes_bits(rows, cols, 2). */
@@ -176,7 +179,7 @@ size_t ds4moe_packed_bytes(int64_t rows, int64_t cols);
  * bits = 2. */
 int ds4moe_pack_q2k(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, void *stream);
 
-/* Repack canonical super-blocks with `bits`-bit codes (2 or 4).
+/* Repack canonical super-blocks with `bits`-bit codes (2, 4, 5 or 6).
  * bits = 2: the blocks and units of ds4moe_pack_q2k.
  * bits = 4: canonical blocks of 148 bytes: scales[16] @0 as above, qs[128]
  *   @16 (weight i at byte i/2, bits 4*(i%2)), d @144, dmin @146; w =
@@ -189,9 +192,21 @@ int ds4moe_pack_q2k(void *dst, const void *canonical, int64_t n_mats, int64_t ro
  *               nibble 2e (e < 4) or 2(e-4)+1 (e >= 4)
  *   [2048,2304) scales and mins per row, as in the 2-bit unit
  *   [2304,2368) per row d | dmin<<16, as in the 2-bit unit
+ * bits = 5 or 6: canonical blocks of 180 or 212 bytes: scales[16] @0 as
+ *   above, the 256 codes as one bit stream from byte 16, lowest bits first
+ *   (weight i at bits b*i .. b*i+b-1: the order of the 2- and 4-bit blocks),
+ *   d and dmin after them; q in 0..2^b-1 (the pages' GLM notes pair 5-bit
+ *   gate/up with down up to 6 bits: molayo1419.me ds4 README translation,
+ *   "Models" section).  Units of 16 rows x 256 columns, 3392 bytes each:
+ *   [0,2048)    the low 4 bits of every code, laid out as the two planes of
+ *               the 4-bit unit
+ *   [2048,3072) the high 2 bits of every code, laid out as the plane of the
+ *               2-bit unit (the top bit is zero for 5-bit codes)
+ *   [3072,3328) scales and mins per row, as in the 2-bit unit
+ *   [3328,3392) per row d | dmin<<16, as in the 2-bit unit
  * Arguments, alignment and status codes as ds4moe_pack_q2k; also
- * DS4MOE_ERR_SHAPE for a width other than 2 or 4, or 2^39 padded weights or
- * more in all.  Exact. */
+ * DS4MOE_ERR_SHAPE for a width other than 2, 4, 5 or 6, or 2^39 padded
+ * weights or more in all.  Exact. */
 int ds4moe_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, int64_t cols, int32_t bits,
                 void *stream);
 
@@ -201,8 +216,9 @@ int ds4moe_pack(void *dst, const void *canonical, int64_t n_mats, int64_t rows, 
  * ds4moe_dequant with bits = 2. */
 int ds4moe_dequant_q2k(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, void *stream);
 
-/* ds4moe_dequant_q2k for units with `bits`-bit codes (2 or 4); products of
- * at most 19 significant bits with 4-bit codes, still one rounding. */
+/* ds4moe_dequant_q2k for units with `bits`-bit codes (2, 4, 5 or 6; 5 and 6
+ * read the same unit); products of at most 21 significant bits, still one
+ * rounding. */
 int ds4moe_dequant(float *dst, const void *packed, int64_t n_mats, int64_t rows, int64_t cols, int32_t bits,
                    void *stream);
 

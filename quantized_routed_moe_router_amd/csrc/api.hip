@@ -437,12 +437,12 @@ const char *ds4moe_status_str(int status) {
 int ds4moe_version(void) { return kVersion; }
 
 size_t ds4moe_packed_bytes_bits(int64_t rows, int64_t cols, int32_t bits) {
-  if (bits != 2 && bits != 4) return 0;
+  if (bits != 2 && bits != 4 && bits != 5 && bits != 6) return 0;
   if (rows <= 0 || cols <= 0 || rows % 16 || cols % 16) return 0;
   if (cols % 256 && 256 % cols) return 0;
   if (rows > ((int64_t)1 << 31) || cols > ((int64_t)1 << 31)) return 0;
   const int64_t nchunks = (cols + 255) / 256;
-  return (size_t)(rows / 16) * (size_t)nchunks * (bits == 4 ? 2368u : 1344u);
+  return (size_t)(rows / 16) * (size_t)nchunks * (bits == 2 ? 1344u : bits == 4 ? 2368u : 3392u);
 }
 
 size_t ds4moe_packed_bytes(int64_t rows, int64_t cols) { return ds4moe_packed_bytes_bits(rows, cols, 2); }

@@ -11,9 +11,12 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 // Packed expert layout: one unit = 16 rows x 256 reduction columns.
-// Unit of B-bit codes (B = 2 or 4): B/2 code planes of 1024 bytes (16 bytes
-// per MFMA lane each), then 16 bytes of scales and mins per row, then
+// Unit of B-bit codes (B = 2, 4 or 6): B/2 code planes of 1024 bytes (16
+// bytes per MFMA lane each), then 16 bytes of scales and mins per row, then
 // d | dmin<<16 per row.  The scale, min and d layouts do not depend on B.
+// The 6-bit unit holds the low 4 bits of each code in two planes laid out as
+// in the 4-bit unit and the high 2 bits in a third plane laid out as in the
+// 2-bit unit; 5-bit codes use it with their top bit zero.
 template <int B>
 struct Unit;
 template <>
@@ -26,6 +29,14 @@ struct Unit<4> {
   static constexpr uint32_t BYTES = 2368, SCALE_OFF = 2048, DD_OFF = 2304;
   static constexpr int LOADS = 4;
 };
+template <>
+struct Unit<6> {
+  static constexpr uint32_t BYTES = 3392, SCALE_OFF = 3072, DD_OFF = 3328;
+  static constexpr int LOADS = 5;
+};
+
+// width of the packed unit that holds `bits`-bit codes (5-bit codes: the 6-bit unit)
+__host__ __device__ constexpr int unit_bits(int bits) { return bits == 5 ? 6 : bits; }
 
 // canonical block of 256 weights with B-bit codes: scales[16], codes, d, dmin
 template <int B>

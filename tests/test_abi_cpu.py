@@ -56,7 +56,11 @@ def test_packed_bytes_bits():
     assert q.ds4moe_packed_bytes_bits(2048, 4096, 4) == 2048 * 4096 // 256 * 148 == 4849664
     assert q.ds4moe_packed_bytes_bits(256, 128, 4) == 16 * 2368
     assert q.ds4moe_packed_bytes_bits(2048, 4096, 2) == q.ds4moe_packed_bytes(2048, 4096)
-    for bits in (0, 1, 3, 8, -2):
+    # 6-bit codes: 212 bytes per 256 weights, 3392 per unit; 5-bit codes share the 6-bit unit
+    assert q.ds4moe_packed_bytes_bits(2048, 4096, 6) == 2048 * 4096 // 256 * 212
+    assert q.ds4moe_packed_bytes_bits(2048, 4096, 5) == q.ds4moe_packed_bytes_bits(2048, 4096, 6)
+    assert q.ds4moe_packed_bytes_bits(256, 128, 6) == 16 * 3392
+    for bits in (0, 1, 3, 7, 8, -2):
         assert q.ds4moe_packed_bytes_bits(16, 256, bits) == 0
     assert q.ds4moe_packed_bytes_bits(15, 256, 4) == 0
     assert q.ds4moe_packed_bytes_bits(16, 384, 4) == 0
@@ -175,7 +179,7 @@ def test_pack_dequant_argument_errors():
     assert L.ds4moe_dequant_q2k(v(16), None, 1, 16, 256, None) == B.DS4MOE_ERR_NULL
     assert L.ds4moe_dequant_q2k(v(16), v(8), 1, 16, 256, None) == B.DS4MOE_ERR_ALIGN
     assert L.ds4moe_dequant_q2k(v(16), v(16), 1, 16, 100, None) == B.DS4MOE_ERR_SHAPE
-    for bits in (2, 4):
+    for bits in (2, 4, 5, 6):
         assert L.ds4moe_pack(v(16), v(16), 1, 15, 256, bits, None) == B.DS4MOE_ERR_SHAPE
         assert L.ds4moe_pack(None, v(16), 1, 16, 256, bits, None) == B.DS4MOE_ERR_NULL
         assert L.ds4moe_pack(v(8), v(16), 1, 16, 256, bits, None) == B.DS4MOE_ERR_ALIGN
@@ -186,6 +190,7 @@ def test_pack_dequant_argument_errors():
         assert L.ds4moe_pack(v(16), v(16), 1 << 20, 4096, 4096, bits, None) == B.DS4MOE_ERR_SHAPE
         assert L.ds4moe_dequant(v(16), v(16), 1 << 20, 4096, 4096, bits, None) == B.DS4MOE_ERR_SHAPE
     assert L.ds4moe_pack(v(16), v(16), 1, 16, 256, 3, None) == B.DS4MOE_ERR_SHAPE
+    assert L.ds4moe_pack(v(16), v(16), 1, 16, 256, 7, None) == B.DS4MOE_ERR_SHAPE
     assert L.ds4moe_dequant(v(16), v(16), 1, 16, 256, 1, None) == B.DS4MOE_ERR_SHAPE
 
 
