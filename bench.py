@@ -4,14 +4,15 @@ fraction of the dominant kernel, with the CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W]
                     [--workload default|decode1|decode16|prefill|skewed|decode1_q4|prefill_q4|decode1_mix|
-                                prefill_mix|decode1_cached|prefill_cached|tiny|all]
+                                prefill_mix|decode1_q56|prefill_q56|decode1_cached|prefill_cached|tiny|all]
 
 A step is one whole layer call (router -> top-k -> permute -> gate/up+SwiGLU ->
 down -> combine [+ shared expert]) on one batch of synthetic tokens whose
 inputs are already resident in HBM.  Decode workloads rotate over several
 copies of the layer's packed experts and over fresh token batches so the
 2.1 GB of expert weights (3.7 GB with 4-bit codes: the *_q4 workloads; 2.7 GB
-with 2-bit gate/up and 4-bit down: the *_mix workloads) stream
+with 2-bit gate/up and 4-bit down: the *_mix workloads; 5.3 GB with 5-bit
+gate/up and 6-bit down, both in 6-bit units: the *_q56 workloads) stream
 from HBM rather than from the 256 MB Infinity Cache.
 
 The default prints ONE JSON line: the one-token decode workload as the
@@ -48,6 +49,8 @@ DEFAULTS = {  # workload: (steps, warmup, layer copies, token batches)
     "prefill_q4": (50, 5, 1, 4),
     "decode1_mix": (2000, 200, 4, 64),
     "prefill_mix": (50, 5, 1, 4),
+    "decode1_q56": (2000, 200, 4, 64),
+    "prefill_q56": (50, 5, 1, 4),
     "decode1_cached": (1000, 300, 1, 1024),
     "prefill_cached": (20, 3, 1, 8),
 }

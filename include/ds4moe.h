@@ -78,10 +78,11 @@ typedef enum { DS4MOE_MODE_ROUTE = 0, DS4MOE_MODE_DECODE = 1, DS4MOE_MODE_PREFIL
  *                 and the result carries 2^2e back exactly (results are
  *                 finite while y itself fits fp32)
  *   router_dtype  dtype of Wr: DS4MOE_F32 or DS4MOE_BF16
- *   expert_bits   code width of the packed routed experts: 2 or 4 (gate and
- *                 up, and down unless down_bits says otherwise)
+ *   expert_bits   code width of the packed routed experts: 2, 4, 5 or 6
+ *                 (gate and up, and down unless down_bits says otherwise;
+ *                 5-bit codes are packed into 6-bit units, see ds4moe_pack)
  *   down_bits     code width of the routed down matrices: 0 (= expert_bits),
- *                 2 or 4.  The pages' quant mixes give the down projection a
+ *                 2, 4, 5 or 6.  The pages' quant mixes give the down projection a
  *                 format of its own (molayo1419.me "antirez-ds4" insight,
  *                 "Models" section: ds4's 2-bit model stores routed gate/up
  *                 and routed down in different block types; the GLM notes

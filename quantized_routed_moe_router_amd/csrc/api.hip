@@ -32,8 +32,9 @@ int validate_dims(const ds4moe_dims *d) {
   if (d->top_k < 1 || d->top_k > 16) return DS4MOE_ERR_SHAPE;
   if (d->n_experts < d->top_k || d->n_experts > 256) return DS4MOE_ERR_SHAPE;
   if (d->shared_inter < 0 || d->shared_inter > 65536 || d->shared_inter % 32) return DS4MOE_ERR_SHAPE;
-  if (d->expert_bits != 2 && d->expert_bits != 4) return DS4MOE_ERR_SHAPE;
-  if (d->down_bits != 0 && d->down_bits != 2 && d->down_bits != 4) return DS4MOE_ERR_SHAPE;
+  auto width_ok = [](int b) { return b == 2 || b == 4 || b == 5 || b == 6; };
+  if (!width_ok(d->expert_bits)) return DS4MOE_ERR_SHAPE;
+  if (d->down_bits != 0 && !width_ok(d->down_bits)) return DS4MOE_ERR_SHAPE;
   return DS4MOE_OK;
 }
 

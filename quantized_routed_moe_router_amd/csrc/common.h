@@ -95,6 +95,25 @@ __device__ __forceinline__ h8 dequant_frag4(uint32_t raw, h2 sc2) {
               CVT_FP8(hi, true) * sc2);
 }
 
+// A-operand fragment of one MFMA step with 6-bit codes (5-bit codes: top bit
+// zero): the low 4 bits of the step's 8 codes as in dequant_frag4 (dword
+// `lo`), the high 2 bits as in dequant_frag (dword `hi`, elements 0-7 or
+// 8-15 of its sub-block by HALF), so element e of both is the same weight.
+// q = l + 16*h, and q*sc = l*sc + h*(16*sc): every term and the sum are exact
+// integers in fp16 (at most 945).
+template <int HALF>
+__device__ __forceinline__ h8 dequant_frag6(uint32_t lo, uint32_t hi, h2 sc2) {
+  const uint32_t l0 = lo & 0x0F0F0F0Fu, l1 = (lo >> 4) & 0x0F0F0F0Fu;
+  const uint32_t nib = (hi >> (2 * HALF)) & 0x33333333u;
+  h2 s16;
+  s16[0] = sc2[0] * (half_t)16.0f;
+  s16[1] = sc2[1] * (half_t)16.0f;
+  return cat8(CVT_FP4(nib, 2.0f, 0) * s16 + CVT_FP8(l0, false) * sc2,
+              CVT_FP4(nib, 2.0f, 1) * s16 + CVT_FP8(l0, true) * sc2,
+              CVT_FP4(nib, 2.0f, 2) * s16 + CVT_FP8(l1, false) * sc2,
+              CVT_FP4(nib, 2.0f, 3) * s16 + CVT_FP8(l1, true) * sc2);
+}
+
 __device__ __forceinline__ h2 splat_h2(float v) {
   h2 r;
   r[0] = (half_t)v;

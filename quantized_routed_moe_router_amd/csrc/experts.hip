@@ -114,7 +114,8 @@ __device__ __forceinline__ h8 step_frag(const UnitRegs<B> &u, const UnitDecoded 
   sc2[0] = pair[Q & 1];
   sc2[1] = pair[Q & 1];
   if constexpr (B == 2) return dequant_frag<(S & 1)>(u.code[0][Q], sc2);
-  else return dequant_frag4(u.code[S >> 2][S & 3], sc2);
+  else if constexpr (B == 4) return dequant_frag4(u.code[S >> 2][S & 3], sc2);
+  else return dequant_frag6<(S & 1)>(u.code[S >> 2][S & 3], u.code[2][Q], sc2);
 }
 
 // offset of the 8 activations a lane (group g) feeds at step S of a super-block
@@ -151,15 +152,16 @@ __device__ __forceinline__ void gemm_load_a(UnitRegs<B> (&u)[R][NM], const GemmC
       u[r][m] = load_unit<B>(c.W[m] + (size_t)rts[r] * c.rt_stride + (size_t)sb * Unit<B>::BYTES, lane);
 }
 
-// The same loads in two parts: PART 0 the code planes but the last, PART 1
-// the last plane (4-bit units: issued once the current super-block's first
-// plane is dead, so that the two super-blocks' units need few registers at
-// once).  The scales and d/dmin go with PART 1 when NM == 1 (down: two row
-// tiles, the larger register set), else with PART 0.
+// The same loads in two parts: PART 0 every code plane but plane 1, PART 1
+// plane 1, which steps 4-7 read (4- and 6-bit units: issued once the current
+// super-block's plane 0, read by steps 0-3 only, is dead, so that the two
+// super-blocks' units need few registers at once).  The scales and d/dmin go
+// with PART 1 when NM == 1 (down: two row tiles, the larger register set),
+// else with PART 0.
 template <int PART, int NM, int R, int B>
 __device__ __forceinline__ void gemm_load_a_part(UnitRegs<B> (&u)[R][NM], const GemmCtx<NM> &c, const int (&rts)[R],
                                                  int sb, int lane) {
-  constexpr int LAST = B / 2 - 1;
+  static_assert(B >= 4, "units with a second code plane");
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -167,9 +169,10 @@ __device__ __forceinline__ void gemm_load_a_part(UnitRegs<B> (&u)[R][NM], const 
       const uint8_t *unit = c.W[m] + (size_t)rts[r] * c.rt_stride + (size_t)sb * Unit<B>::BYTES;
       if (PART == 0) {
 #pragma unroll
-        for (int p = 0; p < LAST; ++p) u[r][m].code[p] = *reinterpret_cast<const u4 *>(unit + 1024 * p + 16 * lane);
+        for (int p = 0; p < B / 2; ++p)
+          if (p != 1) u[r][m].code[p] = *reinterpret_cast<const u4 *>(unit + 1024 * p + 16 * lane);
       } else {
-        u[r][m].code[LAST] = *reinterpret_cast<const u4 *>(unit + 1024 * LAST + 16 * lane);
+        u[r][m].code[1] = *reinterpret_cast<const u4 *>(unit + 1024 + 16 * lane);
       }
       if (PART == (NM == 1 ? 1 : 0)) {
         u[r][m].scale = *reinterpret_cast<const u4 *>(unit + Unit<B>::SCALE_OFF + 16 * (lane & 15));
@@ -482,7 +485,7 @@ __device__ __forceinline__ void pt_compute_sb(const UnitRegs<B> (&u)[R][NM], con
   const char *rowb = slot + r16 * (PT_CH * 16);
   // mid(): 4-bit units, between steps 3 and 4 (see gemm_load_a_part)
   auto mid = [&]() {
-    if constexpr (B == 4) {
+    if constexpr (B >= 4) {
       __builtin_amdgcn_sched_barrier(0);
       if (sb_next >= 0) gemm_load_a_part<1, NM, R, B>(nxt, c, rts, sb_next, lane);
       __builtin_amdgcn_sched_barrier(0);
@@ -632,7 +635,7 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
     __syncthreads();
     if (sb + 1 < nsb) {
       issue(1, sb + 1);
-      if constexpr (B == 4) gemm_load_a_part<0, NM, R, B>(ub, c, rts, sb + 1, lane);
+      if constexpr (B >= 4) gemm_load_a_part<0, NM, R, B>(ub, c, rts, sb + 1, lane);
       else gemm_load_a<NM, R, B>(ub, c, rts, sb + 1, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -643,7 +646,7 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
     __syncthreads();
     if (sb + 2 < nsb) {
       issue(0, sb + 2);
-      if constexpr (B == 4) gemm_load_a_part<0, NM, R, B>(ua, c, rts, sb + 2, lane);
+      if constexpr (B >= 4) gemm_load_a_part<0, NM, R, B>(ua, c, rts, sb + 2, lane);
       else gemm_load_a<NM, R, B>(ua, c, rts, sb + 2, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1857,7 +1860,12 @@ static hipError_t gateup_b(const GemmArgs &a, int max_tiles, hipStream_t s, cons
 
 hipError_t launch_gateup(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
-  return a.bits == 4 ? gateup_b<4>(a, max_tiles, s, tm) : gateup_b<2>(a, max_tiles, s, tm);
+  switch (unit_bits(a.bits)) {
+    case 2: return gateup_b<2>(a, max_tiles, s, tm);
+    case 4: return gateup_b<4>(a, max_tiles, s, tm);
+    case 6: return gateup_b<6>(a, max_tiles, s, tm);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int B>
@@ -1885,7 +1893,12 @@ static hipError_t down_b(const GemmArgs &a, int max_tiles, hipStream_t s, const 
 
 hipError_t launch_down(const GemmArgs &a, int max_tiles, hipStream_t s, const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
-  return a.bits_dn == 4 ? down_b<4>(a, max_tiles, s, tm) : down_b<2>(a, max_tiles, s, tm);
+  switch (unit_bits(a.bits_dn)) {
+    case 2: return down_b<2>(a, max_tiles, s, tm);
+    case 4: return down_b<4>(a, max_tiles, s, tm);
+    case 6: return down_b<6>(a, max_tiles, s, tm);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Small batches (T <= 16).
@@ -1936,7 +1949,12 @@ hipError_t launch_gateup_dec(const GemmArgs &a, int max_tiles, const DecRoute *r
                              const Timing *tm) {
   if (max_tiles <= 0) return hipSuccess;
   if (rr && (a.T > 4 || rr->E > 256 || rr->k > 16)) return hipErrorInvalidValue;
-  return a.bits == 4 ? gateup_dec_b<4>(a, max_tiles, rr, s, tm) : gateup_dec_b<2>(a, max_tiles, rr, s, tm);
+  switch (unit_bits(a.bits)) {
+    case 2: return gateup_dec_b<2>(a, max_tiles, rr, s, tm);
+    case 4: return gateup_dec_b<4>(a, max_tiles, rr, s, tm);
+    case 6: return gateup_dec_b<6>(a, max_tiles, rr, s, tm);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int B>
@@ -1981,7 +1999,12 @@ static hipError_t down_combine_dec_b(const GemmArgs &a, hipStream_t s, const Tim
 }
 
 hipError_t launch_down_combine_dec(const GemmArgs &a, hipStream_t s, const Timing *tm, const Timing *tm_combine) {
-  return a.bits_dn == 4 ? down_combine_dec_b<4>(a, s, tm, tm_combine) : down_combine_dec_b<2>(a, s, tm, tm_combine);
+  switch (unit_bits(a.bits_dn)) {
+    case 2: return down_combine_dec_b<2>(a, s, tm, tm_combine);
+    case 4: return down_combine_dec_b<4>(a, s, tm, tm_combine);
+    case 6: return down_combine_dec_b<6>(a, s, tm, tm_combine);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_combine(const float *yp, const int32_t *pos, const float *w, const int32_t *xexp, const float *ysh,

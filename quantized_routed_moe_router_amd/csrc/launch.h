@@ -73,8 +73,8 @@ struct GemmArgs {
   // routed experts
   const uint8_t *gate, *up, *down;   // packed, E matrices each
   size_t gu_bytes, d_bytes;          // bytes per expert matrix
-  int bits;                          // code width of the packed gate/up units: 2 or 4
-  int bits_dn;                       // code width of the packed down units: 2 or 4
+  int bits;                          // code width of the gate/up codes: 2, 4, 5 or 6 (5: in 6-bit units)
+  int bits_dn;                       // code width of the down codes: 2, 4, 5 or 6
   const TileT *tiles;
   const int32_t *ntiles;             // decode: [1] DecTiles; prefill: [2] tile count, first tile
   const int32_t *perm;

@@ -202,6 +202,11 @@ WORKLOADS = {
                             description="decode, one token, 2-bit gate/up and 4-bit down"),
     "prefill_mix": Workload("prefill_mix", 8, T=2048, H=4096, E=256, I=2048, k=8, layer_id=3, bits=2, bits_down=4,
                             description="prefill chunk of 2048 tokens, 2-bit gate/up and 4-bit down"),
+    # gate/up with 5-bit codes, down with 6-bit codes, the pages' GLM pairing (own layer)
+    "decode1_q56": Workload("decode1_q56", 9, T=1, H=4096, E=256, I=2048, k=8, layer_id=4, bits=5, bits_down=6,
+                            description="decode, one token, 5-bit gate/up and 6-bit down"),
+    "prefill_q56": Workload("prefill_q56", 10, T=2048, H=4096, E=256, I=2048, k=8, layer_id=4, bits=5, bits_down=6,
+                            description="prefill chunk of 2048 tokens, 5-bit gate/up and 6-bit down"),
 }
 
 

@@ -280,7 +280,13 @@ def test_down_bits_validation():
     assert B.ds4moe_workspace_bytes(dims(), 16, B.MODE_DECODE) > 0
     d = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 2, 4)
     assert B.ds4moe_workspace_bytes(d, 16, B.MODE_DECODE) > 0
-    for bad in (1, 3, 8, -2):
+    for gu, dn in ((5, 6), (6, 0), (5, 0), (2, 5), (4, 6)):
+        d = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, gu, dn)
+        assert B.ds4moe_workspace_bytes(d, 16, B.MODE_DECODE) > 0
+    for gu in (1, 3, 7, 8):
+        d = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, gu, 0)
+        assert B.ds4moe_workspace_bytes(d, 16, B.MODE_DECODE) == 0
+    for bad in (1, 3, 7, 8, -2):
         d = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 2, bad)
         assert B.ds4moe_workspace_bytes(d, 16, B.MODE_DECODE) == 0
         w = B.make_weights(256, 256, 256, 256)
@@ -291,3 +297,5 @@ def test_down_bits_validation():
     d2 = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 2, 0)
     d4 = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 2, 4)
     assert B.ds4moe_cache_bytes(d4, 10) - B.ds4moe_cache_bytes(d2, 10) == 10 * (4849664 - 2752512)
+    d56 = B.make_dims(4096, 2048, 256, 8, 0, B.DS4MOE_BF16, B.DS4MOE_BF16, 5, 6)
+    assert B.ds4moe_cache_bytes(d56, 10) - B.ds4moe_cache_bytes(d2, 10) == 10 * 3 * (6946816 - 2752512)

@@ -110,7 +110,7 @@ def _mid(E=64, k=4, bits=2, bits_down=0, I=256):
                           router_sigma=0.05, layer_id=0, bits=bits, bits_down=bits_down)
 
 
-@pytest.mark.parametrize("bits,bits_down", [(2, 0), (4, 0), (2, 4), (4, 2)])
+@pytest.mark.parametrize("bits,bits_down", [(2, 0), (4, 0), (2, 4), (4, 2), (5, 6)])
 def test_cache_matches_resident_with_evictions(bits, bits_down):
     """E = 64, k = 4, 16 slots: batches of 1-4 tokens evict all the time
     (also with the down matrices in the other code width)."""
@@ -233,7 +233,7 @@ def _run_prefill_sequence(L0, dl, cache, Ts, seed_batch0=1, model=None):
     return nbs
 
 
-@pytest.mark.parametrize("bits,bits_down", [(2, 0), (4, 0), (2, 4), (4, 2)])
+@pytest.mark.parametrize("bits,bits_down", [(2, 0), (4, 0), (2, 4), (4, 2), (5, 6)])
 def test_prefill_cache_matches_resident(bits, bits_down):
     """E = 64, k = 4, 16 slots: batches of 1..700 tokens use up to all 64
     experts, so most calls stream their experts through the slots in several

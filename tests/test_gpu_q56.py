@@ -83,3 +83,123 @@ def test_dequant_full_size_experts(b):
         out = _pack_dequant(canon, 3, rows, cols, b)
         ref = oracle.dequant_f32(canon, bits=b).reshape(3, rows, cols)
         assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ layers
+
+# (gate/up width, down width; 0 = the same)
+PAIRS = [(6, 0), (5, 0), (5, 6), (6, 2), (2, 5), (4, 6)]
+
+
+def _wl(name, T, H, I, bits, bits_down, E=8, k=2, Is=0):
+    return synth.Workload(name, 0, T=T, H=H, E=E, I=I, k=k, Is=Is, x_dtype="f32", router_dtype="f32",
+                          router_sigma=0.05, layer_id=0, bits=bits, bits_down=bits_down)
+
+
+def _run(L, mode, dl=None):
+    q = _q()
+    dl = dl if dl is not None else q.from_layer_inputs(L)
+    assert (dl.bits, dl.down_bits) == (L.wl.bits, L.wl.down_width)
+    bufs = dl.routing_buffers(L.T)
+    m = q.MODE_DECODE if mode == "decode" else q.MODE_PREFILL
+    y = dl.forward(dl.x_tensor(L.x), m, routing=bufs)
+    torch.cuda.synchronize()
+    check_routing(bufs, L, label=f"{L.wl.name} {mode} T={L.T}")
+    return y, bufs, dl
+
+
+def _check_all_tokens(L, y, label):
+    ref, _, _ = oracle.layer_inputs(L)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"{label}: per-token rel err {err:.3e}")
+    assert err <= TOL_Y
+
+
+@pytest.mark.parametrize("bits,bits_down", PAIRS)
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 16])
+def test_mid_decode(bits, bits_down, T):
+    """I = 256: every decode class (routing inside gate/up at T <= 4, the
+    LDS-ring and register kernels, the split down of 5..16 tokens)."""
+    L = synth.make_layer(_wl("mid_q56", T, 512, 256, bits, bits_down))
+    y, _, _ = _run(L, "decode")
+    _check_all_tokens(L, y, f"{bits}/{bits_down} mid decode T={T}")
+
+
+@pytest.mark.parametrize("bits,bits_down", [(6, 0), (5, 6)])
+@pytest.mark.parametrize("T", [1, 4, 9])
+def test_tiny_decode_padded(bits, bits_down, T):
+    """I = 128: the padded down projection of small batches."""
+    L = synth.make_layer(_wl("tiny_q56", T, 256, 128, bits, bits_down))
+    y, _, _ = _run(L, "decode")
+    _check_all_tokens(L, y, f"{bits}/{bits_down} tiny decode T={T}")
+
+
+@pytest.mark.parametrize("bits,bits_down", [(6, 0), (5, 6), (2, 5)])
+@pytest.mark.parametrize("T", [17, 65, 257])
+def test_tiny_prefill_64_token_tiles(bits, bits_down, T):
+    """I = 128: the 64-token GEMMs with the padded down projection."""
+    L = synth.make_layer(_wl("tiny_q56", T, 256, 128, bits, bits_down))
+    y, _, _ = _run(L, "prefill")
+    _check_all_tokens(L, y, f"{bits}/{bits_down} tiny prefill T={T}")
+
+
+@pytest.mark.parametrize("bits,bits_down", PAIRS)
+@pytest.mark.parametrize("T", [48, 300, 1000])
+def test_mid_prefill_wide(bits, bits_down, T):
+    """I = 256: 80-token wide tiles, partial n-tiles and ragged last tiles."""
+    L = synth.make_layer(_wl("mid_q56", T, 512, 256, bits, bits_down))
+    y, _, _ = _run(L, "prefill")
+    _check_all_tokens(L, y, f"{bits}/{bits_down} mid prefill T={T}")
+
+
+def test_mid_shared_expert():
+    """5/6-bit routed experts beside a bf16 shared expert (dense GEMMs)."""
+    import dataclasses
+    wl = dataclasses.replace(_wl("mid_q56_sh", 200, 512, 256, 5, 6, Is=96), x_dtype="bf16", router_dtype="bf16")
+    L = synth.make_layer(wl)
+    y, _, _ = _run(L, "prefill")
+    _check_all_tokens(L, y, "5/6 mid shared T=200")
+
+
+# ------------------------------------------------------------------ full size
+
+
+@pytest.fixture(scope="session")
+def full56():
+    q = _q()
+    L = synth.make_layer("prefill_q56")
+    return L, q.from_layer_inputs(L)
+
+
+def test_full_dequant_sample(full56):
+    q = _q()
+    L, dl = full56
+    H, I = L.wl.H, L.wl.I
+    for e in (0, 131, 255):
+        for packed, canon, rows, cols, nb, b in ((dl.up, L.up, I, H, dl.gu_bytes, 5),
+                                                 (dl.down, L.down, H, I, dl.d_bytes, 6)):
+            out = torch.empty(rows, cols, dtype=torch.float32, device=dl.device)
+            q.ds4moe_dequant(out, packed[e * nb:(e + 1) * nb], 1, rows, cols, b)
+            ref = oracle.dequant_f32(canon[e], bits=b).reshape(rows, cols)
+            assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), (e, rows)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_full_decode(full56, T):
+    L0, dl = full56
+    L = synth.derive(L0, "decode1_q56", T=T)
+    y, _, _ = _run(L, "decode", dl)
+    _check_all_tokens(L, y, f"5/6 decode T={T}")
+
+
+def test_full_prefill_all_tokens(full56):
+    """The 2048-token prefill chunk with 5-bit gate/up and 6-bit down, every token."""
+    L0, dl = full56
+    L = synth.derive(L0, "prefill_q56")
+    y, bufs, _ = _run(L, "prefill", dl)
+    idx = bufs["topk_idx"].cpu().numpy()
+    ref, ridx, _ = oracle.layer_inputs(L)
+    assert np.array_equal(ridx, idx)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"5/6 prefill: all {L.T} tokens checked, per-token rel err {err:.3e}")
+    assert err <= TOL_Y
