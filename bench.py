@@ -67,13 +67,16 @@ PROFILES = os.path.join(HERE, "profiles")
 
 
 def source_hash() -> str:
-    """sha256 over the HIP sources, so counter figures taken on other kernels are not reused."""
+    """sha256 over the HIP sources and the build script (its compiler flags), so counter figures
+    taken on other kernels are not reused."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".hip", ".h")):
             h.update(f.encode())
             with open(os.path.join(CSRC, f), "rb") as fh:
                 h.update(fh.read())
+    with open(os.path.join(os.path.dirname(CSRC), "build.py"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()
 
 

@@ -20,6 +20,13 @@ FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared", "-Wa
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # keep MFMA accumulators in VGPRs: the scale corrections read them every super-block
          "-mllvm", "-amdgpu-mfma-vgpr-form=true",
+         # no sinking of common code into a shared successor.  The prefill GEMM has one inlined
+         # multiply instance per live n-tile count; each ends in the same stores, which the sinking
+         # merges into one store fed by a phi of the instances' 128-bit results.  This compiler's
+         # register coalescer then gave lanes 1-3 of one instance's loop-carried accumulator the
+         # registers that its loop uses as temporaries (wrong values in the last n-tile of the second
+         # row tile of the down projection; turning off global copy coalescing removed them too)
+         "-mllvm", "-simplifycfg-sink-common=false",
          "-I", os.path.join(ROOT, "include")]
 
 

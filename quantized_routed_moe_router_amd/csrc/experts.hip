@@ -703,21 +703,16 @@ __device__ __forceinline__ void pt_tile(const GemmArgs &a, const GemmAct &xa, co
   }
 }
 
-// ALL: every tile takes the PT_NTM-n-tile multiply (one instance; empty
-// n-tiles multiply zeros).  The down projection uses it: a build with one
-// instance per n-tile count and two row tiles per wave gave wrong values in
-// its last n-tile, which the single instance does not.
-template <int NM, int R, bool ALL, int B>
+// One multiply instance per live n-tile count, so partial tiles issue no dead
+// MFMAs.  The instances end in identical stores; the library is built with
+// common-code sinking off (see build.py), which keeps those stores apart.
+template <int NM, int R, int B>
 __global__ __launch_bounds__(64 * PT_NW) void k_moe_gemm_wide(GemmArgs a, GemmAct xa, int nrb) {
   __shared__ __attribute__((aligned(16))) char ring[2 * PT_SLOT_BYTES];
   int tile_id, rb;
   xcd_tile(nrb, tile_id, rb);
   if (tile_id >= a.ntiles[0]) return;  // uniform over the workgroup
   const TileT tl = a.tiles[a.ntiles[1] + tile_id];
-  if (ALL) {
-    pt_tile<NM, R, PT_NTM, B>(a, xa, tl, rb, ring);
-    return;
-  }
   switch ((tl.n + 15) >> 4) {  // 1..PT_NTM, uniform
     case 1: pt_tile<NM, R, 1, B>(a, xa, tl, rb, ring); break;
     case 2: pt_tile<NM, R, 2, B>(a, xa, tl, rb, ring); break;
@@ -1846,7 +1841,7 @@ static hipError_t gateup_b(const GemmArgs &a, int max_tiles, hipStream_t s, cons
     GemmAct xa;
     if (a.tile_n > 16 * PT_NTM || !act_window(a.x16, a.xs_hi, a.xs_lo, a.xe16, a.T, a.H, xa)) return hipErrorInvalidValue;
     const int nrb = (a.I + 16 * PT_NW - 1) / (16 * PT_NW);
-    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1, false, B>), gemm_grid(nrb, max_tiles), dim3(64 * PT_NW), 0, s, a, xa,
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<2, 1, B>), gemm_grid(nrb, max_tiles), dim3(64 * PT_NW), 0, s, a, xa,
                nrb);
     return hipGetLastError();
   }
@@ -1876,7 +1871,7 @@ static hipError_t down_b(const GemmArgs &a, int max_tiles, hipStream_t s, const 
         !act_window(a.h, a.hs_hi, a.hs_lo, nullptr, (int64_t)a.T * a.k, a.Ipad, xa))
       return hipErrorInvalidValue;
     const int nrb = (a.H + 32 * PT_NW - 1) / (32 * PT_NW);
-    DS4_LAUNCH(tm, (k_moe_gemm_wide<1, 2, true, B>), gemm_grid(nrb, max_tiles), dim3(64 * PT_NW), 0, s, a, xa,
+    DS4_LAUNCH(tm, (k_moe_gemm_wide<1, 2, B>), gemm_grid(nrb, max_tiles), dim3(64 * PT_NW), 0, s, a, xa,
                nrb);
     return hipGetLastError();
   }

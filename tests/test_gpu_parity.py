@@ -268,6 +268,46 @@ def test_mid_wide_tiles_prefill(T):
     assert err <= TOL_Y
 
 
+# tokens per expert: tiles of 80 tokens with every live n-tile count 1..5, the
+# last n-tile partial and full, and experts with one and with two tiles
+FORCED_COUNTS = ([1, 16, 17, 40, 64, 79, 80, 113], [2, 15, 31, 33, 48, 65, 81, 160])
+
+
+@pytest.mark.parametrize("I", [256, 512])
+@pytest.mark.parametrize("counts", FORCED_COUNTS)
+def test_wide_tiles_every_ntile_count(counts, I):
+    """Each token is steered to a chosen expert (one-hot router rows, the
+    token's own coordinate raised), so the prefill GEMMs see tiles of every
+    live n-tile count on both projections, with one and with two down
+    super-blocks; every token against the oracle.  A build whose instances
+    miscompiled the last n-tile of the down projection's second row tile
+    failed exactly this check."""
+    q = _q()
+    E, H = 8, 512
+    T = int(sum(counts))
+    wl = synth.Workload("forced", 0, T=T, H=H, E=E, I=I, k=1, x_dtype="f32", router_dtype="f32",
+                        router_sigma=0.05, layer_id=0)
+    L = synth.make_layer(wl)
+    rng = np.random.default_rng(7000 + T + I)
+    owner = rng.permutation(np.repeat(np.arange(E), counts))
+    x = L.x.copy()
+    x[:, :E] = 0.0
+    x[np.arange(T), owner] = 6.0
+    wr = np.zeros((E, H), np.float32)
+    wr[np.arange(E), np.arange(E)] = 8.0
+    L.x, L.router_w = np.ascontiguousarray(x), wr
+    dl = q.from_layer_inputs(L)
+    bufs = dl.routing_buffers(T)
+    y = dl.forward(dl.x_tensor(L.x), q.MODE_PREFILL, routing=bufs)
+    torch.cuda.synchronize()
+    idx = check_routing(bufs, L, label=f"forced I={I}")
+    assert np.array_equal(np.bincount(idx[:, 0], minlength=E), counts)
+    ref, _, _ = oracle.layer_inputs(L)
+    err = per_token_err(y.cpu().numpy(), ref)
+    print(f"forced counts {counts} I={I}: all {T} tokens, per-token rel err {err:.3e}")
+    assert err <= TOL_Y
+
+
 @pytest.mark.parametrize("T,Is", [(20, 96), (200, 96), (300, 256)])
 def test_mid_shared_expert_prefill(T, Is):
     """Routed layer plus a bf16 shared expert: T <= 64 on the per-wave kernels,
