@@ -42,6 +42,25 @@ def test_version_and_status_strings():
     assert B.status_str(99) == "unknown status"
 
 
+def test_read_probe_argument_errors():
+    """The streaming-read probe rejects its arguments on the host (fake,
+    never dereferenced addresses: every call returns before a launch)."""
+    L = B.lib()
+    P = ctypes.c_void_p
+    ok, sink = P(0x10000), P(0x20000)
+    ev = P(0x30000)
+    assert L.ds4moe_read_probe(None, 4096, 8, sink, None, None, None) == 1
+    assert L.ds4moe_read_probe(ok, 4096, 8, None, None, None, None) == 1
+    assert L.ds4moe_read_probe(ok, 0, 8, sink, None, None, None) == 2
+    assert L.ds4moe_read_probe(ok, 4104, 8, sink, None, None, None) == 2      # not a multiple of 16
+    assert L.ds4moe_read_probe(ok, 4096, 0, sink, None, None, None) == 2
+    assert L.ds4moe_read_probe(ok, 4096, (1 << 20) + 1, sink, None, None, None) == 2
+    assert L.ds4moe_read_probe(P(0x10008), 4096, 8, sink, None, None, None) == 4
+    assert L.ds4moe_read_probe(ok, 4096, 8, P(0x20002), None, None, None) == 4
+    assert L.ds4moe_read_probe(ok, 4096, 8, sink, ev, None, None) == 1        # one event without the other
+    assert L.ds4moe_read_probe(ok, 4096, 8, sink, None, ev, None) == 1
+
+
 def test_packed_bytes():
     assert q.ds4moe_packed_bytes(2048, 4096) == 2048 * 4096 // 256 * 84 == 2752512
     assert q.ds4moe_packed_bytes(4096, 2048) == 2752512
