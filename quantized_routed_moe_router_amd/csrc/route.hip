@@ -310,107 +310,85 @@ template <bool XB, bool WB, int EW>
 __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x, const void *__restrict__ wr,
                                                      const float *__restrict__ bias, float *__restrict__ logits,
                                                      int T, int E, int H) {
-  // tile: 32 tokens x EW experts (64 or 32); wave (tw, ew) = 16 tokens x EW/2
-  // experts.  K-chunks of 32, staged in LDS as fp32 ([k][token], [k][expert])
-  // from raw registers loaded one chunk ahead; double-buffered, one barrier
-  // per chunk.
-  static_assert(EW == 64 || EW == 32, "expert tile");
-  constexpr int NA = EW / 32;  // 16x16 accumulators per wave
-  constexpr int WPT = EW / 8;  // weights staged per thread and chunk
-  __shared__ float xs[2][32][36];
-  __shared__ float ws[2][32][EW + 4];
+  // tile: 32 tokens x 32 experts; wave (tw, ew) = 16 tokens x 16 experts.
+  // K-chunks of KC, staged in LDS as fp32 ([k][token], [k][expert], rows of
+  // LS floats: LS = 16 mod 32 keeps the operand reads and the staging stores
+  // free of bank conflicts) from raw registers loaded one chunk ahead;
+  // double-buffered, one barrier per chunk.  Each accumulator takes its MFMAs
+  // in ascending k, whatever KC is.
+  static_assert(EW == 32, "expert tile");
+  constexpr int KC = 64, LS = 48, PT = KC / 8;  // values staged per thread and chunk (x and w)
+  __shared__ float xs[2][KC][LS];
+  __shared__ float ws[2][KC][LS];
   const int t0 = blockIdx.x * 32, e0 = blockIdx.y * EW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int tw = wave & 1, ew = wave >> 1;
-  d4 acc[NA];
+  d4 acc = (d4){0.0, 0.0, 0.0, 0.0};
+  // staging: token / expert tid % 32, k (tid / 32) * PT (PT values)
+  const int st = tid & 31, sk = (tid >> 5) * PT;
+  const bool xv = t0 + st < T, wv = e0 + st < E;
+  const int64_t xoff = (int64_t)(xv ? t0 + st : 0) * H + sk;
+  const int64_t woff = (int64_t)(wv ? e0 + st : 0) * H + sk;
+  constexpr int NR = PT / 4;   // 16-byte fp32 loads per operand (PT fp32 values)
+  u4 rx[NR], rw[NR];            // bf16 operands use the first PT/8 (PT bf16 = PT/8 x 16 B)
+  auto ld = [&](const void *p, int64_t off, bool v, bool bf, u4 (&r)[NR]) {
+    if (bf && PT % 8) {  // PT = 4: one 8-byte load
+      const u2 q = v ? *reinterpret_cast<const u2 *>(reinterpret_cast<const uint16_t *>(p) + off) : (u2){0u, 0u};
+      r[0] = (u4){q.x, q.y, 0u, 0u};
+    } else if (bf) {
 #pragma unroll
-  for (int n = 0; n < NA; ++n) acc[n] = (d4){0.0, 0.0, 0.0, 0.0};
-  // staging: x token tid/8, k (tid%8)*4 (4 values); w expert tid/(32/WPT), k (tid%(32/WPT))*WPT
-  const int xt = tid >> 3, xk = (tid & 7) * 4;
-  const int we = tid / (32 / WPT), wk = (tid % (32 / WPT)) * WPT;
-  const bool xv = t0 + xt < T, wv = e0 + we < E;
-  const int64_t xoff = (int64_t)(xv ? t0 + xt : 0) * H + xk;
-  const int64_t woff = (int64_t)(wv ? e0 + we : 0) * H + wk;
-  u4 rx, rw0, rw1;  // raw bits: bf16 x uses rx.xy, bf16 w uses rw0; fp32 uses all
+      for (int i = 0; i < PT / 8; ++i)
+        r[i] = v ? *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(p) + off + 8 * i) : (u4){0u, 0u, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        r[i] = v ? *reinterpret_cast<const u4 *>(reinterpret_cast<const float *>(p) + off + 4 * i) : (u4){0u, 0u, 0u, 0u};
+    }
+  };
   auto load = [&](int k0) {
-    if (XB) {
-      const u2 v = xv ? *reinterpret_cast<const u2 *>(reinterpret_cast<const uint16_t *>(x) + xoff + k0) : (u2){0u, 0u};
-      rx = (u4){v.x, v.y, 0u, 0u};
-    } else {
-      rx = xv ? *reinterpret_cast<const u4 *>(reinterpret_cast<const float *>(x) + xoff + k0) : (u4){0u, 0u, 0u, 0u};
+    ld(x, xoff + k0, xv, XB, rx);
+    ld(wr, woff + k0, wv, WB, rw);
+  };
+  auto val = [&](const u4 (&r)[NR], bool bf, int i) -> float {
+    if (bf) {
+      const uint32_t w = r[i / 8][(i / 2) & 3];
+      return bf16_bits_to_float((uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
     }
-    if (WB && WPT == 8) {
-      rw0 = wv ? *reinterpret_cast<const u4 *>(reinterpret_cast<const uint16_t *>(wr) + woff + k0) : (u4){0u, 0u, 0u, 0u};
-    } else if (WB) {
-      const u2 v = wv ? *reinterpret_cast<const u2 *>(reinterpret_cast<const uint16_t *>(wr) + woff + k0) : (u2){0u, 0u};
-      rw0 = (u4){v.x, v.y, 0u, 0u};
-    } else {
-      const float *p = reinterpret_cast<const float *>(wr) + woff + k0;
-      rw0 = wv ? *reinterpret_cast<const u4 *>(p) : (u4){0u, 0u, 0u, 0u};
-      if (WPT == 8) rw1 = wv ? *reinterpret_cast<const u4 *>(p + 4) : (u4){0u, 0u, 0u, 0u};
-    }
+    return __uint_as_float(r[i / 4][i & 3]);
   };
   auto store = [&](int b) {
-    float xf[4], wf[8];
-    if (XB) {
-      xf[0] = bf16_bits_to_float((uint16_t)(rx.x & 0xFFFFu));
-      xf[1] = bf16_bits_to_float((uint16_t)(rx.x >> 16));
-      xf[2] = bf16_bits_to_float((uint16_t)(rx.y & 0xFFFFu));
-      xf[3] = bf16_bits_to_float((uint16_t)(rx.y >> 16));
-    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xf[i] = __uint_as_float(rx[i]);
+    for (int i = 0; i < PT; ++i) {
+      xs[b][sk + i][st] = val(rx, XB, i);
+      ws[b][sk + i][st] = val(rw, WB, i);
     }
-    if (WB) {
-#pragma unroll
-      for (int i = 0; i < WPT / 2; ++i) {
-        wf[2 * i] = bf16_bits_to_float((uint16_t)(rw0[i] & 0xFFFFu));
-        wf[2 * i + 1] = bf16_bits_to_float((uint16_t)(rw0[i] >> 16));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wf[i] = __uint_as_float(rw0[i]);
-      if (WPT == 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wf[4 + i] = __uint_as_float(rw1[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xs[b][xk + i][xt] = xf[i];
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) ws[b][wk + i][we] = wf[i];
   };
-  const int nk = H / 32;
+  const int nk = H / KC;
   load(0);
   store(0);
   __syncthreads();
   for (int c = 0; c < nk; ++c) {
     const int b = c & 1;
-    if (c + 1 < nk) load((c + 1) * 32);
+    if (c + 1 < nk) load((c + 1) * KC);
 #pragma unroll
-    for (int kk = 0; kk < 32; kk += 4) {
+    for (int kk = 0; kk < KC; kk += 4) {
       const double av = (double)xs[b][kk + g][16 * tw + r16];
-#pragma unroll
-      for (int n = 0; n < NA; ++n) {
-        const double bv = (double)ws[b][kk + g][(EW / 2) * ew + 16 * n + r16];
-        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[n], 0, 0, 0);
-      }
+      const double bv = (double)ws[b][kk + g][16 * ew + r16];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
     }
     if (c + 1 < nk) store(b ^ 1);
     __syncthreads();
   }
   // D (fp64 16x16x4): lane holds rows (tokens) g, g+4, g+8, g+12 of the wave's 16,
   // column (expert) r16
-#pragma unroll
-  for (int n = 0; n < NA; ++n) {
-    const int e = e0 + (EW / 2) * ew + 16 * n + r16;
-    if (e >= E) continue;
+  const int e = e0 + 16 * ew + r16;
+  if (e < E) {
     const double bb = bias ? (double)bias[e] : 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + 16 * tw + g + 4 * i;
-      if (t < T) logits[(int64_t)t * E + e] = (float)(acc[n][i] + bb);
+      if (t < T) logits[(int64_t)t * E + e] = (float)(acc[i] + bb);
     }
   }
 }
