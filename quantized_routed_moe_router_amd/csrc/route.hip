@@ -393,14 +393,16 @@ __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x,
   }
 }
 
-// Large T: one workgroup per chunk of 64 tokens (wave w: tokens 16w..16w+15).
+// Large T: one workgroup per chunk of 16, 32 or 64 tokens (16 waves, each
+// taking a run of the chunk's tokens).
 // Besides top-k and the activation preparation it records, for the stable
 // permutation, the chunk's count per expert and each assignment's rank among
 // the chunk's assignments to the same expert (earlier tokens first).
-// Tokens per chunk: 32 up to 4096 tokens (twice the workgroups of 64, so
-// T = 2048 routes in 18 rather than 33 us), 64 above (the scan over chunks
-// then grows faster than the top-k shrinks).
-static int chunk_size(int T) { return T <= 4096 ? 32 : 64; }
+// Tokens per chunk: 16 up to 2048 tokens (one token per wave: at T = 2048
+// the top-k takes 14 rather than 22 us, the scan over the doubled chunk count
+// 13 rather than 8), 32 up to 4096, 64 above (the scan over chunks then grows
+// faster than the top-k shrinks).
+static int chunk_size(int T) { return T <= 2048 ? 16 : (T <= 4096 ? 32 : 64); }
 
 // One workgroup of 16 waves per chunk of CHUNK tokens; wave w takes tokens
 // TPW*w .. TPW*w+TPW-1 of the chunk: their logits are loaded together, staged in the
@@ -597,7 +599,10 @@ hipError_t launch_router_tiled(const void *x, bool x_bf16, const void *wr, bool 
 
 int chunk_count(int T) { return (T + chunk_size(T) - 1) / chunk_size(T); }
 
-int chunk_count_max(int T) { return (T + 31) / 32; }
+int chunk_count_max(int T) {
+  const int a = ((T < 2048 ? T : 2048) + 15) / 16, b = (T + 31) / 32;  // 16-token chunks up to 2048 tokens
+  return a > b ? a : b;
+}
 
 int router_slices(int H) { return (H + RSLICE - 1) / RSLICE; }
 
@@ -606,7 +611,10 @@ hipError_t launch_route_chunked(const float *logits, int T, int E, int k, int H,
                                 const Timing *tm_perm) {
   const int chunk = chunk_size(T), nchunk = chunk_count(T);
   XPrep x = xp ? *xp : XPrep{nullptr, false, nullptr, nullptr, nullptr};
-  if (chunk == 32)
+  if (chunk == 16)
+    DS4_LAUNCH(tm_topk, k_topk_chunk<16>, dim3(nchunk), dim3(1024), 0, s, logits, T, E, k, H, x, xp != nullptr, ro,
+               ccnt, lrank);
+  else if (chunk == 32)
     DS4_LAUNCH(tm_topk, k_topk_chunk<32>, dim3(nchunk), dim3(1024), 0, s, logits, T, E, k, H, x, xp != nullptr, ro,
                ccnt, lrank);
   else
