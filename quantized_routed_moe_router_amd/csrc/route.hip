@@ -399,9 +399,8 @@ __global__ __launch_bounds__(256) void k_router_mfma(const void *__restrict__ x,
 // permutation, the chunk's count per expert and each assignment's rank among
 // the chunk's assignments to the same expert (earlier tokens first).
 // Tokens per chunk: 16 up to 2048 tokens (one token per wave: at T = 2048
-// the top-k takes 14 rather than 22 us, the scan over the doubled chunk count
-// 13 rather than 8), 32 up to 4096, 64 above (the scan over chunks then grows
-// faster than the top-k shrinks).
+// the top-k takes 14 rather than 22 us), 32 up to 4096, 64 above (the scan
+// over chunks then grows faster than the top-k shrinks).
 static int chunk_size(int T) { return T <= 2048 ? 16 : (T <= 4096 ? 32 : 64); }
 
 // One workgroup of 16 waves per chunk of CHUNK tokens; wave w takes tokens
@@ -479,10 +478,35 @@ __global__ __launch_bounds__(1024) void k_scan_chunks(int T, int E, int k, int n
                                                       const int32_t *__restrict__ ccnt, int32_t *__restrict__ base,
                                                       RouteOut ro) {
   __shared__ int32_t s_cnt[256], s_off[256], s_tb[256];
+  __shared__ int32_t s_part[4][256];
   const int tid = threadIdx.x;
   if (ro.zeros)
     for (int i = tid; i < ro.nzeros; i += 1024) ro.zeros[i] = (half_t)0.0f;
-  if (tid < E) {
+  const int e = tid & 255, j = tid >> 8;
+  const int per = (nchunk + 3) / 4;
+  const int lo = min(nchunk, j * per), hi = min(nchunk, lo + per);
+  // up to 128 chunks: four threads per expert, each with its part's counts in
+  // registers (one round of loads, then the bases from the parts before it);
+  // more chunks: one thread per expert in batches of 8
+  if (per <= 32) {
+    int v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = (e < E && lo + u < hi) ? ccnt[(int64_t)(lo + u) * E + e] : 0;
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) sum += v[u];
+    s_part[j][e] = sum;
+    __syncthreads();
+    int r = 0;
+    for (int jj = 0; jj < j; ++jj) r += s_part[jj][e];
+#pragma unroll
+    for (int u = 0; u < 32; ++u)
+      if (e < E && lo + u < hi) {
+        base[(int64_t)(lo + u) * E + e] = r;
+        r += v[u];
+      }
+    if (j == 3 && e < E) s_cnt[e] = r;
+  } else if (tid < E) {
     int run = 0;
     for (int c0 = 0; c0 < nchunk; c0 += 8) {
       int v[8];
