@@ -42,6 +42,19 @@ def test_version_and_status_strings():
     assert B.status_str(99) == "unknown status"
 
 
+def test_build_keeps_common_code_sinking_off():
+    """The prefill GEMMs inline one multiply instance per live n-tile count;
+    with common-code sinking on, this compiler merged their final stores and
+    then gave part of a loop-carried accumulator to scratch registers (wrong
+    values in the down projection, caught by the GPU test that steers tokens
+    to every n-tile count).  The build must keep the sinking off."""
+    from quantized_routed_moe_router_amd import build
+    flags = build.FLAGS
+    i = flags.index("-simplifycfg-sink-common=false")
+    assert flags[i - 1] == "-mllvm"
+    assert "-Xclang" in flags and "-packed-fp32-ops" in flags   # no packed fp32 instructions
+
+
 def test_read_probe_argument_errors():
     """The streaming-read probe rejects its arguments on the host (fake,
     never dereferenced addresses: every call returns before a launch)."""
