@@ -344,6 +344,7 @@ int forward(const ds4moe_dims *dims, const ds4moe_weights *w, const void *x, int
   ga.yp = dec ? nullptr : at<float>(ws, L.yp);
   ga.zeros = ro.zeros;
   ga.dtiles = dtiles;
+  ga.dt_cap = L.max_tiles;
   ga.wsb = (const uint8_t *)ws;
   ga.ws_len = (uint32_t)(L.total < (size_t)DS4_WS_WINDOW ? L.total : (size_t)DS4_WS_WINDOW);
   ga.o_x16 = (uint32_t)L.x16;

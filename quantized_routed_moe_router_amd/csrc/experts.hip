@@ -739,20 +739,28 @@ __global__ __launch_bounds__(512) void k_down_dec(GemmArgs a) {
   const int rt = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
+  // lane L: expert and token mask of this wave's L-th tile (at most 32), read
+  // together with the tile count from every entry the buffer holds; the lanes
+  // past the count are cleared once it is known
+  int e_l = 0;
+  uint32_t m_l = 0u;
+  if (lane < 32) {
+    const int i = min(wave + 8 * lane, a.dt_cap - 1);
+    e_l = a.dtiles[i].e;
+    m_l = a.dtiles[i].tmask;
+  }
   const int ntl = *a.ntiles;
   const int nsb = a.Ipad >> 8;
   const int nj = a.Ipad >> 4, nj_real = a.I >> 4;
   const int mt = wave < ntl ? (ntl - wave + 7) >> 3 : 0;  // tiles of this wave (<= 32)
   const int nit = mt * nsb;
-  int e_l = 0;        // lane L: expert of this wave's L-th tile
-  uint32_t m_l = 0u;  // ... and its token mask
-  if (lane < mt) {
-    e_l = a.dtiles[wave + 8 * lane].e;
-    m_l = a.dtiles[wave + 8 * lane].tmask;
-  }
   // wait for them here, before any weight load is in flight, so that the
   // pipelined loop below never has to drain the load counter for them
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (lane >= mt) {
+    e_l = 0;
+    m_l = 0u;
+  }
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
   const uint32_t hs_base = ((g >> 1) ? a.o_hs_lo : a.o_hs_hi) + 2u * (8 * (g & 1));
 
@@ -914,9 +922,11 @@ __global__ __launch_bounds__(256) void k_gateup_dec_lds(GemmArgs a, int n_rt, De
     static_assert(sizeof(RouteLds<4>) <= sizeof(ring_lds), "routing LDS must fit in the ring");
     if (!route_take_tile<NT>(ring_lds, rr, a.T, tile_id, e, tmask)) return;  // uniform over the workgroup
   } else {
+    // the tile is read together with the count (the grid covers the buffer)
+    const int ti = min(tile_id, a.dt_cap - 1);
+    e = a.dtiles[ti].e;
+    tmask = a.dtiles[ti].tmask;
     if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
-    e = a.dtiles[tile_id].e;
-    tmask = a.dtiles[tile_id].tmask;
   }
   const int r16 = lane & 15, g = lane >> 4;
   const int rt = RPW * rb + wave / KS, kh = wave % KS;
@@ -1057,21 +1067,29 @@ __global__ __launch_bounds__(512 * KSP) void k_down_dec_lds(GemmArgs a) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wv = wave & 7, kh = wave >> 3;
   const int r16 = lane & 15, g = lane >> 4;
+  // lane L: expert and token mask of this wave's L-th tile (a wave owns at
+  // most 32).  They are read together with the tile count, from every entry
+  // the buffer holds, and the lanes past the count are cleared once it is known.
+  int e_l = 0;
+  uint32_t m_l = 0u;
+  if (lane < 32) {
+    const int i = min(wv + 8 * lane, a.dt_cap - 1);
+    e_l = a.dtiles[i].e;
+    m_l = a.dtiles[i].tmask;
+  }
   const int ntl = *a.ntiles;
   const int nsb = a.Ipad >> 8;
   const int nj = a.Ipad >> 4;
   const int mt = wv < ntl ? (ntl - wv + 7) >> 3 : 0;  // tiles of this wave (<= 32)
   const int nsw = nsb / KSP, sbb = kh * nsw;            // its super-blocks sbb .. sbb + nsw - 1 of each
   const int nit = mt * nsw;
-  int e_l = 0;        // lane L: expert of this wave's L-th tile
-  uint32_t m_l = 0u;  // ... and its token mask
-  if (lane < mt) {
-    e_l = a.dtiles[wv + 8 * lane].e;
-    m_l = a.dtiles[wv + 8 * lane].tmask;
-  }
   // wait for them here, before any weight load is in flight, so that the
   // pipelined loop below never has to drain the load counter for them
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (lane >= mt) {
+    e_l = 0;
+    m_l = 0u;
+  }
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
   // chunk u = 64*q + lane of a slot: token u / XCH, chunk c = u % XCH
   // chunks c < 32: h[p][256*sb + 8c ...]; c = 32..35: sums hi/lo [p][16*sb + 8*(c&1) ...]
@@ -1216,9 +1234,11 @@ __global__ __launch_bounds__(64 * NW) void k_gateup_dec_sh(GemmArgs a, int n_rt,
     static_assert(sizeof(RouteLds<4>) <= sizeof(ring), "routing LDS must fit in the ring");
     if (!route_take_tile<NT>(ring, rr, a.T, tile_id, e, tmask)) return;  // uniform over the workgroup
   } else {
+    // the tile is read together with the count (the grid covers the buffer)
+    const int ti = min(tile_id, a.dt_cap - 1);
+    e = a.dtiles[ti].e;
+    tmask = a.dtiles[ti].tmask;
     if (tile_id >= *a.ntiles) return;  // uniform over the workgroup
-    e = a.dtiles[tile_id].e;
-    tmask = a.dtiles[tile_id].tmask;
   }
   const int rt = NW * rb + wave;
   const int nsb = a.H >> 8;
@@ -1369,21 +1389,29 @@ __global__ __launch_bounds__(512) void k_down_dec2(GemmArgs a) {
   const int rt0 = R * blockIdx.x, half = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
+  const int j0 = half + NH * wave;  // this wave's first tile
+  // lane L: expert and token mask of this wave's L-th tile (at most 16), read
+  // together with the tile count from every entry the buffer holds; the lanes
+  // past the count are cleared once it is known
+  int e_l = 0;
+  uint32_t m_l = 0u;
+  if (lane < 16) {
+    const int i = min(j0 + TS * lane, a.dt_cap - 1);
+    e_l = a.dtiles[i].e;
+    m_l = a.dtiles[i].tmask;
+  }
   const int ntl = *a.ntiles;
   const int nsb = a.Ipad >> 8;
   const int nj = a.Ipad >> 4;
-  const int j0 = half + NH * wave;                         // this wave's first tile
   const int mt = j0 < ntl ? (ntl - j0 + TS - 1) / TS : 0;  // its tiles j0, j0 + TS, ... (<= 16)
   const int nit = mt * nsb;
-  int e_l = 0;        // lane L: expert of this wave's L-th tile
-  uint32_t m_l = 0u;  // ... and its token mask
-  if (lane < mt) {
-    e_l = a.dtiles[j0 + TS * lane].e;
-    m_l = a.dtiles[j0 + TS * lane].tmask;
-  }
   // wait for them here, before any weight load is in flight, so that the
   // pipelined loop below never has to drain the load counter for them
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (lane >= mt) {
+    e_l = 0;
+    m_l = 0u;
+  }
   const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.wsb, a.ws_len);
   const uint32_t hs_base = ((g >> 1) ? a.o_hs_lo : a.o_hs_hi) + 2u * (8 * (g & 1));
   const uint32_t ustride = (uint32_t)nsb * Unit<B>::BYTES;  // bytes per row tile

@@ -91,6 +91,7 @@ struct GemmArgs {
   uint32_t ws_len;
   uint32_t o_x16, o_xs_hi, o_xs_lo, o_h, o_hs_hi, o_hs_lo;
   const DecTile *dtiles;
+  int dt_cap;                        // decode: DecTile entries the tile buffer holds (>= any tile count)
   int T;
   int tile_n;                        // tokens per prefill tile (> 64: wide-tile GEMMs)
   // small batches of 5..16 tokens: the down projection's partial outputs
